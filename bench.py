@@ -1,10 +1,30 @@
 """Benchmark of the selection step (row-wise top-k, then key gather) on one GPU.
 
-Byte accounting (algorithmic bytes: what the method must move):
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2]
+                    [--no-per-config] [--no-cpu-baseline]
+
+Prints ONE JSON line.  The headline workload is the 4 x 204800 bf16 top-k
+(k = 1024, ascending int32 indices plus values); a step is one top-k call
+over one batch.  ``per_config`` adds the same measurement for the five named
+workloads (top-k and, where they have one, the gather).
+
+Timing protocol
+  * inputs are generated on the host from fixed seeds and copied to HBM
+    before timing; each step reads a different copy of the input, and the
+    copies together exceed twice the 256 MB Infinity Cache, so top-k reads
+    come from HBM rather than from cache;
+  * the K timed steps are captured once in a HIP graph and replayed, so the
+    timed region holds no Python launch overhead; the region is bracketed
+    by torch.cuda.synchronize() on both sides and wall-clock timed;
+  * the dominant kernel's duration is measured separately with a HIP event
+    pair around each of its launches, all enqueued behind a GPU sleep so
+    the launches run back to back.
+
+Byte accounting (algorithmic bytes: what the method must move)
   top-k  = sum over rows of the valid-prefix read (a row of valid length
-           n <= k read only when values are returned), + 4*rows for row_end,
-           + rows*k*index bytes, + rows*k*value bytes when values are
-           returned, + rows bytes of NaN flag.
+           n <= k is read only when values are returned), + 4*rows for
+           row_end, + rows*k*index bytes, + rows*k*value bytes when values
+           are returned, + rows bytes of NaN flag;
   gather = written bytes + position bytes read + one compulsory read of each
            distinct key row touched.
 The gather is also reported in the pages' convention (gathered output bytes
@@ -12,9 +32,21 @@ over time; MindSpore hyper-parallel PR #1094, mechanism check).
 """
 from __future__ import annotations
 
+import argparse
+import json
+import os
+import sys
+import time
+
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
 HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+METRIC = "top-k rows/s and achieved HBM GB/s (% of peak) per config; gather GB/s"
 
 
 def output_convention_gbps(out_bytes: float, seconds: float) -> float:
@@ -40,5 +72,266 @@ def gather_algorithmic_bytes(n_positions: int, dim: int, elt: int, pos_elt: int,
     return n_positions * dim * elt + n_positions * pos_elt + distinct_rows * dim * elt
 
 
+# ---------------------------------------------------------------------------
+# GPU measurement helpers
+# ---------------------------------------------------------------------------
+
+def _valid_lengths(case):
+    rows, cols = case.x.shape
+    if case.row_end is None:
+        return np.full(rows, cols, dtype=np.int64)
+    return np.clip(case.row_end.numpy().astype(np.int64), 0, cols)
+
+
+def _copies_for(nbytes: int, cap: int = 4096) -> int:
+    return int(max(2, min(cap, -(-2 * MALL_BYTES // max(nbytes, 1)))))
+
+
+class TopkBench:
+    """Device-resident inputs (rotating copies) and a reusable top-k call."""
+
+    def __init__(self, dsel, torch, case, stream):
+        self.dsel, self.torch, self.case, self.stream = dsel, torch, case, stream
+        x = case.x
+        self.in_bytes = x.numel() * x.element_size()
+        self.ncopy = _copies_for(self.in_bytes)
+        dev = torch.device("cuda")
+        base = x.contiguous().to(dev)
+        self.xs = torch.empty((self.ncopy,) + tuple(x.shape), dtype=x.dtype, device=dev)
+        self.xs.copy_(base.unsqueeze(0).expand_as(self.xs))
+        self.row_end = case.row_end.to(dev) if case.row_end is not None else None
+        torch.cuda.synchronize()
+
+    def call(self, i: int):
+        c = self.case
+        return self.dsel.topk(self.xs[i % self.ncopy], c.k, end=self.row_end,
+                              sorted_index=c.sorted_index, indices_type=c.indices_type,
+                              return_value=c.return_value, stream=self.stream)
+
+    def algorithmic_bytes(self) -> int:
+        c = self.case
+        esz = c.x.element_size()
+        isz = 4 if c.indices_type == self.torch.int32 else 8
+        return topk_algorithmic_bytes(_valid_lengths(c), c.k, esz, isz, c.return_value,
+                                      c.row_end is not None)
+
+
+def graph_time(torch, stream, fn, steps: int, warmup: int, reps: int = 1):
+    """Capture `steps` calls of fn(i) in one HIP graph; return seconds per call."""
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, 1)):
+            fn(i)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            fn(i)
+    g.replay()  # untimed replay: page in the graph
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        best = dt if best is None else min(best, dt)
+    del g
+    return best
+
+
+def event_kernel_time(torch, stream, fn, launches: int) -> float:
+    """Mean seconds per call measured with one HIP event pair per call."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    with torch.cuda.stream(stream):
+        fn(0)
+        stream.synchronize()
+        torch.cuda._sleep(int(5e7))   # hold the queue so the calls run back to back
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(i + 1)
+            b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+
+def measure_topk(dsel, torch, case, stream, steps, warmup):
+    tb = TopkBench(dsel, torch, case, stream)
+    t_step = graph_time(torch, stream, tb.call, steps, warmup, reps=3)
+    t_kern = event_kernel_time(torch, stream, tb.call, min(steps, 50))
+    nbytes = tb.algorithmic_bytes()
+    rows = case.x.shape[0]
+    res = {
+        "rows_per_s": rows / t_step,
+        "us_per_call": t_step * 1e6,
+        "kernel_us": t_kern * 1e6,
+        "algorithmic_bytes": nbytes,
+        "gbps": nbytes / t_step / 1e9,
+        "pct_peak": 100.0 * nbytes / t_step / 1e9 / HBM_PEAK_GBPS,
+        "input_copies": tb.ncopy,
+    }
+    del tb
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_gather(dsel, torch, case, stream, steps, warmup):
+    """Gather(s) of the case's keys at the top-k positions (one call per key)."""
+    dev = torch.device("cuda")
+    _, idx, _ = dsel.topk(case.x.to(dev), case.k, end=case.row_end.to(dev) if case.row_end is not None else None,
+                          indices_type=case.indices_type, return_value=False)
+    B = case.gather_batch
+    R = case.x.shape[0] // B
+    pos = idx.contiguous().view(B, R, case.k)
+    out = []
+    for ki, key in enumerate(case.keys):
+        kd = key.to(dev)
+        D = key.shape[2]
+        dst = torch.empty(B, R, case.k, D, dtype=key.dtype, device=dev)
+
+        def fn(i, kd=kd, dst=dst):
+            return dsel.gather_rows(kd, pos, out=dst, stream=stream)
+
+        t = graph_time(torch, stream, fn, steps, warmup, reps=3)
+        tk = event_kernel_time(torch, stream, fn, min(steps, 20))
+        safe = pos.long().clamp(0, key.shape[1] - 1)
+        distinct = int(sum(torch.unique(safe[b]).numel() for b in range(B)))
+        npos = B * R * case.k
+        esz = key.element_size()
+        psz = pos.element_size()
+        alg = gather_algorithmic_bytes(npos, D, esz, psz, distinct)
+        out_bytes = npos * D * esz
+        out.append({
+            "key": "contiguous" if key.is_contiguous() else "strided view",
+            "us_per_call": t * 1e6,
+            "kernel_us": tk * 1e6,
+            "algorithmic_bytes": alg,
+            "gbps": alg / t / 1e9,
+            "pct_peak": 100.0 * alg / t / 1e9 / HBM_PEAK_GBPS,
+            "output_convention_gbps": output_convention_gbps(out_bytes, t),
+        })
+        del dst, kd
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(case, budget_s: float = 10.0):
+    """The oracle on the host cores, repeated over the same workload for ~budget_s."""
+    import torch
+    import oracle
+    orc = oracle.Oracle()
+    x = case.x
+    xh = x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
+    it = np.int32 if str(case.indices_type).endswith("int32") else np.int64
+    re = case.row_end.numpy() if case.row_end is not None else None
+    threads = min(oracle.host_threads(), x.shape[0])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.topk(xh, case.k, row_end=re, sorted_index=case.sorted_index, indices_type=it,
+                 return_value=case.return_value, threads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": reps * x.shape[0] / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full passes of the {case.name} top-k ({x.shape[0]} rows x "
+                      f"{x.shape[1]}) in {dt:.1f} s, {threads} threads"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg2")
+    ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the selection step shards by rows with no exchange, "
+              "and multi-GPU runs are not part of this build (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+    import sparse_attention_indexer_dsel_amd as dsel
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    cfg_id = int(args.workload.replace("cfg", ""))
+    case = W.make_config(cfg_id)
+
+    # ---- headline: K steps of the workload's top-k -------------------------
+    tb = TopkBench(dsel, torch, case, stream)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            tb.call(i)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(args.steps):
+            tb.call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    del g
+    t_step = elapsed / args.steps
+    nbytes = tb.algorithmic_bytes()
+    rows = case.x.shape[0]
+    t_kern = event_kernel_time(torch, stream, tb.call, min(args.steps, 50))
+    achieved = nbytes / t_kern / 1e9
+    del tb
+    torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC,
+        "value": rows / t_step,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case.x.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded host generator; no datasets or weights)",
+        "config": {"workload": f"{case.name}: top-k {rows}x{case.x.shape[1]} "
+                               f"{'bf16' if case.x.dtype == torch.bfloat16 else 'fp32'}, "
+                               f"k={case.k}, sorted_index={case.sorted_index}, "
+                               f"{str(case.indices_type).split('.')[-1]} indices, "
+                               f"values={case.return_value}",
+                   "global_batch": rows, "seq_len": int(case.x.shape[1]), "parallelism": "none"},
+        "gbps": nbytes / t_step / 1e9,
+        "pct_peak": 100.0 * nbytes / t_step / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "topk_rows_kernel", "kernel_us": t_kern * 1e6,
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+
+    if not args.no_per_config:
+        per = {}
+        for i in sorted(W.CONFIGS):
+            c = case if i == cfg_id else W.make_config(i)
+            entry = {"topk": measure_topk(dsel, torch, c, stream, 20, 3)}
+            if c.keys:
+                entry["gather"] = measure_gather(dsel, torch, c, stream, 10, 2)
+            per[c.name] = entry
+            print(f"# {c.name}: {json.dumps(entry)}", file=sys.stderr, flush=True)
+        line["per_config"] = per
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case)
+
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 if __name__ == "__main__":
-    raise SystemExit("GPU benchmark not built yet")
+    sys.exit(main())

@@ -1,0 +1,140 @@
+/*
+ * dsel: row-wise top-k selection and compressed-key gather on MI355X (gfx950).
+ *
+ * C ABI.  Every pointer is a device pointer unless marked "host".  Every call
+ * is asynchronous on the HIP stream passed as `stream` (a hipStream_t; NULL
+ * means the legacy default stream); the library never allocates, frees or
+ * synchronises, and keeps no state between calls apart from a per-device
+ * cache of device attributes.
+ *
+ * Status codes: every entry point returns DSEL_OK (0) or a negative code.
+ * Host-checkable faults return before anything is launched.  Data conditions
+ * on the device never fault: NaN is reported through the per-row flag,
+ * row ends are clamped to [0, cols] and gather positions to [0, len-1].
+ */
+#ifndef DSEL_H
+#define DSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DSEL_OK = 0,
+    DSEL_ERR_ARG = -1,        /* null required pointer, bad enum, negative size, short stride */
+    DSEL_ERR_K = -2,          /* k outside [1, 4096] */
+    DSEL_ERR_ALIGN = -3,      /* pointer or row stride not a multiple of the alignment */
+    DSEL_ERR_WORKSPACE = -4,  /* workspace smaller than the size query returned */
+    DSEL_ERR_DEVICE = -5      /* no usable device, or a launch failed */
+};
+
+enum { DSEL_BF16 = 0, DSEL_F32 = 1 };  /* value dtype (bf16 = upper half of binary32) */
+enum { DSEL_I32 = 0, DSEL_I64 = 1 };   /* index dtype */
+
+/*
+ * Byte alignment the library needs of row strides and base pointers.
+ *
+ * DeepSelect tutorial ("Sheshisa Imisebenzi ye-PyTorch TopK nge-DeepSelect"),
+ * section "Ukuphatha Ukuqondaniswa Kwe-Stride": a query returns the input
+ * and output row-stride alignments in bytes; an input whose row stride is
+ * not a multiple must be padded, and outputs are laid out with row strides
+ * aligned to the output figure.
+ *
+ * in_align_bytes, out_align_bytes: host pointers, both written (16 and 16:
+ * one 16-byte vector load or store).  Returns DSEL_ERR_ARG if either is NULL.
+ * Needs no device.
+ */
+int dsel_stride_requirement(int64_t *in_align_bytes, int64_t *out_align_bytes);
+
+/*
+ * Row-wise top-k.
+ *
+ * DeepSelect tutorial, sections "Ukusebenzisa i-TopK Okuyisisekelo" (call
+ * shape and outputs), "Ukubuyisa ama-index kuphela" (values optional),
+ * "Ukusebenzisa i-index buffer ekhona" (caller-owned index buffer),
+ * "Ukusebenza Ngemigqa Enobude Obuhlukahlukene" (per-row exclusive end and
+ * OOB fills), "Ukuphathwa kwe-NaN" (NaN check; rows of valid length <= k are
+ * not checked) and "Ukusebenza namathiphu athuthukile" (k <= 4096).
+ *
+ * For row i with valid length n = clamp(row_end ? row_end[i] : cols, 0, cols)
+ * and c = min(k, n), the selected set is the c largest entries of
+ * x[i, 0:n) under: NaN above +inf (all NaNs equal), -0 == +0, and among equal
+ * values the lower column first.  Then
+ *     out_idx[i, 0:c) = the selected columns in ascending column order
+ *     out_idx[i, c:k) = -1
+ *     out_val[i, 0:c) = bit copies of x at those columns (NaN payloads kept)
+ *     out_val[i, c:k) = -inf
+ *     nan_flag[i]     = (n > k) && some x[i, 0:n) is NaN
+ * The selected columns always come out ascending, so `sorted_index` costs
+ * nothing and both settings give the same bytes.
+ *
+ * x             [rows, cols] bf16 or f32 (`dtype`), last dim contiguous,
+ *               row stride `x_row_stride` elements (>= cols).
+ * k             1..4096, else DSEL_ERR_K.
+ * row_end       int32 [rows] or NULL (all rows full length).
+ * sorted_index  0/1 (see above).
+ * indices_type  DSEL_I32 or DSEL_I64.
+ * return_value  0/1; when 0, out_val is ignored and may be NULL.
+ * out_idx       caller-owned [rows, >= k] of the index dtype, row stride
+ *               `idx_row_stride` elements.
+ * out_val       [rows, >= k] of the input dtype, row stride `val_row_stride`.
+ * nan_flag      uint8 [rows] or NULL.
+ * Alignment: x, out_idx, out_val and each row stride in bytes must be
+ *               multiples of 16, else DSEL_ERR_ALIGN.
+ * workspace     device scratch for rows split over several workgroups.
+ *               Pass NULL to query: *workspace_bytes (host) receives the size
+ *               and nothing is launched.  Otherwise *workspace_bytes is the
+ *               size provided (DSEL_ERR_WORKSPACE if smaller than the query).
+ *               The workspace must be zero-filled before its first use; every
+ *               call leaves it zero-filled again, except word 0, which holds
+ *               sticky error bits (bit 0: a split-row rendezvous timed out).
+ *               Calls that share one workspace must be stream-ordered.
+ * rows == 0 launches nothing and returns DSEL_OK.
+ */
+int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
+              int64_t k, const int32_t *row_end,
+              int sorted_index, int indices_type, int return_value,
+              void *out_idx, int64_t idx_row_stride,
+              void *out_val, int64_t val_row_stride,
+              uint8_t *nan_flag,
+              void *workspace, size_t *workspace_bytes,
+              void *stream);
+
+/*
+ * Gather of key rows at selected positions, batch offset folded in.
+ *
+ * MindSpore hyper-parallel PR #1094 (gather compressed keys through one
+ * index_select), English description and the Chinese section on the fix:
+ * the batch offset b*len is folded into each position so the gather is a
+ * single index_select of D-vectors over the flattened key; the result equals
+ * key[batch_ids, positions] bit for bit, also for a non-contiguous key and
+ * for repeated positions.
+ *
+ *   out[b, r, j, :] = key[b, clamp(pos[b, r, j], 0, len-1), :]
+ *
+ * key      [batch, len, dim] of element size 2 (DSEL_BF16) or 4 (DSEL_F32),
+ *          last dim contiguous; element strides key_batch_stride (between
+ *          batches) and key_row_stride (between rows).
+ * pos      [batch, rows_per_batch, >= per_row] of DSEL_I32 or DSEL_I64
+ *          (`pos_type`), row stride pos_row_stride elements, batch stride
+ *          rows_per_batch * pos_row_stride (so a top-k index buffer
+ *          [batch*rows_per_batch, idx_row_stride] feeds in directly).
+ * out      contiguous [batch, rows_per_batch, per_row, dim], key dtype.
+ * Alignment: key, out and dim*elt, key strides*elt must be multiples of 16;
+ *          pos must be aligned to its element size.
+ * Empty shapes (batch, rows_per_batch or per_row == 0) launch nothing.
+ */
+int dsel_gather_rows(const void *key, int dtype, int64_t batch, int64_t len, int64_t dim,
+                     int64_t key_batch_stride, int64_t key_row_stride,
+                     const void *pos, int pos_type, int64_t rows_per_batch, int64_t per_row,
+                     int64_t pos_row_stride,
+                     void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSEL_H */

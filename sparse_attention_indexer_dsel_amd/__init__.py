@@ -1,0 +1,231 @@
+"""Row-wise top-k and compressed-key gather on MI355X, over the ``libdsel.so`` C ABI.
+
+This module only marshals tensors into the C entry points of
+``include/dsel.h`` (same names without the ``dsel_`` prefix); every step of
+the computation runs in the library's HIP kernels.  PyTorch provides device
+memory and the current stream.  Importing fails loudly when the library has
+not been built (``python -m sparse_attention_indexer_dsel_amd.build_lib``).
+
+Call shapes follow the DeepSelect tutorial ("Sheshisa Imisebenzi ye-PyTorch
+TopK nge-DeepSelect"): ``topk(x, k, sorted_index=..., indices_type=...,
+return_value=..., end=..., output_idx=...)`` on a 2-D input whose last dim is
+contiguous and whose row stride is a multiple of ``stride_requirement()[0]``
+bytes; the outputs' row strides are aligned to ``stride_requirement()[1]``
+bytes, so they may be non-contiguous views.  The gather follows MindSpore
+hyper-parallel PR #1094: ``gather_rows(key, pos)`` equals
+``key[batch_ids, pos.clamp(0, L-1)]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["stride_requirement", "topk", "gather_rows", "DselError", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsel.so")
+
+DSEL_OK, DSEL_ERR_ARG, DSEL_ERR_K, DSEL_ERR_ALIGN, DSEL_ERR_WORKSPACE, DSEL_ERR_DEVICE = \
+    0, -1, -2, -3, -4, -5
+DSEL_BF16, DSEL_F32 = 0, 1
+DSEL_I32, DSEL_I64 = 0, 1
+_NAMES = {DSEL_ERR_ARG: "DSEL_ERR_ARG", DSEL_ERR_K: "DSEL_ERR_K", DSEL_ERR_ALIGN: "DSEL_ERR_ALIGN",
+          DSEL_ERR_WORKSPACE: "DSEL_ERR_WORKSPACE", DSEL_ERR_DEVICE: "DSEL_ERR_DEVICE"}
+
+
+class DselError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what} failed: {_NAMES.get(code, code)}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_attention_indexer_dsel_amd.build_lib`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32, szp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)
+    lib.dsel_stride_requirement.restype = i32
+    lib.dsel_stride_requirement.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.dsel_topk.restype = i32
+    lib.dsel_topk.argtypes = [vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, i64, vp, i64,
+                              vp, vp, szp, vp]
+    lib.dsel_gather_rows.restype = i32
+    lib.dsel_gather_rows.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i32, i64, i64, i64,
+                                     vp, vp]
+    return lib
+
+
+_lib = _load()
+
+
+def _check(code: int, what: str) -> None:
+    if code != DSEL_OK:
+        raise DselError(code, what)
+
+
+def stride_requirement() -> Tuple[int, int]:
+    """(input row-stride alignment, output row-stride alignment) in bytes."""
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.dsel_stride_requirement(ctypes.byref(a), ctypes.byref(b)), "dsel_stride_requirement")
+    return int(a.value), int(b.value)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return DSEL_BF16
+    if dt == torch.float32:
+        return DSEL_F32
+    raise TypeError(f"unsupported value dtype {dt} (bf16 or fp32)")
+
+
+def _index_code(dt: torch.dtype) -> int:
+    if dt == torch.int32:
+        return DSEL_I32
+    if dt == torch.int64:
+        return DSEL_I64
+    raise TypeError(f"unsupported index dtype {dt} (int32 or int64)")
+
+
+def _stream_ptr(device: torch.device, stream) -> int:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _aligned_empty(rows: int, k: int, dtype: torch.dtype, device) -> torch.Tensor:
+    """[rows, k] view of a buffer whose row stride is aligned to the output alignment."""
+    _, out_align = stride_requirement()
+    esz = torch.empty((), dtype=dtype).element_size()
+    stride = -(-k * esz // out_align) * out_align // esz
+    return torch.empty(rows, stride, dtype=dtype, device=device)[:, :k]
+
+
+_WORKSPACES = {}
+
+
+def _workspace(device: torch.device, stream_ptr: int, nbytes: int) -> torch.Tensor:
+    """Zero-initialised scratch kept per (device, stream); the library leaves it zeroed."""
+    key = (device.index, stream_ptr)
+    ws = _WORKSPACES.get(key)
+    need = max(int(nbytes), 256)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def _row_stride(t: torch.Tensor) -> int:
+    """Row stride in elements; a one-row tensor's stride is never used for
+    addressing, so report the smallest aligned stride covering its row."""
+    if t.shape[0] > 1:
+        return int(t.stride(0))
+    per = 16 // t.element_size()
+    return -(-max(int(t.shape[1]), 1) // per) * per
+
+
+def _topk_call(x, k, end, sorted_index, itype, return_value, idx, val, flag, ws_ptr, ws_bytes, sptr):
+    return _lib.dsel_topk(
+        x.data_ptr(), _dtype_code(x.dtype), x.shape[0], x.shape[1], _row_stride(x),
+        int(k), end.data_ptr() if end is not None else None,
+        int(bool(sorted_index)), _index_code(itype), int(bool(return_value)),
+        idx.data_ptr(), _row_stride(idx),
+        val.data_ptr() if val is not None else None, _row_stride(val) if val is not None else 0,
+        flag.data_ptr(), ws_ptr, ctypes.byref(ws_bytes), sptr)
+
+
+def _check_input(x: torch.Tensor) -> None:
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows, cols)")
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if x.shape[1] > 1 and x.stride(1) != 1:
+        raise ValueError("the last dim of x must be contiguous")
+
+
+def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
+         sorted_index: bool = False, sorted: Optional[bool] = None,
+         indices_type: torch.dtype = torch.int32, return_value: bool = True,
+         output_idx: Optional[torch.Tensor] = None, stream=None
+         ) -> Tuple[Optional[torch.Tensor], torch.Tensor, torch.Tensor]:
+    """Row-wise top-k of ``x`` [rows, cols] (bf16 or fp32), 1 <= topk <= 4096.
+
+    Returns ``(values or None, indices, nan_flag)``: indices [rows, topk] of
+    ``indices_type`` (ascending per row; -1 past a short row's length),
+    values [rows, topk] of x's dtype (bit copies; -inf padding), and a uint8
+    [rows] NaN flag (set for rows longer than topk holding a NaN in range).
+    ``end`` (int32 [rows]) is each row's exclusive end.  ``sorted`` is
+    accepted as another name for ``sorted_index``.  ``output_idx`` is a
+    caller-owned [rows, >= topk] index buffer with an aligned row stride.
+    """
+    _check_input(x)
+    if sorted is not None:
+        sorted_index = bool(sorted)
+    rows = x.shape[0]
+    dev = x.device
+    if end is not None:
+        if end.dtype != torch.int32 or end.shape != (rows,) or end.device != dev:
+            raise ValueError("end must be an int32 [rows] tensor on x's device")
+        end = end.contiguous()
+    if output_idx is not None:
+        if output_idx.dtype != indices_type:
+            raise ValueError("output_idx dtype must equal indices_type")
+        if output_idx.dim() != 2 or output_idx.shape[0] != rows or output_idx.shape[1] < topk:
+            raise ValueError("output_idx must be [rows, >= topk]")
+        if output_idx.shape[1] > 1 and output_idx.stride(1) != 1:
+            raise ValueError("output_idx's last dim must be contiguous")
+        idx = output_idx
+    else:
+        idx = _aligned_empty(rows, topk, indices_type, dev)
+    val = _aligned_empty(rows, topk, x.dtype, dev) if return_value else None
+    flag = torch.empty(rows, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        sptr = _stream_ptr(dev, stream)
+        nb = ctypes.c_size_t(0)
+        _check(_topk_call(x, topk, end, sorted_index, indices_type, return_value, idx, val, flag,
+                          None, nb, sptr), "dsel_topk (size query)")
+        ws = _workspace(dev, sptr, nb.value)
+        nb = ctypes.c_size_t(ws.numel())
+        _check(_topk_call(x, topk, end, sorted_index, indices_type, return_value, idx, val, flag,
+                          ws.data_ptr(), nb, sptr), "dsel_topk")
+    if output_idx is not None:
+        idx = output_idx[:, :topk]
+    return val, idx, flag
+
+
+def gather_rows(key: torch.Tensor, pos: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """out[b, r, j, :] = key[b, clamp(pos[b, r, j], 0, L-1), :].
+
+    key: [B, L, D] bf16/fp32 with a contiguous last dim (any batch and row
+    strides).  pos: [B, R, P] int32/int64 with a contiguous last dim and
+    pos.stride(0) == R * pos.stride(1) (a [B*R, k] top-k index buffer viewed
+    as [B, R, k] qualifies).  Returns a contiguous [B, R, P, D] tensor.
+    """
+    if key.dim() != 3 or pos.dim() != 3:
+        raise ValueError("key must be [B, L, D] and pos [B, R, P]")
+    B, L, D = key.shape
+    Bp, R, P = pos.shape
+    if Bp != B:
+        raise ValueError("pos and key disagree on the batch size")
+    if D > 1 and key.stride(2) != 1:
+        raise ValueError("key's last dim must be contiguous")
+    if P > 1 and pos.stride(2) != 1:
+        raise ValueError("pos's last dim must be contiguous")
+    prs = pos.stride(1) if R > 1 else max(P, pos.stride(1))
+    if B > 1 and R > 0 and pos.stride(0) != R * prs:
+        raise ValueError("pos batch stride must equal R * row stride")
+    if key.device != pos.device or not key.is_cuda:
+        raise ValueError("key and pos must be GPU tensors on one device")
+    if out is None:
+        out = torch.empty(B, R, P, D, dtype=key.dtype, device=key.device)
+    elif out.shape != (B, R, P, D) or not out.is_contiguous() or out.dtype != key.dtype:
+        raise ValueError("out must be a contiguous [B, R, P, D] tensor of key's dtype")
+    with torch.cuda.device(key.device):
+        sptr = _stream_ptr(key.device, stream)
+        _check(_lib.dsel_gather_rows(
+            key.data_ptr(), _dtype_code(key.dtype), B, L, D,
+            key.stride(0), key.stride(1), pos.data_ptr(), _index_code(pos.dtype), R, P, prs,
+            out.data_ptr(), sptr), "dsel_gather_rows")
+    return out

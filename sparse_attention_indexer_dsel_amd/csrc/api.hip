@@ -1,0 +1,258 @@
+// C ABI of the selection library: argument checks, path planning, workspace
+// sizing and launches on the caller's stream.  No allocation, no sync.
+#include <atomic>
+#include <cstdlib>
+
+#include "../../include/dsel.h"
+#include "dsel_internal.h"
+
+namespace dsel {
+namespace {
+
+constexpr int64_t kAlign = 16;
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute-unit count of the current device (cached per device), or -1.
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cus > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return -1;
+    g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+bool aligned_ptr(const void *p) { return ((uintptr_t)p % kAlign) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct TopkPlan {
+    bool split = false;
+    int G = 1;
+    int ept = 0;
+    int64_t chunk = 0;
+    int64_t cap = 0;
+    int64_t rows_per_launch = 0;
+    int64_t slot_words = 0;
+    size_t ws_bytes = 0;
+};
+
+// Candidate-list capacity: k plus room for the boundary bin of the first
+// digit (a quarter octave of values), within 4096..8192 entries; a row whose
+// candidates exceed it takes the slower in-register path.
+int64_t candidate_cap(int64_t k, int64_t row_len) {
+    int64_t cap = 2 * k + 2048;
+    if (cap < 4096) cap = 4096;
+    if (cap > 8192) cap = 8192;
+    if (row_len < cap) cap = (row_len + 255) / 256 * 256;
+    return cap;
+}
+
+// Smallest instantiated per-thread element count holding `cols` columns.
+int pick_ept(int dtype, int64_t cols) {
+    const int first = dtype == DSEL_BF16 ? 8 : 4;
+    for (int e = first; e <= kMaxEpt; e *= 2)
+        if ((int64_t)kTopkThreads * e >= cols) return e;
+    return 0;
+}
+
+// Workgroups per row: one when the row fits a workgroup and there are enough
+// rows to occupy the GPU, otherwise enough to hold the row and to give the
+// GPU about two workgroups per compute unit, but no fewer than 2048 columns
+// each.  DSEL_BLOCKS_PER_ROW overrides the choice (tuning and tests).
+int choose_G(int64_t rows, int64_t cols, int cus) {
+    const int64_t gmin = cdiv(cols, kBlockCapacity);
+    int64_t G;
+    if (gmin <= 1 && rows >= cus / 2) {
+        G = 1;
+    } else {
+        const int64_t gpar = cdiv(2 * (int64_t)cus, rows > 0 ? rows : 1);
+        const int64_t gchunk = cdiv(cols, 2048);
+        G = gpar < gchunk ? gpar : gchunk;
+        if (G < gmin) G = gmin;
+        if (G < 1) G = 1;
+    }
+    if (const char *env = std::getenv("DSEL_BLOCKS_PER_ROW")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v >= 1) G = v < gmin ? gmin : v;
+    }
+    if (G > kMaxSplit && gmin <= kMaxSplit) G = kMaxSplit;
+    return (int)G;
+}
+
+int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
+    const int cus = cu_count();
+    if (cus <= 0) return DSEL_ERR_DEVICE;
+    const int vec = topk_vec(dtype);
+    int G = choose_G(rows, cols, cus);
+    int64_t chunk = cols;
+    if (G > 1) {
+        chunk = cdiv(cdiv(cols, G), vec) * vec;
+        G = (int)cdiv(cols, chunk);  // rounding may leave fewer workgroups
+    }
+    if (G > kMaxSplit) return DSEL_ERR_ARG;  // row longer than the split limit holds
+    if (G <= 1) {
+        pl->split = false;
+        pl->G = 1;
+        pl->ept = pick_ept(dtype, cols);
+        pl->chunk = cols;
+        pl->cap = candidate_cap(k, cols);
+        pl->rows_per_launch = rows;
+        pl->ws_bytes = 0;
+        return pl->ept ? DSEL_OK : DSEL_ERR_ARG;
+    }
+    const int ept = pick_ept(dtype, chunk);
+    if (!ept) return DSEL_ERR_ARG;
+    const int64_t cap = candidate_cap(k, cols);
+    // every workgroup of a row must be resident at once: size launches by
+    // the number of workgroups the GPU holds
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, topk_kernel_ptr(dtype, ept, true),
+                                                     kTopkThreads, topk_dyn_lds(dtype, cap)) !=
+            hipSuccess ||
+        per_cu <= 0)
+        return DSEL_ERR_DEVICE;
+    const int64_t capacity = (int64_t)per_cu * cus;
+    if (G > capacity) return DSEL_ERR_ARG;  // row longer than the GPU holds on chip
+    int64_t rpl = capacity / G;
+    if (rpl > rows) rpl = rows;
+    pl->split = true;
+    pl->G = G;
+    pl->ept = ept;
+    pl->chunk = chunk;
+    pl->cap = cap;
+    pl->rows_per_launch = rpl;
+    pl->slot_words = slot_words(G, cap);
+    pl->ws_bytes = (size_t)(kHeaderWords + rpl * pl->slot_words) * sizeof(uint32_t);
+    return DSEL_OK;
+}
+
+}  // namespace
+}  // namespace dsel
+
+using namespace dsel;
+
+extern "C" int dsel_stride_requirement(int64_t *in_align_bytes, int64_t *out_align_bytes) {
+    if (!in_align_bytes || !out_align_bytes) return DSEL_ERR_ARG;
+    *in_align_bytes = kAlign;
+    *out_align_bytes = kAlign;
+    return DSEL_OK;
+}
+
+extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
+                         int64_t x_row_stride, int64_t k, const int32_t *row_end,
+                         int sorted_index, int indices_type, int return_value, void *out_idx,
+                         int64_t idx_row_stride, void *out_val, int64_t val_row_stride,
+                         uint8_t *nan_flag, void *workspace, size_t *workspace_bytes,
+                         void *stream) {
+    (void)sorted_index;  // output is ascending by construction
+    if (dtype != DSEL_BF16 && dtype != DSEL_F32) return DSEL_ERR_ARG;
+    if (indices_type != DSEL_I32 && indices_type != DSEL_I64) return DSEL_ERR_ARG;
+    if (rows < 0 || cols < 1) return DSEL_ERR_ARG;
+    if (k < 1 || k > 4096) return DSEL_ERR_K;
+    if (!workspace_bytes) return DSEL_ERR_ARG;
+    if (rows == 0) {
+        if (!workspace) *workspace_bytes = 0;
+        return DSEL_OK;
+    }
+    if (!x || !out_idx || (return_value && !out_val)) return DSEL_ERR_ARG;
+    if (x_row_stride < cols || idx_row_stride < k || (return_value && val_row_stride < k))
+        return DSEL_ERR_ARG;
+    if (indices_type == DSEL_I32 && cols > INT32_MAX) return DSEL_ERR_ARG;
+    const int64_t esz = dtype == DSEL_BF16 ? 2 : 4;
+    const int64_t isz = indices_type == DSEL_I32 ? 4 : 8;
+    if (!aligned_ptr(x) || (x_row_stride * esz) % kAlign || !aligned_ptr(out_idx) ||
+        (idx_row_stride * isz) % kAlign)
+        return DSEL_ERR_ALIGN;
+    if (return_value && (!aligned_ptr(out_val) || (val_row_stride * esz) % kAlign))
+        return DSEL_ERR_ALIGN;
+
+    TopkPlan pl;
+    const int st = plan_topk(dtype, rows, cols, k, &pl);
+    if (st != DSEL_OK) return st;
+    if (!workspace) {
+        *workspace_bytes = pl.ws_bytes;
+        return DSEL_OK;
+    }
+    if (*workspace_bytes < pl.ws_bytes) return DSEL_ERR_WORKSPACE;
+    if (pl.split && !aligned_ptr(workspace)) return DSEL_ERR_ALIGN;
+
+    TopkArgs a{};
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.x_stride = x_row_stride;
+    a.row_end = row_end;
+    a.out_idx = out_idx;
+    a.idx_stride = idx_row_stride;
+    a.out_val = return_value ? out_val : nullptr;
+    a.val_stride = val_row_stride;
+    a.nan_flag = nan_flag;
+    a.ws = reinterpret_cast<uint32_t *>(workspace);
+    a.chunk = pl.chunk;
+    a.slot_words = pl.slot_words;
+    a.cap = pl.cap;
+    a.k = (int)k;
+    a.G = pl.G;
+    a.idx64 = indices_type == DSEL_I64;
+    a.ret_val = return_value ? 1 : 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int64_t r0 = 0; r0 < rows; r0 += pl.rows_per_launch) {
+        const int64_t nr = (rows - r0) < pl.rows_per_launch ? (rows - r0) : pl.rows_per_launch;
+        a.row0 = r0;
+        const int64_t grid = nr * pl.G;
+        if (grid > INT32_MAX) return DSEL_ERR_ARG;
+        if (launch_topk(dtype, pl.ept, pl.split, a, (unsigned)grid, s) != hipSuccess)
+            return DSEL_ERR_DEVICE;
+    }
+    return DSEL_OK;
+}
+
+extern "C" int dsel_gather_rows(const void *key, int dtype, int64_t batch, int64_t len,
+                                int64_t dim, int64_t key_batch_stride, int64_t key_row_stride,
+                                const void *pos, int pos_type, int64_t rows_per_batch,
+                                int64_t per_row, int64_t pos_row_stride, void *out,
+                                void *stream) {
+    if (dtype != DSEL_BF16 && dtype != DSEL_F32) return DSEL_ERR_ARG;
+    if (pos_type != DSEL_I32 && pos_type != DSEL_I64) return DSEL_ERR_ARG;
+    if (batch < 0 || len < 1 || dim < 1 || rows_per_batch < 0 || per_row < 0)
+        return DSEL_ERR_ARG;
+    if (batch == 0 || rows_per_batch == 0 || per_row == 0) return DSEL_OK;
+    if (!key || !pos || !out) return DSEL_ERR_ARG;
+    if (pos_row_stride < per_row || key_batch_stride < 0 || key_row_stride < 0)
+        return DSEL_ERR_ARG;
+    const int64_t esz = dtype == DSEL_BF16 ? 2 : 4;
+    const int64_t psz = pos_type == DSEL_I32 ? 4 : 8;
+    if (!aligned_ptr(key) || !aligned_ptr(out) || (dim * esz) % kAlign ||
+        (key_batch_stride * esz) % kAlign || (key_row_stride * esz) % kAlign ||
+        ((uintptr_t)pos % psz) != 0)
+        return DSEL_ERR_ALIGN;
+    GatherArgs a{};
+    a.key = reinterpret_cast<const char *>(key);
+    a.out = reinterpret_cast<char *>(out);
+    a.pos = pos;
+    a.batch = batch;
+    a.len = len;
+    a.R = rows_per_batch;
+    a.P = per_row;
+    a.key_batch_bytes = key_batch_stride * esz;
+    a.key_row_bytes = key_row_stride * esz;
+    a.pos_row_stride = pos_row_stride;
+    const int64_t rv = dim * esz / 16;
+    if (rv > (1 << 20)) return DSEL_ERR_ARG;
+    a.row_vecs = (int)rv;
+    a.row_vecs_log2 = -1;
+    if ((rv & (rv - 1)) == 0) {
+        int l = 0;
+        while ((1LL << l) < rv) ++l;
+        a.row_vecs_log2 = l;
+    }
+    if (launch_gather(pos_type == DSEL_I64, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return DSEL_ERR_DEVICE;
+    return DSEL_OK;
+}

@@ -1,0 +1,76 @@
+// Internal declarations shared by the library's translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsel {
+
+// Workgroup shape of every top-k kernel: four wave64s.
+constexpr int kTopkThreads = 256;
+// Largest per-thread element count instantiated; on-chip row capacity is
+// kTopkThreads * kMaxEpt elements per workgroup.
+constexpr int kMaxEpt = 64;
+constexpr int64_t kBlockCapacity = (int64_t)kTopkThreads * kMaxEpt;
+// First-pass digit width: 2048 histogram bins in LDS.
+constexpr int kBins = 2048;
+// Workspace header (32-bit words) ahead of the per-row rendezvous slots;
+// word 0 carries sticky error bits.
+constexpr int kHeaderWords = 64;
+constexpr int kSlotHeadWords = 16;
+constexpr int kMaxPasses = 3;
+// Most workgroups one row may be split over.
+constexpr int kMaxSplit = 1024;
+
+// Per-row workspace slot (32-bit words): counters, one histogram per radix
+// pass, per-workgroup counts, and the staged candidate list (keys, columns).
+inline int64_t slot_words(int G, int64_t cap) {
+    return kSlotHeadWords + (int64_t)kMaxPasses * kBins + 4 * (int64_t)G + 2 * cap;
+}
+
+struct TopkArgs {
+    const void *x;
+    int64_t rows;
+    int64_t cols;
+    int64_t x_stride;        // elements
+    const int32_t *row_end;  // nullable
+    void *out_idx;
+    int64_t idx_stride;      // elements of the index type
+    void *out_val;
+    int64_t val_stride;      // elements of the value type
+    uint8_t *nan_flag;       // nullable
+    uint32_t *ws;            // workspace base (split rows only)
+    int64_t row0;            // first row of this launch
+    int64_t chunk;           // columns per workgroup (split rows only)
+    int64_t slot_words;      // 32-bit words per row slot (split rows only)
+    int64_t cap;             // capacity of the candidate list (entries)
+    int k;
+    int G;                   // workgroups per row
+    int idx64;
+    int ret_val;
+};
+
+// Kernel instance for (dtype, elements per thread, split); nullptr if none.
+const void *topk_kernel_ptr(int dtype, int ept, bool split);
+// Elements per 16-byte vector for a dtype.
+inline int topk_vec(int dtype) { return dtype == 0 ? 8 : 4; }
+// Dynamic LDS bytes of a top-k launch with candidate capacity `cap`.
+size_t topk_dyn_lds(int dtype, int64_t cap);
+hipError_t launch_topk(int dtype, int ept, bool split, const TopkArgs &a, unsigned grid,
+                       hipStream_t stream);
+
+struct GatherArgs {
+    const char *key;
+    char *out;
+    const void *pos;
+    int64_t batch, len, R, P;
+    int64_t key_batch_bytes, key_row_bytes;
+    int64_t pos_row_stride;  // elements
+    int row_vecs;            // 16-byte vectors per key row
+    int row_vecs_log2;       // log2(row_vecs) when a power of two, else -1
+};
+
+hipError_t launch_gather(int pos64, const GatherArgs &a, hipStream_t stream);
+
+}  // namespace dsel

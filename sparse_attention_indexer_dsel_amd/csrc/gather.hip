@@ -1,0 +1,73 @@
+// Gather of key rows at selected positions with the batch offset folded in.
+//
+// MindSpore hyper-parallel PR #1094 (English description; Chinese section on
+// the fix): the two-tensor form key[batch_ids, positions] becomes a single
+// index_select of D-vectors over the flattened key at b*len + position; the
+// result is the same bits.  Positions are clamped into [0, len-1], the
+// "safe" positions its call sites pass.
+//
+// Layout here: one workgroup per (batch, query-row) pair walks that row's
+// positions; 16-byte vector copies, cached loads from the key (rows are
+// revisited by neighbouring query rows) and non-temporal stores of the
+// output, which is written once and never re-read.
+#include "dsel_internal.h"
+
+namespace dsel {
+namespace {
+
+constexpr int GT = 256;     // threads per workgroup
+constexpr int UNROLL = 4;   // independent 16-byte copies in flight per thread
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool POS64, bool POW2>
+__global__ __launch_bounds__(GT) void gather_rows_kernel(const GatherArgs a) {
+    const int64_t pairs = a.batch * a.R;
+    const int64_t total = a.P * (int64_t)a.row_vecs;  // vectors per query row
+    for (int64_t br = blockIdx.x; br < pairs; br += gridDim.x) {
+        const int64_t b = br / a.R;
+        const char *kb = a.key + b * a.key_batch_bytes;
+        u32x4 *ob = reinterpret_cast<u32x4 *>(a.out + br * total * 16);
+        const int64_t prow = br * a.pos_row_stride;
+        for (int64_t i0 = threadIdx.x; i0 < total; i0 += (int64_t)GT * UNROLL) {
+            u32x4 v[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t i = i0 + (int64_t)u * GT;
+                if (i < total) {
+                    const int64_t j = POW2 ? (i >> a.row_vecs_log2) : (i / a.row_vecs);
+                    const int64_t vi = i - j * a.row_vecs;
+                    int64_t p = POS64 ? reinterpret_cast<const int64_t *>(a.pos)[prow + j]
+                                      : (int64_t)reinterpret_cast<const int32_t *>(a.pos)[prow + j];
+                    p = p < 0 ? 0 : (p >= a.len ? a.len - 1 : p);
+                    v[u] = *reinterpret_cast<const u32x4 *>(kb + p * a.key_row_bytes + vi * 16);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t i = i0 + (int64_t)u * GT;
+                if (i < total) __builtin_nontemporal_store(v[u], ob + i);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gather(int pos64, const GatherArgs &a, hipStream_t stream) {
+    const int64_t pairs = a.batch * a.R;
+    const unsigned grid = (unsigned)(pairs < (1 << 22) ? pairs : (1 << 22));
+    const bool pow2 = a.row_vecs_log2 >= 0;
+    GatherArgs copy = a;
+    void *args[] = {&copy};
+    const void *fn;
+    if (pos64)
+        fn = pow2 ? reinterpret_cast<const void *>(&gather_rows_kernel<true, true>)
+                  : reinterpret_cast<const void *>(&gather_rows_kernel<true, false>);
+    else
+        fn = pow2 ? reinterpret_cast<const void *>(&gather_rows_kernel<false, true>)
+                  : reinterpret_cast<const void *>(&gather_rows_kernel<false, false>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(GT), args, 0, stream);
+}
+
+}  // namespace dsel

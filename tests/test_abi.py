@@ -1,0 +1,106 @@
+"""The C ABI library loads and exports every entry point include/dsel.h declares.
+
+Only calls that fail host-side argument checks are made here (they return
+before touching a device), so this runs without a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsel.h")
+LIB = os.path.join(ROOT, "sparse_attention_indexer_dsel_amd", "libdsel.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from sparse_attention_indexer_dsel_amd import build_lib
+        build_lib.build()
+    return ctypes.CDLL(LIB)
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\bint\s+(dsel_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    assert declared() == ["dsel_gather_rows", "dsel_stride_requirement", "dsel_topk"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    for name in declared():
+        assert name in exported, name
+        assert getattr(lib, name)
+
+
+def test_stride_requirement_host_only(lib):
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert lib.dsel_stride_requirement(ctypes.byref(a), ctypes.byref(b)) == 0
+    assert (a.value, b.value) == (16, 16)
+    assert lib.dsel_stride_requirement(None, ctypes.byref(b)) == -1
+
+
+def _topk(lib, **kw):
+    args = dict(x=16, dtype=0, rows=4, cols=64, stride=64, k=8, row_end=None, sorted_index=0,
+                itype=0, ret=0, oi=16, ois=16, ov=None, ovs=0, flag=None, ws=None)
+    args.update(kw)
+    nb = ctypes.c_size_t(0)
+    f = lib.dsel_topk
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+    return f(args["x"], args["dtype"], args["rows"], args["cols"], args["stride"], args["k"],
+             args["row_end"], args["sorted_index"], args["itype"], args["ret"], args["oi"],
+             args["ois"], args["ov"], args["ovs"], args["flag"], args["ws"], ctypes.byref(nb), None)
+
+
+def test_topk_host_checks(lib):
+    assert _topk(lib, k=0) == -2
+    assert _topk(lib, k=4097) == -2
+    assert _topk(lib, dtype=7) == -1
+    assert _topk(lib, itype=3) == -1
+    assert _topk(lib, cols=0) == -1
+    assert _topk(lib, rows=-1) == -1
+    assert _topk(lib, x=None) == -1
+    assert _topk(lib, ret=1, ov=None) == -1
+    assert _topk(lib, stride=63) == -1                     # stride < cols
+    assert _topk(lib, ois=7) == -1                         # idx stride < k
+    assert _topk(lib, stride=68) == -3                     # 136 B row stride
+    assert _topk(lib, x=18) == -3                          # misaligned base
+    assert _topk(lib, rows=0) == 0                         # empty: nothing launched
+
+
+def test_gather_host_checks(lib):
+    f = lib.dsel_gather_rows
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    ok = dict(key=16, dt=0, B=2, L=10, D=128, kbs=1280, krs=128, pos=16, pt=0, R=3, P=5, prs=5,
+              out=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["key"], a["dt"], a["B"], a["L"], a["D"], a["kbs"], a["krs"], a["pos"], a["pt"],
+                 a["R"], a["P"], a["prs"], a["out"], None)
+    assert call(dt=5) == -1
+    assert call(pt=5) == -1
+    assert call(L=0) == -1
+    assert call(key=None) == -1
+    assert call(prs=4) == -1
+    assert call(D=100) == -3          # 200 B rows are not 16 B multiples
+    assert call(krs=129) == -3
+    assert call(out=24) == -3
+    assert call(R=0) == 0             # empty: nothing launched

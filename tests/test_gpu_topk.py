@@ -1,0 +1,188 @@
+"""GPU top-k against the CPU oracle, bit for bit, through the C ABI binding."""
+import os
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle_pins as P
+import workloads as W
+from parity import compare_topk, gpu_bits, oracle_topk, say, to_device, valid_lengths
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsel():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_indexer_dsel_amd as d
+    return d
+
+
+class blocks_per_row:
+    """Force the number of workgroups per row (DSEL_BLOCKS_PER_ROW) inside a block."""
+
+    def __init__(self, g):
+        self.g = g
+
+    def __enter__(self):
+        self.old = os.environ.get("DSEL_BLOCKS_PER_ROW")
+        if self.g is None:
+            os.environ.pop("DSEL_BLOCKS_PER_ROW", None)
+        else:
+            os.environ["DSEL_BLOCKS_PER_ROW"] = str(self.g)
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("DSEL_BLOCKS_PER_ROW", None)
+        else:
+            os.environ["DSEL_BLOCKS_PER_ROW"] = self.old
+
+
+def run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value, output_idx=None):
+    xd = to_device(x)
+    re = row_end.cuda() if row_end is not None else None
+    v, i, f = dsel.topk(xd, k, end=re, sorted_index=sorted_index, indices_type=indices_type,
+                        return_value=return_value, output_idx=output_idx)
+    torch.cuda.synchronize()
+    return (gpu_bits(v) if v is not None else None, i.cpu().numpy(), f.cpu().numpy())
+
+
+def check_case(dsel, orc, name, x, k, row_end=None, sorted_index=False,
+               indices_type=torch.int32, return_value=True, G=None):
+    say(f"[topk] {name} shape={tuple(x.shape)} stride={x.stride()} k={k} G={G} "
+        f"sorted={sorted_index} idx={indices_type} val={return_value}")
+    with blocks_per_row(G):
+        got = run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value)
+    want = oracle_topk(orc, x, k, row_end, sorted_index, indices_type, return_value)
+    n = valid_lengths(x.shape[0], x.shape[1], row_end)
+    compare_topk(got, want, n, k, sorted_index, name)
+    # the GPU always returns ascending indices
+    gi = got[1].astype(np.int64)
+    for r in range(min(gi.shape[0], 64)):
+        c = int(min(k, n[r]))
+        assert (np.diff(gi[r, :c]) > 0).all()
+    return got
+
+
+SMALL = [
+    # name, rows, cols, dtype, dist, k
+    ("normal_bf16", 9, 3000, W.BF16, "normal", 100),
+    ("normal_f32", 9, 3000, W.F32, "normal", 100),
+    ("ties_bf16", 7, 5000, W.BF16, "ties", 777),
+    ("ties_f32", 7, 5000, W.F32, "ties", 4096),
+    ("equal_bf16", 3, 4100, W.BF16, "equal", 1000),
+    ("equal_f32", 3, 4100, W.F32, "equal", 4096),
+    ("ascending_f32", 4, 6000, W.F32, "ascending", 300),
+    ("descending_bf16", 4, 6000, W.BF16, "descending", 300),
+    ("special_bf16", 11, 2500, W.BF16, "special", 64),
+    ("special_f32", 11, 2500, W.F32, "special", 64),
+    ("narrow_bf16", 5, 16384, W.BF16, "narrow", 2000),
+    ("ragged_bf16", 6, 2043, W.BF16, "normal", 17),
+    ("ragged_f32", 6, 1037, W.F32, "normal", 1),
+    ("k_ge_cols", 5, 300, W.F32, "normal", 512),
+    ("one_col", 5, 1, W.BF16, "normal", 3),
+]
+
+
+@pytest.mark.parametrize("G", [None, 3, 7])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c[0])
+def test_small_cases(dsel, orc, case, G):
+    name, rows, cols, dt, dist, k = case
+    x = W.random_rows(zlib.crc32(name.encode()) & 0xFFFF, rows, cols, dt, dist)
+    for ret in (True, False):
+        check_case(dsel, orc, f"{name}/G{G}/val{int(ret)}", x, k, None, False, torch.int32, ret, G)
+
+
+@pytest.mark.parametrize("G", [None, 4])
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_row_end_and_nan(dsel, orc, dt, G):
+    x = W.random_rows(21, 64, 3000, dt, "normal")
+    W.plant_nans(x, 22, 40)
+    re = W.random_row_end(23, 64, -50, 3100)
+    re[:4] = torch.tensor([0, 200, 201, 3000], dtype=torch.int32)
+    check_case(dsel, orc, f"row_end_nan/{dt}", x, 200, re, True, torch.int64, True, G)
+    check_case(dsel, orc, f"row_end_nan/{dt}/idx-only", x, 200, re, False, torch.int32, False, G)
+
+
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_padded_stride(dsel, orc, dt):
+    x = W.random_rows(31, 12, 2000, dt, "normal", stride=2048)
+    assert not x.is_contiguous()
+    check_case(dsel, orc, f"padded/{dt}", x, 333, None, True, torch.int32, True)
+    check_case(dsel, orc, f"padded/{dt}/split", x, 333, None, True, torch.int32, True, G=5)
+
+
+def test_k_max_and_long_rows(dsel, orc):
+    x = W.random_rows(41, 3, 70000, W.F32, "normal")
+    check_case(dsel, orc, "k4096_long_f32", x, 4096, None, False, torch.int64, True)
+    x = W.random_rows(42, 2, 100000, W.BF16, "ties")
+    check_case(dsel, orc, "k4096_long_bf16_ties", x, 4096, None, True, torch.int32, True)
+
+
+def test_empty_rows(dsel):
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    v, i, f = dsel.topk(x, 8)
+    assert i.shape == (0, 8) and f.shape == (0,)
+
+
+def test_caller_owned_index_buffer(dsel, orc):
+    x = W.random_rows(51, 10, 4000, W.BF16, "normal")
+    buf = torch.full((10, 520), 7, dtype=torch.int32, device="cuda")
+    v, i, f = dsel.topk(x.cuda(), 500, output_idx=buf, return_value=False)
+    torch.cuda.synchronize()
+    assert i.data_ptr() == buf.data_ptr()
+    assert (buf[:, 500:] == 7).all(), "slots beyond k must be untouched"
+    want = oracle_topk(orc, x, 500, None, True, torch.int32, False)
+    assert np.array_equal(buf[:, :500].cpu().numpy(), want[1])
+
+
+def test_run_to_run_identical(dsel):
+    x = W.random_rows(61, 16, 40000, W.BF16, "ties").cuda()
+    a = dsel.topk(x, 1024)
+    b = dsel.topk(x, 1024)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+
+
+def test_errors(dsel):
+    x = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dsel.DselError) as e:
+        dsel.topk(x, 0)
+    assert e.value.code == -2
+    with pytest.raises(dsel.DselError) as e:
+        dsel.topk(x, 4097)
+    assert e.value.code == -2
+    xs = torch.zeros(4, 70, dtype=torch.bfloat16, device="cuda")[:, :65]  # stride 140 B
+    with pytest.raises(dsel.DselError) as e:
+        dsel.topk(xs, 4)
+    assert e.value.code == -3
+
+
+def test_workspace_left_clean(dsel):
+    x = W.random_rows(71, 8, 50000, W.F32, "normal").cuda()
+    with blocks_per_row(6):
+        dsel.topk(x, 100)
+        dsel.topk(x, 2000)
+    torch.cuda.synchronize()
+    for ws in dsel._WORKSPACES.values():
+        assert int(ws.count_nonzero()) == 0, "workspace must be zero after a call (and no error bit)"
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_workload_topk_full_size(dsel, orc, cfg):
+    case = W.make_config(cfg)
+    check_case(dsel, orc, case.name, case.x, case.k, case.row_end, case.sorted_index,
+               case.indices_type, case.return_value)
+
+
+def test_workload_split_path_cfg1(dsel, orc):
+    case = W.make_config(1)
+    for G in (1, 4):
+        check_case(dsel, orc, f"cfg1/G{G}", case.x, case.k, None, False, torch.int32, True, G)

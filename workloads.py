@@ -141,7 +141,11 @@ def make_config(i: int) -> TopkCase:
 def random_rows(seed: int, rows: int, cols: int, dtype: str = BF16,
                 dist: str = "normal", stride: Optional[int] = None,
                 scale: float = 1.0) -> torch.Tensor:
-    """A [rows, cols] input; ``stride`` > cols gives a padded (strided) view.
+    """A [rows, cols] input whose row stride is ``stride`` elements.
+
+    By default the stride is cols rounded up to a 16-byte multiple (the
+    alignment a row of the input must have); a larger ``stride`` gives a
+    padded view.
 
     ``dist``: "normal" (N(0, scale^2)), "ties" (integers in [-8, 8): heavy
     ties), "equal" (all entries 1.5), "ascending", "descending",
@@ -149,7 +153,8 @@ def random_rows(seed: int, rows: int, cols: int, dtype: str = BF16,
     "narrow" (N(0,1) quantised to a few bf16 steps around one value).
     """
     g = _gen(seed)
-    st = cols if stride is None else int(stride)
+    per = 8 if dtype == BF16 else 4  # elements per 16 bytes
+    st = -(-max(cols, 1) // per) * per if stride is None else int(stride)
     tdt = torch.bfloat16 if dtype == BF16 else torch.float32
     base = torch.empty(rows, max(st, 1), dtype=torch.float32)
     if dist == "normal":
