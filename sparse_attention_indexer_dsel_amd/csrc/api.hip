@@ -38,25 +38,27 @@ struct TopkPlan {
     int64_t chunk = 0;
     int64_t cap = 0;
     int64_t rows_per_launch = 0;
+    int64_t grid = 0;  // workgroups per launch
     int64_t slot_words = 0;
     size_t ws_bytes = 0;
 };
 
 // Candidate-list capacity: k plus room for the boundary bin of the first
-// digit (a quarter octave of values), within 4096..8192 entries; a row whose
-// candidates exceed it takes the slower in-register path.
+// digit (a quarter octave of values), at most 8192 entries and never more
+// than the row; a row whose candidates exceed it takes the slower
+// in-register path.
 int64_t candidate_cap(int64_t k, int64_t row_len) {
-    int64_t cap = 2 * k + 2048;
-    if (cap < 4096) cap = 4096;
+    int64_t cap = k + (k > 1536 ? k : 1536);
     if (cap > 8192) cap = 8192;
-    if (row_len < cap) cap = (row_len + 255) / 256 * 256;
-    return cap;
+    if (row_len < cap) cap = row_len;
+    return (cap + 255) / 256 * 256;
 }
 
-// Smallest instantiated per-thread element count holding `cols` columns.
+// Smallest instantiated per-thread segment (elements) covering `cols`
+// columns with one workgroup.
 int pick_ept(int dtype, int64_t cols) {
-    const int first = dtype == DSEL_BF16 ? 8 : 4;
-    for (int e = first; e <= kMaxEpt; e *= 2)
+    (void)dtype;
+    for (int e = 8; e <= kMaxEpt; e *= 2)
         if ((int64_t)kTopkThreads * e >= cols) return e;
     return 0;
 }
@@ -97,14 +99,25 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     }
     if (G > kMaxSplit) return DSEL_ERR_ARG;  // row longer than the split limit holds
     if (G <= 1) {
+        // persistent workgroups, each walking rows with its next row's loads
+        // in flight: as many as the GPU holds at once
         pl->split = false;
         pl->G = 1;
         pl->ept = pick_ept(dtype, cols);
+        if (!pl->ept) return DSEL_ERR_ARG;
         pl->chunk = cols;
         pl->cap = candidate_cap(k, cols);
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, topk_kernel_ptr(dtype, pl->ept, false), kTopkThreads,
+                topk_dyn_lds(dtype, pl->cap)) != hipSuccess ||
+            per_cu <= 0)
+            return DSEL_ERR_DEVICE;
+        const int64_t slots = (int64_t)per_cu * cus;
         pl->rows_per_launch = rows;
+        pl->grid = rows < slots ? rows : slots;
         pl->ws_bytes = 0;
-        return pl->ept ? DSEL_OK : DSEL_ERR_ARG;
+        return DSEL_OK;
     }
     const int ept = pick_ept(dtype, chunk);
     if (!ept) return DSEL_ERR_ARG;
@@ -127,6 +140,7 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     pl->chunk = chunk;
     pl->cap = cap;
     pl->rows_per_launch = rpl;
+    pl->grid = rpl * G;
     pl->slot_words = slot_words(G, cap);
     pl->ws_bytes = (size_t)(kHeaderWords + rpl * pl->slot_words) * sizeof(uint32_t);
     return DSEL_OK;
@@ -205,7 +219,7 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
     for (int64_t r0 = 0; r0 < rows; r0 += pl.rows_per_launch) {
         const int64_t nr = (rows - r0) < pl.rows_per_launch ? (rows - r0) : pl.rows_per_launch;
         a.row0 = r0;
-        const int64_t grid = nr * pl.G;
+        const int64_t grid = pl.split ? nr * pl.G : pl.grid;
         if (grid > INT32_MAX) return DSEL_ERR_ARG;
         if (launch_topk(dtype, pl.ept, pl.split, a, (unsigned)grid, s) != hipSuccess)
             return DSEL_ERR_DEVICE;
