@@ -1,7 +1,8 @@
 """Benchmark of the selection step (row-wise top-k, then key gather) on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2]
-                    [--no-per-config] [--no-cpu-baseline]
+                    [--no-per-config] [--no-cpu-baseline] [--copy-calibration]
+    python bench.py --traffic-from FETCH.csv WRITE.csv   # no GPU: writes profiles/traffic.json
 
 Prints ONE JSON line.  The headline workload is the 4 x 204800 bf16 top-k
 (k = 1024, ascending int32 indices plus values); a step is one top-k call
@@ -29,10 +30,21 @@ Byte accounting (algorithmic bytes: what the method must move)
            distinct key row touched.
 The gather is also reported in the pages' convention (gathered output bytes
 over time; MindSpore hyper-parallel PR #1094, mechanism check).
+
+HBM traffic (roofline "traffic")
+  Two rocprofv3 counter runs of this script with --copy-calibration give
+  FETCH_SIZE and WRITE_SIZE per dispatch for the dominant top-k kernel and
+  for a plain streaming copy of known size (torch.neg, 256 MiB in, 256 MiB
+  out).  --traffic-from turns them into bytes per launch (counter value x
+  known copy bytes / copy counter value) and stores them in
+  profiles/traffic.json with a hash of the kernel sources; the bench reports
+  them only while that hash still matches, and null otherwise.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -46,6 +58,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
+COPY_CAL_BYTES = 256 << 20
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_indexer_dsel_amd", "csrc", f)
+                  for f in ("topk.hip", "dsel_internal.h", "api.hip")]
 METRIC = "top-k rows/s and achieved HBM GB/s (% of peak) per config; gather GB/s"
 
 
@@ -70,6 +86,95 @@ def topk_algorithmic_bytes(n_valid: np.ndarray, k: int, elt: int, idx_elt: int,
 def gather_algorithmic_bytes(n_positions: int, dim: int, elt: int, pos_elt: int,
                              distinct_rows: int) -> int:
     return n_positions * dim * elt + n_positions * pos_elt + distinct_rows * dim * elt
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters
+# ---------------------------------------------------------------------------
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(torch, stream, launches: int = 3) -> None:
+    """A plain streaming copy of known size for the counter calibration:
+    COPY_CAL_BYTES read and COPY_CAL_BYTES written per launch."""
+    n = COPY_CAL_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(launches):
+            torch.neg(src, out=dst)
+    stream.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def _counter_means(path: str, counter: str):
+    """Mean per dispatch of `counter`, per kernel name, from a rocprofv3
+    counter_collection.csv."""
+    per = {}
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {name: (float(np.mean(v)), len(v)) for name, v in out.items()}
+
+
+def traffic_from(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC_JSON) -> dict:
+    """Per-launch HBM bytes of the top-k kernel, scaled by the copy kernel's
+    reading of the same counters (counter x known bytes / copy counter)."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+
+    def pick(table, pat):
+        names = [n for n in table if pat in n]
+        if not names:
+            raise SystemExit(f"no kernel matching {pat!r} in the counter file")
+        return max(names, key=lambda n: table[n][1])
+
+    copy_f, copy_w = pick(fetch, "neg"), pick(write, "neg")
+    tk_f, tk_w = pick(fetch, "topk_rows"), pick(write, "topk_rows")
+    f_fac = COPY_CAL_BYTES / fetch[copy_f][0]
+    w_fac = COPY_CAL_BYTES / write[copy_w][0]
+    rec = {
+        "kernel": tk_f,
+        "source_hash": kernel_source_hash(),
+        "fetch_counter_per_launch": fetch[tk_f][0],
+        "write_counter_per_launch": write[tk_w][0],
+        "launches_sampled": [fetch[tk_f][1], write[tk_w][1]],
+        "copy_fetch_counter": fetch[copy_f][0],
+        "copy_write_counter": write[copy_w][0],
+        "copy_bytes": COPY_CAL_BYTES,
+        "fetch_factor": f_fac,
+        "write_factor": w_fac,
+        "fetch_bytes": fetch[tk_f][0] * f_fac,
+        "write_bytes": write[tk_w][0] * w_fac,
+    }
+    rec["traffic_bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    return rec
+
+
+def load_traffic():
+    """The stored traffic record, or None when the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    return rec if rec.get("source_hash") == kernel_source_hash() else None
 
 
 # ---------------------------------------------------------------------------
@@ -247,7 +352,14 @@ def main(argv=None):
     ap.add_argument("--workload", default="cfg2")
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run the plain copy kernel the traffic counters are scaled by")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 counter files into profiles/traffic.json")
     args = ap.parse_args(argv)
+    if args.traffic_from:
+        print(json.dumps(traffic_from(*args.traffic_from)))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the selection step shards by rows with no exchange, "
               "and multi-GPU runs are not part of this build (run with --gpus 1)", file=sys.stderr)
@@ -262,6 +374,8 @@ def main(argv=None):
     stream = torch.cuda.Stream()
     cfg_id = int(args.workload.replace("cfg", ""))
     case = W.make_config(cfg_id)
+    if args.copy_calibration:
+        copy_calibration(torch, stream)
 
     # ---- headline: K steps of the workload's top-k -------------------------
     tb = TopkBench(dsel, torch, case, stream)
@@ -285,6 +399,7 @@ def main(argv=None):
     rows = case.x.shape[0]
     t_kern = event_kernel_time(torch, stream, tb.call, min(args.steps, 50))
     achieved = nbytes / t_kern / 1e9
+    traffic = load_traffic() if cfg_id == 2 else None
     del tb
     torch.cuda.empty_cache()
 
@@ -310,8 +425,10 @@ def main(argv=None):
         "gbps": nbytes / t_step / 1e9,
         "pct_peak": 100.0 * nbytes / t_step / 1e9 / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "topk_rows_kernel", "kernel_us": t_kern * 1e6,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic["traffic_bytes"] if traffic else None,
+                     "kernel": traffic["kernel"] if traffic else "dsel_topk (one kernel per call)",
+                     "kernel_us": t_kern * 1e6,
                      "algorithmic_bytes_per_launch": nbytes},
     }
 
