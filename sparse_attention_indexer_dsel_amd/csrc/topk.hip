@@ -13,29 +13,28 @@
 //   * a key is the value's bits mapped to an unsigned integer whose order is
 //     the ranking order (sign-magnitude -> offset binary, so -0 and +0 meet;
 //     every NaN -> the largest key); bf16 keys are formed two per VGPR with
-//     packed 16-bit integer ops;
-//   * pass A streams the workgroup's columns from HBM with coalesced 16-byte
-//     loads, several in flight per thread, and histograms an 11-bit first
-//     digit in LDS; it keeps nothing in VGPRs, so many workgroups fit on a
-//     compute unit and hide the load latency;
-//   * pass B re-reads the columns from cache, each thread a contiguous
-//     segment held in VGPRs; the bin holding the k-th largest key fixes a
-//     threshold T1 and only the C candidates with key >= T1 (about k plus
-//     one bin) are compacted, in column order, into an LDS list (one
-//     workgroup scan);
+//     packed 16-bit integer ops.  The map is invertible except at the +-0
+//     and NaN keys, so a selected value is rebuilt from its key and only
+//     those two keys re-read the row;
+//   * a workgroup holds its columns in VGPRs in the coalesced layout (load j
+//     of thread t holds the 16 bytes at column (j*NT + t)*VEC of its range),
+//     all loads issued at once; it histograms an 11-bit first digit in LDS;
+//   * the bin holding the k-th largest key fixes a threshold T1; only the C
+//     candidates with key >= T1 (about k plus one bin) are compacted, in
+//     column order, into an LDS list of (key, column) entries;
 //   * the rest of the radix select (5 more bits for bf16, 11+10 for fp32)
-//     and the output run on that short list: every key > T plus the first
-//     `need` keys == T in column order, written in column order in rounds
-//     of 256 so the stores coalesce; the output is ascending by
-//     construction and no sort is run;
-//   * a row too long for one workgroup, or too few rows to fill the GPU, is
-//     split over G workgroups: their pass-A histograms meet in a per-row
-//     workspace slot (device-scope relaxed atomics and one rendezvous); each
-//     stages its candidates there and the last workgroup to finish runs the
-//     exact selection for the row;
+//     runs on that short list; the selection, every key > T plus the first
+//     `need` keys == T in column order, is written in column order: each
+//     wave owns a contiguous quarter of the list and ranks its entries with
+//     ballots, so the write needs one cross-wave exchange and no more
+//     barriers.  The output is ascending by construction; no sort is run;
+//   * rows too long for one workgroup, or too few rows to fill the GPU, are
+//     split over G workgroups: their histograms meet in a per-row workspace
+//     slot (device-scope relaxed atomics, one rendezvous); each stages its
+//     candidates there and the last workgroup to finish runs the selection;
 //   * if a row's candidate list would not fit (massive ties at the
-//     threshold), the radix select finishes over the segments in VGPRs
-//     instead (slower, same result).
+//     threshold), the radix select finishes over the keys still in VGPRs
+//     (slower, same result).
 #include "dsel_internal.h"
 
 namespace dsel {
@@ -43,7 +42,6 @@ namespace {
 
 constexpr int NT = kTopkThreads;
 constexpr int NWAVE = NT / 64;
-constexpr int UNROLL_A = 4;  // pass-A 16-byte loads in flight per thread
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 // Hide a value from the optimiser so a comparison repeated after a
@@ -97,6 +95,15 @@ struct Bf16Key {
     __device__ static uint32_t clear_elem(uint32_t kw, int h) {
         return h ? (kw & 0x0000FFFFu) : (kw & 0xFFFF0000u);
     }
+    // raw word with the elements at and past `valid` (0..2 in this word) zeroed
+    __device__ static uint32_t keep_raw(uint32_t w, int valid) {
+        return valid >= 2 ? w : (valid == 1 ? (w & 0xFFFFu) : 0u);
+    }
+    // keys whose value cannot be rebuilt: +-0 and NaN
+    __device__ static bool ambiguous(uint32_t key) { return key == 0x8000u || key == 0xFFFFu; }
+    __device__ static uint32_t value_bits(uint32_t key) {
+        return key >= 0x8000u ? key - 0x8000u : (0x8000u - key) | 0x8000u;
+    }
 };
 
 struct F32Key {
@@ -119,6 +126,13 @@ struct F32Key {
     }
     __device__ static uint32_t elem(uint32_t kw, int) { return kw; }
     __device__ static uint32_t clear_elem(uint32_t, int) { return 0u; }
+    __device__ static uint32_t keep_raw(uint32_t w, int valid) { return valid >= 1 ? w : 0u; }
+    __device__ static bool ambiguous(uint32_t key) {
+        return key == 0x80000000u || key == 0xFFFFFFFFu;
+    }
+    __device__ static uint32_t value_bits(uint32_t key) {
+        return key >= 0x80000000u ? key - 0x80000000u : (0x80000000u - key) | 0x80000000u;
+    }
 };
 
 // Inclusive prefix sum over a wave64 with DPP row shifts and row broadcasts.
@@ -132,9 +146,12 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);
+// Lanes below this one whose bit is set in a wave mask.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
+
+__device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
 // Inclusive prefix sum over the workgroup in thread order; *total receives
 // the workgroup's sum.
@@ -153,17 +170,6 @@ __device__ uint32_t block_incl_scan(uint32_t x, uint32_t *s_red, uint32_t *total
     __syncthreads();
     if (total) *total = tot;
     return w + off;
-}
-
-__device__ uint32_t block_sum(uint32_t x, uint32_t *s_red) {
-    const uint32_t w = wave_sum(x);
-    if ((tid() & 63) == 0) s_red[tid() >> 6] = w;
-    __syncthreads();
-    uint32_t tot = 0;
-#pragma unroll
-    for (int i = 0; i < NWAVE; ++i) tot += s_red[i];
-    __syncthreads();
-    return tot;
 }
 
 struct Digit {
@@ -210,14 +216,19 @@ __device__ Digit find_digit(const uint32_t *hist, int nb, uint32_t need, uint32_
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t ld_agent64(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent64(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t add_agent(uint32_t *p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void drain_memory() { __builtin_amdgcn_s_waitcnt(0); }
-
 
 // Rendezvous of the G workgroups of one row.  `ctr` counts arrivals over the
 // whole launch; the m-th rendezvous completes at m*G.  The wait is bounded:
@@ -240,16 +251,48 @@ __device__ void row_rendezvous(uint32_t *ctr, uint32_t target, uint32_t *err) {
     __syncthreads();
 }
 
+// Publish this workgroup's histogram bins [0, nb) into a row's global
+// histogram (nonzero bins only).
+__device__ __forceinline__ void merge_histogram(const uint32_t *hist, uint32_t *ghist, int nb) {
+    for (int b = tid(); b < nb; b += NT) {
+        const uint32_t h = hist[b];
+        if (h) add_agent(ghist + b, h);
+    }
+}
+
+// Read a row's global histogram bins [0, nb) (nb <= kBins) into LDS, all
+// loads in flight at once.
+__device__ __forceinline__ void fetch_histogram(const uint32_t *ghist, uint32_t *hist, int nb) {
+    constexpr int R = kBins / NT;
+    uint32_t v[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int b = i * NT + tid();
+        v[i] = b < nb ? ld_agent(ghist + b) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int b = i * NT + tid();
+        if (b < nb) hist[b] = v[i];
+    }
+}
+
+// One selected element: its column at output slot `pos`, and its value,
+// rebuilt from the key (read back from the row only for +-0 and NaN keys,
+// whose bits the key does not determine).
 template <class K>
-__device__ __forceinline__ void emit(const TopkArgs &a, int64_t row, uint32_t pos, int64_t col,
-                                     const typename K::raw_t *xr) {
+__device__ __forceinline__ void emit(const TopkArgs &a, int64_t row, uint32_t pos, uint32_t col,
+                                     uint32_t key, const typename K::raw_t *xr) {
     if (pos >= (uint32_t)a.k) return;  // never write past the row's k slots
     if (a.idx64)
-        reinterpret_cast<int64_t *>(a.out_idx)[row * a.idx_stride + pos] = col;
+        reinterpret_cast<int64_t *>(a.out_idx)[row * a.idx_stride + pos] = (int64_t)col;
     else
         reinterpret_cast<int32_t *>(a.out_idx)[row * a.idx_stride + pos] = (int32_t)col;
-    if (a.ret_val)
-        reinterpret_cast<typename K::raw_t *>(a.out_val)[row * a.val_stride + pos] = xr[col];
+    if (a.ret_val) {
+        const typename K::raw_t v =
+            K::ambiguous(key) ? xr[col] : (typename K::raw_t)K::value_bits(key);
+        reinterpret_cast<typename K::raw_t *>(a.out_val)[row * a.val_stride + pos] = v;
+    }
 }
 
 // Rows with n <= k: columns 0..n-1 in order, then padding.  Workgroup c of G
@@ -292,8 +335,8 @@ __device__ void write_short_row(const TopkArgs &a, int64_t row, int64_t n, int c
 // Range-checked view of one row's first `end` columns for raw buffer loads:
 // bytes at or past the (dword-rounded) end read as zero without touching
 // memory, so every 16-byte load is unconditional.  The rounding keeps a
-// partly valid dword whole; the element past the end is cleared by the
-// caller (clear_tail).
+// partly valid dword whole; the element past the end is masked by the
+// caller before it is looked at.
 template <class K>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_view(const typename K::raw_t *xr, int64_t end) {
     const int64_t bytes = end > 0 ? ((end * (int64_t)sizeof(typename K::raw_t) + 3) & ~(int64_t)3) : 0;
@@ -336,6 +379,34 @@ __device__ __forceinline__ void clear_tail(uint32_t *kw, int valid) {
             kw[q] = (q * K::EPW + h >= valid) ? K::clear_elem(kw[q], h) : kw[q];
 }
 
+// Keys of a workgroup's loads in the coalesced layout (load j of thread t
+// holds the VEC columns from (j*NT + t)*VEC of a range of `len` columns).
+// Columns at or past len get key 0 and are not probed for NaN.  Returns
+// whether this thread saw a NaN.
+template <class K, int LOADS>
+__device__ __forceinline__ uint32_t keys_of_loads(const uint4 (&v)[LOADS], int len,
+                                                  uint32_t (&kw)[LOADS * 4]) {
+    constexpr int VEC = K::VEC, EPW = K::EPW;
+    const int full = len / (NT * VEC);  // loads valid for every thread (uniform)
+    uint32_t nan = 0;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        uint4 x = v[j];
+        int valid = VEC;
+        if (j >= full) {
+            valid = len - (j * NT + tid()) * VEC;
+            valid = valid < 0 ? 0 : (valid > VEC ? VEC : valid);
+            x.x = K::keep_raw(x.x, valid);
+            x.y = K::keep_raw(x.y, valid - EPW);
+            x.z = K::keep_raw(x.z, valid - 2 * EPW);
+            x.w = K::keep_raw(x.w, valid - 3 * EPW);
+        }
+        nan |= keys_of<K>(x, &kw[4 * j]) ? 1u : 0u;
+        if (j >= full) clear_tail<K>(&kw[4 * j], valid);
+    }
+    return nan;
+}
+
 // Histogram the first digit of every element of a key word.
 template <class K>
 __device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t kw) {
@@ -354,156 +425,326 @@ __device__ __forceinline__ void hist_add_masked(uint32_t *hist, uint32_t kw, uin
     }
 }
 
-// Pass A of a split row: stream columns [lo, hi) with coalesced 16-byte loads
-// (UNROLL_A per thread in flight) and histogram the first digit.  Returns
-// whether this thread saw a NaN.
-template <class K>
-__device__ uint32_t first_digit_histogram(const typename K::raw_t *xr, int64_t lo, int64_t hi,
-                                          uint32_t *hist) {
-    constexpr int VEC = K::VEC, U = UNROLL_A;
-    const int t = tid();
-    const uint32_t spare = kBins + (t & 63);
-    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, hi);
-    const int64_t span = (int64_t)NT * VEC;  // columns per workgroup-wide load
-    const int64_t len = hi > lo ? hi - lo : 0;
-    const int64_t full = len / span;         // loads valid for every thread
-    uint32_t nan = 0;
-    int64_t j = 0;
-    for (; j + U <= full; j += U) {
-        uint4 v[U];
+// First-digit histogram of a workgroup's keys (hist zeroed, kBins + 64 bins).
+template <class K, int LOADS>
+__device__ __forceinline__ void first_digit_histogram(const uint32_t (&kw)[LOADS * 4], int len,
+                                                      uint32_t *hist) {
+    constexpr int SPAN = NT * K::VEC;
+    const int full = len / SPAN, any = (len + SPAN - 1) / SPAN;
+    const uint32_t spare = kBins + (tid() & 63);
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = load_vec<K>(view, lo + (j + u) * span + (int64_t)t * VEC);
+    for (int j = 0; j < LOADS; ++j) {
+        if (j < full) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            uint32_t kw[4];
-            nan |= keys_of<K>(v[u], kw) ? 1u : 0u;
+            for (int q = 0; q < 4; ++q) hist_add<K>(hist, kw[4 * j + q]);
+        } else if (j < any) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) hist_add<K>(hist, kw[q]);
+            for (int q = 0; q < 4; ++q) hist_add_masked<K>(hist, kw[4 * j + q], spare);
         }
     }
-    for (; j < full; ++j) {
-        uint32_t kw[4];
-        nan |= keys_of<K>(load_vec<K>(view, lo + j * span + (int64_t)t * VEC), kw) ? 1u : 0u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hist_add<K>(hist, kw[q]);
-    }
-    if (full * span < len) {  // the last, partly valid load
-        const int64_t p = lo + full * span + (int64_t)t * VEC;
-        uint32_t kw[4];
-        nan |= keys_of<K>(load_vec<K>(view, p), kw) ? 1u : 0u;
-        const int64_t valid = hi - p;
-        clear_tail<K>(kw, valid < 0 ? 0 : (valid > VEC ? VEC : (int)valid));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hist_add_masked<K>(hist, kw[q], spare);
-    }
-    return nan;
 }
 
-// Pass B load of a split row: this thread's contiguous segment [s0, s1) (at
-// most SL vectors) into VGPRs as keys; slots past s1 get key 0.
-template <class K, int SL>
-__device__ __forceinline__ void load_segment(const typename K::raw_t *xr, int64_t s0, int64_t s1,
-                                             uint32_t (&kw)[SL * 4]) {
-    constexpr int VEC = K::VEC;
-    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, s1);
-    uint4 v[SL];
-#pragma unroll
-    for (int j = 0; j < SL; ++j) v[j] = load_vec<K>(view, s0 + (int64_t)j * VEC);
-#pragma unroll
-    for (int j = 0; j < SL; ++j) {
-        keys_of<K>(v[j], &kw[4 * j]);
-        const int64_t valid = s1 - (s0 + (int64_t)j * VEC);
-        clear_tail<K>(&kw[4 * j], valid < 0 ? 0 : (valid > VEC ? VEC : (int)valid));
-    }
-}
-
-// Finish a row from its candidate list (entries (key, column) in column
-// order; every key's first digit is >= d1.v): resolve the remaining digits
-// of the boundary key among the candidates in the boundary bin, then write
-// the selection in column order, NT candidates per round so stores coalesce.
-template <class K>
-__device__ void select_and_write(const TopkArgs &a, int64_t row, const uint2 *ent, uint32_t C,
-                                 Digit d1, uint32_t *s_hist, uint32_t *s_red, uint32_t *s_out,
-                                 const typename K::raw_t *xr) {
+// Compact the candidates (key >= T1) of a workgroup's keys into ent[0, run)
+// in column order (entry = (key, col0 + column)); returns run.  Every element
+// is written once, the non-candidates to this lane's spare entry at
+// ent[cap + lane], so the loop has no branches.  wtot holds LP*NWAVE words.
+template <class K, int LOADS>
+__device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4], int len,
+                                                       uint32_t T1, uint32_t *wtot, uint2 *ent,
+                                                       uint32_t cap, uint32_t col0) {
+    constexpr int VEC = K::VEC, EPW = K::EPW, LP = (LOADS + 1) / 2, SPAN = NT * VEC;
     const int t = tid();
-    uint32_t need = (uint32_t)a.k - d1.above;
-    uint32_t P = d1.v;
-    int s = K::SH1;
-    if (d1.cnt != need) {
-#pragma unroll 1
-        for (int pass = 1; pass < K::NPASS; ++pass) {
-            const int d = K::digit(pass);
-            const int sh = s - d;
-            const uint32_t dmask = (1u << d) - 1u;
-            const int nb = 1 << d;
-            for (int b = t; b < nb; b += NT) s_hist[b] = 0;
-            __syncthreads();
-            for (uint32_t i = t; i < C; i += NT) {
-                const uint32_t key = ent[i].x;
-                if ((key >> s) == P) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
+    const int lane = t & 63, wid = t >> 6;
+    const int any = (len + SPAN - 1) / SPAN;
+    // per-load counts, two loads per word (each count <= 512 per wave)
+    uint32_t pk[LP];
+#pragma unroll
+    for (int i = 0; i < LP; ++i) pk[i] = 0;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        if (j < any) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int h = 0; h < EPW; ++h) m += K::elem(kw[4 * j + q], h) >= T1 ? 1u : 0u;
+            pk[j >> 1] |= m << ((j & 1) * 16);
+        }
+    }
+    uint32_t ex[LP];
+#pragma unroll
+    for (int i = 0; i < LP; ++i) {
+        const uint32_t incl = wave_incl_scan(pk[i]);
+        ex[i] = incl - pk[i];
+        if (lane == 63) wtot[i * NWAVE + wid] = incl;
+    }
+    __syncthreads();
+    const uint32_t T1w = opaque(T1);
+#pragma unroll
+    for (int w = 0; w < LOADS * 4; ++w) kw[w] = opaque(kw[w]);
+    const uint32_t spare = cap + lane;
+    uint32_t run = 0;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        if (j < any) {
+            const int i = j >> 1, sh = (j & 1) * 16;
+            uint32_t tot = 0, before = 0;
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) {
+                const uint32_t v = (wtot[i * NWAVE + w] >> sh) & 0xFFFFu;
+                tot += v;
+                before += (w < wid) ? v : 0u;
             }
-            __syncthreads();
-            const Digit dg = find_digit(s_hist, nb, need, s_red, s_out);
-            need -= dg.above;
-            P = (P << d) | dg.v;
-            s = sh;
-            if (dg.cnt == need) break;
+            uint32_t pos = run + before + ((ex[i] >> sh) & 0xFFFFu);
+            run += tot;
+            const uint32_t p = col0 + (uint32_t)(j * NT + t) * VEC;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int h = 0; h < EPW; ++h) {
+                    const uint32_t key = K::elem(kw[4 * j + q], h);
+                    const bool cand = key >= T1w;
+                    ent[cand ? pos : spare] = make_uint2(key, p + q * EPW + h);
+                    pos += cand ? 1u : 0u;
+                }
         }
     }
-    // every candidate whose top bits (key >> s) exceed P is taken, plus the
-    // first `need` equal to P
-    uint32_t g0 = 0, q0 = 0;
-    for (uint32_t r0 = 0; r0 < C; r0 += NT) {
-        const uint32_t i = r0 + t;
-        const bool in = i < C;
+    __syncthreads();
+    return run;
+}
+
+// The boundary of a selection: every key whose top bits (key >> s) exceed P
+// is taken, plus the first `need` (in column order) whose top bits equal P.
+struct Bound {
+    uint32_t P;
+    int s;
+    uint32_t need;
+};
+
+// Resolve the digits after the first among the candidate list's entries
+// (every entry's first digit is >= d1.v).
+template <class K>
+__device__ Bound refine_on_list(const uint2 *ent, uint32_t C, Digit d1, uint32_t k,
+                                uint32_t *s_hist, uint32_t *s_red, uint32_t *s_out) {
+    const int t = tid();
+    Bound b{d1.v, K::SH1, k - d1.above};
+    if (d1.cnt == b.need) return b;  // the boundary bin is taken whole
+#pragma unroll 1
+    for (int pass = 1; pass < K::NPASS; ++pass) {
+        const int d = K::digit(pass);
+        const int sh = b.s - d;
+        const uint32_t dmask = (1u << d) - 1u;
+        const int nb = 1 << d;
+        for (int i = t; i < nb; i += NT) s_hist[i] = 0;
+        __syncthreads();
+        for (uint32_t i = t; i < C; i += NT) {
+            const uint32_t key = ent[i].x;
+            if ((key >> b.s) == b.P) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
+        }
+        __syncthreads();
+        const Digit dg = find_digit(s_hist, nb, b.need, s_red, s_out);
+        b.need -= dg.above;
+        b.P = (b.P << d) | dg.v;
+        b.s = sh;
+        if (dg.cnt == b.need) break;
+    }
+    return b;
+}
+
+// Write the selection from a column-ordered candidate list.  Wave w owns
+// entries [w*Q, (w+1)*Q) (Q a multiple of 64); ranks within a wave come from
+// ballots, and one exchange of the waves' counts (through s_red) gives each
+// wave its starting ranks.
+template <class K>
+__device__ void write_from_list(const TopkArgs &a, int64_t row, const uint2 *ent, uint32_t C,
+                                Bound b, uint32_t *s_red, const typename K::raw_t *xr) {
+    const int t = tid();
+    const int lane = t & 63, wid = t >> 6;
+    const uint32_t Q = (C + NT - 1) / NT * 64;
+    const uint32_t b0 = (uint32_t)wid * Q;
+    const uint32_t b1 = min(C, b0 + Q);
+    uint32_t g = 0, q = 0;
+    for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
+        const uint32_t i = i0 + (uint32_t)lane;
+        const bool in = i < b1;
+        const uint32_t pre = in ? (ent[i].x >> b.s) : 0u;
+        g += popc64(__ballot(in && pre > b.P));
+        q += popc64(__ballot(in && pre == b.P));
+    }
+    if (lane == 0) s_red[wid] = g | (q << 16);  // each count <= 8192
+    __syncthreads();
+    uint32_t gb = 0, qb = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+        const uint32_t v = s_red[w];
+        gb += w < wid ? (v & 0xFFFFu) : 0u;
+        qb += w < wid ? (v >> 16) : 0u;
+    }
+    __syncthreads();
+    for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
+        const uint32_t i = i0 + (uint32_t)lane;
+        const bool in = i < b1;
         const uint2 e = in ? ent[i] : make_uint2(0u, 0u);
-        const uint32_t pre = e.x >> s;
-        const bool gt = in && pre > P;
-        const bool eq = in && pre == P;
-        const uint32_t mine = (gt ? 1u : 0u) | (eq ? 0x10000u : 0u);
-        uint32_t tot;
-        const uint32_t ex = block_incl_scan(mine, s_red, &tot) - mine;
-        const uint32_t gb = g0 + (ex & 0xFFFFu), qb = q0 + (ex >> 16);
+        const uint32_t pre = e.x >> b.s;
+        const bool gt = in && pre > b.P;
+        const bool eq = in && pre == b.P;
+        const uint64_t mg = __ballot(gt), mq = __ballot(eq);
+        const uint32_t rg = gb + lanes_below(mg), rq = qb + lanes_below(mq);
         if (gt)
-            emit<K>(a, row, gb + min(qb, need), e.y, xr);
-        else if (eq && qb < need)
-            emit<K>(a, row, gb + qb, e.y, xr);
-        g0 += tot & 0xFFFFu;
-        q0 += tot >> 16;
+            emit<K>(a, row, rg + min(rq, b.need), e.y, e.x, xr);
+        else if (eq && rq < b.need)
+            emit<K>(a, row, rg + rq, e.y, e.x, xr);
+        gb += popc64(mg);
+        qb += popc64(mq);
     }
 }
 
-// Compact the candidates (key >= T1) of a thread's contiguous key segment
-// into ent[pos ..] in column order; every element is written once, the
-// non-candidates to this lane's spare slot past the list, so the loop has
-// no branches.
-template <class K, int W>
-__device__ __forceinline__ void compact_segment(const uint32_t (&kw)[W], uint32_t T1, uint32_t pos,
-                                                uint32_t col0, uint32_t spare, uint2 *ent) {
+// ---- slow path: the candidate list would not fit (massive ties at the
+// threshold).  The radix select finishes over the range's keys re-read from
+// cache one load at a time, so the rare path adds no VGPRs to the common one.
+
+// Keys of load j of a range of `len` columns starting at column `base` of a
+// row view (coalesced layout; columns at or past len get key 0).
+template <class K>
+__device__ __forceinline__ void reload_keys(__amdgpu_buffer_rsrc_t view, int64_t base, int len,
+                                            int j, uint32_t (&w4)[4]) {
+    constexpr int VEC = K::VEC, EPW = K::EPW;
+    const int p = (j * NT + tid()) * VEC;
+    uint4 x = load_vec<K>(view, base + p);
+    int valid = len - p;
+    valid = valid < 0 ? 0 : (valid > VEC ? VEC : valid);
+    x.x = K::keep_raw(x.x, valid);
+    x.y = K::keep_raw(x.y, valid - EPW);
+    x.z = K::keep_raw(x.z, valid - 2 * EPW);
+    x.w = K::keep_raw(x.w, valid - 3 * EPW);
+    keys_of<K>(x, w4);
+    clear_tail<K>(w4, valid);
+}
+
+// Refine-pass histogram: the next digit ((key >> sh) & dmask) of every key
+// whose top bits (key >> s) equal P.
+template <class K>
+__device__ void refine_histogram_stream(__amdgpu_buffer_rsrc_t view, int64_t base, int len,
+                                        uint32_t P, int s, int sh, uint32_t dmask,
+                                        uint32_t *hist) {
+    const int loads = (len + NT * K::VEC - 1) / (NT * K::VEC);
+#pragma unroll 1
+    for (int j = 0; j < loads; ++j) {
+        uint32_t w4[4];
+        reload_keys<K>(view, base, len, j, w4);
 #pragma unroll
-    for (int w = 0; w < W; ++w)
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int h = 0; h < K::EPW; ++h) {
+                const uint32_t key = K::elem(w4[q], h);
+                if (key && (key >> s) == P) atomicAdd(&hist[(key >> sh) & dmask], 1u);
+            }
+    }
+}
+
+// Counts of taken-above (top bits > P) and equal (== P) keys in four key
+// words, packed (equal << 16 | above).
+template <class K>
+__device__ __forceinline__ uint32_t load_counts(const uint32_t (&w4)[4], Bound b) {
+    uint32_t g = 0, q = 0;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
         for (int h = 0; h < K::EPW; ++h) {
-            const uint32_t key = K::elem(kw[w], h);
-            const bool cand = key >= T1;
-            ent[cand ? pos : spare] = make_uint2(key, col0 + w * K::EPW + h);
-            pos += cand ? 1u : 0u;
+            const uint32_t key = K::elem(w4[qq], h);
+            const uint32_t pre = key >> b.s;
+            g += (key && pre > b.P) ? 1u : 0u;
+            q += (key && pre == b.P) ? 1u : 0u;
         }
+    return g | (q << 16);
 }
 
-template <class K, int MAXL>
+// This thread's packed counts over the whole range.
+template <class K>
+__device__ uint32_t range_counts(__amdgpu_buffer_rsrc_t view, int64_t base, int len, Bound b) {
+    const int loads = (len + NT * K::VEC - 1) / (NT * K::VEC);
+    uint32_t mine = 0;
+#pragma unroll 1
+    for (int j = 0; j < loads; ++j) {
+        uint32_t w4[4];
+        reload_keys<K>(view, base, len, j, w4);
+        mine += load_counts<K>(w4, b);
+    }
+    return mine;
+}
+
+// Write the selection of the range (columns base + ...).  gt0 / eq0 are the
+// taken-above and equal counts of the columns before the range; each load is
+// one workgroup scan.
+template <class K>
+__device__ void write_from_stream(const TopkArgs &a, int64_t row, __amdgpu_buffer_rsrc_t view,
+                                  int64_t base, int len, Bound b, uint32_t gt0, uint32_t eq0,
+                                  uint32_t *s_red, const typename K::raw_t *xr) {
+    constexpr int VEC = K::VEC, EPW = K::EPW;
+    const int loads = (len + NT * VEC - 1) / (NT * VEC);
+    uint32_t gb = gt0, qb = eq0;
+#pragma unroll 1
+    for (int j = 0; j < loads; ++j) {
+        uint32_t w4[4];
+        reload_keys<K>(view, base, len, j, w4);
+        const uint32_t mine = load_counts<K>(w4, b);
+        uint32_t tot;
+        const uint32_t ex = block_incl_scan(mine, s_red, &tot) - mine;
+        uint32_t g1 = gb + (ex & 0xFFFFu), q1 = qb + (ex >> 16);
+        const uint32_t p = (uint32_t)(base + (int64_t)(j * NT + tid()) * VEC);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int h = 0; h < EPW; ++h) {
+                const uint32_t key = K::elem(w4[qq], h);
+                const uint32_t pre = key >> b.s;
+                const uint32_t col = p + qq * EPW + h;
+                if (key && pre > b.P) {
+                    emit<K>(a, row, g1 + min(q1, b.need), col, key, xr);
+                    ++g1;
+                } else if (key && pre == b.P) {
+                    if (q1 < b.need) emit<K>(a, row, g1 + q1, col, key, xr);
+                    ++q1;
+                }
+            }
+        gb += tot & 0xFFFFu;
+        qb += tot >> 16;
+    }
+}
+
+__device__ __forceinline__ int64_t valid_length(const TopkArgs &a, int64_t row) {
+    int64_t n = a.cols;
+    if (a.row_end) {
+        const int64_t e = a.row_end[row];
+        n = e < 0 ? 0 : (e > a.cols ? a.cols : e);
+    }
+    return n;
+}
+
+// Shared memory of the top-k kernels (the histogram has one spare bin per
+// lane past kBins).
+template <int LP>
+struct TopkLds {
+    uint32_t hist[kBins + 64];
+    uint32_t wtot[LP * NWAVE];
+    uint32_t red[NWAVE];
+    uint32_t out[8];
+};
+
+// ---------------------------------------------------------------------------
+// Split rows: G workgroups per row, workgroup c owning columns
+// [c*chunk, (c+1)*chunk) of the valid prefix, held in VGPRs.
+// ---------------------------------------------------------------------------
+template <class K, int EPT>
 __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     using raw_t = typename K::raw_t;
     constexpr int VEC = K::VEC;
-    constexpr int EPW = K::EPW;
-    constexpr int SL = MAXL / VEC;  // 16-byte vectors in one thread's segment
-    constexpr int W = SL * 4;       // key words in one thread's segment
-    static_assert(MAXL % VEC == 0, "segment must hold whole vectors");
+    constexpr int LOADS = EPT / VEC;
+    constexpr int LP = (LOADS + 1) / 2;
+    static_assert(EPT % VEC == 0, "EPT must be a multiple of the vector width");
 
     extern __shared__ uint2 s_ent[];  // candidate list (cap entries) + one spare per lane
-    __shared__ uint32_t s_hist[kBins + 64];
-    __shared__ uint32_t s_red[NWAVE];
-    __shared__ uint32_t s_out[8];
+    __shared__ TopkLds<LP> L;
 
     const int t = tid();
     const int G = a.G;
@@ -512,11 +753,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     const int64_t row = a.row0 + lrow;
     if (row >= a.rows) return;  // uniform over the row's workgroups
 
-    int64_t n = a.cols;
-    if (a.row_end) {
-        const int64_t e = a.row_end[row];
-        n = e < 0 ? 0 : (e > a.cols ? a.cols : e);
-    }
+    const int64_t n = valid_length(a, row);
     const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
     if (n <= a.k) {
         write_short_row<K>(a, row, n, c, G, xr);
@@ -528,62 +765,45 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     uint32_t *err = a.ws;
     uint32_t *ghist = slot + kSlotHeadWords;
     uint32_t *gcnt = ghist + kMaxPasses * kBins;
-    uint32_t *stage_key = gcnt + 4 * G;
-    uint32_t *stage_col = stage_key + cap;
+    uint64_t *stage = reinterpret_cast<uint64_t *>(gcnt + 4 * G);
 
-    // this workgroup's columns [lo, hi), and this thread's segment [s0, s1)
+    // ---- this workgroup's columns into VGPRs; first-digit histogram --------
     const int64_t lo = (int64_t)c * a.chunk;
     const int64_t hi = min(lo + a.chunk, n);
-    const int64_t len = hi > lo ? hi - lo : 0;
-    const int64_t L = ((len + NT - 1) / NT + VEC - 1) / VEC * VEC;  // <= MAXL
-    const int64_t s0 = lo + (int64_t)t * L;
-    const int64_t s1 = min(s0 + L, hi);
-
-    // ---- pass A: first-digit histogram (HBM, coalesced) ---------------------
-    for (int b = t; b < kBins + 64; b += NT) s_hist[b] = 0;
-    __syncthreads();
-    const uint32_t thread_nan = first_digit_histogram<K>(xr, lo, hi, s_hist);
-    const uint32_t block_nan = __syncthreads_or((int)thread_nan) ? 1u : 0u;
-
-    // ---- pass B load: this thread's segment into VGPRs (from cache); the
-    // loads are in flight across the rendezvous
-    uint32_t kw[W];
-    load_segment<K, SL>(xr, s0, s1, kw);
-
-    uint32_t nren = 0;
-    for (int b = t; b < kBins; b += NT) {
-        const uint32_t h = s_hist[b];
-        if (h) add_agent(ghist + b, h);
+    const int len = hi > lo ? (int)(hi - lo) : 0;
+    uint32_t kw[LOADS * 4];
+    uint32_t nan;
+    {
+        const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
+        uint4 v[LOADS];
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) v[j] = load_vec<K>(view, lo + (int64_t)(j * NT + t) * VEC);
+        for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
+        nan = keys_of_loads<K, LOADS>(v, len, kw);
     }
-    row_rendezvous(slot, (++nren) * (uint32_t)G, err);
-    for (int b = t; b < kBins; b += NT) s_hist[b] = ld_agent(ghist + b);
+    const uint32_t block_nan = __syncthreads_or((int)nan) ? 1u : 0u;
+    first_digit_histogram<K, LOADS>(kw, len, L.hist);
     __syncthreads();
-    const Digit d1 = find_digit(s_hist, kBins, (uint32_t)a.k, s_red, s_out);
+
+    // ---- merge the histograms of the row's workgroups ----------------------
+    merge_histogram(L.hist, ghist, kBins);
+    uint32_t nren = 1;
+    row_rendezvous(slot, (uint32_t)G, err);
+    fetch_histogram(ghist, L.hist, kBins);
+    __syncthreads();
+    const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
     const uint32_t C = d1.above + d1.cnt;
 
     if (C <= cap) {
-        // ---- compaction of the candidates (key >= T1) in column order -------
-        const uint32_t T1 = d1.v << K::SH1;
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int w = 0; w < W; ++w)
-#pragma unroll
-            for (int h = 0; h < EPW; ++h) cnt += K::elem(kw[w], h) >= T1 ? 1u : 0u;
-        uint32_t run;
-        const uint32_t pos = block_incl_scan(cnt, s_red, &run) - cnt;
-#pragma unroll
-        for (int w = 0; w < W; ++w) kw[w] = opaque(kw[w]);
-        compact_segment<K, W>(kw, opaque(T1), pos, (uint32_t)(s0 - lo), cap + (t & 63), s_ent);
+        // ---- stage this workgroup's candidates; the last one finishes ------
+        const uint32_t run =
+            compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, s_ent, cap, 0u);
+        if (t == 0) L.out[4] = run ? add_agent(slot + 2, run) : 0u;
         __syncthreads();
-        // run == this workgroup's candidate count
-
-        // ---- stage candidates; the last workgroup finishes the row ----------
-        if (t == 0) s_out[4] = add_agent(slot + 2, run);
-        __syncthreads();
-        const uint32_t off = s_out[4];
+        const uint32_t off = L.out[4];
         for (uint32_t i = t; i < run; i += NT) {
-            st_agent(stage_key + off + i, s_ent[i].x);
-            st_agent(stage_col + off + i, s_ent[i].y + (uint32_t)lo);
+            const uint2 e = s_ent[i];
+            st_agent64(stage + off + i, (uint64_t)e.x | ((uint64_t)(e.y + (uint32_t)lo) << 32));
         }
         if (t == 0) {
             st_agent(gcnt + 4 * c + 0, off);
@@ -592,51 +812,65 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         }
         drain_memory();
         __syncthreads();
-        if (t == 0) s_out[3] = (add_agent(slot + 1, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
+        if (t == 0) L.out[3] = (add_agent(slot + 1, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
         __syncthreads();
-        if (!s_out[3]) return;
+        if (!L.out[3]) return;
 
-        // Last workgroup: every other one has staged its candidates.  Pull
-        // them into LDS in workgroup order (= column order).
-        uint32_t nn = 0;
-        for (int i = t; i < G; i += NT) nn |= ld_agent(gcnt + 4 * i + 2);
-        const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
-        // destination offsets (exclusive prefix of the counts) in s_hist[0, G),
-        // source offsets in s_hist[kMaxSplit, kMaxSplit + G)
-        uint32_t base = 0;
+        // Last workgroup: every other one has staged its candidates.  Its
+        // list position = exclusive prefix of the counts in workgroup
+        // (= column) order; the staged position comes from the workgroup's
+        // staging offset.  L.hist[0, G) <- list starts, L.hist[kMaxSplit, +G)
+        // <- staging offsets (G <= kMaxSplit <= kBins / 2).
+        uint32_t nn = 0, base = 0;
         for (int i0 = 0; i0 < G; i0 += NT) {
             const int i = i0 + t;
-            const uint32_t cnt_i = i < G ? ld_agent(gcnt + 4 * i + 1) : 0u;
-            uint32_t tot;
-            const uint32_t incl = block_incl_scan(cnt_i, s_red, &tot);
+            uint32_t cnt_i = 0, off_i = 0;
             if (i < G) {
-                s_hist[i] = base + incl - cnt_i;
-                s_hist[kMaxSplit + i] = ld_agent(gcnt + 4 * i + 0);
+                off_i = ld_agent(gcnt + 4 * i + 0);
+                cnt_i = ld_agent(gcnt + 4 * i + 1);
+                nn |= ld_agent(gcnt + 4 * i + 2);
+            }
+            uint32_t tot;
+            const uint32_t incl = block_incl_scan(cnt_i, L.red, &tot);
+            if (i < G) {
+                L.hist[i] = base + incl - cnt_i;
+                L.hist[kMaxSplit + i] = off_i;
             }
             base += tot;
         }
-        __syncthreads();
-        for (uint32_t idx = t; idx < C; idx += NT) {
-            int lo_b = 0, hi_b = G - 1;  // last workgroup whose range starts at or before idx
-            while (lo_b < hi_b) {
-                const int mid = (lo_b + hi_b + 1) >> 1;
-                if (s_hist[mid] <= idx)
-                    lo_b = mid;
-                else
-                    hi_b = mid - 1;
+        const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
+        constexpr int BATCH = 8;
+        for (uint32_t i0 = 0; i0 < C; i0 += BATCH * NT) {
+            uint64_t v[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const uint32_t idx = i0 + u * NT + t;
+                v[u] = 0;
+                if (idx < C) {
+                    int lo_b = 0, hi_b = G - 1;  // last workgroup starting at or before idx
+                    while (lo_b < hi_b) {
+                        const int mid = (lo_b + hi_b + 1) >> 1;
+                        if (L.hist[mid] <= idx)
+                            lo_b = mid;
+                        else
+                            hi_b = mid - 1;
+                    }
+                    v[u] = ld_agent64(stage + L.hist[kMaxSplit + lo_b] + (idx - L.hist[lo_b]));
+                }
             }
-            const uint32_t src = s_hist[kMaxSplit + lo_b] + (idx - s_hist[lo_b]);
-            s_ent[idx] = make_uint2(ld_agent(stage_key + src), ld_agent(stage_col + src));
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const uint32_t idx = i0 + u * NT + t;
+                if (idx < C) s_ent[idx] = make_uint2((uint32_t)v[u], (uint32_t)(v[u] >> 32));
+            }
         }
         __syncthreads();
-        select_and_write<K>(a, row, s_ent, C, d1, s_hist, s_red, s_out, xr);
+        const Bound b = refine_on_list<K>(s_ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
+        write_from_list<K>(a, row, s_ent, C, b, L.red, xr);
         if (t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)row_nan;
         // return the slot to zero for the next call
-        for (int b = t; b < kBins; b += NT) st_agent(ghist + b, 0u);
-        for (uint32_t i = t; i < C; i += NT) {
-            st_agent(stage_key + i, 0u);
-            st_agent(stage_col + i, 0u);
-        }
+        for (int i = t; i < kBins; i += NT) st_agent(ghist + i, 0u);
+        for (uint32_t i = t; i < C; i += NT) st_agent64(stage + i, 0ull);
         for (int i = t; i < 4 * G; i += NT) st_agent(gcnt + i, 0u);
         drain_memory();
         __syncthreads();
@@ -648,72 +882,36 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         return;
     }
 
-    // ---- fallback: too many candidates.  Finish the radix select by
-    // re-streaming this thread's segment from cache for each pass, so the
-    // rare path costs no extra VGPRs for the common one.
-    const __amdgpu_buffer_rsrc_t seg_view = row_view<K>(xr, s1);
-    uint32_t need = (uint32_t)a.k - d1.above;
-    uint32_t P = d1.v;
-    int s = K::SH1;
-    if (d1.cnt != need) {
+    // ---- slow path: too many candidates for the list.  Finish the radix
+    // select over this workgroup's range re-read from cache, one rendezvous
+    // per pass.
+    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
+    Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
+    if (d1.cnt != b.need) {
 #pragma unroll 1
         for (int pass = 1; pass < K::NPASS; ++pass) {
             const int d = K::digit(pass);
-            const int sh = s - d;
-            const uint32_t dmask = (1u << d) - 1u;
+            const int sh = b.s - d;
             const int nb = 1 << d;
-            for (int b = t; b < nb; b += NT) s_hist[b] = 0;
+            for (int i = t; i < nb; i += NT) L.hist[i] = 0;
             __syncthreads();
-#pragma unroll 1
-            for (int64_t p = s0; p < s1; p += VEC) {
-                uint32_t w4[4];
-                keys_of<K>(load_vec<K>(seg_view, p), w4);
-                clear_tail<K>(w4, p + VEC > s1 ? (int)(s1 - p) : VEC);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int h = 0; h < EPW; ++h) {
-                        const uint32_t kk = K::elem(w4[q], h);
-                        if ((kk >> s) == P) atomicAdd(&s_hist[(kk >> sh) & dmask], 1u);
-                    }
-            }
+            refine_histogram_stream<K>(view, lo, len, b.P, b.s, sh, (1u << d) - 1u, L.hist);
             __syncthreads();
             uint32_t *g = ghist + pass * kBins;
-            for (int b = t; b < nb; b += NT) {
-                const uint32_t h = s_hist[b];
-                if (h) add_agent(g + b, h);
-            }
+            merge_histogram(L.hist, g, nb);
             row_rendezvous(slot, (++nren) * (uint32_t)G, err);
-            for (int b = t; b < nb; b += NT) s_hist[b] = ld_agent(g + b);
+            fetch_histogram(g, L.hist, nb);
             __syncthreads();
-            const Digit dg = find_digit(s_hist, nb, need, s_red, s_out);
-            need -= dg.above;
-            P = (P << d) | dg.v;
-            s = sh;
-            if (dg.cnt == need) break;  // the boundary bin is taken whole
+            const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
+            b.need -= dg.above;
+            b.P = (b.P << d) | dg.v;
+            b.s = sh;
+            if (dg.cnt == b.need) break;  // the boundary bin is taken whole
         }
     }
-
-    // stable compaction over the segment: count, scan, then write in order
-    uint32_t g = 0, q = 0;
-#pragma unroll 1
-    for (int64_t p = s0; p < s1; p += VEC) {
-        uint32_t w4[4];
-        keys_of<K>(load_vec<K>(seg_view, p), w4);
-        clear_tail<K>(w4, p + VEC > s1 ? (int)(s1 - p) : VEC);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-            for (int h = 0; h < EPW; ++h) {
-                const uint32_t pre = K::elem(w4[qq], h) >> s;
-                g += pre > P ? 1u : 0u;
-                q += pre == P ? 1u : 0u;
-            }
-    }
-    const uint32_t mine = g | (q << 16);
+    // this workgroup's totals, then the totals of the workgroups before it
     uint32_t tot;
-    const uint32_t ex = block_incl_scan(mine, s_red, &tot) - mine;
-
+    block_incl_scan(range_counts<K>(view, lo, len, b), L.red, &tot);
     if (t == 0) {
         st_agent(gcnt + 4 * c + 0, tot & 0xFFFFu);
         st_agent(gcnt + 4 * c + 1, tot >> 16);
@@ -728,33 +926,11 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         }
         nn |= ld_agent(gcnt + 4 * i + 2);
     }
-    const uint32_t gt0 = block_sum(gg, s_red);
-    const uint32_t eq0 = block_sum(qq, s_red);
+    uint32_t gt0, eq0;
+    block_incl_scan(gg, L.red, &gt0);
+    block_incl_scan(qq, L.red, &eq0);
     const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
-    {
-        uint32_t gb = gt0 + (ex & 0xFFFFu);
-        uint32_t qb = eq0 + (ex >> 16);
-#pragma unroll 1
-        for (int64_t p = s0; p < s1; p += VEC) {
-            uint32_t w4[4];
-            keys_of<K>(load_vec<K>(seg_view, p), w4);
-            clear_tail<K>(w4, p + VEC > s1 ? (int)(s1 - p) : VEC);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-                for (int h = 0; h < EPW; ++h) {
-                    const uint32_t pre = K::elem(w4[q4], h) >> s;
-                    const int64_t col = p + q4 * EPW + h;
-                    if (pre > P) {
-                        emit<K>(a, row, gb + min(qb, need), col, xr);
-                        ++gb;
-                    } else if (pre == P) {
-                        if (qb < need) emit<K>(a, row, gb + qb, col, xr);
-                        ++qb;
-                    }
-                }
-        }
-    }
+    write_from_stream<K>(a, row, view, lo, len, b, gt0, eq0, L.red, xr);
     if (c == 0 && t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)row_nan;
 
     // Leave the slot zeroed for the next call (whose slot layout may differ):
@@ -767,9 +943,9 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     for (int i = z0 + t; i < z1; i += NT) st_agent(ghist + i, 0u);
     drain_memory();
     __syncthreads();
-    if (t == 0) s_out[3] = (add_agent(slot + 1, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
+    if (t == 0) L.out[3] = (add_agent(slot + 1, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
     __syncthreads();
-    if (s_out[3]) {
+    if (L.out[3]) {
         for (int i = t; i < 4 * G; i += NT) st_agent(gcnt + i, 0u);
         drain_memory();
         __syncthreads();
@@ -794,220 +970,54 @@ __device__ __forceinline__ void prefetch_row(const typename K::raw_t *xr, int64_
     for (int j = 0; j < LOADS; ++j) v[j] = load_vec<K>(view, (int64_t)(j * NT + tid()) * K::VEC);
 }
 
-// Slow path of a whole row (candidates exceed the LDS list): finish the radix
-// select by re-streaming the row from cache; the compaction walks the
-// coalesced layout one load at a time with a workgroup scan per load.
-template <class K, int LOADS>
-__device__ void select_row_streaming(const TopkArgs &a, int64_t row, int64_t n, Digit d1,
-                                     const typename K::raw_t *xr, uint32_t *s_hist,
-                                     uint32_t *s_red, uint32_t *s_out) {
-    constexpr int VEC = K::VEC, EPW = K::EPW;
-    const int t = tid();
-    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
-    uint32_t need = (uint32_t)a.k - d1.above;
-    uint32_t P = d1.v;
-    int s = K::SH1;
-    if (d1.cnt != need) {
-#pragma unroll 1
-        for (int pass = 1; pass < K::NPASS; ++pass) {
-            const int d = K::digit(pass);
-            const int sh = s - d;
-            const uint32_t dmask = (1u << d) - 1u;
-            const int nb = 1 << d;
-            for (int b = t; b < nb; b += NT) s_hist[b] = 0;
-            __syncthreads();
-#pragma unroll 1
-            for (int j = 0; j < LOADS; ++j) {
-                const int64_t p = (int64_t)(j * NT + t) * VEC;
-                if (p >= n) continue;
-                uint32_t w4[4];
-                keys_of<K>(load_vec<K>(view, p), w4);
-                clear_tail<K>(w4, p + VEC > n ? (int)(n - p) : VEC);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int h = 0; h < EPW; ++h) {
-                        const uint32_t kk = K::elem(w4[q], h);
-                        if ((kk >> s) == P) atomicAdd(&s_hist[(kk >> sh) & dmask], 1u);
-                    }
-            }
-            __syncthreads();
-            const Digit dg = find_digit(s_hist, nb, need, s_red, s_out);
-            need -= dg.above;
-            P = (P << d) | dg.v;
-            s = sh;
-            if (dg.cnt == need) break;
-        }
-    }
-    uint32_t gb = 0, qb = 0;  // taken-above and equal counts before the current load
-#pragma unroll 1
-    for (int j = 0; j < LOADS; ++j) {
-        const int64_t p = (int64_t)(j * NT + t) * VEC;
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
-        if (p < n) {
-            keys_of<K>(load_vec<K>(view, p), w4);
-            clear_tail<K>(w4, p + VEC > n ? (int)(n - p) : VEC);
-        }
-        uint32_t g = 0, q = 0;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-            for (int h = 0; h < EPW; ++h) {
-                const uint32_t pre = K::elem(w4[qq], h) >> s;
-                g += pre > P ? 1u : 0u;
-                q += pre == P ? 1u : 0u;
-            }
-        const uint32_t mine = g | (q << 16);
-        uint32_t tot;
-        const uint32_t ex = block_incl_scan(mine, s_red, &tot) - mine;
-        uint32_t g1 = gb + (ex & 0xFFFFu), q1 = qb + (ex >> 16);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-            for (int h = 0; h < EPW; ++h) {
-                const uint32_t pre = K::elem(w4[qq], h) >> s;
-                const int64_t col = p + qq * EPW + h;
-                if (pre > P) {
-                    emit<K>(a, row, g1 + min(q1, need), col, xr);
-                    ++g1;
-                } else if (pre == P) {
-                    if (q1 < need) emit<K>(a, row, g1 + q1, col, xr);
-                    ++q1;
-                }
-            }
-        gb += tot & 0xFFFFu;
-        qb += tot >> 16;
-    }
-}
-
-// Shared memory of the whole-row kernel (the histogram has one spare bin per
-// lane past kBins).
-template <int LP>
-struct RowLds {
-    uint32_t hist[kBins + 64];
-    uint32_t wtot[LP * NWAVE];
-    uint32_t red[NWAVE];
-    uint32_t out[8];
-};
-
 // One row of valid length n > k whose raw 16-byte vectors are in buf
-// (coalesced layout: load j of thread t holds columns (j*NT + t)*VEC ..).
+// (coalesced layout).
 template <class K, int LOADS>
 __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64_t n,
                                            const uint4 (&buf)[LOADS],
-                                           RowLds<(LOADS + 1) / 2> &L, uint2 *ent) {
+                                           TopkLds<(LOADS + 1) / 2> &L, uint2 *ent) {
     using raw_t = typename K::raw_t;
-    constexpr int VEC = K::VEC;
-    constexpr int EPW = K::EPW;
-    constexpr int W = LOADS * 4;
-    constexpr int LP = (LOADS + 1) / 2;
-    constexpr int SPAN = NT * VEC;  // columns per workgroup-wide load
     const int t = tid();
-    const int lane = t & 63, wid = t >> 6;
     const uint32_t cap = (uint32_t)a.cap;
     const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
-    const int ni = (int)n;
-    const int full = ni / SPAN;                 // loads valid for every thread
-    const int any = (ni + SPAN - 1) / SPAN;     // loads holding some valid column
+    const int len = (int)n;
 
-    // ---- keys, NaN probe, first-digit histogram -----------------------------
-    uint32_t kw[W];
-    uint32_t nan = 0;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) nan |= keys_of<K>(buf[j], &kw[4 * j]) ? 1u : 0u;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-        if (j >= full) {
-            const int valid = ni - (j * NT + t) * VEC;
-            clear_tail<K>(&kw[4 * j], valid < 0 ? 0 : (valid > VEC ? VEC : valid));
-        }
-    }
+    uint32_t kw[LOADS * 4];
+    const uint32_t nan = keys_of_loads<K, LOADS>(buf, len, kw);
     for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
     const uint32_t block_nan = __syncthreads_or((int)nan) ? 1u : 0u;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-        if (j < full) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) hist_add<K>(L.hist, kw[4 * j + q]);
-        } else if (j < any) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) hist_add_masked<K>(L.hist, kw[4 * j + q], kBins + lane);
-        }
-    }
+    first_digit_histogram<K, LOADS>(kw, len, L.hist);
     __syncthreads();
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
     const uint32_t C = d1.above + d1.cnt;
 
     if (C <= cap) {
-        // ---- candidates (key >= T1) to LDS in column order ------------------
-        const uint32_t T1 = d1.v << K::SH1;
-        uint32_t pk[LP];
-#pragma unroll
-        for (int i = 0; i < LP; ++i) pk[i] = 0;
-#pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            if (j < any) {
-                uint32_t m = 0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int h = 0; h < EPW; ++h) m += K::elem(kw[4 * j + q], h) >= T1 ? 1u : 0u;
-                pk[j >> 1] |= m << ((j & 1) * 16);
-            }
-        }
-        uint32_t ex[LP];
-#pragma unroll
-        for (int i = 0; i < LP; ++i) {
-            const uint32_t incl = wave_incl_scan(pk[i]);
-            ex[i] = incl - pk[i];
-            if (lane == 63) L.wtot[i * NWAVE + wid] = incl;
-        }
-        __syncthreads();
-        const uint32_t T1w = opaque(T1);
-#pragma unroll
-        for (int w = 0; w < W; ++w) kw[w] = opaque(kw[w]);
-        const uint32_t spare = cap + lane;
-        uint32_t run = 0;
-#pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            if (j < any) {
-                const int i = j >> 1, sh = (j & 1) * 16;
-                uint32_t tot = 0, before = 0;
-#pragma unroll
-                for (int w = 0; w < NWAVE; ++w) {
-                    const uint32_t v = (L.wtot[i * NWAVE + w] >> sh) & 0xFFFFu;
-                    tot += v;
-                    before += (w < wid) ? v : 0u;
-                }
-                uint32_t pos = run + before + ((ex[i] >> sh) & 0xFFFFu);
-                run += tot;
-                const uint32_t p = (uint32_t)(j * NT + t) * VEC;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int h = 0; h < EPW; ++h) {
-                        const uint32_t key = K::elem(kw[4 * j + q], h);
-                        const bool cand = key >= T1w;
-                        ent[cand ? pos : spare] = make_uint2(key, p + q * EPW + h);
-                        pos += cand ? 1u : 0u;
-                    }
-            }
-        }
-        __syncthreads();
-        select_and_write<K>(a, row, ent, C, d1, L.hist, L.red, L.out, xr);
+        compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, ent, cap, 0u);
+        const Bound b = refine_on_list<K>(ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
+        write_from_list<K>(a, row, ent, C, b, L.red, xr);
     } else {
-        select_row_streaming<K, LOADS>(a, row, n, d1, xr, L.hist, L.red, L.out);
+        const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
+        Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
+        if (d1.cnt != b.need) {
+#pragma unroll 1
+            for (int pass = 1; pass < K::NPASS; ++pass) {
+                const int d = K::digit(pass);
+                const int sh = b.s - d;
+                const int nb = 1 << d;
+                for (int i = t; i < nb; i += NT) L.hist[i] = 0;
+                __syncthreads();
+                refine_histogram_stream<K>(view, 0, len, b.P, b.s, sh, (1u << d) - 1u, L.hist);
+                __syncthreads();
+                const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
+                b.need -= dg.above;
+                b.P = (b.P << d) | dg.v;
+                b.s = sh;
+                if (dg.cnt == b.need) break;
+            }
+        }
+        write_from_stream<K>(a, row, view, 0, len, b, 0u, 0u, L.red, xr);
     }
     if (t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)block_nan;
-}
-
-__device__ __forceinline__ int64_t valid_length(const TopkArgs &a, int64_t row) {
-    int64_t n = a.cols;
-    if (a.row_end) {
-        const int64_t e = a.row_end[row];
-        n = e < 0 ? 0 : (e > a.cols ? a.cols : e);
-    }
-    return n;
 }
 
 // A workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x, ...: while it
@@ -1020,7 +1030,7 @@ __global__ __launch_bounds__(NT) void topk_rows_pipelined(const TopkArgs a) {
     constexpr int LOADS = EPT / K::VEC;
     static_assert(EPT % K::VEC == 0, "EPT must be a multiple of the vector width");
     extern __shared__ uint2 s_ent[];  // candidate list (cap entries) + one spare per lane
-    __shared__ RowLds<(LOADS + 1) / 2> L;
+    __shared__ TopkLds<(LOADS + 1) / 2> L;
 
     const int64_t stride = gridDim.x;
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
@@ -1049,15 +1059,15 @@ __global__ __launch_bounds__(NT) void topk_rows_pipelined(const TopkArgs a) {
     }
 }
 
-template <class K, int MAXL, bool SPLIT>
+template <class K, int EPT, bool SPLIT>
 const void *kptr() {
-    if (SPLIT) return reinterpret_cast<const void *>(&topk_rows_split<K, MAXL>);
-    return reinterpret_cast<const void *>(&topk_rows_pipelined<K, MAXL>);
+    if (SPLIT) return reinterpret_cast<const void *>(&topk_rows_split<K, EPT>);
+    return reinterpret_cast<const void *>(&topk_rows_pipelined<K, EPT>);
 }
 
 template <class K, bool SPLIT>
-const void *pick(int maxl) {
-    switch (maxl) {
+const void *pick(int ept) {
+    switch (ept) {
         case 8: return kptr<K, 8, SPLIT>();
         case 16: return kptr<K, 16, SPLIT>();
         case 32: return kptr<K, 32, SPLIT>();
@@ -1068,11 +1078,11 @@ const void *pick(int maxl) {
 
 }  // namespace
 
-// Split rows: topk_rows_split (maxl = longest per-thread segment).  Whole
-// rows: topk_rows_pipelined (maxl = columns per thread).
-const void *topk_kernel_ptr(int dtype, int maxl, bool split) {
-    if (dtype == 0) return split ? pick<Bf16Key, true>(maxl) : pick<Bf16Key, false>(maxl);
-    return split ? pick<F32Key, true>(maxl) : pick<F32Key, false>(maxl);
+// ept = columns per thread of one workgroup's range (the whole row, or one
+// split chunk).
+const void *topk_kernel_ptr(int dtype, int ept, bool split) {
+    if (dtype == 0) return split ? pick<Bf16Key, true>(ept) : pick<Bf16Key, false>(ept);
+    return split ? pick<F32Key, true>(ept) : pick<F32Key, false>(ept);
 }
 
 // Candidate entries (key, column) plus one spare entry per lane.
@@ -1081,9 +1091,9 @@ size_t topk_dyn_lds(int dtype, int64_t cap) {
     return (size_t)(cap + 64) * sizeof(uint2);
 }
 
-hipError_t launch_topk(int dtype, int maxl, bool split, const TopkArgs &a, unsigned grid,
+hipError_t launch_topk(int dtype, int ept, bool split, const TopkArgs &a, unsigned grid,
                        hipStream_t stream) {
-    const void *fn = topk_kernel_ptr(dtype, maxl, split);
+    const void *fn = topk_kernel_ptr(dtype, ept, split);
     if (!fn) return hipErrorInvalidValue;
     TopkArgs copy = a;
     void *args[] = {&copy};

@@ -79,6 +79,8 @@ SMALL = [
     ("descending_bf16", 4, 6000, W.BF16, "descending", 300),
     ("special_bf16", 11, 2500, W.BF16, "special", 64),
     ("special_f32", 11, 2500, W.F32, "special", 64),
+    ("special_bf16_bigk", 5, 2500, W.BF16, "special", 2000),
+    ("special_f32_bigk", 5, 2500, W.F32, "special", 2000),
     ("narrow_bf16", 5, 16384, W.BF16, "narrow", 2000),
     ("ragged_bf16", 6, 2043, W.BF16, "normal", 17),
     ("ragged_f32", 6, 1037, W.F32, "normal", 1),
@@ -105,6 +107,24 @@ def test_row_end_and_nan(dsel, orc, dt, G):
     re[:4] = torch.tensor([0, 200, 201, 3000], dtype=torch.int32)
     check_case(dsel, orc, f"row_end_nan/{dt}", x, 200, re, True, torch.int64, True, G)
     check_case(dsel, orc, f"row_end_nan/{dt}/idx-only", x, 200, re, False, torch.int32, False, G)
+
+
+@pytest.mark.parametrize("G", [None, 4, 7])
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_nan_just_past_row_end(dsel, orc, dt, G):
+    """A NaN at column n (just past a row's end) is out of range: no flag, and
+    it must not reach the selection; odd n puts it in the same 32-bit word as
+    the last valid bf16 element."""
+    rows, cols = 24, 3001
+    x = W.random_rows(25, rows, cols, dt, "normal")
+    ends = [1001, 1003, 1500, 1501, 2047, 2049, 2999, 3000, 3001, 257, 511, 777,
+            1025, 1999, 2001, 2221, 2500, 2501, 2887, 2901, 1203, 1333, 1777, 2993]
+    re = torch.tensor(ends, dtype=torch.int32)
+    for r, n in enumerate(ends):
+        if n < cols:
+            x[r, n] = float("nan")
+    got = check_case(dsel, orc, f"nan_past_end/{dt}", x, 200, re, False, torch.int32, True, G)
+    assert not got[2].any(), "no row holds a NaN in range"
 
 
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
