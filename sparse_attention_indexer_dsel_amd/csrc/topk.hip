@@ -277,22 +277,33 @@ __device__ __forceinline__ void fetch_histogram(const uint32_t *ghist, uint32_t 
     }
 }
 
+// Output slot `pos` of a row: its column, and (with values) the value bits.
+__device__ __forceinline__ void store_index(const TopkArgs &a, int64_t row, uint32_t pos,
+                                            uint32_t col) {
+    if (pos >= (uint32_t)a.k) return;  // never write past the row's k slots
+    if (a.idx64)
+        reinterpret_cast<int64_t *>(a.out_idx)[row * a.idx_stride + pos] = (int64_t)col;
+    else
+        reinterpret_cast<int32_t *>(a.out_idx)[row * a.idx_stride + pos] = (int32_t)col;
+}
+
+template <class K>
+__device__ __forceinline__ void store_value(const TopkArgs &a, int64_t row, uint32_t pos,
+                                            uint32_t bits) {
+    if (pos >= (uint32_t)a.k) return;
+    reinterpret_cast<typename K::raw_t *>(a.out_val)[row * a.val_stride + pos] =
+        (typename K::raw_t)bits;
+}
+
 // One selected element: its column at output slot `pos`, and its value,
 // rebuilt from the key (read back from the row only for +-0 and NaN keys,
 // whose bits the key does not determine).
 template <class K>
 __device__ __forceinline__ void emit(const TopkArgs &a, int64_t row, uint32_t pos, uint32_t col,
                                      uint32_t key, const typename K::raw_t *xr) {
-    if (pos >= (uint32_t)a.k) return;  // never write past the row's k slots
-    if (a.idx64)
-        reinterpret_cast<int64_t *>(a.out_idx)[row * a.idx_stride + pos] = (int64_t)col;
-    else
-        reinterpret_cast<int32_t *>(a.out_idx)[row * a.idx_stride + pos] = (int32_t)col;
-    if (a.ret_val) {
-        const typename K::raw_t v =
-            K::ambiguous(key) ? xr[col] : (typename K::raw_t)K::value_bits(key);
-        reinterpret_cast<typename K::raw_t *>(a.out_val)[row * a.val_stride + pos] = v;
-    }
+    store_index(a, row, pos, col);
+    if (a.ret_val)
+        store_value<K>(a, row, pos, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
 }
 
 // Rows with n <= k: columns 0..n-1 in order, then padding.  Workgroup c of G
@@ -554,33 +565,42 @@ __device__ Bound refine_on_list(const uint2 *ent, uint32_t C, Digit d1, uint32_t
 // Write the selection from a column-ordered candidate list.  Wave w owns
 // entries [w*Q, (w+1)*Q) (Q a multiple of 64); ranks within a wave come from
 // ballots, and one exchange of the waves' counts (through s_red) gives each
-// wave its starting ranks.
+// wave its starting ranks.  Values are rebuilt from keys, so the write loop
+// issues no loads (a load in it would make every store wait for the ones
+// before it); the rare +-0 / NaN keys get their bits from the row in a
+// second pass, run only when some wave holds one.
 template <class K>
 __device__ void write_from_list(const TopkArgs &a, int64_t row, const uint2 *ent, uint32_t C,
                                 Bound b, uint32_t *s_red, const typename K::raw_t *xr) {
     const int t = tid();
     const int lane = t & 63, wid = t >> 6;
-    const uint32_t Q = (C + NT - 1) / NT * 64;
+    const uint32_t Q = (C + NT - 1) / NT * 64;  // <= 2048
     const uint32_t b0 = (uint32_t)wid * Q;
     const uint32_t b1 = min(C, b0 + Q);
     uint32_t g = 0, q = 0;
+    uint64_t amb = 0;
     for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
         const uint32_t i = i0 + (uint32_t)lane;
         const bool in = i < b1;
-        const uint32_t pre = in ? (ent[i].x >> b.s) : 0u;
-        g += popc64(__ballot(in && pre > b.P));
-        q += popc64(__ballot(in && pre == b.P));
+        const uint32_t key = in ? ent[i].x : 0u;
+        const uint32_t pre = key >> b.s;
+        const bool gt = in && pre > b.P, eq = in && pre == b.P;
+        g += popc64(__ballot(gt));
+        q += popc64(__ballot(eq));
+        amb |= __ballot((gt || eq) && K::ambiguous(key));
     }
-    if (lane == 0) s_red[wid] = g | (q << 16);  // each count <= 8192
+    if (lane == 0) s_red[wid] = g | (q << 12) | (amb ? 1u << 24 : 0u);
     __syncthreads();
-    uint32_t gb = 0, qb = 0;
+    uint32_t gb = 0, qb = 0, any_amb = 0;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) {
         const uint32_t v = s_red[w];
-        gb += w < wid ? (v & 0xFFFFu) : 0u;
-        qb += w < wid ? (v >> 16) : 0u;
+        gb += w < wid ? (v & 0xFFFu) : 0u;
+        qb += w < wid ? ((v >> 12) & 0xFFFu) : 0u;
+        any_amb |= v >> 24;
     }
     __syncthreads();
+    const uint32_t gb0 = gb, qb0 = qb;
     for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
         const uint32_t i = i0 + (uint32_t)lane;
         const bool in = i < b1;
@@ -590,10 +610,30 @@ __device__ void write_from_list(const TopkArgs &a, int64_t row, const uint2 *ent
         const bool eq = in && pre == b.P;
         const uint64_t mg = __ballot(gt), mq = __ballot(eq);
         const uint32_t rg = gb + lanes_below(mg), rq = qb + lanes_below(mq);
-        if (gt)
-            emit<K>(a, row, rg + min(rq, b.need), e.y, e.x, xr);
-        else if (eq && rq < b.need)
-            emit<K>(a, row, rg + rq, e.y, e.x, xr);
+        const bool take = gt || (eq && rq < b.need);
+        const uint32_t pos = gt ? rg + min(rq, b.need) : rg + rq;
+        if (take) {
+            store_index(a, row, pos, e.y);
+            if (a.ret_val) store_value<K>(a, row, pos, K::value_bits(e.x));
+        }
+        gb += popc64(mg);
+        qb += popc64(mq);
+    }
+    if (!(any_amb && a.ret_val)) return;
+    gb = gb0;
+    qb = qb0;
+    for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
+        const uint32_t i = i0 + (uint32_t)lane;
+        const bool in = i < b1;
+        const uint2 e = in ? ent[i] : make_uint2(0u, 0u);
+        const uint32_t pre = e.x >> b.s;
+        const bool gt = in && pre > b.P;
+        const bool eq = in && pre == b.P;
+        const uint64_t mg = __ballot(gt), mq = __ballot(eq);
+        const uint32_t rg = gb + lanes_below(mg), rq = qb + lanes_below(mq);
+        const bool take = gt || (eq && rq < b.need);
+        const uint32_t pos = gt ? rg + min(rq, b.need) : rg + rq;
+        if (take && K::ambiguous(e.x)) store_value<K>(a, row, pos, (uint32_t)xr[e.y]);
         gb += popc64(mg);
         qb += popc64(mq);
     }
@@ -839,24 +879,29 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
             base += tot;
         }
         const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
-        constexpr int BATCH = 8;
+        // each entry's workgroup: the last one whose list start is <= idx,
+        // found by binary lifting (all BATCH searches interleaved)
+        int top = 1;
+        while (top * 2 <= G) top *= 2;
+        constexpr int BATCH = 16;
         for (uint32_t i0 = 0; i0 < C; i0 += BATCH * NT) {
+            int blk[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) blk[u] = 0;
+            for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u) {
+                    const uint32_t idx = i0 + u * NT + t;
+                    const int cand = blk[u] + step;
+                    if (cand < G && L.hist[cand] <= idx) blk[u] = cand;
+                }
+            }
             uint64_t v[BATCH];
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
                 const uint32_t idx = i0 + u * NT + t;
-                v[u] = 0;
-                if (idx < C) {
-                    int lo_b = 0, hi_b = G - 1;  // last workgroup starting at or before idx
-                    while (lo_b < hi_b) {
-                        const int mid = (lo_b + hi_b + 1) >> 1;
-                        if (L.hist[mid] <= idx)
-                            lo_b = mid;
-                        else
-                            hi_b = mid - 1;
-                    }
-                    v[u] = ld_agent64(stage + L.hist[kMaxSplit + lo_b] + (idx - L.hist[lo_b]));
-                }
+                v[u] = idx < C ? ld_agent64(stage + L.hist[kMaxSplit + blk[u]] + (idx - L.hist[blk[u]]))
+                               : 0ull;
             }
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
@@ -868,12 +913,12 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         const Bound b = refine_on_list<K>(s_ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
         write_from_list<K>(a, row, s_ent, C, b, L.red, xr);
         if (t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)row_nan;
-        // return the slot to zero for the next call
+        // Return the slot to zero for the next call, whose slot layout may
+        // differ (every other workgroup of the row is done with it; the
+        // stores complete before the launch does).
         for (int i = t; i < kBins; i += NT) st_agent(ghist + i, 0u);
-        for (uint32_t i = t; i < C; i += NT) st_agent64(stage + i, 0ull);
         for (int i = t; i < 4 * G; i += NT) st_agent(gcnt + i, 0u);
-        drain_memory();
-        __syncthreads();
+        for (uint32_t i = t; i < C; i += NT) st_agent64(stage + i, 0ull);
         if (t == 0) {
             st_agent(slot + 0, 0u);
             st_agent(slot + 1, 0u);

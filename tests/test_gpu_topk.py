@@ -181,11 +181,18 @@ def test_errors(dsel):
     assert e.value.code == -3
 
 
-def test_workspace_left_clean(dsel):
-    x = W.random_rows(71, 8, 50000, W.F32, "normal").cuda()
-    with blocks_per_row(6):
-        dsel.topk(x, 100)
-        dsel.topk(x, 2000)
+def test_workspace_reuse(dsel, orc):
+    """One workspace serves calls of different shapes (so different per-row
+    slot layouts) back to back: each call returns it to zero, and no
+    rendezvous times out (error word 0 stays clear)."""
+    dsel._WORKSPACES.clear()
+    cases = [(W.random_rows(71, 8, 50000, W.F32, "normal"), 100, 6),
+             (W.random_rows(72, 8, 50000, W.F32, "normal"), 2000, 6),
+             (W.random_rows(73, 5, 30000, W.BF16, "ties"), 1500, 9),
+             (W.random_rows(74, 8, 50000, W.F32, "equal"), 300, 4),
+             (W.random_rows(71, 8, 50000, W.F32, "normal"), 100, 6)]
+    for i, (x, k, G) in enumerate(cases):
+        check_case(dsel, orc, f"reuse{i}", x, k, None, False, torch.int32, True, G)
     torch.cuda.synchronize()
     for ws in dsel._WORKSPACES.values():
         assert int(ws.count_nonzero()) == 0, "workspace must be zero after a call (and no error bit)"
