@@ -153,9 +153,13 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
-// Inclusive prefix sum over the workgroup in thread order; *total receives
-// the workgroup's sum.
-__device__ uint32_t block_incl_scan(uint32_t x, uint32_t *s_red, uint32_t *total = nullptr) {
+// Inclusive prefix sum over the workgroup in thread order, and the
+// workgroup's total.
+struct Scan {
+    uint32_t incl, total;
+};
+
+__device__ Scan block_scan(uint32_t x, uint32_t *s_red) {
     const int t = tid();
     const uint32_t w = wave_incl_scan(x);
     if ((t & 63) == 63) s_red[t >> 6] = w;
@@ -168,8 +172,7 @@ __device__ uint32_t block_incl_scan(uint32_t x, uint32_t *s_red, uint32_t *total
         tot += v;
     }
     __syncthreads();
-    if (total) *total = tot;
-    return w + off;
+    return Scan{w + off, tot};
 }
 
 struct Digit {
@@ -189,7 +192,7 @@ __device__ Digit find_digit(const uint32_t *hist, int nb, uint32_t need, uint32_
     uint32_t local = 0;
     if (t < nact)
         for (int i = 1; i <= bpt; ++i) local += hist[top - i];
-    const uint32_t incl = block_incl_scan(local, s_red);
+    const uint32_t incl = block_scan(local, s_red).incl;
     const uint32_t excl = incl - local;
     if (t < nact && excl < need && need <= incl) {
         uint32_t acc = excl;
@@ -277,39 +280,56 @@ __device__ __forceinline__ void fetch_histogram(const uint32_t *ghist, uint32_t 
     }
 }
 
-// Output slot `pos` of a row: its column, and (with values) the value bits.
-__device__ __forceinline__ void store_index(const TopkArgs &a, int64_t row, uint32_t pos,
-                                            uint32_t col) {
-    if (pos >= (uint32_t)a.k) return;  // never write past the row's k slots
-    if (a.idx64)
-        reinterpret_cast<int64_t *>(a.out_idx)[row * a.idx_stride + pos] = (int64_t)col;
+// A row's output slots, resolved once per row (uniform: held in SGPRs).
+struct RowOut {
+    char *idx;  // the row's index slots
+    char *val;  // the row's value slots, or nullptr without values
+    uint32_t k;
+    int idx64;
+};
+
+template <class K>
+__device__ __forceinline__ RowOut row_out(const TopkArgs &a, int64_t row) {
+    RowOut o;
+    o.idx = reinterpret_cast<char *>(a.out_idx) + row * a.idx_stride * (a.idx64 ? 8 : 4);
+    o.val = a.ret_val ? reinterpret_cast<char *>(a.out_val) +
+                            row * a.val_stride * (int64_t)sizeof(typename K::raw_t)
+                      : nullptr;
+    o.k = (uint32_t)a.k;
+    o.idx64 = a.idx64;
+    return o;
+}
+
+// Output slot `pos`: its column, and (with values) the value bits.
+__device__ __forceinline__ void store_index(const RowOut &o, uint32_t pos, uint32_t col) {
+    if (pos >= o.k) return;  // never write past the row's k slots
+    if (o.idx64)
+        reinterpret_cast<int64_t *>(o.idx)[pos] = (int64_t)col;
     else
-        reinterpret_cast<int32_t *>(a.out_idx)[row * a.idx_stride + pos] = (int32_t)col;
+        reinterpret_cast<int32_t *>(o.idx)[pos] = (int32_t)col;
 }
 
 template <class K>
-__device__ __forceinline__ void store_value(const TopkArgs &a, int64_t row, uint32_t pos,
-                                            uint32_t bits) {
-    if (pos >= (uint32_t)a.k) return;
-    reinterpret_cast<typename K::raw_t *>(a.out_val)[row * a.val_stride + pos] =
-        (typename K::raw_t)bits;
+__device__ __forceinline__ void store_value(const RowOut &o, uint32_t pos, uint32_t bits) {
+    if (pos >= o.k) return;
+    reinterpret_cast<typename K::raw_t *>(o.val)[pos] = (typename K::raw_t)bits;
 }
 
 // One selected element: its column at output slot `pos`, and its value,
 // rebuilt from the key (read back from the row only for +-0 and NaN keys,
 // whose bits the key does not determine).
 template <class K>
-__device__ __forceinline__ void emit(const TopkArgs &a, int64_t row, uint32_t pos, uint32_t col,
-                                     uint32_t key, const typename K::raw_t *xr) {
-    store_index(a, row, pos, col);
-    if (a.ret_val)
-        store_value<K>(a, row, pos, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
+__device__ __forceinline__ void emit(const RowOut &o, uint32_t pos, uint32_t col, uint32_t key,
+                                     const typename K::raw_t *xr) {
+    store_index(o, pos, col);
+    if (o.val)
+        store_value<K>(o, pos, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
 }
 
 // Rows with n <= k: columns 0..n-1 in order, then padding.  Workgroup c of G
 // writes slots [c*S, (c+1)*S) with S = ceil(k / G).
 template <class K>
-__device__ void write_short_row(const TopkArgs &a, int64_t row, int64_t n, int c, int G,
+__device__ __forceinline__ void write_short_row(const TopkArgs &a, int64_t row, int64_t n, int c, int G,
                                 const typename K::raw_t *xr) {
     const int S = (a.k + G - 1) / G;
     const int s0 = c * S;
@@ -570,8 +590,10 @@ __device__ Bound refine_on_list(const uint2 *ent, uint32_t C, Digit d1, uint32_t
 // before it); the rare +-0 / NaN keys get their bits from the row in a
 // second pass, run only when some wave holds one.
 template <class K>
-__device__ void write_from_list(const TopkArgs &a, int64_t row, const uint2 *ent, uint32_t C,
-                                Bound b, uint32_t *s_red, const typename K::raw_t *xr) {
+__device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, const uint2 *ent,
+                                                uint32_t C, Bound b, uint32_t *s_red,
+                                                const typename K::raw_t *xr) {
+    const RowOut o = row_out<K>(a, row);
     const int t = tid();
     const int lane = t & 63, wid = t >> 6;
     const uint32_t Q = (C + NT - 1) / NT * 64;  // <= 2048
@@ -613,13 +635,13 @@ __device__ void write_from_list(const TopkArgs &a, int64_t row, const uint2 *ent
         const bool take = gt || (eq && rq < b.need);
         const uint32_t pos = gt ? rg + min(rq, b.need) : rg + rq;
         if (take) {
-            store_index(a, row, pos, e.y);
-            if (a.ret_val) store_value<K>(a, row, pos, K::value_bits(e.x));
+            store_index(o, pos, e.y);
+            if (o.val) store_value<K>(o, pos, K::value_bits(e.x));
         }
         gb += popc64(mg);
         qb += popc64(mq);
     }
-    if (!(any_amb && a.ret_val)) return;
+    if (!(any_amb && o.val)) return;
     gb = gb0;
     qb = qb0;
     for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
@@ -633,7 +655,7 @@ __device__ void write_from_list(const TopkArgs &a, int64_t row, const uint2 *ent
         const uint32_t rg = gb + lanes_below(mg), rq = qb + lanes_below(mq);
         const bool take = gt || (eq && rq < b.need);
         const uint32_t pos = gt ? rg + min(rq, b.need) : rg + rq;
-        if (take && K::ambiguous(e.x)) store_value<K>(a, row, pos, (uint32_t)xr[e.y]);
+        if (take && K::ambiguous(e.x)) store_value<K>(o, pos, (uint32_t)xr[e.y]);
         gb += popc64(mg);
         qb += popc64(mq);
     }
@@ -717,9 +739,11 @@ __device__ uint32_t range_counts(__amdgpu_buffer_rsrc_t view, int64_t base, int 
 // taken-above and equal counts of the columns before the range; each load is
 // one workgroup scan.
 template <class K>
-__device__ void write_from_stream(const TopkArgs &a, int64_t row, __amdgpu_buffer_rsrc_t view,
-                                  int64_t base, int len, Bound b, uint32_t gt0, uint32_t eq0,
-                                  uint32_t *s_red, const typename K::raw_t *xr) {
+__device__ __forceinline__ void write_from_stream(const TopkArgs &a, int64_t row,
+                                                  __amdgpu_buffer_rsrc_t view, int64_t base,
+                                                  int len, Bound b, uint32_t gt0, uint32_t eq0,
+                                                  uint32_t *s_red, const typename K::raw_t *xr) {
+    const RowOut o = row_out<K>(a, row);
     constexpr int VEC = K::VEC, EPW = K::EPW;
     const int loads = (len + NT * VEC - 1) / (NT * VEC);
     uint32_t gb = gt0, qb = eq0;
@@ -728,8 +752,8 @@ __device__ void write_from_stream(const TopkArgs &a, int64_t row, __amdgpu_buffe
         uint32_t w4[4];
         reload_keys<K>(view, base, len, j, w4);
         const uint32_t mine = load_counts<K>(w4, b);
-        uint32_t tot;
-        const uint32_t ex = block_incl_scan(mine, s_red, &tot) - mine;
+        const Scan sc = block_scan(mine, s_red);
+        const uint32_t ex = sc.incl - mine, tot = sc.total;
         uint32_t g1 = gb + (ex & 0xFFFFu), q1 = qb + (ex >> 16);
         const uint32_t p = (uint32_t)(base + (int64_t)(j * NT + tid()) * VEC);
 #pragma unroll
@@ -740,10 +764,10 @@ __device__ void write_from_stream(const TopkArgs &a, int64_t row, __amdgpu_buffe
                 const uint32_t pre = key >> b.s;
                 const uint32_t col = p + qq * EPW + h;
                 if (key && pre > b.P) {
-                    emit<K>(a, row, g1 + min(q1, b.need), col, key, xr);
+                    emit<K>(o, g1 + min(q1, b.need), col, key, xr);
                     ++g1;
                 } else if (key && pre == b.P) {
-                    if (q1 < b.need) emit<K>(a, row, g1 + q1, col, key, xr);
+                    if (q1 < b.need) emit<K>(o, g1 + q1, col, key, xr);
                     ++q1;
                 }
             }
@@ -870,13 +894,12 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
                 cnt_i = ld_agent(gcnt + 4 * i + 1);
                 nn |= ld_agent(gcnt + 4 * i + 2);
             }
-            uint32_t tot;
-            const uint32_t incl = block_incl_scan(cnt_i, L.red, &tot);
+            const Scan sc = block_scan(cnt_i, L.red);
             if (i < G) {
-                L.hist[i] = base + incl - cnt_i;
+                L.hist[i] = base + sc.incl - cnt_i;
                 L.hist[kMaxSplit + i] = off_i;
             }
-            base += tot;
+            base += sc.total;
         }
         const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
         // each entry's workgroup: the last one whose list start is <= idx,
@@ -955,8 +978,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         }
     }
     // this workgroup's totals, then the totals of the workgroups before it
-    uint32_t tot;
-    block_incl_scan(range_counts<K>(view, lo, len, b), L.red, &tot);
+    const uint32_t tot = block_scan(range_counts<K>(view, lo, len, b), L.red).total;
     if (t == 0) {
         st_agent(gcnt + 4 * c + 0, tot & 0xFFFFu);
         st_agent(gcnt + 4 * c + 1, tot >> 16);
@@ -971,9 +993,8 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         }
         nn |= ld_agent(gcnt + 4 * i + 2);
     }
-    uint32_t gt0, eq0;
-    block_incl_scan(gg, L.red, &gt0);
-    block_incl_scan(qq, L.red, &eq0);
+    const uint32_t gt0 = block_scan(gg, L.red).total;
+    const uint32_t eq0 = block_scan(qq, L.red).total;
     const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
     write_from_stream<K>(a, row, view, lo, len, b, gt0, eq0, L.red, xr);
     if (c == 0 && t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)row_nan;
