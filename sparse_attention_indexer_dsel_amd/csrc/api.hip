@@ -54,27 +54,39 @@ int64_t candidate_cap(int64_t k, int64_t row_len) {
     return (cap + 255) / 256 * 256;
 }
 
-// Smallest instantiated per-thread segment (elements) covering `cols`
-// columns with one workgroup.
-int pick_ept(int dtype, int64_t cols) {
-    (void)dtype;
-    for (int e = 8; e <= kMaxEpt; e *= 2)
+// A split row's workgroup lists only its own chunk's candidates: room for
+// twice an even share of the row's, plus 512, and never more than the chunk
+// or the whole-row capacity.  A workgroup holding more (ties, or values that
+// crowd into one chunk) takes the slower path.
+int64_t chunk_cap(int64_t k, int64_t cols, int64_t chunk, int G) {
+    const int64_t row_cap = candidate_cap(k, cols);
+    int64_t cap = 2 * row_cap / G + 512;
+    if (cap > row_cap) cap = row_cap;
+    if (cap > chunk) cap = chunk;
+    return (cap + 255) / 256 * 256;
+}
+
+// Smallest instantiated per-thread element count covering `cols` columns
+// with one workgroup (up to `max_ept`).
+int pick_ept(int64_t cols, int max_ept) {
+    for (int e = 8; e <= max_ept; e *= 2)
         if ((int64_t)kTopkThreads * e >= cols) return e;
     return 0;
 }
 
 // Workgroups per row: one when the row fits a workgroup and there are enough
-// rows to occupy the GPU, otherwise enough to hold the row and to give the
-// GPU about two workgroups per compute unit, but no fewer than 2048 columns
-// each.  DSEL_BLOCKS_PER_ROW overrides the choice (tuning and tests).
+// rows to occupy the GPU; otherwise enough to give the GPU about four
+// workgroups per compute unit, but no fewer than 4096 columns each, and at
+// least enough to hold the row in VGPRs.  DSEL_BLOCKS_PER_ROW overrides the
+// choice (tuning and tests).
 int choose_G(int64_t rows, int64_t cols, int cus) {
-    const int64_t gmin = cdiv(cols, kBlockCapacity);
+    const int64_t gmin = cdiv(cols, kChunkCapacity);
     int64_t G;
-    if (gmin <= 1 && rows >= cus / 2) {
+    if (cols <= kBlockCapacity && rows >= cus / 2) {
         G = 1;
     } else {
-        const int64_t gpar = cdiv(2 * (int64_t)cus, rows > 0 ? rows : 1);
-        const int64_t gchunk = cdiv(cols, 2048);
+        const int64_t gpar = cdiv(4 * (int64_t)cus, rows > 0 ? rows : 1);
+        const int64_t gchunk = cdiv(cols, 4096);
         G = gpar < gchunk ? gpar : gchunk;
         if (G < gmin) G = gmin;
         if (G < 1) G = 1;
@@ -98,12 +110,12 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
         G = (int)cdiv(cols, chunk);  // rounding may leave fewer workgroups
     }
     if (G > kMaxSplit) return DSEL_ERR_ARG;  // row longer than the split limit holds
-    if (G <= 1) {
+    if (G <= 1 && cols <= kBlockCapacity) {
         // persistent workgroups, each walking rows with its next row's loads
         // in flight: as many as the GPU holds at once
         pl->split = false;
         pl->G = 1;
-        pl->ept = pick_ept(dtype, cols);
+        pl->ept = pick_ept(cols, kMaxEpt);
         if (!pl->ept) return DSEL_ERR_ARG;
         pl->chunk = cols;
         pl->cap = candidate_cap(k, cols);
@@ -119,9 +131,9 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
         pl->ws_bytes = 0;
         return DSEL_OK;
     }
-    const int ept = pick_ept(dtype, chunk);
+    const int ept = pick_ept(chunk, kMaxSplitEpt);
     if (!ept) return DSEL_ERR_ARG;
-    const int64_t cap = candidate_cap(k, cols);
+    const int64_t cap = chunk_cap(k, cols, chunk, G);
     // every workgroup of a row must be resident at once: size launches by
     // the number of workgroups the GPU holds
     int per_cu = 0;
@@ -141,7 +153,7 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     pl->cap = cap;
     pl->rows_per_launch = rpl;
     pl->grid = rpl * G;
-    pl->slot_words = slot_words(G, cap);
+    pl->slot_words = slot_words(G);
     pl->ws_bytes = (size_t)(kHeaderWords + rpl * pl->slot_words) * sizeof(uint32_t);
     return DSEL_OK;
 }

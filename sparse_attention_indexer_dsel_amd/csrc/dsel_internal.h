@@ -9,10 +9,13 @@ namespace dsel {
 
 // Workgroup shape of every top-k kernel: four wave64s.
 constexpr int kTopkThreads = 256;
-// Largest per-thread element count instantiated; on-chip row capacity is
-// kTopkThreads * kMaxEpt elements per workgroup.
+// Largest per-thread element count of a whole row (one workgroup per row,
+// the next row's loads double-buffered in VGPRs) and of one split-row chunk
+// (single-buffered); a workgroup holds kTopkThreads times that many columns.
 constexpr int kMaxEpt = 64;
+constexpr int kMaxSplitEpt = 128;
 constexpr int64_t kBlockCapacity = (int64_t)kTopkThreads * kMaxEpt;
+constexpr int64_t kChunkCapacity = (int64_t)kTopkThreads * kMaxSplitEpt;
 // First-pass digit width: 2048 histogram bins in LDS.
 constexpr int kBins = 2048;
 // Workspace header (32-bit words) ahead of the per-row rendezvous slots;
@@ -24,9 +27,9 @@ constexpr int kMaxPasses = 3;
 constexpr int kMaxSplit = 1024;
 
 // Per-row workspace slot (32-bit words): counters, one histogram per radix
-// pass, per-workgroup counts, and the staged candidate list (keys, columns).
-inline int64_t slot_words(int G, int64_t cap) {
-    return kSlotHeadWords + (int64_t)kMaxPasses * kBins + 4 * (int64_t)G + 2 * cap;
+// pass and per-workgroup counts.
+inline int64_t slot_words(int G) {
+    return kSlotHeadWords + (int64_t)kMaxPasses * kBins + 4 * (int64_t)G;
 }
 
 struct TopkArgs {
@@ -44,7 +47,7 @@ struct TopkArgs {
     int64_t row0;            // first row of this launch
     int64_t chunk;           // columns per workgroup (split rows only)
     int64_t slot_words;      // 32-bit words per row slot (split rows only)
-    int64_t cap;             // capacity of the candidate list (entries)
+    int64_t cap;             // capacity of a workgroup's candidate list (entries)
     int k;
     int G;                   // workgroups per row
     int idx64;

@@ -29,12 +29,14 @@
 //     ballots, so the write needs one cross-wave exchange and no more
 //     barriers.  The output is ascending by construction; no sort is run;
 //   * rows too long for one workgroup, or too few rows to fill the GPU, are
-//     split over G workgroups: their histograms meet in a per-row workspace
-//     slot (device-scope relaxed atomics, one rendezvous); each stages its
-//     candidates there and the last workgroup to finish runs the selection;
-//   * if a row's candidate list would not fit (massive ties at the
-//     threshold), the radix select finishes over the keys still in VGPRs
-//     (slower, same result).
+//     split over G workgroups, each holding one chunk: their histograms meet
+//     in a per-row workspace slot (device-scope relaxed atomics and a
+//     rendezvous per radix pass); each workgroup lists its own candidates,
+//     and after one more exchange (the counts of the chunks before it) writes
+//     its part of the row's output;
+//   * if a candidate list would not fit (massive ties at the threshold), the
+//     radix select finishes over the range re-read from cache (slower, same
+//     result).
 #include "dsel_internal.h"
 
 namespace dsel {
@@ -219,13 +221,7 @@ __device__ Digit find_digit(const uint32_t *hist, int nb, uint32_t need, uint32_
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t ld_agent64(const uint64_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent64(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t add_agent(uint32_t *p, uint32_t v) {
@@ -475,13 +471,27 @@ __device__ __forceinline__ void first_digit_histogram(const uint32_t (&kw)[LOADS
     }
 }
 
-// Compact the candidates (key >= T1) of a workgroup's keys into ent[0, run)
-// in column order (entry = (key, col0 + column)); returns run.  Every element
-// is written once, the non-candidates to this lane's spare entry at
-// ent[cap + lane], so the loop has no branches.  wtot holds LP*NWAVE words.
-template <class K, int LOADS>
+// A candidate list in LDS: keys and columns in separate arrays (so a key and
+// its column never have to sit in adjacent VGPRs for one 64-bit store), cap
+// entries plus one spare entry per lane.
+struct List {
+    uint32_t *key;
+    uint32_t *col;
+};
+
+__device__ __forceinline__ List list_of(uint32_t *s_dyn, uint32_t cap) {
+    return List{s_dyn, s_dyn + cap + 64};
+}
+
+// Compact the candidates (key >= T1, T1 > 0) of a workgroup's keys into
+// ent[0, run) in column order (entry = (key, col0 + column)); returns run.
+// Every element is written once, the non-candidates to this lane's spare
+// entry at ent[cap + lane], so the loop has no branches.  CHECKED: when more
+// than `cap` qualify nothing is written (the count is still returned).  wtot
+// holds LP*NWAVE words.
+template <class K, int LOADS, bool CHECKED = false>
 __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4], int len,
-                                                       uint32_t T1, uint32_t *wtot, uint2 *ent,
+                                                       uint32_t T1, uint32_t *wtot, List ent,
                                                        uint32_t cap, uint32_t col0) {
     constexpr int VEC = K::VEC, EPW = K::EPW, LP = (LOADS + 1) / 2, SPAN = NT * VEC;
     const int t = tid();
@@ -510,6 +520,15 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
         if (lane == 63) wtot[i * NWAVE + wid] = incl;
     }
     __syncthreads();
+    if (CHECKED) {
+        uint32_t total = 0;
+#pragma unroll
+        for (int i = 0; i < LP * NWAVE; ++i) {
+            const uint32_t v = wtot[i];
+            total += (v & 0xFFFFu) + (v >> 16);
+        }
+        if (total > cap) return total;  // uniform
+    }
     const uint32_t T1w = opaque(T1);
 #pragma unroll
     for (int w = 0; w < LOADS * 4; ++w) kw[w] = opaque(kw[w]);
@@ -535,7 +554,9 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
                 for (int h = 0; h < EPW; ++h) {
                     const uint32_t key = K::elem(kw[4 * j + q], h);
                     const bool cand = key >= T1w;
-                    ent[cand ? pos : spare] = make_uint2(key, p + q * EPW + h);
+                    const uint32_t d = cand ? pos : spare;
+                    ent.key[d] = key;
+                    ent.col[d] = p + q * EPW + h;
                     pos += cand ? 1u : 0u;
                 }
         }
@@ -552,10 +573,30 @@ struct Bound {
     uint32_t need;
 };
 
+// Histogram of the next digit ((key >> sh) & dmask) of the list entries
+// whose top bits (key >> s) equal P (hist zeroed).  Reads are unconditional
+// (clamped index, masked result) so several are in flight.
+__device__ __forceinline__ void list_refine_histogram(List ent, uint32_t C, uint32_t P, int s,
+                                                      int sh, uint32_t dmask, uint32_t *hist) {
+    constexpr int U = 4;
+    for (uint32_t i0 = 0; i0 < C; i0 += U * NT) {
+        uint32_t key[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i = i0 + u * NT + tid();
+            const uint32_t kk = ent.key[i < C ? i : 0u];
+            key[u] = i < C ? kk : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (key[u] && (key[u] >> s) == P) atomicAdd(&hist[(key[u] >> sh) & dmask], 1u);
+    }
+}
+
 // Resolve the digits after the first among the candidate list's entries
 // (every entry's first digit is >= d1.v).
 template <class K>
-__device__ Bound refine_on_list(const uint2 *ent, uint32_t C, Digit d1, uint32_t k,
+__device__ Bound refine_on_list(List ent, uint32_t C, Digit d1, uint32_t k,
                                 uint32_t *s_hist, uint32_t *s_red, uint32_t *s_out) {
     const int t = tid();
     Bound b{d1.v, K::SH1, k - d1.above};
@@ -564,14 +605,10 @@ __device__ Bound refine_on_list(const uint2 *ent, uint32_t C, Digit d1, uint32_t
     for (int pass = 1; pass < K::NPASS; ++pass) {
         const int d = K::digit(pass);
         const int sh = b.s - d;
-        const uint32_t dmask = (1u << d) - 1u;
         const int nb = 1 << d;
         for (int i = t; i < nb; i += NT) s_hist[i] = 0;
         __syncthreads();
-        for (uint32_t i = t; i < C; i += NT) {
-            const uint32_t key = ent[i].x;
-            if ((key >> b.s) == b.P) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
-        }
+        list_refine_histogram(ent, C, b.P, b.s, sh, (1u << d) - 1u, s_hist);
         __syncthreads();
         const Digit dg = find_digit(s_hist, nb, b.need, s_red, s_out);
         b.need -= dg.above;
@@ -582,38 +619,60 @@ __device__ Bound refine_on_list(const uint2 *ent, uint32_t C, Digit d1, uint32_t
     return b;
 }
 
-// Write the selection from a column-ordered candidate list.  Wave w owns
-// entries [w*Q, (w+1)*Q) (Q a multiple of 64); ranks within a wave come from
-// ballots, and one exchange of the waves' counts (through s_red) gives each
-// wave its starting ranks.  Values are rebuilt from keys, so the write loop
+// This workgroup's list totals: entries taken above the boundary (top bits >
+// P) and entries at it (== P), packed (equal << 16 | above).
+__device__ uint32_t list_counts(List ent, uint32_t C, Bound b, uint32_t *s_red) {
+    uint32_t g = 0, q = 0;
+    for (uint32_t i0 = 0; i0 < C; i0 += NT) {
+        const uint32_t i = i0 + tid();
+        const uint32_t kk = ent.key[i < C ? i : 0u];
+        const uint32_t key = i < C ? kk : 0u;
+        g += (key && (key >> b.s) > b.P) ? 1u : 0u;
+        q += (key && (key >> b.s) == b.P) ? 1u : 0u;
+    }
+    return block_scan(g | (q << 16), s_red).total;
+}
+
+// Write the selection from a column-ordered candidate list whose columns are
+// relative to col0; gt0 / eq0 are the taken-above and equal counts of the
+// row's columns before the list's.  Wave w owns entries [w*Q, (w+1)*Q) (Q a
+// multiple of 64); ranks within a wave come from ballots, and one exchange
+// of the waves' counts (through s_red) gives each wave its starting ranks.  Values are rebuilt from keys, so the write loop
 // issues no loads (a load in it would make every store wait for the ones
 // before it); the rare +-0 / NaN keys get their bits from the row in a
 // second pass, run only when some wave holds one.
 template <class K>
-__device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, const uint2 *ent,
+__device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, List ent,
                                                 uint32_t C, Bound b, uint32_t *s_red,
-                                                const typename K::raw_t *xr) {
+                                                const typename K::raw_t *xr, uint32_t gt0 = 0,
+                                                uint32_t eq0 = 0, uint32_t col0 = 0) {
     const RowOut o = row_out<K>(a, row);
     const int t = tid();
     const int lane = t & 63, wid = t >> 6;
     const uint32_t Q = (C + NT - 1) / NT * 64;  // <= 2048
     const uint32_t b0 = (uint32_t)wid * Q;
     const uint32_t b1 = min(C, b0 + Q);
+    // entry i of this wave's range, read unconditionally (clamped, then
+    // masked) so several reads can be in flight
+    auto entry = [&](uint32_t i) {
+        const uint32_t j = i < b1 ? i : 0u;
+        const uint32_t key = ent.key[j], col = ent.col[j];
+        return i < b1 ? make_uint2(key, col) : make_uint2(0u, 0u);
+    };
     uint32_t g = 0, q = 0;
     uint64_t amb = 0;
-    for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
-        const uint32_t i = i0 + (uint32_t)lane;
-        const bool in = i < b1;
-        const uint32_t key = in ? ent[i].x : 0u;
-        const uint32_t pre = key >> b.s;
-        const bool gt = in && pre > b.P, eq = in && pre == b.P;
-        g += popc64(__ballot(gt));
-        q += popc64(__ballot(eq));
-        amb |= __ballot((gt || eq) && K::ambiguous(key));
+    for (uint32_t i0 = b0; i0 < b1; i0 += 128) {
+        const uint2 e0 = entry(i0 + (uint32_t)lane), e1 = entry(i0 + 64 + (uint32_t)lane);
+        const uint32_t p0 = e0.x >> b.s, p1 = e1.x >> b.s;
+        const bool gt0 = e0.x && p0 > b.P, eq0 = e0.x && p0 == b.P;
+        const bool gt1 = e1.x && p1 > b.P, eq1 = e1.x && p1 == b.P;
+        g += popc64(__ballot(gt0)) + popc64(__ballot(gt1));
+        q += popc64(__ballot(eq0)) + popc64(__ballot(eq1));
+        amb |= __ballot(((gt0 || eq0) && K::ambiguous(e0.x)) || ((gt1 || eq1) && K::ambiguous(e1.x)));
     }
     if (lane == 0) s_red[wid] = g | (q << 12) | (amb ? 1u << 24 : 0u);
     __syncthreads();
-    uint32_t gb = 0, qb = 0, any_amb = 0;
+    uint32_t gb = gt0, qb = eq0, any_amb = 0;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) {
         const uint32_t v = s_red[w];
@@ -623,39 +682,39 @@ __device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, 
     }
     __syncthreads();
     const uint32_t gb0 = gb, qb0 = qb;
-    for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
-        const uint32_t i = i0 + (uint32_t)lane;
-        const bool in = i < b1;
-        const uint2 e = in ? ent[i] : make_uint2(0u, 0u);
-        const uint32_t pre = e.x >> b.s;
-        const bool gt = in && pre > b.P;
-        const bool eq = in && pre == b.P;
-        const uint64_t mg = __ballot(gt), mq = __ballot(eq);
-        const uint32_t rg = gb + lanes_below(mg), rq = qb + lanes_below(mq);
-        const bool take = gt || (eq && rq < b.need);
-        const uint32_t pos = gt ? rg + min(rq, b.need) : rg + rq;
-        if (take) {
-            store_index(o, pos, e.y);
-            if (o.val) store_value<K>(o, pos, K::value_bits(e.x));
+    for (uint32_t i0 = b0; i0 < b1; i0 += 128) {
+        const uint2 ee[2] = {entry(i0 + (uint32_t)lane), entry(i0 + 64 + (uint32_t)lane)};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint2 e = ee[h];
+            const uint32_t pre = e.x >> b.s;
+            const bool gt = e.x && pre > b.P;
+            const bool eq = e.x && pre == b.P;
+            const uint64_t mg = __ballot(gt), mq = __ballot(eq);
+            const uint32_t rg = gb + lanes_below(mg), rq = qb + lanes_below(mq);
+            const bool take = gt || (eq && rq < b.need);
+            const uint32_t pos = gt ? rg + min(rq, b.need) : rg + rq;
+            if (take) {
+                store_index(o, pos, e.y + col0);
+                if (o.val) store_value<K>(o, pos, K::value_bits(e.x));
+            }
+            gb += popc64(mg);
+            qb += popc64(mq);
         }
-        gb += popc64(mg);
-        qb += popc64(mq);
     }
     if (!(any_amb && o.val)) return;
     gb = gb0;
     qb = qb0;
     for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
-        const uint32_t i = i0 + (uint32_t)lane;
-        const bool in = i < b1;
-        const uint2 e = in ? ent[i] : make_uint2(0u, 0u);
+        const uint2 e = entry(i0 + (uint32_t)lane);
         const uint32_t pre = e.x >> b.s;
-        const bool gt = in && pre > b.P;
-        const bool eq = in && pre == b.P;
+        const bool gt = e.x && pre > b.P;
+        const bool eq = e.x && pre == b.P;
         const uint64_t mg = __ballot(gt), mq = __ballot(eq);
         const uint32_t rg = gb + lanes_below(mg), rq = qb + lanes_below(mq);
         const bool take = gt || (eq && rq < b.need);
         const uint32_t pos = gt ? rg + min(rq, b.need) : rg + rq;
-        if (take && K::ambiguous(e.x)) store_value<K>(o, pos, (uint32_t)xr[e.y]);
+        if (take && K::ambiguous(e.x)) store_value<K>(o, pos, (uint32_t)xr[e.y + col0]);
         gb += popc64(mg);
         qb += popc64(mq);
     }
@@ -807,7 +866,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     constexpr int LP = (LOADS + 1) / 2;
     static_assert(EPT % VEC == 0, "EPT must be a multiple of the vector width");
 
-    extern __shared__ uint2 s_ent[];  // candidate list (cap entries) + one spare per lane
+    extern __shared__ uint32_t s_dyn[];  // candidate list (cap entries + one spare per lane)
     __shared__ TopkLds<LP> L;
 
     const int t = tid();
@@ -825,11 +884,11 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     }
 
     const uint32_t cap = (uint32_t)a.cap;
+    const List ent = list_of(s_dyn, cap);
     uint32_t *slot = a.ws + kHeaderWords + lrow * a.slot_words;
     uint32_t *err = a.ws;
     uint32_t *ghist = slot + kSlotHeadWords;
     uint32_t *gcnt = ghist + kMaxPasses * kBins;
-    uint64_t *stage = reinterpret_cast<uint64_t *>(gcnt + 4 * G);
 
     // ---- this workgroup's columns into VGPRs; first-digit histogram --------
     const int64_t lo = (int64_t)c * a.chunk;
@@ -856,132 +915,73 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     fetch_histogram(ghist, L.hist, kBins);
     __syncthreads();
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
-    const uint32_t C = d1.above + d1.cnt;
 
-    if (C <= cap) {
-        // ---- stage this workgroup's candidates; the last one finishes ------
-        const uint32_t run =
-            compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, s_ent, cap, 0u);
-        if (t == 0) L.out[4] = run ? add_agent(slot + 2, run) : 0u;
-        __syncthreads();
-        const uint32_t off = L.out[4];
-        for (uint32_t i = t; i < run; i += NT) {
-            const uint2 e = s_ent[i];
-            st_agent64(stage + off + i, (uint64_t)e.x | ((uint64_t)(e.y + (uint32_t)lo) << 32));
-        }
-        if (t == 0) {
-            st_agent(gcnt + 4 * c + 0, off);
-            st_agent(gcnt + 4 * c + 1, run);
-            st_agent(gcnt + 4 * c + 2, block_nan);
-        }
-        drain_memory();
-        __syncthreads();
-        if (t == 0) L.out[3] = (add_agent(slot + 1, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
-        __syncthreads();
-        if (!L.out[3]) return;
-
-        // Last workgroup: every other one has staged its candidates.  Its
-        // list position = exclusive prefix of the counts in workgroup
-        // (= column) order; the staged position comes from the workgroup's
-        // staging offset.  L.hist[0, G) <- list starts, L.hist[kMaxSplit, +G)
-        // <- staging offsets (G <= kMaxSplit <= kBins / 2).
-        uint32_t nn = 0, base = 0;
-        for (int i0 = 0; i0 < G; i0 += NT) {
-            const int i = i0 + t;
-            uint32_t cnt_i = 0, off_i = 0;
-            if (i < G) {
-                off_i = ld_agent(gcnt + 4 * i + 0);
-                cnt_i = ld_agent(gcnt + 4 * i + 1);
-                nn |= ld_agent(gcnt + 4 * i + 2);
-            }
-            const Scan sc = block_scan(cnt_i, L.red);
-            if (i < G) {
-                L.hist[i] = base + sc.incl - cnt_i;
-                L.hist[kMaxSplit + i] = off_i;
-            }
-            base += sc.total;
-        }
-        const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
-        // each entry's workgroup: the last one whose list start is <= idx,
-        // found by binary lifting (all BATCH searches interleaved)
-        int top = 1;
-        while (top * 2 <= G) top *= 2;
-        constexpr int BATCH = 16;
-        for (uint32_t i0 = 0; i0 < C; i0 += BATCH * NT) {
-            int blk[BATCH];
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u) blk[u] = 0;
-            for (int step = top; step > 0; step >>= 1) {
-#pragma unroll
-                for (int u = 0; u < BATCH; ++u) {
-                    const uint32_t idx = i0 + u * NT + t;
-                    const int cand = blk[u] + step;
-                    if (cand < G && L.hist[cand] <= idx) blk[u] = cand;
-                }
-            }
-            uint64_t v[BATCH];
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                const uint32_t idx = i0 + u * NT + t;
-                v[u] = idx < C ? ld_agent64(stage + L.hist[kMaxSplit + blk[u]] + (idx - L.hist[blk[u]]))
-                               : 0ull;
-            }
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                const uint32_t idx = i0 + u * NT + t;
-                if (idx < C) s_ent[idx] = make_uint2((uint32_t)v[u], (uint32_t)(v[u] >> 32));
-            }
-        }
-        __syncthreads();
-        const Bound b = refine_on_list<K>(s_ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
-        write_from_list<K>(a, row, s_ent, C, b, L.red, xr);
-        if (t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)row_nan;
-        // Return the slot to zero for the next call, whose slot layout may
-        // differ (every other workgroup of the row is done with it; the
-        // stores complete before the launch does).
-        for (int i = t; i < kBins; i += NT) st_agent(ghist + i, 0u);
-        for (int i = t; i < 4 * G; i += NT) st_agent(gcnt + i, 0u);
-        for (uint32_t i = t; i < C; i += NT) st_agent64(stage + i, 0ull);
-        if (t == 0) {
-            st_agent(slot + 0, 0u);
-            st_agent(slot + 1, 0u);
-            st_agent(slot + 2, 0u);
-        }
-        return;
-    }
-
-    // ---- slow path: too many candidates for the list.  Finish the radix
-    // select over this workgroup's range re-read from cache, one rendezvous
-    // per pass.
-    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
+    // ---- this workgroup's candidates (key >= T1) to an LDS list; the rest of
+    // the radix select runs on the lists, one rendezvous per pass.  A
+    // workgroup whose candidates do not fit its list (massive ties, or a row
+    // whose largest values crowd into one chunk) re-reads its range from
+    // cache instead; both ways take part in the same rendezvous.
     Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
-    if (d1.cnt != b.need) {
+    uint32_t mine;  // this workgroup's (equal << 16 | above) counts at the boundary
+    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
+    const uint32_t run =
+        compact_candidates<K, LOADS, true>(kw, len, d1.v << K::SH1, L.wtot, ent, cap, 0u);
+    const bool listed = run <= cap;  // uniform over the workgroup
+    if (listed) {
+        if (d1.cnt != b.need) {
 #pragma unroll 1
-        for (int pass = 1; pass < K::NPASS; ++pass) {
-            const int d = K::digit(pass);
-            const int sh = b.s - d;
-            const int nb = 1 << d;
-            for (int i = t; i < nb; i += NT) L.hist[i] = 0;
-            __syncthreads();
-            refine_histogram_stream<K>(view, lo, len, b.P, b.s, sh, (1u << d) - 1u, L.hist);
-            __syncthreads();
-            uint32_t *g = ghist + pass * kBins;
-            merge_histogram(L.hist, g, nb);
-            row_rendezvous(slot, (++nren) * (uint32_t)G, err);
-            fetch_histogram(g, L.hist, nb);
-            __syncthreads();
-            const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
-            b.need -= dg.above;
-            b.P = (b.P << d) | dg.v;
-            b.s = sh;
-            if (dg.cnt == b.need) break;  // the boundary bin is taken whole
+            for (int pass = 1; pass < K::NPASS; ++pass) {
+                const int d = K::digit(pass);
+                const int sh = b.s - d;
+                const int nb = 1 << d;
+                for (int i = t; i < nb; i += NT) L.hist[i] = 0;
+                __syncthreads();
+                list_refine_histogram(ent, run, b.P, b.s, sh, (1u << d) - 1u, L.hist);
+                __syncthreads();
+                uint32_t *g = ghist + pass * kBins;
+                merge_histogram(L.hist, g, nb);
+                row_rendezvous(slot, (++nren) * (uint32_t)G, err);
+                fetch_histogram(g, L.hist, nb);
+                __syncthreads();
+                const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
+                b.need -= dg.above;
+                b.P = (b.P << d) | dg.v;
+                b.s = sh;
+                if (dg.cnt == b.need) break;  // the boundary bin is taken whole
+            }
         }
+        mine = list_counts(ent, run, b, L.red);
+    } else {
+        if (d1.cnt != b.need) {
+#pragma unroll 1
+            for (int pass = 1; pass < K::NPASS; ++pass) {
+                const int d = K::digit(pass);
+                const int sh = b.s - d;
+                const int nb = 1 << d;
+                for (int i = t; i < nb; i += NT) L.hist[i] = 0;
+                __syncthreads();
+                refine_histogram_stream<K>(view, lo, len, b.P, b.s, sh, (1u << d) - 1u, L.hist);
+                __syncthreads();
+                uint32_t *g = ghist + pass * kBins;
+                merge_histogram(L.hist, g, nb);
+                row_rendezvous(slot, (++nren) * (uint32_t)G, err);
+                fetch_histogram(g, L.hist, nb);
+                __syncthreads();
+                const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
+                b.need -= dg.above;
+                b.P = (b.P << d) | dg.v;
+                b.s = sh;
+                if (dg.cnt == b.need) break;  // the boundary bin is taken whole
+            }
+        }
+        mine = block_scan(range_counts<K>(view, lo, len, b), L.red).total;
     }
-    // this workgroup's totals, then the totals of the workgroups before it
-    const uint32_t tot = block_scan(range_counts<K>(view, lo, len, b), L.red).total;
+
+    // ---- the counts of the workgroups before this one; each writes its own
+    // part of the row's output ----------------------------------------------
     if (t == 0) {
-        st_agent(gcnt + 4 * c + 0, tot & 0xFFFFu);
-        st_agent(gcnt + 4 * c + 1, tot >> 16);
+        st_agent(gcnt + 4 * c + 0, mine & 0xFFFFu);
+        st_agent(gcnt + 4 * c + 1, mine >> 16);
         st_agent(gcnt + 4 * c + 2, block_nan);
     }
     row_rendezvous(slot, (++nren) * (uint32_t)G, err);
@@ -996,13 +996,17 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     const uint32_t gt0 = block_scan(gg, L.red).total;
     const uint32_t eq0 = block_scan(qq, L.red).total;
     const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
-    write_from_stream<K>(a, row, view, lo, len, b, gt0, eq0, L.red, xr);
+    if (listed)
+        write_from_list<K>(a, row, ent, run, b, L.red, xr, gt0, eq0, (uint32_t)lo);
+    else
+        write_from_stream<K>(a, row, view, lo, len, b, gt0, eq0, L.red, xr);
     if (c == 0 && t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)row_nan;
 
     // Leave the slot zeroed for the next call (whose slot layout may differ):
     // every workgroup has read the histograms before the last rendezvous, so
     // each clears a share now; the last workgroup out, once every workgroup
-    // has read the counts, clears them and resets the counters.
+    // has read the counts, clears them and resets the counters.  The stores
+    // complete before the launch does.
     constexpr int HW = kMaxPasses * kBins;
     const int per = (HW + G - 1) / G;
     const int z0 = c * per, z1 = min(HW, z0 + per);
@@ -1013,8 +1017,6 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     __syncthreads();
     if (L.out[3]) {
         for (int i = t; i < 4 * G; i += NT) st_agent(gcnt + i, 0u);
-        drain_memory();
-        __syncthreads();
         if (t == 0) {
             st_agent(slot + 0, 0u);
             st_agent(slot + 1, 0u);
@@ -1041,7 +1043,7 @@ __device__ __forceinline__ void prefetch_row(const typename K::raw_t *xr, int64_
 template <class K, int LOADS>
 __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64_t n,
                                            const uint4 (&buf)[LOADS],
-                                           TopkLds<(LOADS + 1) / 2> &L, uint2 *ent) {
+                                           TopkLds<(LOADS + 1) / 2> &L, List ent) {
     using raw_t = typename K::raw_t;
     const int t = tid();
     const uint32_t cap = (uint32_t)a.cap;
@@ -1052,6 +1054,7 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
     const uint32_t nan = keys_of_loads<K, LOADS>(buf, len, kw);
     for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
     const uint32_t block_nan = __syncthreads_or((int)nan) ? 1u : 0u;
+
     first_digit_histogram<K, LOADS>(kw, len, L.hist);
     __syncthreads();
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
@@ -1095,8 +1098,9 @@ __global__ __launch_bounds__(NT) void topk_rows_pipelined(const TopkArgs a) {
     using raw_t = typename K::raw_t;
     constexpr int LOADS = EPT / K::VEC;
     static_assert(EPT % K::VEC == 0, "EPT must be a multiple of the vector width");
-    extern __shared__ uint2 s_ent[];  // candidate list (cap entries) + one spare per lane
+    extern __shared__ uint32_t s_dyn[];  // candidate list (cap entries + one spare per lane)
     __shared__ TopkLds<(LOADS + 1) / 2> L;
+    const List ent = list_of(s_dyn, (uint32_t)a.cap);
 
     const int64_t stride = gridDim.x;
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
@@ -1115,7 +1119,7 @@ __global__ __launch_bounds__(NT) void topk_rows_pipelined(const TopkArgs a) {
         if (n <= a.k)
             write_short_row<K>(a, row, n, 0, 1, x + row * a.x_stride);
         else
-            select_row<K, LOADS>(a, row, n, cur, L, s_ent);
+            select_row<K, LOADS>(a, row, n, cur, L, ent);
         __syncthreads();  // LDS is reused by the next row
         // the next row's vectors had this whole row's work to arrive
 #pragma unroll
@@ -1127,8 +1131,10 @@ __global__ __launch_bounds__(NT) void topk_rows_pipelined(const TopkArgs a) {
 
 template <class K, int EPT, bool SPLIT>
 const void *kptr() {
-    if (SPLIT) return reinterpret_cast<const void *>(&topk_rows_split<K, EPT>);
-    return reinterpret_cast<const void *>(&topk_rows_pipelined<K, EPT>);
+    if constexpr (SPLIT)
+        return reinterpret_cast<const void *>(&topk_rows_split<K, EPT>);
+    else
+        return reinterpret_cast<const void *>(&topk_rows_pipelined<K, EPT>);
 }
 
 template <class K, bool SPLIT>
@@ -1138,6 +1144,9 @@ const void *pick(int ept) {
         case 16: return kptr<K, 16, SPLIT>();
         case 32: return kptr<K, 32, SPLIT>();
         case 64: return kptr<K, 64, SPLIT>();
+        case 128:
+            if constexpr (SPLIT) return kptr<K, 128, true>();
+            return nullptr;
         default: return nullptr;
     }
 }
@@ -1151,7 +1160,8 @@ const void *topk_kernel_ptr(int dtype, int ept, bool split) {
     return split ? pick<F32Key, true>(ept) : pick<F32Key, false>(ept);
 }
 
-// Candidate entries (key, column) plus one spare entry per lane.
+// Candidate entries (key, column) plus one spare entry per lane, as two
+// arrays.
 size_t topk_dyn_lds(int dtype, int64_t cap) {
     (void)dtype;
     return (size_t)(cap + 64) * sizeof(uint2);
