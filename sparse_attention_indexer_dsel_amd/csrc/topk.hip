@@ -844,14 +844,30 @@ __device__ __forceinline__ int64_t valid_length(const TopkArgs &a, int64_t row) 
     return n;
 }
 
-// Shared memory of the top-k kernels (the histogram has one spare bin per
-// lane past kBins).
+// Dynamic LDS of the top-k kernels: the first-digit histogram (kBins bins
+// plus one spare bin per lane) at word 0, and the candidate list from word
+// list_base.  For bf16 the later radix pass needs only 32 bins, so the list
+// overlays the histogram once the first digit is found (the histogram is
+// dead by then); fp32's later passes need the full histogram beside it.
+template <class K>
+__host__ __device__ constexpr uint32_t list_base() {
+    return K::NPASS == 2 ? 64u : (uint32_t)(kBins + 64);
+}
+
+// Static LDS of the top-k kernels.
 template <int LP>
-struct TopkLds {
-    uint32_t hist[kBins + 64];
+struct TopkShared {
     uint32_t wtot[LP * NWAVE];
     uint32_t red[NWAVE];
     uint32_t out[8];
+};
+
+// The kernels' view of their LDS.
+struct TopkLds {
+    uint32_t *hist;
+    uint32_t *wtot;
+    uint32_t *red;
+    uint32_t *out;
 };
 
 // ---------------------------------------------------------------------------
@@ -866,8 +882,9 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     constexpr int LP = (LOADS + 1) / 2;
     static_assert(EPT % VEC == 0, "EPT must be a multiple of the vector width");
 
-    extern __shared__ uint32_t s_dyn[];  // candidate list (cap entries + one spare per lane)
-    __shared__ TopkLds<LP> L;
+    extern __shared__ uint32_t s_dyn[];  // histogram, candidate list
+    __shared__ TopkShared<LP> S;
+    const TopkLds L{s_dyn, S.wtot, S.red, S.out};
 
     const int t = tid();
     const int G = a.G;
@@ -884,7 +901,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     }
 
     const uint32_t cap = (uint32_t)a.cap;
-    const List ent = list_of(s_dyn, cap);
+    const List ent = list_of(s_dyn + list_base<K>(), cap);
     uint32_t *slot = a.ws + kHeaderWords + lrow * a.slot_words;
     uint32_t *err = a.ws;
     uint32_t *ghist = slot + kSlotHeadWords;
@@ -1043,7 +1060,7 @@ __device__ __forceinline__ void prefetch_row(const typename K::raw_t *xr, int64_
 template <class K, int LOADS>
 __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64_t n,
                                            const uint4 (&buf)[LOADS],
-                                           TopkLds<(LOADS + 1) / 2> &L, List ent) {
+                                           const TopkLds &L, List ent) {
     using raw_t = typename K::raw_t;
     const int t = tid();
     const uint32_t cap = (uint32_t)a.cap;
@@ -1098,9 +1115,10 @@ __global__ __launch_bounds__(NT) void topk_rows_pipelined(const TopkArgs a) {
     using raw_t = typename K::raw_t;
     constexpr int LOADS = EPT / K::VEC;
     static_assert(EPT % K::VEC == 0, "EPT must be a multiple of the vector width");
-    extern __shared__ uint32_t s_dyn[];  // candidate list (cap entries + one spare per lane)
-    __shared__ TopkLds<(LOADS + 1) / 2> L;
-    const List ent = list_of(s_dyn, (uint32_t)a.cap);
+    extern __shared__ uint32_t s_dyn[];  // histogram, candidate list
+    __shared__ TopkShared<(LOADS + 1) / 2> S;
+    const TopkLds L{s_dyn, S.wtot, S.red, S.out};
+    const List ent = list_of(s_dyn + list_base<K>(), (uint32_t)a.cap);
 
     const int64_t stride = gridDim.x;
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
@@ -1160,11 +1178,12 @@ const void *topk_kernel_ptr(int dtype, int ept, bool split) {
     return split ? pick<F32Key, true>(ept) : pick<F32Key, false>(ept);
 }
 
-// Candidate entries (key, column) plus one spare entry per lane, as two
-// arrays.
+// The histogram, and the candidate list (cap entries plus one spare per
+// lane, keys and columns) from list_base.
 size_t topk_dyn_lds(int dtype, int64_t cap) {
-    (void)dtype;
-    return (size_t)(cap + 64) * sizeof(uint2);
+    const uint64_t base = dtype == 0 ? list_base<Bf16Key>() : list_base<F32Key>();
+    const uint64_t words = base + 2 * (uint64_t)(cap + 64);
+    return (size_t)(words > (uint64_t)(kBins + 64) ? words : (uint64_t)(kBins + 64)) * 4;
 }
 
 hipError_t launch_topk(int dtype, int ept, bool split, const TopkArgs &a, unsigned grid,
