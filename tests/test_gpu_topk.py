@@ -127,6 +127,19 @@ def test_nan_just_past_row_end(dsel, orc, dt, G):
     assert not got[2].any(), "no row holds a NaN in range"
 
 
+@pytest.mark.parametrize("dist", ["ascending", "descending", "ties", "narrow"])
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_split_crowded_chunks(dsel, orc, dt, dist):
+    """Split rows whose candidates crowd into one chunk (ascending: the last,
+    descending: the first), so one workgroup's list overflows and it re-reads
+    its range while the others use their lists; ties and narrow ranges put
+    many keys at the boundary."""
+    x = W.random_rows(81 + len(dist), 5, 40000, dt, dist)
+    for k, G in ((2000, 8), (4096, 5), (37, 16)):
+        check_case(dsel, orc, f"crowded/{dist}/{dt}/k{k}/G{G}", x, k, None, True,
+                   torch.int64, True, G)
+
+
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
 def test_padded_stride(dsel, orc, dt):
     x = W.random_rows(31, 12, 2000, dt, "normal", stride=2048)
