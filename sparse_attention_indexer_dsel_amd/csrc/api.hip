@@ -122,7 +122,7 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                 &per_cu, topk_kernel_ptr(dtype, pl->ept, false), kTopkThreads,
-                topk_dyn_lds(dtype, pl->cap)) != hipSuccess ||
+                topk_dyn_lds(dtype, pl->cap, pl->ept, false)) != hipSuccess ||
             per_cu <= 0)
             return DSEL_ERR_DEVICE;
         const int64_t slots = (int64_t)per_cu * cus;
@@ -138,7 +138,7 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     // the number of workgroups the GPU holds
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, topk_kernel_ptr(dtype, ept, true),
-                                                     kTopkThreads, topk_dyn_lds(dtype, cap)) !=
+                                                     kTopkThreads, topk_dyn_lds(dtype, cap, ept, true)) !=
             hipSuccess ||
         per_cu <= 0)
         return DSEL_ERR_DEVICE;

@@ -59,7 +59,7 @@ const void *topk_kernel_ptr(int dtype, int ept, bool split);
 // Elements per 16-byte vector for a dtype.
 inline int topk_vec(int dtype) { return dtype == 0 ? 8 : 4; }
 // Dynamic LDS bytes of a top-k launch with candidate capacity `cap`.
-size_t topk_dyn_lds(int dtype, int64_t cap);
+size_t topk_dyn_lds(int dtype, int64_t cap, int ept, bool split);
 hipError_t launch_topk(int dtype, int ept, bool split, const TopkArgs &a, unsigned grid,
                        hipStream_t stream);
 

@@ -835,6 +835,83 @@ __device__ __forceinline__ void write_from_stream(const TopkArgs &a, int64_t row
     }
 }
 
+// ---- small ranges (at most two 16-byte loads per thread): no candidate
+// list.  The later radix passes and the ranked write work straight from the
+// keys in VGPRs, one workgroup scan per load, which costs less than listing
+// and re-reading the candidates when each thread holds a few elements.
+
+// Refine-pass histogram of keys held in VGPRs: the next digit of every key
+// whose top bits (key >> s) equal P.
+template <class K, int LOADS>
+__device__ __forceinline__ void refine_histogram_regs(const uint32_t (&kw)[LOADS * 4], uint32_t P,
+                                                      int s, int sh, uint32_t dmask,
+                                                      uint32_t *hist) {
+#pragma unroll
+    for (int w = 0; w < LOADS * 4; ++w)
+#pragma unroll
+        for (int h = 0; h < K::EPW; ++h) {
+            const uint32_t key = K::elem(kw[w], h);
+            if (key && (key >> s) == P) atomicAdd(&hist[(key >> sh) & dmask], 1u);
+        }
+}
+
+// This thread's (equal << 16 | above) counts over its keys.
+template <class K, int LOADS>
+__device__ __forceinline__ uint32_t counts_regs(const uint32_t (&kw)[LOADS * 4], Bound b) {
+    uint32_t g = 0, q = 0;
+#pragma unroll
+    for (int w = 0; w < LOADS * 4; ++w)
+#pragma unroll
+        for (int h = 0; h < K::EPW; ++h) {
+            const uint32_t key = K::elem(kw[w], h);
+            const uint32_t pre = key >> b.s;
+            g += (key && pre > b.P) ? 1u : 0u;
+            q += (key && pre == b.P) ? 1u : 0u;
+        }
+    return g | (q << 16);
+}
+
+// Write the selection from keys held in VGPRs (coalesced layout, columns
+// col0 + (j*NT + t)*VEC + ...); gt0 / eq0 are the taken-above and equal
+// counts of the row's columns before this range.  Values are rebuilt from
+// keys (+-0 / NaN keys read their bits back from the row).
+template <class K, int LOADS>
+__device__ __forceinline__ void write_from_regs(const TopkArgs &a, int64_t row,
+                                                const uint32_t (&kw)[LOADS * 4], int len, Bound b,
+                                                uint32_t gt0, uint32_t eq0, uint32_t col0,
+                                                uint32_t *s_red, const typename K::raw_t *xr) {
+    constexpr int VEC = K::VEC, EPW = K::EPW, SPAN = NT * VEC;
+    const RowOut o = row_out<K>(a, row);
+    const int t = tid();
+    const int any = (len + SPAN - 1) / SPAN;
+    uint32_t gb = gt0, qb = eq0;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        if (j < any) {
+            const uint32_t mine = counts_regs<K, 1>(
+                *reinterpret_cast<const uint32_t(*)[4]>(&kw[4 * j]), b);
+            const Scan sc = block_scan(mine, s_red);
+            uint32_t g1 = gb + ((sc.incl - mine) & 0xFFFFu), q1 = qb + ((sc.incl - mine) >> 16);
+            const uint32_t p = col0 + (uint32_t)(j * NT + t) * VEC;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                for (int h = 0; h < EPW; ++h) {
+                    const uint32_t key = K::elem(kw[4 * j + qq], h);
+                    const uint32_t pre = key >> b.s;
+                    const bool gt = key && pre > b.P, eq = key && pre == b.P;
+                    const bool take = gt || (eq && q1 < b.need);
+                    const uint32_t pos = gt ? g1 + min(q1, b.need) : g1 + q1;
+                    if (take) emit<K>(o, pos, p + qq * EPW + h, key, xr);
+                    g1 += gt ? 1u : 0u;
+                    q1 += eq ? 1u : 0u;
+                }
+            gb += sc.total & 0xFFFFu;
+            qb += sc.total >> 16;
+        }
+    }
+}
+
 __device__ __forceinline__ int64_t valid_length(const TopkArgs &a, int64_t row) {
     int64_t n = a.cols;
     if (a.row_end) {
@@ -1077,7 +1154,27 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
     const uint32_t C = d1.above + d1.cnt;
 
-    if (C <= cap) {
+    if constexpr (LOADS <= 2) {
+        Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
+        if (d1.cnt != b.need) {
+#pragma unroll 1
+            for (int pass = 1; pass < K::NPASS; ++pass) {
+                const int d = K::digit(pass);
+                const int sh = b.s - d;
+                const int nb = 1 << d;
+                for (int i = t; i < nb; i += NT) L.hist[i] = 0;
+                __syncthreads();
+                refine_histogram_regs<K, LOADS>(kw, b.P, b.s, sh, (1u << d) - 1u, L.hist);
+                __syncthreads();
+                const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
+                b.need -= dg.above;
+                b.P = (b.P << d) | dg.v;
+                b.s = sh;
+                if (dg.cnt == b.need) break;
+            }
+        }
+        write_from_regs<K, LOADS>(a, row, kw, len, b, 0u, 0u, 0u, L.red, xr);
+    } else if (C <= cap) {
         compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, ent, cap, 0u);
         const Bound b = refine_on_list<K>(ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
         write_from_list<K>(a, row, ent, C, b, L.red, xr);
@@ -1178,12 +1275,16 @@ const void *topk_kernel_ptr(int dtype, int ept, bool split) {
     return split ? pick<F32Key, true>(ept) : pick<F32Key, false>(ept);
 }
 
-// The histogram, and the candidate list (cap entries plus one spare per
-// lane, keys and columns) from list_base.
-size_t topk_dyn_lds(int dtype, int64_t cap) {
+// The histogram, and (unless the workgroup holds at most two loads per
+// thread of a whole row, which needs no list) the candidate list: cap entries
+// plus one spare per lane, keys and columns, from list_base.
+size_t topk_dyn_lds(int dtype, int64_t cap, int ept, bool split) {
+    const int loads = ept / topk_vec(dtype);
+    const uint64_t hist = (uint64_t)(kBins + 64);
+    if (!split && loads <= 2) return (size_t)hist * 4;
     const uint64_t base = dtype == 0 ? list_base<Bf16Key>() : list_base<F32Key>();
     const uint64_t words = base + 2 * (uint64_t)(cap + 64);
-    return (size_t)(words > (uint64_t)(kBins + 64) ? words : (uint64_t)(kBins + 64)) * 4;
+    return (size_t)(words > hist ? words : hist) * 4;
 }
 
 hipError_t launch_topk(int dtype, int ept, bool split, const TopkArgs &a, unsigned grid,
@@ -1192,7 +1293,8 @@ hipError_t launch_topk(int dtype, int ept, bool split, const TopkArgs &a, unsign
     if (!fn) return hipErrorInvalidValue;
     TopkArgs copy = a;
     void *args[] = {&copy};
-    return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, topk_dyn_lds(dtype, a.cap), stream);
+    return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, topk_dyn_lds(dtype, a.cap, ept, split),
+                           stream);
 }
 
 }  // namespace dsel
