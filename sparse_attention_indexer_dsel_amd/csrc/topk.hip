@@ -871,20 +871,24 @@ __device__ __forceinline__ uint32_t counts_regs(const uint32_t (&kw)[LOADS * 4],
     return g | (q << 16);
 }
 
-// Write the selection from keys held in VGPRs (coalesced layout, columns
-// col0 + (j*NT + t)*VEC + ...); gt0 / eq0 are the taken-above and equal
-// counts of the row's columns before this range.  Values are rebuilt from
-// keys (+-0 / NaN keys read their bits back from the row).
+// Write the selection from keys held in VGPRs (coalesced layout: this
+// range's columns base + (j*NT + t)*VEC + ..., the range a view of the row);
+// gt0 / eq0 are the taken-above and equal counts of the row's columns before
+// the range.  Values are rebuilt from keys, so the loop issues no loads (a
+// load there would make every store wait for the ones before it); if a +-0
+// or NaN key was taken, whose bits the key does not determine, the range is
+// written again from the row.
 template <class K, int LOADS>
 __device__ __forceinline__ void write_from_regs(const TopkArgs &a, int64_t row,
                                                 const uint32_t (&kw)[LOADS * 4], int len, Bound b,
-                                                uint32_t gt0, uint32_t eq0, uint32_t col0,
+                                                uint32_t gt0, uint32_t eq0,
+                                                __amdgpu_buffer_rsrc_t view, int64_t base,
                                                 uint32_t *s_red, const typename K::raw_t *xr) {
     constexpr int VEC = K::VEC, EPW = K::EPW, SPAN = NT * VEC;
     const RowOut o = row_out<K>(a, row);
     const int t = tid();
     const int any = (len + SPAN - 1) / SPAN;
-    uint32_t gb = gt0, qb = eq0;
+    uint32_t gb = gt0, qb = eq0, amb = 0;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         if (j < any) {
@@ -892,7 +896,7 @@ __device__ __forceinline__ void write_from_regs(const TopkArgs &a, int64_t row,
                 *reinterpret_cast<const uint32_t(*)[4]>(&kw[4 * j]), b);
             const Scan sc = block_scan(mine, s_red);
             uint32_t g1 = gb + ((sc.incl - mine) & 0xFFFFu), q1 = qb + ((sc.incl - mine) >> 16);
-            const uint32_t p = col0 + (uint32_t)(j * NT + t) * VEC;
+            const uint32_t p = (uint32_t)(base + (int64_t)(j * NT + t) * VEC);
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
@@ -902,7 +906,11 @@ __device__ __forceinline__ void write_from_regs(const TopkArgs &a, int64_t row,
                     const bool gt = key && pre > b.P, eq = key && pre == b.P;
                     const bool take = gt || (eq && q1 < b.need);
                     const uint32_t pos = gt ? g1 + min(q1, b.need) : g1 + q1;
-                    if (take) emit<K>(o, pos, p + qq * EPW + h, key, xr);
+                    if (take) {
+                        store_index(o, pos, p + qq * EPW + h);
+                        if (o.val) store_value<K>(o, pos, K::value_bits(key));
+                        amb |= K::ambiguous(key) ? 1u : 0u;
+                    }
                     g1 += gt ? 1u : 0u;
                     q1 += eq ? 1u : 0u;
                 }
@@ -910,6 +918,8 @@ __device__ __forceinline__ void write_from_regs(const TopkArgs &a, int64_t row,
             qb += sc.total >> 16;
         }
     }
+    if (o.val && __syncthreads_or((int)amb))
+        write_from_stream<K>(a, row, view, base, len, b, gt0, eq0, s_red, xr);
 }
 
 __device__ __forceinline__ int64_t valid_length(const TopkArgs &a, int64_t row) {
@@ -1010,66 +1020,61 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     __syncthreads();
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
 
-    // ---- this workgroup's candidates (key >= T1) to an LDS list; the rest of
-    // the radix select runs on the lists, one rendezvous per pass.  A
-    // workgroup whose candidates do not fit its list (massive ties, or a row
-    // whose largest values crowd into one chunk) re-reads its range from
-    // cache instead; both ways take part in the same rendezvous.
+    // ---- the rest of the radix select, one rendezvous per pass.  Each
+    // workgroup histograms its own keys at the boundary: straight from VGPRs
+    // when it holds a few keys per thread and candidates are dense, else from
+    // an LDS list of its candidates (key >= T1), else (its candidates do not
+    // fit the list: massive ties, or a row whose largest values crowd into
+    // one chunk) from its range re-read from cache.  All three take part in
+    // the same rendezvous.
     Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
-    uint32_t mine;  // this workgroup's (equal << 16 | above) counts at the boundary
     const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
-    const uint32_t run =
-        compact_candidates<K, LOADS, true>(kw, len, d1.v << K::SH1, L.wtot, ent, cap, 0u);
-    const bool listed = run <= cap;  // uniform over the workgroup
-    if (listed) {
-        if (d1.cnt != b.need) {
-#pragma unroll 1
-            for (int pass = 1; pass < K::NPASS; ++pass) {
-                const int d = K::digit(pass);
-                const int sh = b.s - d;
-                const int nb = 1 << d;
-                for (int i = t; i < nb; i += NT) L.hist[i] = 0;
-                __syncthreads();
-                list_refine_histogram(ent, run, b.P, b.s, sh, (1u << d) - 1u, L.hist);
-                __syncthreads();
-                uint32_t *g = ghist + pass * kBins;
-                merge_histogram(L.hist, g, nb);
-                row_rendezvous(slot, (++nren) * (uint32_t)G, err);
-                fetch_histogram(g, L.hist, nb);
-                __syncthreads();
-                const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
-                b.need -= dg.above;
-                b.P = (b.P << d) | dg.v;
-                b.s = sh;
-                if (dg.cnt == b.need) break;  // the boundary bin is taken whole
-            }
-        }
-        mine = list_counts(ent, run, b, L.red);
-    } else {
-        if (d1.cnt != b.need) {
-#pragma unroll 1
-            for (int pass = 1; pass < K::NPASS; ++pass) {
-                const int d = K::digit(pass);
-                const int sh = b.s - d;
-                const int nb = 1 << d;
-                for (int i = t; i < nb; i += NT) L.hist[i] = 0;
-                __syncthreads();
-                refine_histogram_stream<K>(view, lo, len, b.P, b.s, sh, (1u << d) - 1u, L.hist);
-                __syncthreads();
-                uint32_t *g = ghist + pass * kBins;
-                merge_histogram(L.hist, g, nb);
-                row_rendezvous(slot, (++nren) * (uint32_t)G, err);
-                fetch_histogram(g, L.hist, nb);
-                __syncthreads();
-                const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
-                b.need -= dg.above;
-                b.P = (b.P << d) | dg.v;
-                b.s = sh;
-                if (dg.cnt == b.need) break;  // the boundary bin is taken whole
-            }
-        }
-        mine = block_scan(range_counts<K>(view, lo, len, b), L.red).total;
+    // dense: at least a quarter of the row are candidates (uniform over it)
+    const bool regs = LOADS <= 2 && 4 * (int64_t)(d1.above + d1.cnt) >= n;
+    uint32_t run = 0;
+    bool listed = false;
+    if (!regs) {
+        run = compact_candidates<K, LOADS, true>(kw, len, d1.v << K::SH1, L.wtot, ent, cap, 0u);
+        listed = run <= cap;  // uniform over the workgroup
     }
+    auto local_histogram = [&](uint32_t P, int s, int sh, uint32_t dmask) {
+        if (regs)
+            refine_histogram_regs<K, LOADS>(kw, P, s, sh, dmask, L.hist);
+        else if (listed)
+            list_refine_histogram(ent, run, P, s, sh, dmask, L.hist);
+        else
+            refine_histogram_stream<K>(view, lo, len, P, s, sh, dmask, L.hist);
+    };
+    if (d1.cnt != b.need) {
+#pragma unroll 1
+        for (int pass = 1; pass < K::NPASS; ++pass) {
+            const int d = K::digit(pass);
+            const int sh = b.s - d;
+            const int nb = 1 << d;
+            for (int i = t; i < nb; i += NT) L.hist[i] = 0;
+            __syncthreads();
+            local_histogram(b.P, b.s, sh, (1u << d) - 1u);
+            __syncthreads();
+            uint32_t *g = ghist + pass * kBins;
+            merge_histogram(L.hist, g, nb);
+            row_rendezvous(slot, (++nren) * (uint32_t)G, err);
+            fetch_histogram(g, L.hist, nb);
+            __syncthreads();
+            const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
+            b.need -= dg.above;
+            b.P = (b.P << d) | dg.v;
+            b.s = sh;
+            if (dg.cnt == b.need) break;  // the boundary bin is taken whole
+        }
+    }
+    // this workgroup's (equal << 16 | above) counts at the boundary
+    uint32_t mine;
+    if (regs)
+        mine = block_scan(counts_regs<K, LOADS>(kw, b), L.red).total;
+    else if (listed)
+        mine = list_counts(ent, run, b, L.red);
+    else
+        mine = block_scan(range_counts<K>(view, lo, len, b), L.red).total;
 
     // ---- the counts of the workgroups before this one; each writes its own
     // part of the row's output ----------------------------------------------
@@ -1090,7 +1095,9 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     const uint32_t gt0 = block_scan(gg, L.red).total;
     const uint32_t eq0 = block_scan(qq, L.red).total;
     const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
-    if (listed)
+    if (regs)
+        write_from_regs<K, LOADS>(a, row, kw, len, b, gt0, eq0, view, lo, L.red, xr);
+    else if (listed)
         write_from_list<K>(a, row, ent, run, b, L.red, xr, gt0, eq0, (uint32_t)lo);
     else
         write_from_stream<K>(a, row, view, lo, len, b, gt0, eq0, L.red, xr);
@@ -1154,7 +1161,8 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
     const uint32_t C = d1.above + d1.cnt;
 
-    if constexpr (LOADS <= 2) {
+    if (LOADS <= 2 && 4 * (int64_t)C >= n) {
+        // a few keys per thread and dense candidates: no list
         Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
         if (d1.cnt != b.need) {
 #pragma unroll 1
@@ -1173,7 +1181,7 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
                 if (dg.cnt == b.need) break;
             }
         }
-        write_from_regs<K, LOADS>(a, row, kw, len, b, 0u, 0u, 0u, L.red, xr);
+        write_from_regs<K, LOADS>(a, row, kw, len, b, 0u, 0u, row_view<K>(xr, n), 0, L.red, xr);
     } else if (C <= cap) {
         compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, ent, cap, 0u);
         const Bound b = refine_on_list<K>(ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
@@ -1275,13 +1283,12 @@ const void *topk_kernel_ptr(int dtype, int ept, bool split) {
     return split ? pick<F32Key, true>(ept) : pick<F32Key, false>(ept);
 }
 
-// The histogram, and (unless the workgroup holds at most two loads per
-// thread of a whole row, which needs no list) the candidate list: cap entries
-// plus one spare per lane, keys and columns, from list_base.
+// The histogram, and the candidate list: cap entries plus one spare per
+// lane, keys and columns, from list_base.
 size_t topk_dyn_lds(int dtype, int64_t cap, int ept, bool split) {
-    const int loads = ept / topk_vec(dtype);
+    (void)ept;
+    (void)split;
     const uint64_t hist = (uint64_t)(kBins + 64);
-    if (!split && loads <= 2) return (size_t)hist * 4;
     const uint64_t base = dtype == 0 ? list_base<Bf16Key>() : list_base<F32Key>();
     const uint64_t words = base + 2 * (uint64_t)(cap + 64);
     return (size_t)(words > hist ? words : hist) * 4;
