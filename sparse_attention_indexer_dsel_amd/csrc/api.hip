@@ -153,7 +153,7 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     pl->cap = cap;
     pl->rows_per_launch = rpl;
     pl->grid = rpl * G;
-    pl->slot_words = slot_words(G);
+    pl->slot_words = slot_words(G, dtype);
     pl->ws_bytes = (size_t)(kHeaderWords + rpl * pl->slot_words) * sizeof(uint32_t);
     return DSEL_OK;
 }

@@ -26,10 +26,15 @@ constexpr int kMaxPasses = 3;
 // Most workgroups one row may be split over.
 constexpr int kMaxSplit = 1024;
 
+// Bins of the last radix pass: 5 bits for bf16 keys, 10 for fp32.
+inline int last_pass_bins(int dtype) { return dtype == 0 ? 32 : 1024; }
+
 // Per-row workspace slot (32-bit words): counters, one histogram per radix
-// pass and per-workgroup counts.
-inline int64_t slot_words(int G) {
-    return kSlotHeadWords + (int64_t)kMaxPasses * kBins + 4 * (int64_t)G;
+// pass, per-workgroup counts, and each workgroup's suffix counts over the
+// last pass's bins.
+inline int64_t slot_words(int G, int dtype) {
+    return kSlotHeadWords + (int64_t)kMaxPasses * kBins + 4 * (int64_t)G +
+           (int64_t)G * (last_pass_bins(dtype) + 1);
 }
 
 struct TopkArgs {

@@ -74,6 +74,7 @@ struct Bf16Key {
     static constexpr int SH1 = 5;  // first digit = key >> 5 (11 bits)
     static constexpr uint32_t NEG_INF = 0xFF80u;
     __device__ static int digit(int pass) { return pass == 0 ? 11 : 5; }
+    static constexpr int digit_last() { return 5; }
     // offset binary of both halves: 0x8000 +/- magnitude (packed int16 ops);
     // magmax collects the largest magnitude bits for the NaN probe
     __device__ static uint32_t keyword(uint32_t w, uint32_t &magmax) {
@@ -116,6 +117,7 @@ struct F32Key {
     static constexpr int SH1 = 21;
     static constexpr uint32_t NEG_INF = 0xFF800000u;
     __device__ static int digit(int pass) { return pass == 2 ? 10 : 11; }
+    static constexpr int digit_last() { return 10; }
     __device__ static uint32_t keyword(uint32_t w, uint32_t &magmax) {
         const uint32_t mag = w & 0x7FFFFFFFu;
         magmax = max(magmax, mag);
@@ -274,6 +276,29 @@ __device__ __forceinline__ void fetch_histogram(const uint32_t *ghist, uint32_t 
         const int b = i * NT + tid();
         if (b < nb) hist[b] = v[i];
     }
+}
+
+// Publish a workgroup's counts at the last radix pass, given its histogram
+// of that pass's digit (nb bins) and `above`, its keys above the current
+// prefix: word j of dst (j in [0, nb]) = above + its keys at the prefix
+// whose digit is >= j.  Once the digit v is known, words v+1 and v are the
+// chunk's taken-above count and (by difference) its count at the boundary.
+__device__ __forceinline__ void publish_suffix(const uint32_t *hist, int nb, uint32_t above,
+                                               uint32_t *dst, uint32_t *s_red) {
+    const int t = tid();
+    const int bpt = nb > NT ? nb / NT : 1;
+    const int nact = nb / bpt;
+    const int top = nb - t * bpt;  // exclusive upper bin of this thread
+    uint32_t local = 0;
+    if (t < nact)
+        for (int i = 1; i <= bpt; ++i) local += hist[top - i];
+    uint32_t acc = above + block_scan(local, s_red).incl - local;
+    if (t < nact)
+        for (int i = 1; i <= bpt; ++i) {
+            acc += hist[top - i];
+            st_agent(dst + top - i, acc);
+        }
+    if (t == 0) st_agent(dst + nb, above);
 }
 
 // A row's output slots, resolved once per row (uniform: held in SGPRs).
@@ -993,6 +1018,8 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     uint32_t *err = a.ws;
     uint32_t *ghist = slot + kSlotHeadWords;
     uint32_t *gcnt = ghist + kMaxPasses * kBins;
+    constexpr int LASTB = 1 << K::digit_last();  // bins of the last pass
+    uint32_t *pub = gcnt + 4 * G;                // G x (LASTB + 1) suffix counts
 
     // ---- this workgroup's columns into VGPRs; first-digit histogram --------
     const int64_t lo = (int64_t)c * a.chunk;
@@ -1008,7 +1035,8 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
         nan = keys_of_loads<K, LOADS>(v, len, kw);
     }
-    const uint32_t block_nan = __syncthreads_or((int)nan) ? 1u : 0u;
+    if (__syncthreads_or((int)nan) && t == 0)
+        __hip_atomic_fetch_or(slot + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     first_digit_histogram<K, LOADS>(kw, len, L.hist);
     __syncthreads();
 
@@ -1026,7 +1054,9 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     // an LDS list of its candidates (key >= T1), else (its candidates do not
     // fit the list: massive ties, or a row whose largest values crowd into
     // one chunk) from its range re-read from cache.  All three take part in
-    // the same rendezvous.
+    // the same rendezvous.  In the last pass each workgroup also publishes its
+    // suffix counts, so the counts of the chunks before it come with that
+    // pass's rendezvous.
     Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
     const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
     // dense: at least a quarter of the row are candidates (uniform over it)
@@ -1037,6 +1067,13 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         run = compact_candidates<K, LOADS, true>(kw, len, d1.v << K::SH1, L.wtot, ent, cap, 0u);
         listed = run <= cap;  // uniform over the workgroup
     }
+    // this workgroup's (equal << 16 | above) counts at a bound
+    auto local_counts = [&](Bound bb) -> uint32_t {
+        if (regs) return block_scan(counts_regs<K, LOADS>(kw, bb), L.red).total;
+        if (listed) return list_counts(ent, run, bb, L.red);
+        return block_scan(range_counts<K>(view, lo, len, bb), L.red).total;
+    };
+    bool folded = false;  // the last pass published this workgroup's counts
     auto local_histogram = [&](uint32_t P, int s, int sh, uint32_t dmask) {
         if (regs)
             refine_histogram_regs<K, LOADS>(kw, P, s, sh, dmask, L.hist);
@@ -1055,6 +1092,11 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
             __syncthreads();
             local_histogram(b.P, b.s, sh, (1u << d) - 1u);
             __syncthreads();
+            if (pass == K::NPASS - 1) {
+                publish_suffix(L.hist, nb, local_counts(b) & 0xFFFFu,
+                               pub + (int64_t)c * (LASTB + 1), L.red);
+                folded = true;
+            }
             uint32_t *g = ghist + pass * kBins;
             merge_histogram(L.hist, g, nb);
             row_rendezvous(slot, (++nren) * (uint32_t)G, err);
@@ -1067,60 +1109,65 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
             if (dg.cnt == b.need) break;  // the boundary bin is taken whole
         }
     }
-    // this workgroup's (equal << 16 | above) counts at the boundary
-    uint32_t mine;
-    if (regs)
-        mine = block_scan(counts_regs<K, LOADS>(kw, b), L.red).total;
-    else if (listed)
-        mine = list_counts(ent, run, b, L.red);
-    else
-        mine = block_scan(range_counts<K>(view, lo, len, b), L.red).total;
-
-    // ---- the counts of the workgroups before this one; each writes its own
-    // part of the row's output ----------------------------------------------
-    if (t == 0) {
-        st_agent(gcnt + 4 * c + 0, mine & 0xFFFFu);
-        st_agent(gcnt + 4 * c + 1, mine >> 16);
-        st_agent(gcnt + 4 * c + 2, block_nan);
-    }
-    row_rendezvous(slot, (++nren) * (uint32_t)G, err);
-    uint32_t gg = 0, qq = 0, nn = 0;
-    for (int i = t; i < G; i += NT) {
-        if (i < c) {
-            gg += ld_agent(gcnt + 4 * i + 0);
-            qq += ld_agent(gcnt + 4 * i + 1);
+    // ---- the taken-above and equal counts of the chunks before this one:
+    // from the last pass's suffix counts, or (the selection ended at an
+    // earlier digit) one more exchange.  Each workgroup then writes its own
+    // part of the row's output.
+    uint32_t gg = 0, qq = 0;
+    if (folded) {
+        const uint32_t v = b.P & (uint32_t)(LASTB - 1);
+        for (int i = t; i < c; i += NT) {
+            const uint32_t *w = pub + (int64_t)i * (LASTB + 1) + v;
+            const uint32_t at = ld_agent(w), above = ld_agent(w + 1);
+            gg += above;
+            qq += at - above;
         }
-        nn |= ld_agent(gcnt + 4 * i + 2);
+    } else {
+        const uint32_t mine = local_counts(b);
+        if (t == 0) {
+            st_agent(gcnt + 2 * c + 0, mine & 0xFFFFu);
+            st_agent(gcnt + 2 * c + 1, mine >> 16);
+        }
+        row_rendezvous(slot, (++nren) * (uint32_t)G, err);
+        for (int i = t; i < c; i += NT) {
+            gg += ld_agent(gcnt + 2 * i + 0);
+            qq += ld_agent(gcnt + 2 * i + 1);
+        }
     }
     const uint32_t gt0 = block_scan(gg, L.red).total;
     const uint32_t eq0 = block_scan(qq, L.red).total;
-    const uint32_t row_nan = __syncthreads_or((int)nn) ? 1u : 0u;
     if (regs)
         write_from_regs<K, LOADS>(a, row, kw, len, b, gt0, eq0, view, lo, L.red, xr);
     else if (listed)
         write_from_list<K>(a, row, ent, run, b, L.red, xr, gt0, eq0, (uint32_t)lo);
     else
         write_from_stream<K>(a, row, view, lo, len, b, gt0, eq0, L.red, xr);
-    if (c == 0 && t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)row_nan;
+    // every workgroup's NaN bit was in before the first rendezvous
+    if (c == 0 && t == 0 && a.nan_flag) a.nan_flag[row] = ld_agent(slot + 2) ? 1u : 0u;
 
-    // Leave the slot zeroed for the next call (whose slot layout may differ):
-    // every workgroup has read the histograms before the last rendezvous, so
-    // each clears a share now; the last workgroup out, once every workgroup
-    // has read the counts, clears them and resets the counters.  The stores
+    // Leave the slot zeroed for the next call (whose slot layout may differ).
+    // The histograms of all passes but the last were read before the last
+    // rendezvous, so each workgroup clears a share of them now; the last
+    // workgroup out, once every workgroup has read what it needs, clears the
+    // last pass's histogram, the counts and the counters.  The stores
     // complete before the launch does.
-    constexpr int HW = kMaxPasses * kBins;
+    constexpr int HW = (K::NPASS - 1) * kBins;
     const int per = (HW + G - 1) / G;
     const int z0 = c * per, z1 = min(HW, z0 + per);
     for (int i = z0 + t; i < z1; i += NT) st_agent(ghist + i, 0u);
-    drain_memory();
     __syncthreads();
     if (t == 0) L.out[3] = (add_agent(slot + 1, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
     __syncthreads();
     if (L.out[3]) {
-        for (int i = t; i < 4 * G; i += NT) st_agent(gcnt + i, 0u);
+        for (int i = t; i < LASTB; i += NT) st_agent(ghist + HW + i, 0u);
+        if (folded)
+            for (int i = t; i < G * (LASTB + 1); i += NT) st_agent(pub + i, 0u);
+        else
+            for (int i = t; i < 2 * G; i += NT) st_agent(gcnt + i, 0u);
         if (t == 0) {
             st_agent(slot + 0, 0u);
             st_agent(slot + 1, 0u);
+            st_agent(slot + 2, 0u);
         }
     }
 }
