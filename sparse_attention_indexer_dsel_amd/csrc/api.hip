@@ -74,19 +74,21 @@ int pick_ept(int64_t cols, int max_ept) {
     return 0;
 }
 
-// Workgroups per row: one when the row fits a workgroup and there are enough
-// rows to occupy the GPU; otherwise enough to give the GPU about four
-// workgroups per compute unit, but no fewer than 4096 columns each, and at
-// least enough to hold the row in VGPRs.  DSEL_BLOCKS_PER_ROW overrides the
-// choice (tuning and tests).
+// Workgroups per row: one when the row fits a workgroup (a split row pays a
+// cross-workgroup rendezvous per radix pass, a few microseconds each, more
+// than one workgroup takes over a row it can hold); otherwise enough to give
+// the GPU about four workgroups per compute unit, but no fewer than 8192
+// columns each (more workgroups per row contend on the row's histogram
+// atomics), and at least enough to hold the row in VGPRs.
+// DSEL_BLOCKS_PER_ROW overrides the choice (tuning and tests).
 int choose_G(int64_t rows, int64_t cols, int cus) {
     const int64_t gmin = cdiv(cols, kChunkCapacity);
     int64_t G;
-    if (cols <= kBlockCapacity && rows >= cus / 2) {
+    if (cols <= kBlockCapacity) {
         G = 1;
     } else {
         const int64_t gpar = cdiv(4 * (int64_t)cus, rows > 0 ? rows : 1);
-        const int64_t gchunk = cdiv(cols, 4096);
+        const int64_t gchunk = cdiv(cols, 8192);
         G = gpar < gchunk ? gpar : gchunk;
         if (G < gmin) G = gmin;
         if (G < 1) G = 1;
