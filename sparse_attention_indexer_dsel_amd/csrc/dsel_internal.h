@@ -9,9 +9,9 @@ namespace dsel {
 
 // Workgroup shape of every top-k kernel: four wave64s.
 constexpr int kTopkThreads = 256;
-// Largest per-thread element count of a whole row (one workgroup per row,
-// the next row's loads double-buffered in VGPRs) and of one split-row chunk
-// (single-buffered); a workgroup holds kTopkThreads times that many columns.
+// Largest per-thread element count of a whole row (one workgroup per row)
+// and of one split-row chunk; a workgroup holds kTopkThreads times that many
+// columns in VGPRs.
 constexpr int kMaxEpt = 64;
 constexpr int kMaxSplitEpt = 128;
 constexpr int64_t kBlockCapacity = (int64_t)kTopkThreads * kMaxEpt;

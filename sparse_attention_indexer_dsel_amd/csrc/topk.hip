@@ -1173,13 +1173,13 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Whole rows: one workgroup per row, persistent and software-pipelined.
+// Whole rows: one workgroup per row.
 // ---------------------------------------------------------------------------
 
 // Issue the loads of one row's first NT*EPT columns (columns at or past n
 // read as zero).
 template <class K, int LOADS>
-__device__ __forceinline__ void prefetch_row(const typename K::raw_t *xr, int64_t n,
+__device__ __forceinline__ void load_row(const typename K::raw_t *xr, int64_t n,
                                              uint4 (&v)[LOADS]) {
     const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
 #pragma unroll
@@ -1258,12 +1258,13 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
     if (t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)block_nan;
 }
 
-// A workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x, ...: while it
-// selects from one row (keys in VGPRs), the 16-byte loads of its next row are
-// already in flight into a second register buffer, and the row after that
-// has its row_end read, so neither latency sits between two rows.
+// A workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x, ... (one row
+// each when the grid covers the rows).  A row's loads are issued when the
+// workgroup reaches it; other workgroups on the compute unit hide their
+// latency.  Holding only one row in VGPRs keeps more workgroups resident,
+// which pays more than double-buffering the next row's loads.
 template <class K, int EPT>
-__global__ __launch_bounds__(NT) void topk_rows_pipelined(const TopkArgs a) {
+__global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     using raw_t = typename K::raw_t;
     constexpr int LOADS = EPT / K::VEC;
     static_assert(EPT % K::VEC == 0, "EPT must be a multiple of the vector width");
@@ -1271,31 +1272,20 @@ __global__ __launch_bounds__(NT) void topk_rows_pipelined(const TopkArgs a) {
     __shared__ TopkShared<(LOADS + 1) / 2> S;
     const TopkLds L{s_dyn, S.wtot, S.red, S.out};
     const List ent = list_of(s_dyn + list_base<K>(), (uint32_t)a.cap);
-
-    const int64_t stride = gridDim.x;
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
-    int64_t row = a.row0 + blockIdx.x;
-    if (row >= a.rows) return;
-    int64_t n = valid_length(a, row);
-    int64_t n2 = row + stride < a.rows ? valid_length(a, row + stride) : 0;
-    uint4 cur[LOADS], nxt[LOADS];
-    if (n > a.k) prefetch_row<K, LOADS>(x + row * a.x_stride, n, cur);
 
 #pragma unroll 1
-    for (; row < a.rows; row += stride) {
-        const int64_t row2 = row + stride;
-        if (row2 < a.rows && n2 > a.k) prefetch_row<K, LOADS>(x + row2 * a.x_stride, n2, nxt);
-        const int64_t n3 = row2 + stride < a.rows ? valid_length(a, row2 + stride) : 0;
-        if (n <= a.k)
-            write_short_row<K>(a, row, n, 0, 1, x + row * a.x_stride);
-        else
-            select_row<K, LOADS>(a, row, n, cur, L, ent);
+    for (int64_t row = a.row0 + blockIdx.x; row < a.rows; row += gridDim.x) {
+        const int64_t n = valid_length(a, row);
+        const raw_t *xr = x + row * a.x_stride;
+        if (n <= a.k) {
+            write_short_row<K>(a, row, n, 0, 1, xr);
+        } else {
+            uint4 v[LOADS];
+            load_row<K, LOADS>(xr, n, v);
+            select_row<K, LOADS>(a, row, n, v, L, ent);
+        }
         __syncthreads();  // LDS is reused by the next row
-        // the next row's vectors had this whole row's work to arrive
-#pragma unroll
-        for (int j = 0; j < LOADS; ++j) cur[j] = nxt[j];
-        n = n2;
-        n2 = n3;
     }
 }
 
@@ -1304,7 +1294,7 @@ const void *kptr() {
     if constexpr (SPLIT)
         return reinterpret_cast<const void *>(&topk_rows_split<K, EPT>);
     else
-        return reinterpret_cast<const void *>(&topk_rows_pipelined<K, EPT>);
+        return reinterpret_cast<const void *>(&topk_rows_whole<K, EPT>);
 }
 
 template <class K, bool SPLIT>
