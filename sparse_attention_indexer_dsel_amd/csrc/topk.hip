@@ -72,6 +72,7 @@ struct Bf16Key {
     static constexpr int EPW = 2;  // elements per key word
     static constexpr int NPASS = 2;
     static constexpr int SH1 = 5;  // first digit = key >> 5 (11 bits)
+    static constexpr bool PACK = true;  // list entry = key << 16 | column
     static constexpr uint32_t NEG_INF = 0xFF80u;
     __device__ static int digit(int pass) { return pass == 0 ? 11 : 5; }
     static constexpr int digit_last() { return 5; }
@@ -115,6 +116,7 @@ struct F32Key {
     static constexpr int EPW = 1;
     static constexpr int NPASS = 3;
     static constexpr int SH1 = 21;
+    static constexpr bool PACK = false;  // list entry = (key, column) in two arrays
     static constexpr uint32_t NEG_INF = 0xFF800000u;
     __device__ static int digit(int pass) { return pass == 2 ? 10 : 11; }
     static constexpr int digit_last() { return 10; }
@@ -496,20 +498,50 @@ __device__ __forceinline__ void first_digit_histogram(const uint32_t (&kw)[LOADS
     }
 }
 
-// A candidate list in LDS: keys and columns in separate arrays (so a key and
-// its column never have to sit in adjacent VGPRs for one 64-bit store), cap
-// entries plus one spare entry per lane.
+// A candidate list in LDS, cap entries plus one spare entry per lane.  A
+// bf16 entry is one word, key << 16 | column (columns of a workgroup's range
+// are below 2^16), so compaction stores and list reads are one LDS access
+// each; an fp32 entry keeps key and column in separate arrays (so the two
+// never have to sit in adjacent VGPRs for one 64-bit store).
 struct List {
     uint32_t *key;
-    uint32_t *col;
+    uint32_t *col;  // fp32 only
 };
 
+template <class K>
 __device__ __forceinline__ List list_of(uint32_t *s_dyn, uint32_t cap) {
-    return List{s_dyn, s_dyn + cap + 64};
+    return List{s_dyn, K::PACK ? nullptr : s_dyn + cap + 64};
+}
+
+template <class K>
+__device__ __forceinline__ void list_put(List ent, uint32_t i, uint32_t key, uint32_t col) {
+    if constexpr (K::PACK) {
+        ent.key[i] = (key << 16) | col;
+    } else {
+        ent.key[i] = key;
+        ent.col[i] = col;
+    }
+}
+
+template <class K>
+__device__ __forceinline__ uint32_t list_key(List ent, uint32_t i) {
+    if constexpr (K::PACK) return ent.key[i] >> 16;
+    return ent.key[i];
+}
+
+// (key, column) of entry i
+template <class K>
+__device__ __forceinline__ uint2 list_entry(List ent, uint32_t i) {
+    if constexpr (K::PACK) {
+        const uint32_t e = ent.key[i];
+        return make_uint2(e >> 16, e & 0xFFFFu);
+    }
+    return make_uint2(ent.key[i], ent.col[i]);
 }
 
 // Compact the candidates (key >= T1, T1 > 0) of a workgroup's keys into
-// ent[0, run) in column order (entry = (key, col0 + column)); returns run.
+// ent[0, run) in column order (entry = (key, column within the range));
+// returns run.
 // Every element is written once, the non-candidates to this lane's spare
 // entry at ent[cap + lane], so the loop has no branches.  CHECKED: when more
 // than `cap` qualify nothing is written (the count is still returned).  wtot
@@ -517,7 +549,7 @@ __device__ __forceinline__ List list_of(uint32_t *s_dyn, uint32_t cap) {
 template <class K, int LOADS, bool CHECKED = false>
 __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4], int len,
                                                        uint32_t T1, uint32_t *wtot, List ent,
-                                                       uint32_t cap, uint32_t col0) {
+                                                       uint32_t cap) {
     constexpr int VEC = K::VEC, EPW = K::EPW, LP = (LOADS + 1) / 2, SPAN = NT * VEC;
     const int t = tid();
     const int lane = t & 63, wid = t >> 6;
@@ -572,16 +604,14 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
             }
             uint32_t pos = run + before + ((ex[i] >> sh) & 0xFFFFu);
             run += tot;
-            const uint32_t p = col0 + (uint32_t)(j * NT + t) * VEC;
+            const uint32_t p = (uint32_t)(j * NT + t) * VEC;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int h = 0; h < EPW; ++h) {
                     const uint32_t key = K::elem(kw[4 * j + q], h);
                     const bool cand = key >= T1w;
-                    const uint32_t d = cand ? pos : spare;
-                    ent.key[d] = key;
-                    ent.col[d] = p + q * EPW + h;
+                    list_put<K>(ent, cand ? pos : spare, key, p + q * EPW + h);
                     pos += cand ? 1u : 0u;
                 }
         }
@@ -601,6 +631,7 @@ struct Bound {
 // Histogram of the next digit ((key >> sh) & dmask) of the list entries
 // whose top bits (key >> s) equal P (hist zeroed).  Reads are unconditional
 // (clamped index, masked result) so several are in flight.
+template <class K>
 __device__ __forceinline__ void list_refine_histogram(List ent, uint32_t C, uint32_t P, int s,
                                                       int sh, uint32_t dmask, uint32_t *hist) {
     constexpr int U = 4;
@@ -609,7 +640,7 @@ __device__ __forceinline__ void list_refine_histogram(List ent, uint32_t C, uint
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t i = i0 + u * NT + tid();
-            const uint32_t kk = ent.key[i < C ? i : 0u];
+            const uint32_t kk = list_key<K>(ent, i < C ? i : 0u);
             key[u] = i < C ? kk : 0u;
         }
 #pragma unroll
@@ -633,7 +664,7 @@ __device__ Bound refine_on_list(List ent, uint32_t C, Digit d1, uint32_t k,
         const int nb = 1 << d;
         for (int i = t; i < nb; i += NT) s_hist[i] = 0;
         __syncthreads();
-        list_refine_histogram(ent, C, b.P, b.s, sh, (1u << d) - 1u, s_hist);
+        list_refine_histogram<K>(ent, C, b.P, b.s, sh, (1u << d) - 1u, s_hist);
         __syncthreads();
         const Digit dg = find_digit(s_hist, nb, b.need, s_red, s_out);
         b.need -= dg.above;
@@ -646,11 +677,12 @@ __device__ Bound refine_on_list(List ent, uint32_t C, Digit d1, uint32_t k,
 
 // This workgroup's list totals: entries taken above the boundary (top bits >
 // P) and entries at it (== P), packed (equal << 16 | above).
+template <class K>
 __device__ uint32_t list_counts(List ent, uint32_t C, Bound b, uint32_t *s_red) {
     uint32_t g = 0, q = 0;
     for (uint32_t i0 = 0; i0 < C; i0 += NT) {
         const uint32_t i = i0 + tid();
-        const uint32_t kk = ent.key[i < C ? i : 0u];
+        const uint32_t kk = list_key<K>(ent, i < C ? i : 0u);
         const uint32_t key = i < C ? kk : 0u;
         g += (key && (key >> b.s) > b.P) ? 1u : 0u;
         q += (key && (key >> b.s) == b.P) ? 1u : 0u;
@@ -680,9 +712,8 @@ __device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, 
     // entry i of this wave's range, read unconditionally (clamped, then
     // masked) so several reads can be in flight
     auto entry = [&](uint32_t i) {
-        const uint32_t j = i < b1 ? i : 0u;
-        const uint32_t key = ent.key[j], col = ent.col[j];
-        return i < b1 ? make_uint2(key, col) : make_uint2(0u, 0u);
+        const uint2 e = list_entry<K>(ent, i < b1 ? i : 0u);
+        return i < b1 ? e : make_uint2(0u, 0u);
     };
     uint32_t g = 0, q = 0;
     uint64_t amb = 0;
@@ -1013,7 +1044,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     }
 
     const uint32_t cap = (uint32_t)a.cap;
-    const List ent = list_of(s_dyn + list_base<K>(), cap);
+    const List ent = list_of<K>(s_dyn + list_base<K>(), cap);
     uint32_t *slot = a.ws + kHeaderWords + lrow * a.slot_words;
     uint32_t *err = a.ws;
     uint32_t *ghist = slot + kSlotHeadWords;
@@ -1064,13 +1095,13 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     uint32_t run = 0;
     bool listed = false;
     if (!regs) {
-        run = compact_candidates<K, LOADS, true>(kw, len, d1.v << K::SH1, L.wtot, ent, cap, 0u);
+        run = compact_candidates<K, LOADS, true>(kw, len, d1.v << K::SH1, L.wtot, ent, cap);
         listed = run <= cap;  // uniform over the workgroup
     }
     // this workgroup's (equal << 16 | above) counts at a bound
     auto local_counts = [&](Bound bb) -> uint32_t {
         if (regs) return block_scan(counts_regs<K, LOADS>(kw, bb), L.red).total;
-        if (listed) return list_counts(ent, run, bb, L.red);
+        if (listed) return list_counts<K>(ent, run, bb, L.red);
         return block_scan(range_counts<K>(view, lo, len, bb), L.red).total;
     };
     bool folded = false;  // the last pass published this workgroup's counts
@@ -1078,7 +1109,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         if (regs)
             refine_histogram_regs<K, LOADS>(kw, P, s, sh, dmask, L.hist);
         else if (listed)
-            list_refine_histogram(ent, run, P, s, sh, dmask, L.hist);
+            list_refine_histogram<K>(ent, run, P, s, sh, dmask, L.hist);
         else
             refine_histogram_stream<K>(view, lo, len, P, s, sh, dmask, L.hist);
     };
@@ -1230,7 +1261,7 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
         }
         write_from_regs<K, LOADS>(a, row, kw, len, b, 0u, 0u, row_view<K>(xr, n), 0, L.red, xr);
     } else if (C <= cap) {
-        compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, ent, cap, 0u);
+        compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, ent, cap);
         const Bound b = refine_on_list<K>(ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
         write_from_list<K>(a, row, ent, C, b, L.red, xr);
     } else {
@@ -1271,7 +1302,7 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     extern __shared__ uint32_t s_dyn[];  // histogram, candidate list
     __shared__ TopkShared<(LOADS + 1) / 2> S;
     const TopkLds L{s_dyn, S.wtot, S.red, S.out};
-    const List ent = list_of(s_dyn + list_base<K>(), (uint32_t)a.cap);
+    const List ent = list_of<K>(s_dyn + list_base<K>(), (uint32_t)a.cap);
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
 
 #pragma unroll 1
@@ -1321,13 +1352,13 @@ const void *topk_kernel_ptr(int dtype, int ept, bool split) {
 }
 
 // The histogram, and the candidate list: cap entries plus one spare per
-// lane, keys and columns, from list_base.
+// lane (one word per bf16 entry, two per fp32 entry), from list_base.
 size_t topk_dyn_lds(int dtype, int64_t cap, int ept, bool split) {
     (void)ept;
     (void)split;
     const uint64_t hist = (uint64_t)(kBins + 64);
     const uint64_t base = dtype == 0 ? list_base<Bf16Key>() : list_base<F32Key>();
-    const uint64_t words = base + 2 * (uint64_t)(cap + 64);
+    const uint64_t words = base + (dtype == 0 ? 1u : 2u) * (uint64_t)(cap + 64);
     return (size_t)(words > hist ? words : hist) * 4;
 }
 
