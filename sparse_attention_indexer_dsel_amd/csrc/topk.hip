@@ -435,16 +435,23 @@ __device__ __forceinline__ void clear_tail(uint32_t *kw, int valid) {
 
 // Keys of a workgroup's loads in the coalesced layout (load j of thread t
 // holds the VEC columns from (j*NT + t)*VEC of a range of `len` columns).
-// Columns at or past len get key 0 and are not probed for NaN.  Returns
-// whether this thread saw a NaN.
+// Columns at or past len get key 0 and are not probed for NaN; loads wholly
+// past len are not transformed at all.  Returns whether this thread saw a
+// NaN.
 template <class K, int LOADS>
 __device__ __forceinline__ uint32_t keys_of_loads(const uint4 (&v)[LOADS], int len,
                                                   uint32_t (&kw)[LOADS * 4]) {
     constexpr int VEC = K::VEC, EPW = K::EPW;
     const int full = len / (NT * VEC);  // loads valid for every thread (uniform)
+    const int any = (len + NT * VEC - 1) / (NT * VEC);
     uint32_t nan = 0;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
+        if (j >= any) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) kw[4 * j + q] = 0u;
+            continue;
+        }
         uint4 x = v[j];
         int valid = VEC;
         if (j >= full) {
@@ -692,87 +699,83 @@ __device__ uint32_t list_counts(List ent, uint32_t C, Bound b, uint32_t *s_red) 
 
 // Write the selection from a column-ordered candidate list whose columns are
 // relative to col0; gt0 / eq0 are the taken-above and equal counts of the
-// row's columns before the list's.  Wave w owns entries [w*Q, (w+1)*Q) (Q a
-// multiple of 64); ranks within a wave come from ballots, and one exchange
-// of the waves' counts (through s_red) gives each wave its starting ranks.  Values are rebuilt from keys, so the write loop
-// issues no loads (a load in it would make every store wait for the ones
-// before it); the rare +-0 / NaN keys get their bits from the row in a
-// second pass, run only when some wave holds one.
+// row's columns before the list's.  Thread t owns the contiguous entries
+// [t*E, (t+1)*E) (E = ceil(C / NT)): it counts them, one workgroup scan
+// gives its starting ranks, and it writes them.  Values are rebuilt from
+// keys, so the write loop issues no loads (a load there would make every
+// store wait for the ones before it); the rare +-0 / NaN keys get their bits
+// from the row in a third pass, run only when some thread holds one.
 template <class K>
 __device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, List ent,
                                                 uint32_t C, Bound b, uint32_t *s_red,
                                                 const typename K::raw_t *xr, uint32_t gt0 = 0,
                                                 uint32_t eq0 = 0, uint32_t col0 = 0) {
+    constexpr int U = 4;
     const RowOut o = row_out<K>(a, row);
-    const int t = tid();
-    const int lane = t & 63, wid = t >> 6;
-    const uint32_t Q = (C + NT - 1) / NT * 64;  // <= 2048
-    const uint32_t b0 = (uint32_t)wid * Q;
-    const uint32_t b1 = min(C, b0 + Q);
-    // entry i of this wave's range, read unconditionally (clamped, then
+    const uint32_t E = (C + NT - 1) / NT;
+    const uint32_t i0 = (uint32_t)tid() * E;
+    const uint32_t i1 = min(C, i0 + E);
+    // entry i of this thread's range, read unconditionally (clamped, then
     // masked) so several reads can be in flight
     auto entry = [&](uint32_t i) {
-        const uint2 e = list_entry<K>(ent, i < b1 ? i : 0u);
-        return i < b1 ? e : make_uint2(0u, 0u);
+        const uint2 e = list_entry<K>(ent, i < i1 ? i : 0u);
+        return i < i1 ? e : make_uint2(0u, 0u);
     };
-    uint32_t g = 0, q = 0;
-    uint64_t amb = 0;
-    for (uint32_t i0 = b0; i0 < b1; i0 += 128) {
-        const uint2 e0 = entry(i0 + (uint32_t)lane), e1 = entry(i0 + 64 + (uint32_t)lane);
-        const uint32_t p0 = e0.x >> b.s, p1 = e1.x >> b.s;
-        const bool gt0 = e0.x && p0 > b.P, eq0 = e0.x && p0 == b.P;
-        const bool gt1 = e1.x && p1 > b.P, eq1 = e1.x && p1 == b.P;
-        g += popc64(__ballot(gt0)) + popc64(__ballot(gt1));
-        q += popc64(__ballot(eq0)) + popc64(__ballot(eq1));
-        amb |= __ballot(((gt0 || eq0) && K::ambiguous(e0.x)) || ((gt1 || eq1) && K::ambiguous(e1.x)));
-    }
-    if (lane == 0) s_red[wid] = g | (q << 12) | (amb ? 1u << 24 : 0u);
-    __syncthreads();
-    uint32_t gb = gt0, qb = eq0, any_amb = 0;
+    uint32_t g = 0, q = 0, amb = 0;
+    for (uint32_t i = i0; i < i0 + E; i += U) {
+        uint32_t key[U];
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
-        const uint32_t v = s_red[w];
-        gb += w < wid ? (v & 0xFFFu) : 0u;
-        qb += w < wid ? ((v >> 12) & 0xFFFu) : 0u;
-        any_amb |= v >> 24;
-    }
-    __syncthreads();
-    const uint32_t gb0 = gb, qb0 = qb;
-    for (uint32_t i0 = b0; i0 < b1; i0 += 128) {
-        const uint2 ee[2] = {entry(i0 + (uint32_t)lane), entry(i0 + 64 + (uint32_t)lane)};
+        for (int u = 0; u < U; ++u) key[u] = entry(i + u).x;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint2 e = ee[h];
-            const uint32_t pre = e.x >> b.s;
-            const bool gt = e.x && pre > b.P;
-            const bool eq = e.x && pre == b.P;
-            const uint64_t mg = __ballot(gt), mq = __ballot(eq);
-            const uint32_t rg = gb + lanes_below(mg), rq = qb + lanes_below(mq);
-            const bool take = gt || (eq && rq < b.need);
-            const uint32_t pos = gt ? rg + min(rq, b.need) : rg + rq;
-            if (take) {
-                store_index(o, pos, e.y + col0);
-                if (o.val) store_value<K>(o, pos, K::value_bits(e.x));
-            }
-            gb += popc64(mg);
-            qb += popc64(mq);
+        for (int u = 0; u < U; ++u) {
+            const uint32_t pre = key[u] >> b.s;
+            const bool gt = key[u] && pre > b.P, eq = key[u] && pre == b.P;
+            g += gt ? 1u : 0u;
+            q += eq ? 1u : 0u;
+            amb |= ((gt || eq) && K::ambiguous(key[u])) ? 1u : 0u;
         }
     }
-    if (!(any_amb && o.val)) return;
+    // packed (equal << 16 | above): above < 2^12 and equal <= C < 2^16
+    const uint32_t mine = g | (q << 16);
+    const uint32_t ex = block_scan(mine, s_red).incl - mine;
+    const uint32_t gb0 = gt0 + (ex & 0xFFFFu), qb0 = eq0 + (ex >> 16);
+    uint32_t gb = gb0, qb = qb0;
+    for (uint32_t i = i0; i < i0 + E; i += U) {
+        uint2 e[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) e[u] = entry(i + u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t pre = e[u].x >> b.s;
+            if (e[u].x && pre > b.P) {
+                const uint32_t pos = gb + min(qb, b.need);
+                store_index(o, pos, e[u].y + col0);
+                if (o.val) store_value<K>(o, pos, K::value_bits(e[u].x));
+                ++gb;
+            } else if (e[u].x && pre == b.P) {
+                if (qb < b.need) {
+                    store_index(o, gb + qb, e[u].y + col0);
+                    if (o.val) store_value<K>(o, gb + qb, K::value_bits(e[u].x));
+                }
+                ++qb;
+            }
+        }
+    }
+    if (!(o.val && __syncthreads_or((int)amb))) return;
     gb = gb0;
     qb = qb0;
-    for (uint32_t i0 = b0; i0 < b1; i0 += 64) {
-        const uint2 e = entry(i0 + (uint32_t)lane);
+    for (uint32_t i = i0; i < i1; ++i) {
+        const uint2 e = entry(i);
         const uint32_t pre = e.x >> b.s;
-        const bool gt = e.x && pre > b.P;
-        const bool eq = e.x && pre == b.P;
-        const uint64_t mg = __ballot(gt), mq = __ballot(eq);
-        const uint32_t rg = gb + lanes_below(mg), rq = qb + lanes_below(mq);
-        const bool take = gt || (eq && rq < b.need);
-        const uint32_t pos = gt ? rg + min(rq, b.need) : rg + rq;
-        if (take && K::ambiguous(e.x)) store_value<K>(o, pos, (uint32_t)xr[e.y + col0]);
-        gb += popc64(mg);
-        qb += popc64(mq);
+        if (e.x && pre > b.P) {
+            if (K::ambiguous(e.x))
+                store_value<K>(o, gb + min(qb, b.need), (uint32_t)xr[e.y + col0]);
+            ++gb;
+        } else if (e.x && pre == b.P) {
+            if (qb < b.need && K::ambiguous(e.x))
+                store_value<K>(o, gb + qb, (uint32_t)xr[e.y + col0]);
+            ++qb;
+        }
     }
 }
 
