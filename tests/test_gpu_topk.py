@@ -140,6 +140,18 @@ def test_split_crowded_chunks(dsel, orc, dt, dist):
                    torch.int64, True, G)
 
 
+@pytest.mark.parametrize("G", [40, 80])
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_split_many_workgroups(dsel, orc, dt, G):
+    """Rows split over many workgroups (short chunks, most of them without a
+    candidate), with ragged row ends."""
+    x = W.random_rows(91 + G, 3, 100000, dt, "normal")
+    re = torch.tensor([100000, 77777, 3001], dtype=torch.int32)
+    for k, sorted_index in ((1000, True), (64, False)):
+        check_case(dsel, orc, f"many/{dt}/G{G}/k{k}", x, k, re, sorted_index, torch.int32,
+                   True, G)
+
+
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
 def test_padded_stride(dsel, orc, dt):
     x = W.random_rows(31, 12, 2000, dt, "normal", stride=2048)
