@@ -17,9 +17,9 @@ Timing protocol
   * the K timed steps are captured once in a HIP graph and replayed, so the
     timed region holds no Python launch overhead; the region is bracketed
     by torch.cuda.synchronize() on both sides and wall-clock timed;
-  * the dominant kernel's duration is measured separately with a HIP event
-    pair around each of its launches, all enqueued behind a GPU sleep so
-    the launches run back to back.
+  * a HIP event pair on the kernels' stream brackets the same replay: each
+    step is one top-k kernel, so events / K is that kernel's mean duration
+    back to back (the roofline figure), comparable with rocprofv3's.
 
 Byte accounting (algorithmic bytes: what the method must move)
   top-k  = sum over rows of the valid-prefix read (a row of valid length
@@ -222,7 +222,10 @@ class TopkBench:
 
 
 def graph_time(torch, stream, fn, steps: int, warmup: int, reps: int = 1):
-    """Capture `steps` calls of fn(i) in one HIP graph; return seconds per call."""
+    """Capture `steps` calls of fn(i) (one kernel each) in one HIP graph and
+    replay it; return (wall seconds per call, event seconds per call).  The
+    event pair brackets the replay on the stream the kernels run on, so the
+    second figure is the kernels' mean duration back to back."""
     with torch.cuda.stream(stream):
         for i in range(max(warmup, 1)):
             fn(i)
@@ -231,40 +234,30 @@ def graph_time(torch, stream, fn, steps: int, warmup: int, reps: int = 1):
     with torch.cuda.graph(g, stream=stream):
         for i in range(steps):
             fn(i)
-    g.replay()  # untimed replay: page in the graph
+    with torch.cuda.stream(stream):
+        g.replay()  # untimed replay: page in the graph
     torch.cuda.synchronize()
-    best = None
+    best = best_ev = None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(reps):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        g.replay()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / steps
+        de = e0.elapsed_time(e1) * 1e-3 / steps
         best = dt if best is None else min(best, dt)
+        best_ev = de if best_ev is None else min(best_ev, de)
     del g
-    return best
-
-
-def event_kernel_time(torch, stream, fn, launches: int) -> float:
-    """Mean seconds per call measured with one HIP event pair per call."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(launches)]
-    with torch.cuda.stream(stream):
-        fn(0)
-        stream.synchronize()
-        torch.cuda._sleep(int(5e7))   # hold the queue so the calls run back to back
-        for i, (a, b) in enumerate(evs):
-            a.record(stream)
-            fn(i + 1)
-            b.record(stream)
-    torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    return best, best_ev
 
 
 def measure_topk(dsel, torch, case, stream, steps, warmup):
     tb = TopkBench(dsel, torch, case, stream)
-    t_step = graph_time(torch, stream, tb.call, steps, warmup, reps=3)
-    t_kern = event_kernel_time(torch, stream, tb.call, min(steps, 50))
+    t_step, t_kern = graph_time(torch, stream, tb.call, steps, warmup, reps=3)
     nbytes = tb.algorithmic_bytes()
     rows = case.x.shape[0]
     res = {
@@ -298,8 +291,7 @@ def measure_gather(dsel, torch, case, stream, steps, warmup):
         def fn(i, kd=kd, dst=dst):
             return dsel.gather_rows(kd, pos, out=dst, stream=stream)
 
-        t = graph_time(torch, stream, fn, steps, warmup, reps=3)
-        tk = event_kernel_time(torch, stream, fn, min(steps, 20))
+        t, tk = graph_time(torch, stream, fn, steps, warmup, reps=3)
         safe = pos.long().clamp(0, key.shape[1] - 1)
         distinct = int(sum(torch.unique(safe[b]).numel() for b in range(B)))
         npos = B * R * case.k
@@ -387,17 +379,25 @@ def main(argv=None):
     with torch.cuda.graph(g, stream=stream):
         for i in range(args.steps):
             tb.call(i)
-    g.replay()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    # the timed region: one replay of the K steps, HIP events on the kernels'
+    # stream inside the host clock
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    g.replay()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    t_kern = e0.elapsed_time(e1) * 1e-3 / args.steps
     del g
     t_step = elapsed / args.steps
     nbytes = tb.algorithmic_bytes()
     rows = case.x.shape[0]
-    t_kern = event_kernel_time(torch, stream, tb.call, min(args.steps, 50))
     achieved = nbytes / t_kern / 1e9
     traffic = load_traffic() if cfg_id == 2 else None
     del tb
