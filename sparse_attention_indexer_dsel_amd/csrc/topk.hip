@@ -507,50 +507,57 @@ __device__ __forceinline__ void first_digit_histogram(const uint32_t (&kw)[LOADS
 
 // A candidate list in LDS, cap entries plus one spare entry per lane.  A
 // bf16 entry is one word, key << 16 | column (columns of a workgroup's range
-// are below 2^16), so compaction stores and list reads are one LDS access
-// each; an fp32 entry keeps key and column in separate arrays (so the two
-// never have to sit in adjacent VGPRs for one 64-bit store).
+// are below 2^16); an fp32 entry is two words, key then column.  Either way
+// an entry sits at one address (the column at immediate offset 4), so a
+// compaction store needs no per-element address arithmetic beyond one
+// select.
 struct List {
-    uint32_t *key;
-    uint32_t *col;  // fp32 only
+    uint32_t *w;
 };
 
 template <class K>
-__device__ __forceinline__ List list_of(uint32_t *s_dyn, uint32_t cap) {
-    return List{s_dyn, K::PACK ? nullptr : s_dyn + cap + 64};
+__device__ __forceinline__ List list_of(uint32_t *s_dyn) {
+    return List{s_dyn};
 }
 
+// Words per entry.
 template <class K>
-__device__ __forceinline__ void list_put(List ent, uint32_t i, uint32_t key, uint32_t col) {
+__host__ __device__ constexpr uint32_t list_words() {
+    return K::PACK ? 1u : 2u;
+}
+
+// Store an entry at p (an entry slot of a list).
+template <class K>
+__device__ __forceinline__ void list_store(uint32_t *p, uint32_t key, uint32_t col) {
     if constexpr (K::PACK) {
-        ent.key[i] = (key << 16) | col;
+        p[0] = (key << 16) | col;
     } else {
-        ent.key[i] = key;
-        ent.col[i] = col;
+        p[0] = key;
+        p[1] = col;
     }
 }
 
 template <class K>
 __device__ __forceinline__ uint32_t list_key(List ent, uint32_t i) {
-    if constexpr (K::PACK) return ent.key[i] >> 16;
-    return ent.key[i];
+    if constexpr (K::PACK) return ent.w[i] >> 16;
+    return ent.w[2 * i];
 }
 
 // (key, column) of entry i
 template <class K>
 __device__ __forceinline__ uint2 list_entry(List ent, uint32_t i) {
     if constexpr (K::PACK) {
-        const uint32_t e = ent.key[i];
+        const uint32_t e = ent.w[i];
         return make_uint2(e >> 16, e & 0xFFFFu);
     }
-    return make_uint2(ent.key[i], ent.col[i]);
+    return *reinterpret_cast<const uint2 *>(ent.w + 2 * i);
 }
 
 // Compact the candidates (key >= T1, T1 > 0) of a workgroup's keys into
 // ent[0, run) in column order (entry = (key, column within the range));
 // returns run.
 // Every element is written once, the non-candidates to this lane's spare
-// entry at ent[cap + lane], so the loop has no branches.  CHECKED: when more
+// entry (entry cap + lane), so the loop has no branches.  CHECKED: when more
 // than `cap` qualify nothing is written (the count is still returned).  wtot
 // holds LP*NWAVE words.
 template <class K, int LOADS, bool CHECKED = false>
@@ -596,7 +603,8 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
     const uint32_t T1w = opaque(T1);
 #pragma unroll
     for (int w = 0; w < LOADS * 4; ++w) kw[w] = opaque(kw[w]);
-    const uint32_t spare = cap + lane;
+    constexpr uint32_t WPE = list_words<K>();
+    uint32_t *const spare = ent.w + WPE * (cap + lane);
     uint32_t run = 0;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -609,7 +617,8 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
                 tot += v;
                 before += (w < wid) ? v : 0u;
             }
-            uint32_t pos = run + before + ((ex[i] >> sh) & 0xFFFFu);
+            // slot of this thread's next candidate of this load
+            uint32_t *next = ent.w + WPE * (run + before + ((ex[i] >> sh) & 0xFFFFu));
             run += tot;
             const uint32_t p = (uint32_t)(j * NT + t) * VEC;
 #pragma unroll
@@ -618,8 +627,8 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
                 for (int h = 0; h < EPW; ++h) {
                     const uint32_t key = K::elem(kw[4 * j + q], h);
                     const bool cand = key >= T1w;
-                    list_put<K>(ent, cand ? pos : spare, key, p + q * EPW + h);
-                    pos += cand ? 1u : 0u;
+                    list_store<K>(cand ? next : spare, key, p + q * EPW + h);
+                    next += cand ? WPE : 0u;
                 }
         }
     }
@@ -1047,7 +1056,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     }
 
     const uint32_t cap = (uint32_t)a.cap;
-    const List ent = list_of<K>(s_dyn + list_base<K>(), cap);
+    const List ent = list_of<K>(s_dyn + list_base<K>());
     uint32_t *slot = a.ws + kHeaderWords + lrow * a.slot_words;
     uint32_t *err = a.ws;
     uint32_t *ghist = slot + kSlotHeadWords;
@@ -1305,7 +1314,7 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     extern __shared__ uint32_t s_dyn[];  // histogram, candidate list
     __shared__ TopkShared<(LOADS + 1) / 2> S;
     const TopkLds L{s_dyn, S.wtot, S.red, S.out};
-    const List ent = list_of<K>(s_dyn + list_base<K>(), (uint32_t)a.cap);
+    const List ent = list_of<K>(s_dyn + list_base<K>());
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
 
 #pragma unroll 1
