@@ -559,11 +559,13 @@ __device__ __forceinline__ uint2 list_entry(List ent, uint32_t i) {
 // Every element is written once, the non-candidates to this lane's spare
 // entry (entry cap + lane), so the loop has no branches.  CHECKED: when more
 // than `cap` qualify nothing is written (the count is still returned).  wtot
-// holds LP*NWAVE words.
+// holds LP*NWAVE words, base LOADS*NWAVE + 1: one wave turns the per-(load,
+// wave) counts into list offsets once, so each load costs a thread one LDS
+// read.
 template <class K, int LOADS, bool CHECKED = false>
 __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4], int len,
-                                                       uint32_t T1, uint32_t *wtot, List ent,
-                                                       uint32_t cap) {
+                                                       uint32_t T1, uint32_t *wtot,
+                                                       uint32_t *base, List ent, uint32_t cap) {
     constexpr int VEC = K::VEC, EPW = K::EPW, LP = (LOADS + 1) / 2, SPAN = NT * VEC;
     const int t = tid();
     const int lane = t & 63, wid = t >> 6;
@@ -591,35 +593,37 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
         if (lane == 63) wtot[i * NWAVE + wid] = incl;
     }
     __syncthreads();
-    if (CHECKED) {
-        uint32_t total = 0;
+    // wave 0: exclusive prefix of the (load, wave) counts in column order
+    // (load-major), two entries per lane
+    constexpr int NE = LOADS * NWAVE;
+    static_assert(NE <= 128, "two (load, wave) entries per lane of one wave");
+    if (wid == 0) {
+        uint32_t c[2];
 #pragma unroll
-        for (int i = 0; i < LP * NWAVE; ++i) {
-            const uint32_t v = wtot[i];
-            total += (v & 0xFFFFu) + (v >> 16);
+        for (int u = 0; u < 2; ++u) {
+            const int e = 2 * lane + u, j = e / NWAVE, w = e % NWAVE;
+            c[u] = e < NE ? (wtot[(j >> 1) * NWAVE + w] >> ((j & 1) * 16)) & 0xFFFFu : 0u;
         }
-        if (total > cap) return total;  // uniform
+        const uint32_t pair = c[0] + c[1];
+        const uint32_t incl = wave_incl_scan(pair);
+        if (2 * lane < NE) base[2 * lane] = incl - pair;
+        if (2 * lane + 1 < NE) base[2 * lane + 1] = incl - c[1];
+        if (lane == 63) base[NE] = incl;
     }
+    __syncthreads();
+    const uint32_t total = base[NE];
+    if (CHECKED && total > cap) return total;  // uniform
     const uint32_t T1w = opaque(T1);
 #pragma unroll
     for (int w = 0; w < LOADS * 4; ++w) kw[w] = opaque(kw[w]);
     constexpr uint32_t WPE = list_words<K>();
     uint32_t *const spare = ent.w + WPE * (cap + lane);
-    uint32_t run = 0;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         if (j < any) {
             const int i = j >> 1, sh = (j & 1) * 16;
-            uint32_t tot = 0, before = 0;
-#pragma unroll
-            for (int w = 0; w < NWAVE; ++w) {
-                const uint32_t v = (wtot[i * NWAVE + w] >> sh) & 0xFFFFu;
-                tot += v;
-                before += (w < wid) ? v : 0u;
-            }
             // slot of this thread's next candidate of this load
-            uint32_t *next = ent.w + WPE * (run + before + ((ex[i] >> sh) & 0xFFFFu));
-            run += tot;
+            uint32_t *next = ent.w + WPE * (base[j * NWAVE + wid] + ((ex[i] >> sh) & 0xFFFFu));
             const uint32_t p = (uint32_t)(j * NT + t) * VEC;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -633,7 +637,7 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
         }
     }
     __syncthreads();
-    return run;
+    return total;
 }
 
 // The boundary of a selection: every key whose top bits (key >> s) exceed P
@@ -1009,10 +1013,11 @@ __host__ __device__ constexpr uint32_t list_base() {
     return K::NPASS == 2 ? 64u : (uint32_t)(kBins + 64);
 }
 
-// Static LDS of the top-k kernels.
-template <int LP>
+// Static LDS of the top-k kernels (LOADS 16-byte loads per thread).
+template <int LOADS>
 struct TopkShared {
-    uint32_t wtot[LP * NWAVE];
+    uint32_t wtot[(LOADS + 1) / 2 * NWAVE];  // compaction: per-wave counts
+    uint32_t base[LOADS * NWAVE + 1];        // compaction: list offsets
     uint32_t red[NWAVE];
     uint32_t out[8];
 };
@@ -1021,6 +1026,7 @@ struct TopkShared {
 struct TopkLds {
     uint32_t *hist;
     uint32_t *wtot;
+    uint32_t *base;
     uint32_t *red;
     uint32_t *out;
 };
@@ -1038,8 +1044,8 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     static_assert(EPT % VEC == 0, "EPT must be a multiple of the vector width");
 
     extern __shared__ uint32_t s_dyn[];  // histogram, candidate list
-    __shared__ TopkShared<LP> S;
-    const TopkLds L{s_dyn, S.wtot, S.red, S.out};
+    __shared__ TopkShared<LOADS> S;
+    const TopkLds L{s_dyn, S.wtot, S.base, S.red, S.out};
 
     const int t = tid();
     const int G = a.G;
@@ -1107,7 +1113,8 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     uint32_t run = 0;
     bool listed = false;
     if (!regs) {
-        run = compact_candidates<K, LOADS, true>(kw, len, d1.v << K::SH1, L.wtot, ent, cap);
+        run = compact_candidates<K, LOADS, true>(kw, len, d1.v << K::SH1, L.wtot, L.base, ent,
+                                                 cap);
         listed = run <= cap;  // uniform over the workgroup
     }
     // this workgroup's (equal << 16 | above) counts at a bound
@@ -1273,7 +1280,7 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
         }
         write_from_regs<K, LOADS>(a, row, kw, len, b, 0u, 0u, row_view<K>(xr, n), 0, L.red, xr);
     } else if (C <= cap) {
-        compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, ent, cap);
+        compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, L.base, ent, cap);
         const Bound b = refine_on_list<K>(ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
         write_from_list<K>(a, row, ent, C, b, L.red, xr);
     } else {
@@ -1312,8 +1319,8 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     constexpr int LOADS = EPT / K::VEC;
     static_assert(EPT % K::VEC == 0, "EPT must be a multiple of the vector width");
     extern __shared__ uint32_t s_dyn[];  // histogram, candidate list
-    __shared__ TopkShared<(LOADS + 1) / 2> S;
-    const TopkLds L{s_dyn, S.wtot, S.red, S.out};
+    __shared__ TopkShared<LOADS> S;
+    const TopkLds L{s_dyn, S.wtot, S.base, S.red, S.out};
     const List ent = list_of<K>(s_dyn + list_base<K>());
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
 
