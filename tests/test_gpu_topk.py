@@ -152,6 +152,24 @@ def test_split_many_workgroups(dsel, orc, dt, G):
                    True, G)
 
 
+@pytest.mark.parametrize("dist", ["normal", "ties", "equal", "ascending", "descending",
+                                  "narrow", "special"])
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_long_whole_rows(dsel, orc, dt, dist):
+    """Whole rows of up to 16384 columns (the widest one workgroup takes)
+    with ragged ends from 2048 to 16384, every value distribution, NaN rows,
+    k from 1 to 2000."""
+    rows, cols = 24, 16384
+    x = W.random_rows(101 + len(dist), rows, cols, dt, dist)
+    W.plant_nans(x, 102, 3)
+    ends = [16384, 16383, 9000, 8191, 4096, 4095, 5001, 12345, 16000, 7777, 3000, 2048,
+            16384, 10000, 4500, 6001, 15999, 8192, 4097, 11111, 13000, 2500, 14000, 9999]
+    re = torch.tensor(ends, dtype=torch.int32)
+    for k, sorted_index, itype, ret in ((1, False, torch.int32, True), (64, True, torch.int64, True),
+                                        (500, False, torch.int32, False), (2000, True, torch.int32, True)):
+        check_case(dsel, orc, f"long/{dist}/{dt}/k{k}", x, k, re, sorted_index, itype, ret)
+
+
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
 def test_padded_stride(dsel, orc, dt):
     x = W.random_rows(31, 12, 2000, dt, "normal", stride=2048)
