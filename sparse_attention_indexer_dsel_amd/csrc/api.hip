@@ -32,6 +32,7 @@ bool aligned_ptr(const void *p) { return ((uintptr_t)p % kAlign) == 0; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct TopkPlan {
+    int kind = kTopkWhole;
     bool split = false;
     int G = 1;
     int ept = 0;
@@ -112,9 +113,33 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
         G = (int)cdiv(cols, chunk);  // rounding may leave fewer workgroups
     }
     if (G > kMaxSplit) return DSEL_ERR_ARG;  // row longer than the split limit holds
+    if (cols <= kWaveCapacity) {
+        // one wave per row; workgroups of four waves walk the rows, as many
+        // as the GPU holds at once
+        pl->kind = kTopkWave;
+        pl->split = false;
+        pl->G = 1;
+        pl->ept = 8;
+        while ((int64_t)64 * pl->ept < cols) pl->ept *= 2;  // columns per lane
+        pl->chunk = cols;
+        pl->cap = 0;
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, topk_kernel_ptr(dtype, pl->ept, kTopkWave), kTopkThreads,
+                topk_dyn_lds(dtype, 0, pl->ept, kTopkWave)) != hipSuccess ||
+            per_cu <= 0)
+            return DSEL_ERR_DEVICE;
+        const int64_t slots = (int64_t)per_cu * cus;
+        const int64_t wgs = cdiv(rows, kTopkThreads / 64);
+        pl->rows_per_launch = rows;
+        pl->grid = wgs < slots ? wgs : slots;
+        pl->ws_bytes = 0;
+        return DSEL_OK;
+    }
     if (G <= 1 && cols <= kBlockCapacity) {
-        // persistent workgroups, each walking rows with its next row's loads
-        // in flight: as many as the GPU holds at once
+        // one workgroup per row: as many as the GPU holds at once, each
+        // walking rows
+        pl->kind = kTopkWhole;
         pl->split = false;
         pl->G = 1;
         pl->ept = pick_ept(cols, kMaxEpt);
@@ -123,8 +148,8 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
         pl->cap = candidate_cap(k, cols);
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, topk_kernel_ptr(dtype, pl->ept, false), kTopkThreads,
-                topk_dyn_lds(dtype, pl->cap, pl->ept, false)) != hipSuccess ||
+                &per_cu, topk_kernel_ptr(dtype, pl->ept, kTopkWhole), kTopkThreads,
+                topk_dyn_lds(dtype, pl->cap, pl->ept, kTopkWhole)) != hipSuccess ||
             per_cu <= 0)
             return DSEL_ERR_DEVICE;
         const int64_t slots = (int64_t)per_cu * cus;
@@ -139,8 +164,8 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     // every workgroup of a row must be resident at once: size launches by
     // the number of workgroups the GPU holds
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, topk_kernel_ptr(dtype, ept, true),
-                                                     kTopkThreads, topk_dyn_lds(dtype, cap, ept, true)) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, topk_kernel_ptr(dtype, ept, kTopkSplit),
+                                                     kTopkThreads, topk_dyn_lds(dtype, cap, ept, kTopkSplit)) !=
             hipSuccess ||
         per_cu <= 0)
         return DSEL_ERR_DEVICE;
@@ -148,6 +173,7 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     if (G > capacity) return DSEL_ERR_ARG;  // row longer than the GPU holds on chip
     int64_t rpl = capacity / G;
     if (rpl > rows) rpl = rows;
+    pl->kind = kTopkSplit;
     pl->split = true;
     pl->G = G;
     pl->ept = ept;
@@ -235,7 +261,7 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
         a.row0 = r0;
         const int64_t grid = pl.split ? nr * pl.G : pl.grid;
         if (grid > INT32_MAX) return DSEL_ERR_ARG;
-        if (launch_topk(dtype, pl.ept, pl.split, a, (unsigned)grid, s) != hipSuccess)
+        if (launch_topk(dtype, pl.ept, pl.kind, a, (unsigned)grid, s) != hipSuccess)
             return DSEL_ERR_DEVICE;
     }
     return DSEL_OK;

@@ -59,13 +59,19 @@ struct TopkArgs {
     int ret_val;
 };
 
-// Kernel instance for (dtype, elements per thread, split); nullptr if none.
-const void *topk_kernel_ptr(int dtype, int ept, bool split);
+// Top-k kernel kinds: one workgroup per row, G workgroups per row, one wave
+// per row.
+enum { kTopkWhole = 0, kTopkSplit = 1, kTopkWave = 2 };
+// Rows of at most this many columns take one wave each.
+constexpr int64_t kWaveCapacity = 64 * 32;
+
+// Kernel instance for (dtype, elements per thread, kind); nullptr if none.
+const void *topk_kernel_ptr(int dtype, int ept, int kind);
 // Elements per 16-byte vector for a dtype.
 inline int topk_vec(int dtype) { return dtype == 0 ? 8 : 4; }
 // Dynamic LDS bytes of a top-k launch with candidate capacity `cap`.
-size_t topk_dyn_lds(int dtype, int64_t cap, int ept, bool split);
-hipError_t launch_topk(int dtype, int ept, bool split, const TopkArgs &a, unsigned grid,
+size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind);
+hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned grid,
                        hipStream_t stream);
 
 struct GatherArgs {

@@ -350,10 +350,12 @@ __device__ __forceinline__ void emit(const RowOut &o, uint32_t pos, uint32_t col
 }
 
 // Rows with n <= k: columns 0..n-1 in order, then padding.  Workgroup c of G
-// writes slots [c*S, (c+1)*S) with S = ceil(k / G).
+// writes slots [c*S, (c+1)*S) with S = ceil(k / G); `me` of `nthr` threads
+// (a workgroup's, or one wave's lanes) share them.
 template <class K>
 __device__ __forceinline__ void write_short_row(const TopkArgs &a, int64_t row, int64_t n, int c, int G,
-                                const typename K::raw_t *xr) {
+                                const typename K::raw_t *xr, int me = tid(),
+                                int nthr = NT) {
     const int S = (a.k + G - 1) / G;
     const int s0 = c * S;
     const int s1 = min(a.k, s0 + S);
@@ -361,7 +363,7 @@ __device__ __forceinline__ void write_short_row(const TopkArgs &a, int64_t row, 
         // index-only int32: four slots per 16-byte store
         int32_t *o = reinterpret_cast<int32_t *>(a.out_idx) + row * a.idx_stride;
         const int nv = (s1 - s0) >> 2;
-        for (int v = tid(); v < nv; v += NT) {
+        for (int v = me; v < nv; v += nthr) {
             const int s = s0 + 4 * v;
             int4 q;
             q.x = s < n ? s : -1;
@@ -370,9 +372,9 @@ __device__ __forceinline__ void write_short_row(const TopkArgs &a, int64_t row, 
             q.w = s + 3 < n ? s + 3 : -1;
             *reinterpret_cast<int4 *>(o + s) = q;
         }
-        for (int s = s0 + 4 * nv + tid(); s < s1; s += NT) o[s] = s < n ? s : -1;
+        for (int s = s0 + 4 * nv + me; s < s1; s += nthr) o[s] = s < n ? s : -1;
     } else {
-        for (int s = s0 + tid(); s < s1; s += NT) {
+        for (int s = s0 + me; s < s1; s += nthr) {
             const bool in = s < n;
             if (a.idx64)
                 reinterpret_cast<int64_t *>(a.out_idx)[row * a.idx_stride + s] = in ? (int64_t)s : -1;
@@ -383,7 +385,7 @@ __device__ __forceinline__ void write_short_row(const TopkArgs &a, int64_t row, 
                     in ? xr[s] : (typename K::raw_t)K::NEG_INF;
         }
     }
-    if (c == 0 && tid() == 0 && a.nan_flag) a.nan_flag[row] = 0;
+    if (c == 0 && me == 0 && a.nan_flag) a.nan_flag[row] = 0;
 }
 
 // Range-checked view of one row's first `end` columns for raw buffer loads:
@@ -434,16 +436,17 @@ __device__ __forceinline__ void clear_tail(uint32_t *kw, int valid) {
 }
 
 // Keys of a workgroup's loads in the coalesced layout (load j of thread t
-// holds the VEC columns from (j*NT + t)*VEC of a range of `len` columns).
+// holds the VEC columns from (j*TW + t)*VEC of a range of `len` columns; TW
+// is NT, or 64 for one wave's lanes).
 // Columns at or past len get key 0 and are not probed for NaN; loads wholly
 // past len are not transformed at all.  Returns whether this thread saw a
 // NaN.
-template <class K, int LOADS>
+template <class K, int LOADS, int TW = NT>
 __device__ __forceinline__ uint32_t keys_of_loads(const uint4 (&v)[LOADS], int len,
-                                                  uint32_t (&kw)[LOADS * 4]) {
+                                                  uint32_t (&kw)[LOADS * 4], int me = tid()) {
     constexpr int VEC = K::VEC, EPW = K::EPW;
-    const int full = len / (NT * VEC);  // loads valid for every thread (uniform)
-    const int any = (len + NT * VEC - 1) / (NT * VEC);
+    const int full = len / (TW * VEC);  // loads valid for every thread (uniform)
+    const int any = (len + TW * VEC - 1) / (TW * VEC);
     uint32_t nan = 0;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -455,7 +458,7 @@ __device__ __forceinline__ uint32_t keys_of_loads(const uint4 (&v)[LOADS], int l
         uint4 x = v[j];
         int valid = VEC;
         if (j >= full) {
-            valid = len - (j * NT + tid()) * VEC;
+            valid = len - (j * TW + me) * VEC;
             valid = valid < 0 ? 0 : (valid > VEC ? VEC : valid);
             x.x = K::keep_raw(x.x, valid);
             x.y = K::keep_raw(x.y, valid - EPW);
@@ -1339,6 +1342,276 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Short rows (at most 64 x EPL columns): one wave per row.  The keys stay in
+// VGPRs, each wave has its own LDS histogram and every scan is a wave scan,
+// so a row needs no workgroup barrier: four rows run side by side in a
+// workgroup, and many more rows are in flight per compute unit than with a
+// workgroup per row.
+// ---------------------------------------------------------------------------
+
+// Digit plan of the wave kernel: bf16 10 + 6 bits (a 1024-bin first
+// histogram, 4 KB per wave), fp32 11 + 11 + 10.
+template <class K>
+struct WaveDigits;
+template <>
+struct WaveDigits<Bf16Key> {
+    static constexpr int NPASS = 2, HB = 1024, SH1 = 6;
+    __device__ static int bits(int pass) { return pass == 0 ? 10 : 6; }
+};
+template <>
+struct WaveDigits<F32Key> {
+    static constexpr int NPASS = 3, HB = 2048, SH1 = 21;
+    __device__ static int bits(int pass) { return pass == 2 ? 10 : 11; }
+};
+
+// LDS words per wave: its histogram and one spare bin per lane.
+template <class K>
+__host__ __device__ constexpr uint32_t wave_lds_words() {
+    return (uint32_t)WaveDigits<K>::HB + 64;
+}
+
+// Order this wave's LDS accesses (one wave's LDS operations execute in
+// order; this keeps the compiler from moving them across phases).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// find_digit for one wave: lane l sums the bins [nb - (l+1)*bpt, nb - l*bpt)
+// from the top, one wave scan finds the lane holding the need-th largest
+// element, and that lane walks its bins.
+__device__ __forceinline__ Digit wave_find_digit(const uint32_t *hist, int nb, uint32_t need) {
+    const int lane = tid() & 63;
+    const int bpt = nb > 64 ? nb / 64 : 1;
+    const int nact = nb / bpt;
+    const int top = nb - lane * bpt;
+    uint32_t local = 0;
+    if (lane < nact)
+        for (int i = 1; i <= bpt; ++i) local += hist[top - i];
+    const uint32_t incl = wave_incl_scan(local);
+    const uint32_t excl = incl - local;
+    const uint64_t m = __ballot(lane < nact && excl < need && need <= incl);
+    const int L = (int)__builtin_ctzll(m);  // uniform; m != 0 when the bins hold >= need
+    uint32_t v = 0, above = 0, cnt = 0;
+    if (lane == L) {
+        uint32_t acc = excl;
+        for (int i = 1; i <= bpt; ++i) {
+            const uint32_t h = hist[top - i];
+            if (acc + h >= need) {
+                v = (uint32_t)(top - i);
+                above = acc;
+                cnt = h;
+                break;
+            }
+            acc += h;
+        }
+    }
+    return Digit{(uint32_t)__builtin_amdgcn_readlane((int)v, L),
+                 (uint32_t)__builtin_amdgcn_readlane((int)above, L),
+                 (uint32_t)__builtin_amdgcn_readlane((int)cnt, L)};
+}
+
+// A row's outputs as range-checked buffer views: a store at an offset past
+// the row's k slots is dropped by the hardware, so a lane that takes no
+// element stores to kDrop and the write needs no branch.
+struct RowViews {
+    __amdgpu_buffer_rsrc_t idx, val;
+    int idx64, has_val;
+};
+constexpr uint32_t kDrop = 0x80000000u;
+
+template <class K>
+__device__ __forceinline__ RowViews row_views(const TopkArgs &a, int64_t row) {
+    RowViews v;
+    const int isz = a.idx64 ? 8 : 4;
+    v.idx = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<char *>(a.out_idx) + row * a.idx_stride * isz, (short)0, a.k * isz,
+        0x00020000);
+    v.val = __builtin_amdgcn_make_buffer_rsrc(
+        a.ret_val ? reinterpret_cast<char *>(a.out_val) +
+                        row * a.val_stride * (int64_t)sizeof(typename K::raw_t)
+                  : reinterpret_cast<char *>(a.out_idx),
+        (short)0, a.ret_val ? a.k * (int)sizeof(typename K::raw_t) : 0, 0x00020000);
+    v.idx64 = a.idx64;
+    v.has_val = a.ret_val;
+    return v;
+}
+
+// Slot `pos` (or nothing, when !take): the value bits.
+template <class K>
+__device__ __forceinline__ void view_store_value(const RowViews &v, bool take, uint32_t pos,
+                                                 uint32_t bits) {
+    if constexpr (sizeof(typename K::raw_t) == 2)
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, v.val, take ? pos * 2u : kDrop,
+                                              0u, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b32(bits, v.val, take ? pos * 4u : kDrop, 0u, 0);
+}
+
+// Slot `pos` (or nothing, when !take): the column, and the value bits.
+template <class K>
+__device__ __forceinline__ void view_store(const RowViews &v, bool take, uint32_t pos, uint32_t col,
+                                           uint32_t bits) {
+    if (v.idx64) {
+        const uint64_t c = col;
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, c), v.idx,
+            take ? pos * 8u : kDrop, 0u, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(col, v.idx, take ? pos * 4u : kDrop, 0u, 0);
+    }
+    if (v.has_val) view_store_value<K>(v, take, pos, bits);
+}
+
+// Write one wave's row from its keys in VGPRs (coalesced layout, load j of
+// lane l at columns (j*64 + l)*VEC...).  First pass (fix = false): indices,
+// and values rebuilt from the keys; amb reports whether a +-0 / NaN key was
+// taken.  Second pass (fix = true): only those keys' values, from the row.
+template <class K, int LPL>
+__device__ __forceinline__ void wave_write(const RowViews &o, uint32_t (&kw)[LPL * 4], int len,
+                                           Bound b, int lane, const typename K::raw_t *xr,
+                                           bool fix, uint32_t &amb) {
+    constexpr int VEC = K::VEC, EPW = K::EPW, SPAN = 64 * VEC;
+    const int any = (len + SPAN - 1) / SPAN;
+    uint32_t G = 0, Q = 0;  // taken-above and equal counts of earlier loads
+#pragma unroll
+    for (int j = 0; j < LPL; ++j) {
+        if (j >= any) continue;
+        uint32_t g = 0, q = 0;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int h = 0; h < EPW; ++h) {
+                const uint32_t key = K::elem(kw[4 * j + qq], h);
+                const uint32_t pre = key >> b.s;
+                g += (key && pre > b.P) ? 1u : 0u;
+                q += (key && pre == b.P) ? 1u : 0u;
+            }
+        const uint32_t mine = g | (q << 16);
+        const uint32_t incl = wave_incl_scan(mine);
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        uint32_t gb = G + ((incl - mine) & 0xFFFFu), qb = Q + ((incl - mine) >> 16);
+        const uint32_t p = (uint32_t)(j * 64 + lane) * VEC;
+        // recompute the comparisons below rather than keep a lane mask per
+        // element alive across the scan
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) kw[4 * j + qq] = opaque(kw[4 * j + qq]);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int h = 0; h < EPW; ++h) {
+                const uint32_t key = K::elem(kw[4 * j + qq], h);
+                const uint32_t pre = key >> b.s;
+                const bool gt = key && pre > b.P, eq = key && pre == b.P;
+                const bool take = gt || (eq && qb < b.need);
+                const uint32_t pos = gt ? gb + min(qb, b.need) : gb + qb;
+                const uint32_t col = p + qq * EPW + h;
+                if (!fix) {
+                    view_store<K>(o, take, pos, col, K::value_bits(key));
+                    amb |= (take && K::ambiguous(key)) ? 1u : 0u;
+                } else if (take && K::ambiguous(key)) {
+                    view_store_value<K>(o, true, pos, (uint32_t)xr[col]);
+                }
+                gb += gt ? 1u : 0u;
+                qb += eq ? 1u : 0u;
+            }
+        G += tot & 0xFFFFu;
+        Q += tot >> 16;
+    }
+}
+
+// EPL = columns per lane (a multiple of VEC); rows of n <= k are padded.
+template <class K, int EPL>
+__global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
+    using raw_t = typename K::raw_t;
+    using D = WaveDigits<K>;
+    constexpr int VEC = K::VEC, EPW = K::EPW, LPL = EPL / VEC, SPAN = 64 * VEC;
+    static_assert(EPL % VEC == 0, "EPL must be a multiple of the vector width");
+    extern __shared__ uint32_t s_dyn[];  // one histogram per wave
+    const int lane = tid() & 63, wid = tid() >> 6;
+    uint32_t *hist = s_dyn + wid * wave_lds_words<K>();
+    const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
+    const int64_t step = (int64_t)gridDim.x * NWAVE;
+
+#pragma unroll 1
+    for (int64_t row = a.row0 + (int64_t)blockIdx.x * NWAVE + wid; row < a.rows; row += step) {
+        const int64_t n = valid_length(a, row);
+        const raw_t *xr = x + row * a.x_stride;
+        if (n <= a.k) {
+            write_short_row<K>(a, row, n, 0, 1, xr, lane, 64);
+            continue;
+        }
+        const int len = (int)n;
+        uint4 v[LPL];
+        {
+            const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
+#pragma unroll
+            for (int j = 0; j < LPL; ++j) v[j] = load_vec<K>(view, (int64_t)(j * 64 + lane) * VEC);
+        }
+        wave_sync();  // the previous row's reads of the histogram are done
+        for (int i = lane; i < D::HB + 64; i += 64) hist[i] = 0;
+        uint32_t kw[LPL * 4];
+        const bool row_nan = __ballot(keys_of_loads<K, LPL, 64>(v, len, kw, lane) != 0u) != 0;
+        wave_sync();
+
+        // first digit
+        const int full = len / SPAN, any = (len + SPAN - 1) / SPAN;
+        const uint32_t spare = (uint32_t)D::HB + (uint32_t)lane;
+#pragma unroll
+        for (int j = 0; j < LPL; ++j)
+            if (j < any)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int h = 0; h < EPW; ++h) {
+                        const uint32_t key = K::elem(kw[4 * j + q], h);
+                        atomicAdd(&hist[(j < full || key) ? (key >> D::SH1) : spare], 1u);
+                    }
+        wave_sync();
+        const Digit d1 = wave_find_digit(hist, D::HB, (uint32_t)a.k);
+
+        // the later digits, from the keys in VGPRs
+        Bound b{d1.v, D::SH1, (uint32_t)a.k - d1.above};
+        if (d1.cnt != b.need) {
+#pragma unroll 1
+            for (int pass = 1; pass < D::NPASS; ++pass) {
+                const int d = D::bits(pass);
+                const int sh = b.s - d;
+                const int nb = 1 << d;
+                wave_sync();
+                for (int i = lane; i < nb; i += 64) hist[i] = 0;
+                wave_sync();
+#pragma unroll
+                for (int w = 0; w < LPL * 4; ++w)
+#pragma unroll
+                    for (int h = 0; h < EPW; ++h) {
+                        const uint32_t key = K::elem(kw[w], h);
+                        if (key && (key >> b.s) == b.P)
+                            atomicAdd(&hist[(key >> sh) & (uint32_t)(nb - 1)], 1u);
+                    }
+                wave_sync();
+                const Digit dg = wave_find_digit(hist, nb, b.need);
+                b.need -= dg.above;
+                b.P = (b.P << d) | dg.v;
+                b.s = sh;
+                if (dg.cnt == b.need) break;
+            }
+        }
+
+        // the selection in column order: per load, a wave scan of the lanes'
+        // (equal << 16 | above) counts gives each lane its ranks.  Values come
+        // from the keys, so the stores wait for no load; +-0 / NaN keys get
+        // their bits from the row in a second pass, run only if one was taken.
+        const RowViews o = row_views<K>(a, row);
+        uint32_t amb = 0;
+        wave_write<K, LPL>(o, kw, len, b, lane, xr, false, amb);
+        if (o.has_val && __ballot(amb != 0u)) wave_write<K, LPL>(o, kw, len, b, lane, xr, true, amb);
+        if (lane == 0 && a.nan_flag) a.nan_flag[row] = row_nan ? 1u : 0u;
+    }
+}
+
 template <class K, int EPT, bool SPLIT>
 const void *kptr() {
     if constexpr (SPLIT)
@@ -1363,31 +1636,44 @@ const void *pick(int ept) {
 
 }  // namespace
 
+template <class K>
+const void *pick_wave(int epl) {
+    switch (epl) {
+        case 8: return reinterpret_cast<const void *>(&topk_rows_wave<K, 8>);
+        case 16: return reinterpret_cast<const void *>(&topk_rows_wave<K, 16>);
+        case 32: return reinterpret_cast<const void *>(&topk_rows_wave<K, 32>);
+        default: return nullptr;
+    }
+}
+
 // ept = columns per thread of one workgroup's range (the whole row, or one
-// split chunk).
-const void *topk_kernel_ptr(int dtype, int ept, bool split) {
+// split chunk), or per lane of a wave's row (kTopkWave).
+const void *topk_kernel_ptr(int dtype, int ept, int kind) {
+    if (kind == kTopkWave) return dtype == 0 ? pick_wave<Bf16Key>(ept) : pick_wave<F32Key>(ept);
+    const bool split = kind == kTopkSplit;
     if (dtype == 0) return split ? pick<Bf16Key, true>(ept) : pick<Bf16Key, false>(ept);
     return split ? pick<F32Key, true>(ept) : pick<F32Key, false>(ept);
 }
 
 // The histogram, and the candidate list: cap entries plus one spare per
 // lane (one word per bf16 entry, two per fp32 entry), from list_base.
-size_t topk_dyn_lds(int dtype, int64_t cap, int ept, bool split) {
+size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind) {
     (void)ept;
-    (void)split;
+    if (kind == kTopkWave)
+        return (size_t)NWAVE * (dtype == 0 ? wave_lds_words<Bf16Key>() : wave_lds_words<F32Key>()) * 4;
     const uint64_t hist = (uint64_t)(kBins + 64);
     const uint64_t base = dtype == 0 ? list_base<Bf16Key>() : list_base<F32Key>();
     const uint64_t words = base + (dtype == 0 ? 1u : 2u) * (uint64_t)(cap + 64);
     return (size_t)(words > hist ? words : hist) * 4;
 }
 
-hipError_t launch_topk(int dtype, int ept, bool split, const TopkArgs &a, unsigned grid,
+hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned grid,
                        hipStream_t stream) {
-    const void *fn = topk_kernel_ptr(dtype, ept, split);
+    const void *fn = topk_kernel_ptr(dtype, ept, kind);
     if (!fn) return hipErrorInvalidValue;
     TopkArgs copy = a;
     void *args[] = {&copy};
-    return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, topk_dyn_lds(dtype, a.cap, ept, split),
+    return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, topk_dyn_lds(dtype, a.cap, ept, kind),
                            stream);
 }
 

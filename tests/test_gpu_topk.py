@@ -170,6 +170,25 @@ def test_long_whole_rows(dsel, orc, dt, dist):
         check_case(dsel, orc, f"long/{dist}/{dt}/k{k}", x, k, re, sorted_index, itype, ret)
 
 
+@pytest.mark.parametrize("cols", [1, 37, 512, 513, 1024, 1500, 2048])
+@pytest.mark.parametrize("dist", ["normal", "ties", "equal", "special", "ascending"])
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_short_rows_one_wave(dsel, orc, dt, dist, cols):
+    """Rows of at most 2048 columns, one wave each: ragged ends, NaN rows,
+    every output form, k below, at and above the row length."""
+    rows = 70
+    x = W.random_rows(111 + cols + len(dist), rows, cols, dt, dist)
+    W.plant_nans(x, 112 + cols, 5)
+    re = W.random_row_end(113 + cols, rows, -3, cols + 3)
+    re[:3] = torch.tensor([cols, 0, max(cols - 1, 0)], dtype=torch.int32)
+    for k, sorted_index, itype, ret in ((1, False, torch.int32, True), (17, True, torch.int64, True),
+                                        (max(cols // 2, 1), False, torch.int32, False),
+                                        (cols, True, torch.int32, True), (cols + 5, False, torch.int64, True)):
+        if k > 4096:
+            continue
+        check_case(dsel, orc, f"wave/{dist}/{dt}/c{cols}/k{k}", x, k, re, sorted_index, itype, ret)
+
+
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
 def test_padded_stride(dsel, orc, dt):
     x = W.random_rows(31, 12, 2000, dt, "normal", stride=2048)
