@@ -1530,7 +1530,9 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
     constexpr int VEC = K::VEC, EPW = K::EPW, LPL = EPL / VEC, SPAN = 64 * VEC;
     static_assert(EPL % VEC == 0, "EPL must be a multiple of the vector width");
     extern __shared__ uint32_t s_dyn[];  // one histogram per wave
-    const int lane = tid() & 63, wid = tid() >> 6;
+    // the wave index, uniform (in an SGPR): the row, its views and the
+    // output descriptors are then scalar, not per-lane values
+    const int lane = tid() & 63, wid = __builtin_amdgcn_readfirstlane(tid() >> 6);
     uint32_t *hist = s_dyn + wid * wave_lds_words<K>();
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
     const int64_t step = (int64_t)gridDim.x * NWAVE;
