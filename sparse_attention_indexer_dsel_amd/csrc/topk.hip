@@ -1522,6 +1522,98 @@ __device__ __forceinline__ void wave_write(const RowViews &o, uint32_t (&kw)[LPL
     }
 }
 
+// Bytes of a row's staged output: k indices, then (16-byte aligned) k values.
+__device__ __forceinline__ uint32_t stage_value_offset(const TopkArgs &a) {
+    return ((uint32_t)a.k * (a.idx64 ? 8u : 4u) + 15u) & ~15u;
+}
+template <class K>
+__device__ __forceinline__ uint32_t stage_bytes(const TopkArgs &a) {
+    return stage_value_offset(a) + (a.ret_val ? (uint32_t)a.k * (uint32_t)sizeof(typename K::raw_t) : 0u);
+}
+
+// Copy `bytes` bytes (a multiple of 2) from LDS to a 16-byte aligned global
+// row: 16 bytes per lane and store while they last, then words, then a last
+// half word.
+__device__ __forceinline__ void wave_copy_out(const char *src, char *dst, uint32_t bytes, int lane) {
+    const uint32_t full = bytes & ~15u;
+    for (uint32_t off = (uint32_t)lane * 16u; off < full; off += 64u * 16u)
+        *reinterpret_cast<uint4 *>(dst + off) = *reinterpret_cast<const uint4 *>(src + off);
+    const uint32_t words = bytes & ~3u;
+    const uint32_t w = full + (uint32_t)lane * 4u;
+    if (w < words) *reinterpret_cast<uint32_t *>(dst + w) = *reinterpret_cast<const uint32_t *>(src + w);
+    if ((bytes & 2u) && lane == 0)
+        *reinterpret_cast<uint16_t *>(dst + words) = *reinterpret_cast<const uint16_t *>(src + words);
+}
+
+// Write one wave's row through LDS (the row's k slots fit the wave's LDS
+// region): the ranked elements fill the slots in LDS, then the wave copies
+// them out with contiguous stores.  Every slot is filled: the row holds more
+// than k keys, so exactly k are taken.
+template <class K, int LPL>
+__device__ __forceinline__ void wave_write_staged(const TopkArgs &a, int64_t row,
+                                                  uint32_t (&kw)[LPL * 4], int len, Bound b,
+                                                  int lane, const typename K::raw_t *xr,
+                                                  char *stage) {
+    using raw_t = typename K::raw_t;
+    constexpr int VEC = K::VEC, EPW = K::EPW, SPAN = 64 * VEC;
+    const int any = (len + SPAN - 1) / SPAN;
+    const uint32_t voff = stage_value_offset(a);
+    uint32_t G = 0, Q = 0;
+#pragma unroll
+    for (int j = 0; j < LPL; ++j) {
+        if (j >= any) continue;
+        uint32_t g = 0, q = 0;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int h = 0; h < EPW; ++h) {
+                const uint32_t key = K::elem(kw[4 * j + qq], h);
+                const uint32_t pre = key >> b.s;
+                g += (key && pre > b.P) ? 1u : 0u;
+                q += (key && pre == b.P) ? 1u : 0u;
+            }
+        const uint32_t mine = g | (q << 16);
+        const uint32_t incl = wave_incl_scan(mine);
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        uint32_t gb = G + ((incl - mine) & 0xFFFFu), qb = Q + ((incl - mine) >> 16);
+        const uint32_t p = (uint32_t)(j * 64 + lane) * VEC;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) kw[4 * j + qq] = opaque(kw[4 * j + qq]);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int h = 0; h < EPW; ++h) {
+                const uint32_t key = K::elem(kw[4 * j + qq], h);
+                const uint32_t pre = key >> b.s;
+                const bool gt = key && pre > b.P, eq = key && pre == b.P;
+                const bool take = gt || (eq && qb < b.need);
+                const uint32_t pos = gt ? gb + min(qb, b.need) : gb + qb;
+                const uint32_t col = p + qq * EPW + h;
+                if (take) {
+                    if (a.idx64)
+                        reinterpret_cast<uint64_t *>(stage)[pos] = col;
+                    else
+                        reinterpret_cast<uint32_t *>(stage)[pos] = col;
+                    if (a.ret_val)
+                        reinterpret_cast<raw_t *>(stage + voff)[pos] =
+                            K::ambiguous(key) ? xr[col] : (raw_t)K::value_bits(key);
+                }
+                gb += gt ? 1u : 0u;
+                qb += eq ? 1u : 0u;
+            }
+        G += tot & 0xFFFFu;
+        Q += tot >> 16;
+    }
+    wave_sync();
+    const int isz = a.idx64 ? 8 : 4;
+    wave_copy_out(stage, reinterpret_cast<char *>(a.out_idx) + row * a.idx_stride * isz,
+                  (uint32_t)a.k * (uint32_t)isz, lane);
+    if (a.ret_val)
+        wave_copy_out(stage + voff,
+                      reinterpret_cast<char *>(a.out_val) + row * a.val_stride * (int64_t)sizeof(raw_t),
+                      (uint32_t)a.k * (uint32_t)sizeof(raw_t), lane);
+}
+
 // EPL = columns per lane (a multiple of VEC); rows of n <= k are padded.
 template <class K, int EPL>
 __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
@@ -1606,10 +1698,16 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
         // (equal << 16 | above) counts gives each lane its ranks.  Values come
         // from the keys, so the stores wait for no load; +-0 / NaN keys get
         // their bits from the row in a second pass, run only if one was taken.
-        const RowViews o = row_views<K>(a, row);
-        uint32_t amb = 0;
-        wave_write<K, LPL>(o, kw, len, b, lane, xr, false, amb);
-        if (o.has_val && __ballot(amb != 0u)) wave_write<K, LPL>(o, kw, len, b, lane, xr, true, amb);
+        if (stage_bytes<K>(a) <= wave_lds_words<K>() * 4u) {
+            wave_sync();  // the histogram is dead: its space holds the row's slots
+            wave_write_staged<K, LPL>(a, row, kw, len, b, lane, xr, reinterpret_cast<char *>(hist));
+        } else {
+            const RowViews o = row_views<K>(a, row);
+            uint32_t amb = 0;
+            wave_write<K, LPL>(o, kw, len, b, lane, xr, false, amb);
+            if (o.has_val && __ballot(amb != 0u))
+                wave_write<K, LPL>(o, kw, len, b, lane, xr, true, amb);
+        }
         if (lane == 0 && a.nan_flag) a.nan_flag[row] = row_nan ? 1u : 0u;
     }
 }
