@@ -672,11 +672,14 @@ __device__ __forceinline__ void list_refine_histogram(List ent, uint32_t C, uint
     }
 }
 
-// Resolve the digits after the first among the candidate list's entries
-// (every entry's first digit is >= d1.v).
-template <class K>
-__device__ Bound refine_on_list(List ent, uint32_t C, Digit d1, uint32_t k,
-                                uint32_t *s_hist, uint32_t *s_red, uint32_t *s_out) {
+// The radix passes after the first digit d1, within one workgroup: each
+// zeroes the pass's bins, has fill(P, s, sh, dmask) histogram the next digit
+// ((key >> sh) & dmask) of the keys whose top bits (key >> s) equal P, and
+// finds the digit holding the need-th key.  They stop early when a boundary
+// bin is taken whole.
+template <class K, class Fill>
+__device__ __forceinline__ Bound refine_passes(Digit d1, uint32_t k, uint32_t *s_hist,
+                                               uint32_t *s_red, uint32_t *s_out, Fill fill) {
     const int t = tid();
     Bound b{d1.v, K::SH1, k - d1.above};
     if (d1.cnt == b.need) return b;  // the boundary bin is taken whole
@@ -687,7 +690,7 @@ __device__ Bound refine_on_list(List ent, uint32_t C, Digit d1, uint32_t k,
         const int nb = 1 << d;
         for (int i = t; i < nb; i += NT) s_hist[i] = 0;
         __syncthreads();
-        list_refine_histogram<K>(ent, C, b.P, b.s, sh, (1u << d) - 1u, s_hist);
+        fill(b.P, b.s, sh, (1u << d) - 1u);
         __syncthreads();
         const Digit dg = find_digit(s_hist, nb, b.need, s_red, s_out);
         b.need -= dg.above;
@@ -696,6 +699,17 @@ __device__ Bound refine_on_list(List ent, uint32_t C, Digit d1, uint32_t k,
         if (dg.cnt == b.need) break;
     }
     return b;
+}
+
+// Resolve the digits after the first among the candidate list's entries
+// (every entry's first digit is >= d1.v).
+template <class K>
+__device__ Bound refine_on_list(List ent, uint32_t C, Digit d1, uint32_t k,
+                                uint32_t *s_hist, uint32_t *s_red, uint32_t *s_out) {
+    return refine_passes<K>(d1, k, s_hist, s_red, s_out,
+                            [&](uint32_t P, int s, int sh, uint32_t dmask) {
+                                list_refine_histogram<K>(ent, C, P, s, sh, dmask, s_hist);
+                            });
 }
 
 // This workgroup's list totals: entries taken above the boundary (top bits >
@@ -1043,7 +1057,6 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     using raw_t = typename K::raw_t;
     constexpr int VEC = K::VEC;
     constexpr int LOADS = EPT / VEC;
-    constexpr int LP = (LOADS + 1) / 2;
     static_assert(EPT % VEC == 0, "EPT must be a multiple of the vector width");
 
     extern __shared__ uint32_t s_dyn[];  // histogram, candidate list
@@ -1263,49 +1276,24 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
 
     if (LOADS <= 2 && 4 * (int64_t)C >= n) {
         // a few keys per thread and dense candidates: no list
-        Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
-        if (d1.cnt != b.need) {
-#pragma unroll 1
-            for (int pass = 1; pass < K::NPASS; ++pass) {
-                const int d = K::digit(pass);
-                const int sh = b.s - d;
-                const int nb = 1 << d;
-                for (int i = t; i < nb; i += NT) L.hist[i] = 0;
-                __syncthreads();
-                refine_histogram_regs<K, LOADS>(kw, b.P, b.s, sh, (1u << d) - 1u, L.hist);
-                __syncthreads();
-                const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
-                b.need -= dg.above;
-                b.P = (b.P << d) | dg.v;
-                b.s = sh;
-                if (dg.cnt == b.need) break;
-            }
-        }
+        const Bound b = refine_passes<K>(d1, (uint32_t)a.k, L.hist, L.red, L.out,
+                                         [&](uint32_t P, int s, int sh, uint32_t dmask) {
+                                             refine_histogram_regs<K, LOADS>(kw, P, s, sh, dmask,
+                                                                             L.hist);
+                                         });
         write_from_regs<K, LOADS>(a, row, kw, len, b, 0u, 0u, row_view<K>(xr, n), 0, L.red, xr);
     } else if (C <= cap) {
         compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, L.base, ent, cap);
         const Bound b = refine_on_list<K>(ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
         write_from_list<K>(a, row, ent, C, b, L.red, xr);
     } else {
+        // the candidates do not fit the list: the passes re-read the row
         const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
-        Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
-        if (d1.cnt != b.need) {
-#pragma unroll 1
-            for (int pass = 1; pass < K::NPASS; ++pass) {
-                const int d = K::digit(pass);
-                const int sh = b.s - d;
-                const int nb = 1 << d;
-                for (int i = t; i < nb; i += NT) L.hist[i] = 0;
-                __syncthreads();
-                refine_histogram_stream<K>(view, 0, len, b.P, b.s, sh, (1u << d) - 1u, L.hist);
-                __syncthreads();
-                const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
-                b.need -= dg.above;
-                b.P = (b.P << d) | dg.v;
-                b.s = sh;
-                if (dg.cnt == b.need) break;
-            }
-        }
+        const Bound b = refine_passes<K>(d1, (uint32_t)a.k, L.hist, L.red, L.out,
+                                         [&](uint32_t P, int s, int sh, uint32_t dmask) {
+                                             refine_histogram_stream<K>(view, 0, len, P, s, sh,
+                                                                        dmask, L.hist);
+                                         });
         write_from_stream<K>(a, row, view, 0, len, b, 0u, 0u, L.red, xr);
     }
     if (t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)block_nan;
