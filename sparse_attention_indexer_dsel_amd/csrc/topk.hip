@@ -21,19 +21,25 @@
 //     all loads issued at once; it histograms an 11-bit first digit in LDS;
 //   * the bin holding the k-th largest key fixes a threshold T1; only the C
 //     candidates with key >= T1 (about k plus one bin) are compacted, in
-//     column order, into an LDS list of (key, column) entries;
+//     column order, into an LDS list (bf16: one word per entry, key << 16 |
+//     column; fp32: key and column words side by side);
 //   * the rest of the radix select (5 more bits for bf16, 11+10 for fp32)
 //     runs on that short list; the selection, every key > T plus the first
 //     `need` keys == T in column order, is written in column order: each
-//     wave owns a contiguous quarter of the list and ranks its entries with
-//     ballots, so the write needs one cross-wave exchange and no more
-//     barriers.  The output is ascending by construction; no sort is run;
-//   * rows too long for one workgroup, or too few rows to fill the GPU, are
-//     split over G workgroups, each holding one chunk: their histograms meet
-//     in a per-row workspace slot (device-scope relaxed atomics and a
-//     rendezvous per radix pass); each workgroup lists its own candidates,
-//     and after one more exchange (the counts of the chunks before it) writes
-//     its part of the row's output;
+//     thread owns a contiguous run of the list and one workgroup scan gives
+//     its ranks.  The output is ascending by construction; no sort is run;
+//   * a workgroup holding at most two loads per thread with dense candidates
+//     skips the list: the later passes and the write work on its VGPRs;
+//   * rows of at most 2048 columns take one wave each: the keys in VGPRs, a
+//     per-wave LDS histogram and wave scans only, so no row waits on a
+//     workgroup barrier and four rows run side by side per workgroup;
+//   * rows longer than one workgroup holds (16384 columns) are split over G
+//     workgroups, each holding one chunk: their histograms meet in a per-row
+//     workspace slot (device-scope relaxed atomics and a rendezvous per
+//     radix pass); each workgroup lists its own candidates; the last pass
+//     also carries each workgroup's counts, which give every workgroup the
+//     ranks of the chunks before its own, and each writes its part of the
+//     row's output;
 //   * if a candidate list would not fit (massive ties at the threshold), the
 //     radix select finishes over the range re-read from cache (slower, same
 //     result).
