@@ -1065,7 +1065,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     constexpr int LOADS = EPT / VEC;
     static_assert(EPT % VEC == 0, "EPT must be a multiple of the vector width");
 
-    extern __shared__ uint32_t s_dyn[];  // histogram, candidate list
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // histogram, candidate list
     __shared__ TopkShared<LOADS> S;
     const TopkLds L{s_dyn, S.wtot, S.base, S.red, S.out};
 
@@ -1315,7 +1315,7 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     using raw_t = typename K::raw_t;
     constexpr int LOADS = EPT / K::VEC;
     static_assert(EPT % K::VEC == 0, "EPT must be a multiple of the vector width");
-    extern __shared__ uint32_t s_dyn[];  // histogram, candidate list
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // histogram, candidate list
     __shared__ TopkShared<LOADS> S;
     const TopkLds L{s_dyn, S.wtot, S.base, S.red, S.out};
     const List ent = list_of<K>(s_dyn + list_base<K>());
@@ -1615,7 +1615,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
     using D = WaveDigits<K>;
     constexpr int VEC = K::VEC, EPW = K::EPW, LPL = EPL / VEC, SPAN = 64 * VEC;
     static_assert(EPL % VEC == 0, "EPL must be a multiple of the vector width");
-    extern __shared__ uint32_t s_dyn[];  // one histogram per wave
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // one histogram per wave
     // the wave index, uniform (in an SGPR): the row, its views and the
     // output descriptors are then scalar, not per-lane values
     const int lane = tid() & 63, wid = __builtin_amdgcn_readfirstlane(tid() >> 6);
