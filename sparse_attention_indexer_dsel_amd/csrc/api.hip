@@ -46,8 +46,8 @@ struct TopkPlan {
 
 // Candidate-list capacity: k plus room for the boundary bin of the first
 // digit (a quarter octave of values), at most 8192 entries and never more
-// than the row; a row whose candidates exceed it takes the slower
-// in-register path.
+// than the row; a row whose candidates exceed it takes the slower path that
+// re-reads the row for each later radix pass.
 int64_t candidate_cap(int64_t k, int64_t row_len) {
     int64_t cap = k + (k > 1536 ? k : 1536);
     if (cap > 8192) cap = 8192;
