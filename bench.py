@@ -353,8 +353,8 @@ def main(argv=None):
         print(json.dumps(traffic_from(*args.traffic_from)))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the selection step shards by rows with no exchange, "
-              "and multi-GPU runs are not part of this build (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU (run with --gpus 1): the selection step shards by "
+              "rows with no exchange, so N GPUs run N independent row slices", file=sys.stderr)
         return 2
 
     import torch
