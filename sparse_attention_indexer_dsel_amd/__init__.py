@@ -4,7 +4,7 @@ This module only marshals tensors into the C entry points of
 ``include/dsel.h`` (same names without the ``dsel_`` prefix); every step of
 the computation runs in the library's HIP kernels.  PyTorch provides device
 memory and the current stream.  Importing fails loudly when the library has
-not been built (``python -m sparse_attention_indexer_dsel_amd.build_lib``).
+not been built (``python sparse_attention_indexer_dsel_amd/build_lib.py``).
 
 Call shapes follow the DeepSelect tutorial ("Sheshisa Imisebenzi ye-PyTorch
 TopK nge-DeepSelect"): ``topk(x, k, sorted_index=..., indices_type=...,
@@ -44,7 +44,7 @@ class DselError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m sparse_attention_indexer_dsel_amd.build_lib`")
+                          "`python sparse_attention_indexer_dsel_amd/build_lib.py`")
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, i32, szp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)
     lib.dsel_stride_requirement.restype = i32

@@ -1,6 +1,6 @@
 """Build ``libdsel.so`` in-tree with hipcc for gfx950.
 
-Usage: ``python -m sparse_attention_indexer_dsel_amd.build_lib`` (or call
+Usage: ``python sparse_attention_indexer_dsel_amd/build_lib.py`` (or call
 ``build()``).  Each ``csrc/*.hip`` file is compiled to an object in
 ``_build/`` and linked into ``sparse_attention_indexer_dsel_amd/libdsel.so``.
 """

@@ -18,7 +18,12 @@ LIB = os.path.join(ROOT, "sparse_attention_indexer_dsel_amd", "libdsel.so")
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from sparse_attention_indexer_dsel_amd import build_lib
+        # by path: the package's __init__ needs the library this builds
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_dsel_build_lib", os.path.join(ROOT, "sparse_attention_indexer_dsel_amd", "build_lib.py"))
+        build_lib = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(build_lib)
         build_lib.build()
     return ctypes.CDLL(LIB)
 
