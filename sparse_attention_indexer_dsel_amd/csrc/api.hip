@@ -42,6 +42,7 @@ struct TopkPlan {
     int64_t grid = 0;  // workgroups per launch
     int64_t slot_words = 0;
     size_t ws_bytes = 0;
+    bool one = false;  // split bf16 rows try the one-exchange select
 };
 
 // Candidate-list capacity: k plus room for the boundary bin of the first
@@ -160,7 +161,18 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     }
     const int ept = pick_ept(chunk, kMaxSplitEpt);
     if (!ept) return DSEL_ERR_ARG;
-    const int64_t cap = chunk_cap(k, cols, chunk, G);
+    int64_t cap = chunk_cap(k, cols, chunk, G);
+    // One exchange (bf16, at most kOneMaxSplit workgroups per row): a
+    // workgroup lists every key from the floor of its own top-k bin, about k
+    // plus one bin, so its list needs the whole-row capacity.
+    // DSEL_SPLIT_ONE_EXCHANGE=0 turns it off (tests of the multi-pass path).
+    bool one = dtype == DSEL_BF16 && G <= kOneMaxSplit && ept <= kOneMaxEpt;
+    if (const char *env = std::getenv("DSEL_SPLIT_ONE_EXCHANGE"))
+        if (std::strtol(env, nullptr, 10) == 0) one = false;
+    if (one) {
+        const int64_t own = candidate_cap(k, chunk);
+        if (own > cap) cap = own;
+    }
     // every workgroup of a row must be resident at once: size launches by
     // the number of workgroups the GPU holds
     int per_cu = 0;
@@ -181,6 +193,7 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     pl->cap = cap;
     pl->rows_per_launch = rpl;
     pl->grid = rpl * G;
+    pl->one = one;
     pl->slot_words = slot_words(G, dtype);
     pl->ws_bytes = (size_t)(kHeaderWords + rpl * pl->slot_words) * sizeof(uint32_t);
     return DSEL_OK;
@@ -255,6 +268,7 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
     a.G = pl.G;
     a.idx64 = indices_type == DSEL_I64;
     a.ret_val = return_value ? 1 : 0;
+    a.one = pl.one ? 1 : 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     for (int64_t r0 = 0; r0 < rows; r0 += pl.rows_per_launch) {
         const int64_t nr = (rows - r0) < pl.rows_per_launch ? (rows - r0) : pl.rows_per_launch;

@@ -29,12 +29,23 @@ constexpr int kMaxSplit = 1024;
 // Bins of the last radix pass: 5 bits for bf16 keys, 10 for fp32.
 inline int last_pass_bins(int dtype) { return dtype == 0 ? 32 : 1024; }
 
+// One-exchange split rows (bf16 keys, at most kOneMaxSplit workgroups per
+// row): each workgroup publishes a header word and the suffix counts of its
+// keys over the kOneKeys keys (16 first-digit bins of 32 keys) from the
+// floor of its own top-k bin.
+constexpr int kOneKeys = 512;
+constexpr int kOneWords = 1 + kOneKeys;
+constexpr int kOneMaxSplit = 64;
+// ... and at most this many columns per thread (wider chunks would spill the
+// exchange's registers).
+constexpr int kOneMaxEpt = 64;
+
 // Per-row workspace slot (32-bit words): counters, one histogram per radix
-// pass, per-workgroup counts, and each workgroup's suffix counts over the
-// last pass's bins.
+// pass, per-workgroup counts, each workgroup's suffix counts over the last
+// pass's bins, and (bf16) each workgroup's one-exchange area.
 inline int64_t slot_words(int G, int dtype) {
     return kSlotHeadWords + (int64_t)kMaxPasses * kBins + 4 * (int64_t)G +
-           (int64_t)G * (last_pass_bins(dtype) + 1);
+           (int64_t)G * (last_pass_bins(dtype) + 1) + (dtype == 0 ? (int64_t)G * kOneWords : 0);
 }
 
 struct TopkArgs {
@@ -57,6 +68,7 @@ struct TopkArgs {
     int G;                   // workgroups per row
     int idx64;
     int ret_val;
+    int one;                 // split bf16 rows: try the one-exchange select first
 };
 
 // Top-k kernel kinds: one workgroup per row, G workgroups per row, one wave

@@ -815,6 +815,170 @@ __device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, 
     }
 }
 
+// A row's output slots as range-checked buffer views: a store at offset
+// kDrop (past every view's end) is dropped, so a store loop needs no branch.
+struct RowViews {
+    __amdgpu_buffer_rsrc_t idx, val;
+    int idx64, has_val;
+};
+constexpr uint32_t kDrop = 0x80000000u;
+
+template <class K>
+__device__ __forceinline__ RowViews row_views(const TopkArgs &a, int64_t row) {
+    RowViews v;
+    const int isz = a.idx64 ? 8 : 4;
+    v.idx = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<char *>(a.out_idx) + row * a.idx_stride * isz, (short)0, a.k * isz,
+        0x00020000);
+    v.val = __builtin_amdgcn_make_buffer_rsrc(
+        a.ret_val ? reinterpret_cast<char *>(a.out_val) +
+                        row * a.val_stride * (int64_t)sizeof(typename K::raw_t)
+                  : reinterpret_cast<char *>(a.out_idx),
+        (short)0, a.ret_val ? a.k * (int)sizeof(typename K::raw_t) : 0, 0x00020000);
+    v.idx64 = a.idx64;
+    v.has_val = a.ret_val;
+    return v;
+}
+
+// Slot `pos` (or nothing, when !take): the value bits.
+template <class K>
+__device__ __forceinline__ void view_store_value(const RowViews &v, bool take, uint32_t pos,
+                                                 uint32_t bits) {
+    if constexpr (sizeof(typename K::raw_t) == 2)
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, v.val, take ? pos * 2u : kDrop,
+                                              0u, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b32(bits, v.val, take ? pos * 4u : kDrop, 0u, 0);
+}
+
+// Slot `pos` (or nothing, when !take): the column, and the value bits.
+template <class K>
+__device__ __forceinline__ void view_store(const RowViews &v, bool take, uint32_t pos, uint32_t col,
+                                           uint32_t bits) {
+    if (v.idx64) {
+        const uint64_t c = col;
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, c), v.idx,
+            take ? pos * 8u : kDrop, 0u, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(col, v.idx, take ? pos * 4u : kDrop, 0u, 0);
+    }
+    if (v.has_val) view_store_value<K>(v, take, pos, bits);
+}
+
+// Write the selection from a column-ordered list when the boundary is an
+// exact key T: every entry with key > T, and the first `need` (in column
+// order, counting the eq0 before the list) with key == T.  Same ranks as
+// write_from_list.  The workgroup's selected entries fill one contiguous run
+// of output slots; when the run fits `stage` (kStageSlots slots: columns,
+// then 16-bit values), each thread puts its entries there by rank and the
+// run is copied out with consecutive stores (a list holds many more entries
+// than it selects, so stores straight from the list would scatter a few
+// lanes over many store instructions).
+constexpr uint32_t kStageSlots = 1024;
+
+template <class K>
+__device__ __forceinline__ void write_exact(const TopkArgs &a, int64_t row, List ent, uint32_t C,
+                                            uint32_t T, uint32_t need, uint32_t gt0, uint32_t eq0,
+                                            uint32_t col0, uint32_t *s_red, uint32_t *stage,
+                                            const typename K::raw_t *xr) {
+    static_assert(sizeof(typename K::raw_t) == 2, "staged values are 16-bit");
+    constexpr int U = 4;
+    const RowOut o = row_out<K>(a, row);
+    const RowViews v = row_views<K>(a, row);
+    const uint32_t E = (C + NT - 1) / NT;
+    const uint32_t i0 = (uint32_t)tid() * E;
+    const uint32_t i1 = min(C, i0 + E);
+    auto entry = [&](uint32_t i) {
+        const uint2 e = list_entry<K>(ent, i < i1 ? i : 0u);
+        return i < i1 ? e : make_uint2(0u, 0u);
+    };
+    uint32_t g = 0, q = 0;
+    for (uint32_t i = i0; i < i0 + E; i += U) {
+        uint32_t key[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) key[u] = entry(i + u).x;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            g += key[u] > T ? 1u : 0u;
+            q += key[u] == T ? 1u : 0u;
+        }
+    }
+    const uint32_t mine = g | (q << 16);
+    const Scan sc = block_scan(mine, s_red);
+    const uint32_t ex = sc.incl - mine;
+    const uint32_t gb0 = gt0 + (ex & 0xFFFFu), qb0 = eq0 + (ex >> 16);
+    // this workgroup's run of slots [p0, p1)
+    const uint32_t p0 = gt0 + min(eq0, need);
+    const uint32_t p1 = gt0 + (sc.total & 0xFFFFu) + min(eq0 + (sc.total >> 16), need);
+    uint32_t gb = gb0, qb = qb0;
+    if (p1 - p0 <= kStageSlots) {
+        // columns and keys by rank; no global access in this loop (a load
+        // here would make each iteration wait for every outstanding one)
+        uint32_t *s_col = stage;
+        uint16_t *s_key = reinterpret_cast<uint16_t *>(stage + kStageSlots);
+        for (uint32_t i = i0; i < i0 + E; i += U) {
+            uint2 e[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) e[u] = entry(i + u);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool gt = e[u].x > T, eq = e[u].x == T;
+                const uint32_t pos = gt ? gb + min(qb, need) : gb + qb;
+                if (gt || (eq && qb < need)) {
+                    s_col[pos - p0] = e[u].y + col0;
+                    s_key[pos - p0] = (uint16_t)e[u].x;
+                }
+                gb += gt ? 1u : 0u;
+                qb += eq ? 1u : 0u;
+            }
+        }
+        __syncthreads();
+        uint32_t amb = 0;
+        for (uint32_t j = (uint32_t)tid(); j < p1 - p0; j += NT) {
+            const uint32_t key = s_key[j];
+            store_index(o, p0 + j, s_col[j]);
+            if (o.val) store_value<K>(o, p0 + j, K::value_bits(key));
+            amb |= K::ambiguous(key) ? 1u : 0u;
+        }
+        // +-0 (and NaN) keys: the value bits come from the row (the same
+        // thread rewrites the same slot, so this store lands last)
+        if (o.val && __syncthreads_or((int)amb))
+            for (uint32_t j = (uint32_t)tid(); j < p1 - p0; j += NT)
+                if (K::ambiguous(s_key[j])) store_value<K>(o, p0 + j, (uint32_t)xr[s_col[j]]);
+        return;
+    }
+    uint32_t amb = 0;
+    for (uint32_t i = i0; i < i0 + E; i += U) {
+        uint2 e[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) e[u] = entry(i + u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool gt = e[u].x > T, eq = e[u].x == T;
+            const bool take = gt || (eq && qb < need);
+            const uint32_t pos = gt ? gb + min(qb, need) : gb + qb;
+            view_store<K>(v, take, pos, e[u].y + col0, K::value_bits(e[u].x));
+            amb |= (take && K::ambiguous(e[u].x)) ? 1u : 0u;
+            gb += gt ? 1u : 0u;
+            qb += eq ? 1u : 0u;
+        }
+    }
+    if (!(o.val && __syncthreads_or((int)amb))) return;
+    // +-0 (and NaN) keys: the value bits come from the row
+    gb = gb0;
+    qb = qb0;
+    for (uint32_t i = i0; i < i1; ++i) {
+        const uint2 e = entry(i);
+        const bool gt = e.x > T, eq = e.x == T;
+        const uint32_t pos = gt ? gb + min(qb, need) : gb + qb;
+        if ((gt || (eq && qb < need)) && K::ambiguous(e.x))
+            store_value<K>(o, pos, (uint32_t)xr[e.y + col0]);
+        gb += gt ? 1u : 0u;
+        qb += eq ? 1u : 0u;
+    }
+}
+
 // ---- slow path: the candidate list would not fit (massive ties at the
 // threshold).  The radix select finishes over the range's keys re-read from
 // cache one load at a time, so the rare path adds no VGPRs to the common one.
@@ -1036,6 +1200,11 @@ __host__ __device__ constexpr uint32_t list_base() {
     return K::NPASS == 2 ? 64u : (uint32_t)(kBins + 64);
 }
 
+// Split rows keep the list past the histogram for either key type: the
+// one-exchange select builds its list before the row's boundary is known
+// and then needs the histogram's space for the exchanged counts.
+__host__ __device__ constexpr uint32_t split_list_base() { return (uint32_t)(kBins + 64); }
+
 // Static LDS of the top-k kernels (LOADS 16-byte loads per thread).
 template <int LOADS>
 struct TopkShared {
@@ -1053,6 +1222,222 @@ struct TopkLds {
     uint32_t *red;
     uint32_t *out;
 };
+
+// ---------------------------------------------------------------------------
+// One-exchange select of a split bf16 row (G <= kOneMaxSplit workgroups).
+//
+// Let b_c be the first-digit bin of chunk c's own k-th largest key.  The
+// row holds at least k keys at or above that bin (chunk c's own top k), so
+// the row's k-th largest key T lies in a bin >= b_c, for every chunk c with
+// at least k keys.  Each workgroup therefore lists its keys from the floor
+// of b_c (its own top k plus that bin), histograms them over the 512 keys
+// from the floor, and publishes the suffix counts: word j = its keys >=
+// floor + j.  After one rendezvous every workgroup reads every header and
+// the counts at bin boundaries, finds T's bin B (the largest bin whose keys
+// at or above it number >= k), reads every chunk's 33 counts around B, and
+// gets T, the count `need` still to take at T, and the keys above / equal to
+// T in the chunks before its own: all it needs to write its part.
+//
+// The exchange holds when every chunk's list fits, every chunk's keys from
+// its floor span at most 512 keys, some chunk has >= k keys, and no shorter
+// chunk's floor lies above the full chunks' highest floor.  Otherwise (ties,
+// NaN, spikes, short chunks) the caller runs the multi-pass select; every
+// workgroup reads the same headers, so the choice is uniform over the row.
+//
+// LDS: hist[0, 512) the fine histogram; after the rendezvous hist[512, 576)
+// the headers and hist[576, 1600) the counts at bin boundaries, then
+// hist[0, 33 G) the counts around B.  The list lies past the histogram.
+// ---------------------------------------------------------------------------
+struct OneResult {
+    bool ok;
+    bool nan;           // some chunk of the row holds a NaN
+    Bound b;
+    uint32_t gt0, eq0;  // keys above / at T in the chunks before this one
+    uint32_t run;       // this workgroup's list length
+};
+
+// Sum over the lanes of one wave (every lane gets it).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+    return x;
+}
+
+template <class K, int LOADS>
+__device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
+                                  uint32_t (&kw)[LOADS * 4], bool blk_nan, const TopkLds &L,
+                                  List ent, uint32_t cap, uint32_t *area, uint32_t *slot,
+                                  uint32_t *err) {
+    static_assert(K::PACK && K::SH1 == 5, "one exchange: 16-bit keys, 32 keys per first-digit bin");
+    static_assert(kOneKeys == 2 * NT, "two fine bins per thread");
+    constexpr int NBIN = kOneKeys / 32;  // first-digit bins a chunk's region may span
+    const int t = tid();
+    const int lane = t & 63;
+    const uint32_t k = (uint32_t)a.k;
+    OneResult r{};
+
+    // ---- this chunk's floor bin b_c and its list of keys from the floor ----
+    uint32_t bc = 0, full = 0, ok = 1, run = 0;
+    if (len > 0) {
+        const uint32_t need = len >= (int)k ? k : (uint32_t)len;
+        bc = find_digit(L.hist, kBins, need, L.red, L.out).v;
+        full = len >= (int)k ? 1u : 0u;
+        run = compact_candidates<K, LOADS, true>(kw, len, bc << K::SH1, L.wtot, L.base, ent, cap);
+        ok = run <= cap ? 1u : 0u;  // uniform
+    }
+    // ---- fine histogram of the list over the 512 keys from the floor -------
+    uint32_t *fh = L.hist;  // the first-digit histogram is dead
+    fh[t] = 0;
+    fh[t + NT] = 0;
+    __syncthreads();
+    const uint32_t lo = bc << K::SH1;
+    uint32_t over = 0;
+    if (ok)
+        for (uint32_t i = (uint32_t)t; i < run; i += NT) {
+            const uint32_t off = list_key<K>(ent, i) - lo;
+            if (off < (uint32_t)kOneKeys)
+                atomicAdd(&fh[off], 1u);
+            else
+                over = 1;
+        }
+    if (__syncthreads_or((int)over)) ok = 0;
+    // (Polling these words instead of a rendezvous counter was measured
+    // slower: every workgroup's loads of the same few lines queue at one
+    // memory channel.)
+    uint32_t *mine = area + (int64_t)c * kOneWords;
+    if (ok) {
+        // suffix counts from the top: thread t owns keys top-1, top-2
+        const int top = kOneKeys - 2 * t;
+        const uint32_t h1 = fh[top - 1], h0 = fh[top - 2];
+        const uint32_t incl = block_scan(h1 + h0, L.red).incl;
+        st_agent(mine + 1 + (top - 1), incl - h0);
+        st_agent(mine + 1 + (top - 2), incl);
+    }
+    if (t == 0) st_agent(mine, bc | (full << 16) | (ok << 17) | (blk_nan ? 1u << 18 : 0u));
+    row_rendezvous(slot, (uint32_t)G, err);
+
+    // ---- every chunk's header and counts at its bin boundaries -------------
+    uint32_t *s_hdr = L.hist + kOneKeys;       // [64]
+    uint32_t *s_cs = L.hist + kOneKeys + 64;   // [64][NBIN]
+    {
+        constexpr int PER = NBIN + 1;
+        constexpr int R1 = (kOneMaxSplit * PER + NT - 1) / NT;
+        const int total = G * PER;
+        uint32_t v[R1];
+#pragma unroll
+        for (int q = 0; q < R1; ++q) {
+            const int i = q * NT + t;
+            const int ii = i < total ? i : 0;
+            const int cc = ii / PER, j = ii % PER;
+            v[q] = ld_agent(area + (int64_t)cc * kOneWords + (j == NBIN ? 0 : 1 + 32 * j));
+        }
+#pragma unroll
+        for (int q = 0; q < R1; ++q) {
+            const int i = q * NT + t;
+            if (i < total) {
+                const int cc = i / PER, j = i % PER;
+                if (j == NBIN)
+                    s_hdr[cc] = v[q];
+                else
+                    s_cs[cc * NBIN + j] = v[q];
+            }
+        }
+    }
+    __syncthreads();
+    // every wave finds B on its own (no barrier to share it): lane = chunk
+    const uint32_t h = lane < G ? s_hdr[lane] : (1u << 17);
+    const uint32_t hb = h & 0x7FFu, hfull = (h >> 16) & 1u, hok = (h >> 17) & 1u;
+    r.nan = __ballot(((h >> 18) & 1u) != 0u) != 0ull;
+    const uint32_t maxb = wave_max_u32(hfull ? hb : 0u);
+    const bool any_full = __ballot(hfull != 0u) != 0ull;
+    const bool fits = __ballot(!hok || (!hfull && hb > maxb)) == 0ull;
+    if (!(any_full && fits)) {
+        r.ok = false;
+        __syncthreads();  // the caller reuses the histogram's space
+        return r;
+    }
+    // keys at or above bin maxb + j, j < 16: lane = j + 16 * (chunk group)
+    uint32_t part = 0;
+    {
+        // chunks lane>>4, +4, ...: four header reads, then four count reads,
+        // in flight together
+        constexpr int M = 4;
+        const int j = lane & (NBIN - 1);
+#pragma unroll 1
+        for (int c0 = lane >> 4; c0 < G; c0 += 4 * M) {
+            uint32_t hbv[M], cv[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const int cc = c0 + 4 * m;
+                hbv[m] = s_hdr[cc < G ? cc : 0] & 0x7FFu;
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const int cc = c0 + 4 * m;
+                const uint32_t idx = maxb + (uint32_t)j - hbv[m];
+                cv[m] = s_cs[(cc < G ? cc : 0) * NBIN + (idx < (uint32_t)NBIN ? idx : 0u)];
+                cv[m] = (cc < G && idx < (uint32_t)NBIN) ? cv[m] : 0u;
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) part += cv[m];
+        }
+        part += (uint32_t)__shfl_xor((int)part, 16);
+        part += (uint32_t)__shfl_xor((int)part, 32);
+    }
+    const uint64_t geb = __ballot(lane < NBIN && part >= k);
+    const uint32_t B = maxb + (uint32_t)__popcll(geb) - 1u;
+    // ---- every chunk's counts at the 33 keys from B's floor ----------------
+    {
+        constexpr int PER = 33;
+        constexpr int R2 = (kOneMaxSplit * PER + NT - 1) / NT;
+        const int total = G * PER;
+        // word index of each of this thread's counts (past the 512 keys: 0)
+        uint32_t idx[R2];
+#pragma unroll
+        for (int q = 0; q < R2; ++q) {
+            const int i = q * NT + t;
+            const int ii = i < total ? i : 0;
+            idx[q] = 32u * (B - (s_hdr[ii / PER] & 0x7FFu)) + (uint32_t)(ii % PER);
+        }
+        uint32_t v[R2];
+#pragma unroll
+        for (int q = 0; q < R2; ++q) {
+            const int i = q * NT + t;
+            const int ii = i < total ? i : 0;
+            v[q] = ld_agent(area + (int64_t)(ii / PER) * kOneWords + 1 +
+                            (idx[q] < (uint32_t)kOneKeys ? idx[q] : 0u));
+        }
+        __syncthreads();  // every wave is done with the headers and boundary counts
+#pragma unroll
+        for (int q = 0; q < R2; ++q) {
+            const int i = q * NT + t;
+            if (i < total) L.hist[i] = idx[q] < (uint32_t)kOneKeys ? v[q] : 0u;
+        }
+    }
+    __syncthreads();
+    // keys >= B's floor + j over the row (lanes 0..32), then T = floor + j*
+    uint32_t gf = 0;
+    if (lane <= 32) {
+#pragma unroll 8
+        for (int cc = 0; cc < G; ++cc) gf += L.hist[cc * 33 + lane];
+    }
+    const uint32_t js = (uint32_t)__popcll(__ballot(lane <= 32 && gf >= k)) - 1u;  // <= 31
+    const uint32_t above = (uint32_t)__shfl((int)gf, (int)js + 1);
+    // keys above / at T in the chunks before this one: lane = chunk
+    const uint32_t s1 = lane < c ? L.hist[lane * 33 + js + 1] : 0u;
+    const uint32_t s0 = lane < c ? L.hist[lane * 33 + js] : 0u;
+    r.gt0 = wave_sum(s1);
+    r.eq0 = wave_sum(s0 - s1);
+    r.b = Bound{(B << K::SH1) | js, 0, k - above};
+    r.run = run;
+    r.ok = true;
+    __syncthreads();  // the exchanged counts are read; the caller may reuse the space
+    return r;
+}
 
 // ---------------------------------------------------------------------------
 // Split rows: G workgroups per row, workgroup c owning columns
@@ -1084,13 +1469,14 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     }
 
     const uint32_t cap = (uint32_t)a.cap;
-    const List ent = list_of<K>(s_dyn + list_base<K>());
+    const List ent = list_of<K>(s_dyn + split_list_base());
     uint32_t *slot = a.ws + kHeaderWords + lrow * a.slot_words;
     uint32_t *err = a.ws;
     uint32_t *ghist = slot + kSlotHeadWords;
     uint32_t *gcnt = ghist + kMaxPasses * kBins;
     constexpr int LASTB = 1 << K::digit_last();  // bins of the last pass
     uint32_t *pub = gcnt + 4 * G;                // G x (LASTB + 1) suffix counts
+    uint32_t *one_area = pub + G * (LASTB + 1);  // bf16: G x kOneWords
 
     // ---- this workgroup's columns into VGPRs; first-digit histogram --------
     const int64_t lo = (int64_t)c * a.chunk;
@@ -1106,15 +1492,66 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
         for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
         nan = keys_of_loads<K, LOADS>(v, len, kw);
     }
-    if (__syncthreads_or((int)nan) && t == 0)
+    const bool blk_nan = __syncthreads_or((int)nan) != 0;
+    constexpr bool ONE = K::PACK && EPT <= kOneMaxEpt;
+    // the row's NaN bit, drained by the multi-pass select's first rendezvous
+    // (in the one exchange each workgroup's bit travels in its header; if it
+    // falls back to the multi-pass select, the bit is set then)
+    if ((!ONE || !a.one) && blk_nan && t == 0)
         __hip_atomic_fetch_or(slot + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     first_digit_histogram<K, LOADS>(kw, len, L.hist);
     __syncthreads();
+    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
+
+    // ---- one exchange (bf16): the whole boundary from one rendezvous -------
+    uint32_t nren = 0;
+    if constexpr (ONE) {
+        if (a.one) {
+            const OneResult r = one_exchange<K, LOADS>(a, c, G, len, kw, blk_nan, L, ent, cap,
+                                                       one_area, slot, err);
+            nren = 1;
+            if (r.ok) {
+                // every read of the row's shared words is done: depart now, so
+                // the returning atomic overlaps the write.  (The address is
+                // hidden from uniformity analysis: a uniform atomic is
+                // aggregated over the wave and its result waited for at once,
+                // which would put a round trip before the write.)
+                uint32_t dep = 0;
+                if (t == 0) dep = add_agent(slot + 1 + opaque(0u), 1u);
+                // the histogram's space (free again) stages the output run
+                write_exact<K>(a, row, ent, r.run, r.b.P, r.b.need, r.gt0, r.eq0, (uint32_t)lo,
+                               L.red, L.hist, xr);
+                if (t == 0) {
+                    if (c == 0 && a.nan_flag) a.nan_flag[row] = r.nan ? 1u : 0u;
+                    L.out[3] = dep == (uint32_t)G - 1u ? 1u : 0u;
+                }
+                __syncthreads();
+                if (L.out[3]) {
+                    // last out: every workgroup has read what it needs, so the
+                    // exchanged words and the counters go back to zero
+                    for (int i = t; i < G * kOneWords; i += NT) st_agent(one_area + i, 0u);
+                    if (t == 0) {
+                        st_agent(slot + 0, 0u);
+                        st_agent(slot + 1, 0u);
+                    }
+                }
+                return;
+            }
+            // the exchange does not hold for this row: set the NaN bit, rebuild
+            // the first-digit histogram (its space was reused) and run the
+            // radix passes
+            if (blk_nan && t == 0)
+                __hip_atomic_fetch_or(slot + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
+            __syncthreads();
+            first_digit_histogram<K, LOADS>(kw, len, L.hist);
+            __syncthreads();
+        }
+    }
 
     // ---- merge the histograms of the row's workgroups ----------------------
     merge_histogram(L.hist, ghist, kBins);
-    uint32_t nren = 1;
-    row_rendezvous(slot, (uint32_t)G, err);
+    row_rendezvous(slot, (++nren) * (uint32_t)G, err);
     fetch_histogram(ghist, L.hist, kBins);
     __syncthreads();
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
@@ -1129,7 +1566,6 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     // suffix counts, so the counts of the chunks before it come with that
     // pass's rendezvous.
     Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
-    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
     // dense: at least a quarter of the row are candidates (uniform over it)
     const bool regs = LOADS <= 2 && 4 * (int64_t)(d1.above + d1.cnt) >= n;
     uint32_t run = 0;
@@ -1236,6 +1672,8 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
             for (int i = t; i < G * (LASTB + 1); i += NT) st_agent(pub + i, 0u);
         else
             for (int i = t; i < 2 * G; i += NT) st_agent(gcnt + i, 0u);
+        if (K::PACK && EPT <= kOneMaxEpt && a.one)  // the one-exchange attempt's words
+            for (int i = t; i < G * kOneWords; i += NT) st_agent(one_area + i, 0u);
         if (t == 0) {
             st_agent(slot + 0, 0u);
             st_agent(slot + 1, 0u);
@@ -1410,55 +1848,6 @@ __device__ __forceinline__ Digit wave_find_digit(const uint32_t *hist, int nb, u
 // A row's outputs as range-checked buffer views: a store at an offset past
 // the row's k slots is dropped by the hardware, so a lane that takes no
 // element stores to kDrop and the write needs no branch.
-struct RowViews {
-    __amdgpu_buffer_rsrc_t idx, val;
-    int idx64, has_val;
-};
-constexpr uint32_t kDrop = 0x80000000u;
-
-template <class K>
-__device__ __forceinline__ RowViews row_views(const TopkArgs &a, int64_t row) {
-    RowViews v;
-    const int isz = a.idx64 ? 8 : 4;
-    v.idx = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<char *>(a.out_idx) + row * a.idx_stride * isz, (short)0, a.k * isz,
-        0x00020000);
-    v.val = __builtin_amdgcn_make_buffer_rsrc(
-        a.ret_val ? reinterpret_cast<char *>(a.out_val) +
-                        row * a.val_stride * (int64_t)sizeof(typename K::raw_t)
-                  : reinterpret_cast<char *>(a.out_idx),
-        (short)0, a.ret_val ? a.k * (int)sizeof(typename K::raw_t) : 0, 0x00020000);
-    v.idx64 = a.idx64;
-    v.has_val = a.ret_val;
-    return v;
-}
-
-// Slot `pos` (or nothing, when !take): the value bits.
-template <class K>
-__device__ __forceinline__ void view_store_value(const RowViews &v, bool take, uint32_t pos,
-                                                 uint32_t bits) {
-    if constexpr (sizeof(typename K::raw_t) == 2)
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, v.val, take ? pos * 2u : kDrop,
-                                              0u, 0);
-    else
-        __builtin_amdgcn_raw_buffer_store_b32(bits, v.val, take ? pos * 4u : kDrop, 0u, 0);
-}
-
-// Slot `pos` (or nothing, when !take): the column, and the value bits.
-template <class K>
-__device__ __forceinline__ void view_store(const RowViews &v, bool take, uint32_t pos, uint32_t col,
-                                           uint32_t bits) {
-    if (v.idx64) {
-        const uint64_t c = col;
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, c), v.idx,
-            take ? pos * 8u : kDrop, 0u, 0);
-    } else {
-        __builtin_amdgcn_raw_buffer_store_b32(col, v.idx, take ? pos * 4u : kDrop, 0u, 0);
-    }
-    if (v.has_val) view_store_value<K>(v, take, pos, bits);
-}
-
 // Write one wave's row from its keys in VGPRs (coalesced layout, load j of
 // lane l at columns (j*64 + l)*VEC...).  First pass (fix = false): indices,
 // and values rebuilt from the keys; amb reports whether a +-0 / NaN key was
@@ -1756,7 +2145,9 @@ size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind) {
     if (kind == kTopkWave)
         return (size_t)NWAVE * (dtype == 0 ? wave_lds_words<Bf16Key>() : wave_lds_words<F32Key>()) * 4;
     const uint64_t hist = (uint64_t)(kBins + 64);
-    const uint64_t base = dtype == 0 ? list_base<Bf16Key>() : list_base<F32Key>();
+    const uint64_t base = kind == kTopkSplit ? split_list_base()
+                          : dtype == 0      ? list_base<Bf16Key>()
+                                            : list_base<F32Key>();
     const uint64_t words = base + (dtype == 0 ? 1u : 2u) * (uint64_t)(cap + 64);
     return (size_t)(words > hist ? words : hist) * 4;
 }

@@ -41,6 +41,27 @@ class blocks_per_row:
             os.environ["DSEL_BLOCKS_PER_ROW"] = self.old
 
 
+class one_exchange:
+    """Turn the one-exchange select of split bf16 rows on or off
+    (DSEL_SPLIT_ONE_EXCHANGE) inside a block; None keeps the default (on)."""
+
+    def __init__(self, on):
+        self.on = on
+
+    def __enter__(self):
+        self.old = os.environ.get("DSEL_SPLIT_ONE_EXCHANGE")
+        if self.on is None:
+            os.environ.pop("DSEL_SPLIT_ONE_EXCHANGE", None)
+        else:
+            os.environ["DSEL_SPLIT_ONE_EXCHANGE"] = "1" if self.on else "0"
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("DSEL_SPLIT_ONE_EXCHANGE", None)
+        else:
+            os.environ["DSEL_SPLIT_ONE_EXCHANGE"] = self.old
+
+
 def run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value, output_idx=None):
     xd = to_device(x)
     re = row_end.cuda() if row_end is not None else None
@@ -51,10 +72,10 @@ def run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value, outpu
 
 
 def check_case(dsel, orc, name, x, k, row_end=None, sorted_index=False,
-               indices_type=torch.int32, return_value=True, G=None):
-    say(f"[topk] {name} shape={tuple(x.shape)} stride={x.stride()} k={k} G={G} "
+               indices_type=torch.int32, return_value=True, G=None, one=None):
+    say(f"[topk] {name} shape={tuple(x.shape)} stride={x.stride()} k={k} G={G} one={one} "
         f"sorted={sorted_index} idx={indices_type} val={return_value}")
-    with blocks_per_row(G):
+    with blocks_per_row(G), one_exchange(one):
         got = run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value)
     want = oracle_topk(orc, x, k, row_end, sorted_index, indices_type, return_value)
     n = valid_lengths(x.shape[0], x.shape[1], row_end)
@@ -89,13 +110,40 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("G", [None, 3, 7])
+@pytest.mark.parametrize("G,one", [(None, None), (3, None), (7, None), (3, False), (7, False)])
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: c[0])
-def test_small_cases(dsel, orc, case, G):
+def test_small_cases(dsel, orc, case, G, one):
     name, rows, cols, dt, dist, k = case
     x = W.random_rows(zlib.crc32(name.encode()) & 0xFFFF, rows, cols, dt, dist)
     for ret in (True, False):
-        check_case(dsel, orc, f"{name}/G{G}/val{int(ret)}", x, k, None, False, torch.int32, ret, G)
+        check_case(dsel, orc, f"{name}/G{G}/val{int(ret)}", x, k, None, False, torch.int32, ret,
+                   G, one)
+
+
+@pytest.mark.parametrize("one", [True, False])
+@pytest.mark.parametrize("G", [7, 25, 64])
+def test_split_one_exchange(dsel, orc, G, one):
+    """bf16 rows split over G workgroups, through the one-exchange select
+    (on) and the multi-pass select (off): full chunks, a short last chunk,
+    chunks wholly past the row end, rows too short for any chunk to hold k
+    keys, a NaN row and a row with a few huge values (both must leave the
+    one exchange for the multi-pass select), k from 1 to 4096."""
+    rows, cols = 9, 100000
+    x = W.random_rows(131 + G, rows, cols, W.BF16, "normal")
+    x[6, 4321] = float("nan")
+    x[7, [5, 50000, 99990]] = torch.tensor([300.0, -250.0, 1e30]).to(x.dtype)
+    ends = [100000, 99999, 61234, 40001, 20000, 8193, 100000, 77777, 4097]
+    re = torch.tensor(ends, dtype=torch.int32)
+    for k, sorted_index, itype, ret in ((1, False, torch.int32, True),
+                                        (100, True, torch.int64, True),
+                                        (1024, True, torch.int32, True),
+                                        (1024, False, torch.int32, False),
+                                        (4096, False, torch.int32, True)):
+        check_case(dsel, orc, f"one/G{G}/on{int(one)}/k{k}", x, k, re, sorted_index, itype, ret,
+                   G, one)
+    torch.cuda.synchronize()
+    for ws in dsel._WORKSPACES.values():
+        assert int(ws.count_nonzero()) == 0, "workspace must be zero after a call (and no error bit)"
 
 
 @pytest.mark.parametrize("G", [None, 4])
@@ -136,8 +184,9 @@ def test_split_crowded_chunks(dsel, orc, dt, dist):
     many keys at the boundary."""
     x = W.random_rows(81 + len(dist), 5, 40000, dt, dist)
     for k, G in ((2000, 8), (4096, 5), (37, 16)):
-        check_case(dsel, orc, f"crowded/{dist}/{dt}/k{k}/G{G}", x, k, None, True,
-                   torch.int64, True, G)
+        for one in (None, False):
+            check_case(dsel, orc, f"crowded/{dist}/{dt}/k{k}/G{G}", x, k, None, True,
+                       torch.int64, True, G, one)
 
 
 @pytest.mark.parametrize("G", [40, 80])
@@ -148,8 +197,9 @@ def test_split_many_workgroups(dsel, orc, dt, G):
     x = W.random_rows(91 + G, 3, 100000, dt, "normal")
     re = torch.tensor([100000, 77777, 3001], dtype=torch.int32)
     for k, sorted_index in ((1000, True), (64, False)):
-        check_case(dsel, orc, f"many/{dt}/G{G}/k{k}", x, k, re, sorted_index, torch.int32,
-                   True, G)
+        for one in (None, False):
+            check_case(dsel, orc, f"many/{dt}/G{G}/k{k}", x, k, re, sorted_index, torch.int32,
+                       True, G, one)
 
 
 @pytest.mark.parametrize("dist", ["normal", "ties", "equal", "ascending", "descending",
@@ -253,6 +303,9 @@ def test_workspace_reuse(dsel, orc):
              (W.random_rows(73, 5, 30000, W.BF16, "ties"), 1500, 9),
              (W.random_rows(74, 8, 50000, W.F32, "equal"), 300, 4),
              (W.random_rows(71, 8, 50000, W.F32, "normal"), 100, 6)]
+    cases += [(W.random_rows(75, 4, 60000, W.BF16, "normal"), 1024, 8),
+              (W.random_rows(76, 4, 60000, W.BF16, "normal"), 64, 20),
+              (W.random_rows(73, 5, 30000, W.BF16, "ties"), 1500, 9)]
     for i, (x, k, G) in enumerate(cases):
         check_case(dsel, orc, f"reuse{i}", x, k, None, False, torch.int32, True, G)
     torch.cuda.synchronize()
@@ -275,3 +328,10 @@ def test_workload_split_path_cfg1(dsel, orc):
     case = W.make_config(1)
     for G in (1, 4):
         check_case(dsel, orc, f"cfg1/G{G}", case.x, case.k, None, False, torch.int32, True, G)
+
+
+def test_workload_cfg2_multipass(dsel, orc):
+    """The 4 x 204800 workload through the multi-pass split select too."""
+    case = W.make_config(2)
+    check_case(dsel, orc, "cfg2/multipass", case.x, case.k, case.row_end, case.sorted_index,
+               case.indices_type, case.return_value, None, False)
