@@ -41,6 +41,7 @@ struct TopkPlan {
     int64_t rows_per_launch = 0;
     int64_t grid = 0;  // workgroups per launch
     int64_t slot_words = 0;
+    int64_t slot0 = 0;
     size_t ws_bytes = 0;
     bool one = false;  // split bf16 rows try the one-exchange select
 };
@@ -193,9 +194,12 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
     pl->cap = cap;
     pl->rows_per_launch = rpl;
     pl->grid = rpl * G;
-    pl->one = one;
+    // the exchange region is part of every split layout (so no slot of any
+    // layout ever overlaps it) and holds one area per resident workgroup
+    pl->one = one && rpl * G <= (int64_t)kOneWgPerCu * cus;
     pl->slot_words = slot_words(G, dtype);
-    pl->ws_bytes = (size_t)(kHeaderWords + rpl * pl->slot_words) * sizeof(uint32_t);
+    pl->slot0 = kHeaderWords + one_region_words(cus);
+    pl->ws_bytes = (size_t)(pl->slot0 + rpl * pl->slot_words) * sizeof(uint32_t);
     return DSEL_OK;
 }
 
@@ -263,6 +267,7 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
     a.ws = reinterpret_cast<uint32_t *>(workspace);
     a.chunk = pl.chunk;
     a.slot_words = pl.slot_words;
+    a.slot0 = pl.slot0;
     a.cap = pl.cap;
     a.k = (int)k;
     a.G = pl.G;

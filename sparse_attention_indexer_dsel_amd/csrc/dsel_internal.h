@@ -32,20 +32,27 @@ inline int last_pass_bins(int dtype) { return dtype == 0 ? 32 : 1024; }
 // One-exchange split rows (bf16 keys, at most kOneMaxSplit workgroups per
 // row): each workgroup publishes a header word and the suffix counts of its
 // keys over the kOneKeys keys (16 first-digit bins of 32 keys) from the
-// floor of its own top-k bin.
+// floor of its own top-k bin, in its own area of an exchange region that
+// follows the workspace header.  The region has one area per workgroup the
+// GPU can hold (kOneWgPerCu per compute unit), lies at the same place for
+// every call and every slot layout, and is never cleared: a reader uses
+// only words the header says were written by this call.  The row slots
+// (counters, histograms) follow it.
 constexpr int kOneKeys = 512;
 constexpr int kOneWords = 1 + kOneKeys;
 constexpr int kOneMaxSplit = 64;
+constexpr int kOneWgPerCu = 8;
+inline int64_t one_region_words(int cus) { return (int64_t)kOneWgPerCu * cus * kOneWords; }
 // ... and at most this many columns per thread (wider chunks would spill the
 // exchange's registers).
 constexpr int kOneMaxEpt = 64;
 
 // Per-row workspace slot (32-bit words): counters, one histogram per radix
-// pass, per-workgroup counts, each workgroup's suffix counts over the last
-// pass's bins, and (bf16) each workgroup's one-exchange area.
+// pass, per-workgroup counts, and each workgroup's suffix counts over the
+// last pass's bins.
 inline int64_t slot_words(int G, int dtype) {
     return kSlotHeadWords + (int64_t)kMaxPasses * kBins + 4 * (int64_t)G +
-           (int64_t)G * (last_pass_bins(dtype) + 1) + (dtype == 0 ? (int64_t)G * kOneWords : 0);
+           (int64_t)G * (last_pass_bins(dtype) + 1);
 }
 
 struct TopkArgs {
@@ -63,6 +70,7 @@ struct TopkArgs {
     int64_t row0;            // first row of this launch
     int64_t chunk;           // columns per workgroup (split rows only)
     int64_t slot_words;      // 32-bit words per row slot (split rows only)
+    int64_t slot0;           // word offset of the first row slot (split rows only)
     int64_t cap;             // capacity of a workgroup's candidate list (entries)
     int k;
     int G;                   // workgroups per row

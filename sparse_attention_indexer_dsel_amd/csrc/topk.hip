@@ -1308,16 +1308,28 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
     // (Polling these words instead of a rendezvous counter was measured
     // slower: every workgroup's loads of the same few lines queue at one
     // memory channel.)
+    // The header records nz, the number of counts from the floor that are
+    // nonzero; only those are stored, and a reader takes every count at or
+    // past nz as zero (the area is not cleared between calls).
     uint32_t *mine = area + (int64_t)c * kOneWords;
+    uint32_t nz = 0;
     if (ok) {
         // suffix counts from the top: thread t owns keys top-1, top-2
         const int top = kOneKeys - 2 * t;
         const uint32_t h1 = fh[top - 1], h0 = fh[top - 2];
         const uint32_t incl = block_scan(h1 + h0, L.red).incl;
-        st_agent(mine + 1 + (top - 1), incl - h0);
-        st_agent(mine + 1 + (top - 2), incl);
+        if (incl - h0) st_agent(mine + 1 + (top - 1), incl - h0);
+        if (incl) st_agent(mine + 1 + (top - 2), incl);
+        // words [0, nz) hold nonzero counts: nz = highest nonzero key + 1
+        const uint32_t last = h1 ? (uint32_t)top : (h0 ? (uint32_t)top - 1u : 0u);
+        const uint32_t wm = wave_max_u32(last);
+        if (lane == 0) L.red[t >> 6] = wm;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) nz = max(nz, L.red[w]);
     }
-    if (t == 0) st_agent(mine, bc | (full << 16) | (ok << 17) | (blk_nan ? 1u << 18 : 0u));
+    if (t == 0)
+        st_agent(mine, bc | (full << 16) | (ok << 17) | (blk_nan ? 1u << 18 : 0u) | (nz << 20));
     row_rendezvous(slot, (uint32_t)G, err);
 
     // ---- every chunk's header and counts at its bin boundaries -------------
@@ -1373,14 +1385,15 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int cc = c0 + 4 * m;
-                hbv[m] = s_hdr[cc < G ? cc : 0] & 0x7FFu;
+                hbv[m] = s_hdr[cc < G ? cc : 0];
             }
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int cc = c0 + 4 * m;
-                const uint32_t idx = maxb + (uint32_t)j - hbv[m];
+                const uint32_t idx = maxb + (uint32_t)j - (hbv[m] & 0x7FFu);
+                const uint32_t nzc = (hbv[m] >> 20) & 0x3FFu;
                 cv[m] = s_cs[(cc < G ? cc : 0) * NBIN + (idx < (uint32_t)NBIN ? idx : 0u)];
-                cv[m] = (cc < G && idx < (uint32_t)NBIN) ? cv[m] : 0u;
+                cv[m] = (cc < G && idx < (uint32_t)NBIN && 32u * idx < nzc) ? cv[m] : 0u;
             }
 #pragma unroll
             for (int m = 0; m < M; ++m) part += cv[m];
@@ -1396,12 +1409,14 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
         constexpr int R2 = (kOneMaxSplit * PER + NT - 1) / NT;
         const int total = G * PER;
         // word index of each of this thread's counts (past the 512 keys: 0)
-        uint32_t idx[R2];
+        uint32_t idx[R2], nzv[R2];
 #pragma unroll
         for (int q = 0; q < R2; ++q) {
             const int i = q * NT + t;
             const int ii = i < total ? i : 0;
-            idx[q] = 32u * (B - (s_hdr[ii / PER] & 0x7FFu)) + (uint32_t)(ii % PER);
+            const uint32_t hh = s_hdr[ii / PER];
+            idx[q] = 32u * (B - (hh & 0x7FFu)) + (uint32_t)(ii % PER);
+            nzv[q] = (hh >> 20) & 0x3FFu;
         }
         uint32_t v[R2];
 #pragma unroll
@@ -1409,13 +1424,13 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
             const int i = q * NT + t;
             const int ii = i < total ? i : 0;
             v[q] = ld_agent(area + (int64_t)(ii / PER) * kOneWords + 1 +
-                            (idx[q] < (uint32_t)kOneKeys ? idx[q] : 0u));
+                            (idx[q] < nzv[q] ? idx[q] : 0u));
         }
         __syncthreads();  // every wave is done with the headers and boundary counts
 #pragma unroll
         for (int q = 0; q < R2; ++q) {
             const int i = q * NT + t;
-            if (i < total) L.hist[i] = idx[q] < (uint32_t)kOneKeys ? v[q] : 0u;
+            if (i < total) L.hist[i] = idx[q] < nzv[q] ? v[q] : 0u;
         }
     }
     __syncthreads();
@@ -1470,13 +1485,14 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
 
     const uint32_t cap = (uint32_t)a.cap;
     const List ent = list_of<K>(s_dyn + split_list_base());
-    uint32_t *slot = a.ws + kHeaderWords + lrow * a.slot_words;
+    uint32_t *slot = a.ws + a.slot0 + lrow * a.slot_words;
     uint32_t *err = a.ws;
     uint32_t *ghist = slot + kSlotHeadWords;
     uint32_t *gcnt = ghist + kMaxPasses * kBins;
     constexpr int LASTB = 1 << K::digit_last();  // bins of the last pass
     uint32_t *pub = gcnt + 4 * G;                // G x (LASTB + 1) suffix counts
-    uint32_t *one_area = pub + G * (LASTB + 1);  // bf16: G x kOneWords
+    // the row's G exchange areas (bf16), in the region after the header
+    uint32_t *one_area = a.ws + kHeaderWords + lrow * G * kOneWords;
 
     // ---- this workgroup's columns into VGPRs; first-digit histogram --------
     const int64_t lo = (int64_t)c * a.chunk;
@@ -1526,14 +1542,12 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
                     L.out[3] = dep == (uint32_t)G - 1u ? 1u : 0u;
                 }
                 __syncthreads();
-                if (L.out[3]) {
-                    // last out: every workgroup has read what it needs, so the
-                    // exchanged words and the counters go back to zero
-                    for (int i = t; i < G * kOneWords; i += NT) st_agent(one_area + i, 0u);
-                    if (t == 0) {
-                        st_agent(slot + 0, 0u);
-                        st_agent(slot + 1, 0u);
-                    }
+                // last out: every workgroup is past the rendezvous, so the
+                // counters go back to zero (the exchanged words need no
+                // clearing: a reader trusts only words its header vouches for)
+                if (L.out[3] && t == 0) {
+                    st_agent(slot + 0, 0u);
+                    st_agent(slot + 1, 0u);
                 }
                 return;
             }
@@ -1672,8 +1686,6 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
             for (int i = t; i < G * (LASTB + 1); i += NT) st_agent(pub + i, 0u);
         else
             for (int i = t; i < 2 * G; i += NT) st_agent(gcnt + i, 0u);
-        if (K::PACK && EPT <= kOneMaxEpt && a.one)  // the one-exchange attempt's words
-            for (int i = t; i < G * kOneWords; i += NT) st_agent(one_area + i, 0u);
         if (t == 0) {
             st_agent(slot + 0, 0u);
             st_agent(slot + 1, 0u);

@@ -62,6 +62,18 @@ class one_exchange:
             os.environ["DSEL_SPLIT_ONE_EXCHANGE"] = self.old
 
 
+def assert_workspaces_clean(dsel):
+    """Every workspace is back in the state the next call needs: word 0 (error
+    bits) clear and every word past the exchange region (the 64-word header,
+    then 8 * CUs * 513 words of per-workgroup scratch) zero."""
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    region = (64 + 8 * cus * 513) * 4
+    for ws in dsel._WORKSPACES.values():
+        assert int(ws[:4].count_nonzero()) == 0, "an error bit is set (a rendezvous timed out)"
+        assert int(ws[region:].count_nonzero()) == 0, "row slots must be zero after a call"
+
+
 def run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value, output_idx=None):
     xd = to_device(x)
     re = row_end.cuda() if row_end is not None else None
@@ -141,9 +153,7 @@ def test_split_one_exchange(dsel, orc, G, one):
                                         (4096, False, torch.int32, True)):
         check_case(dsel, orc, f"one/G{G}/on{int(one)}/k{k}", x, k, re, sorted_index, itype, ret,
                    G, one)
-    torch.cuda.synchronize()
-    for ws in dsel._WORKSPACES.values():
-        assert int(ws.count_nonzero()) == 0, "workspace must be zero after a call (and no error bit)"
+    assert_workspaces_clean(dsel)
 
 
 @pytest.mark.parametrize("G", [None, 4])
@@ -295,7 +305,7 @@ def test_errors(dsel):
 
 def test_workspace_reuse(dsel, orc):
     """One workspace serves calls of different shapes (so different per-row
-    slot layouts) back to back: each call returns it to zero, and no
+    slot layouts) back to back: each call returns its slots to zero, and no
     rendezvous times out (error word 0 stays clear)."""
     dsel._WORKSPACES.clear()
     cases = [(W.random_rows(71, 8, 50000, W.F32, "normal"), 100, 6),
@@ -308,9 +318,7 @@ def test_workspace_reuse(dsel, orc):
               (W.random_rows(73, 5, 30000, W.BF16, "ties"), 1500, 9)]
     for i, (x, k, G) in enumerate(cases):
         check_case(dsel, orc, f"reuse{i}", x, k, None, False, torch.int32, True, G)
-    torch.cuda.synchronize()
-    for ws in dsel._WORKSPACES.values():
-        assert int(ws.count_nonzero()) == 0, "workspace must be zero after a call (and no error bit)"
+    assert_workspaces_clean(dsel)
 
 
 # ---------------------------------------------------------------------------
@@ -328,6 +336,29 @@ def test_workload_split_path_cfg1(dsel, orc):
     case = W.make_config(1)
     for G in (1, 4):
         check_case(dsel, orc, f"cfg1/G{G}", case.x, case.k, None, False, torch.int32, True, G)
+
+
+def test_exchange_region_garbage(dsel, orc):
+    """The exchange region may hold anything between calls: with random bits
+    written over it (headers and counts included), the one-exchange select
+    of the 4 x 204800 workload and of ragged split rows still matches the
+    oracle, and the row slots come back zero."""
+    case = W.make_config(2)
+    x2 = W.random_rows(141, 5, 70000, W.BF16, "normal")
+    re2 = torch.tensor([70000, 65000, 30001, 9000, 0], dtype=torch.int32)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    region = (64 + 8 * cus * 513) * 4
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for rep in range(3):
+        check_case(dsel, orc, f"garbage{rep}/cfg2", case.x, case.k, case.row_end,
+                   case.sorted_index, case.indices_type, case.return_value)
+        check_case(dsel, orc, f"garbage{rep}/ragged", x2, 700, re2, True, torch.int32, True, 9)
+        torch.cuda.synchronize()
+        for ws in dsel._WORKSPACES.values():
+            if ws.numel() > region:
+                ws[256:region] = torch.randint(0, 256, (region - 256,), generator=gen,
+                                               dtype=torch.uint8, device=ws.device)
+    assert_workspaces_clean(dsel)
 
 
 def test_workload_cfg2_multipass(dsel, orc):
