@@ -92,7 +92,7 @@ int dsel_stride_requirement(int64_t *in_align_bytes, int64_t *out_align_bytes);
  *               call leaves it zero-filled again, except (a) word 0, which
  *               holds sticky error bits (bit 0: a split-row rendezvous timed
  *               out), and (b) the exchange region that follows the 64-word
- *               header, 8 * (compute units) * 513 words, which holds scratch
+ *               header, 8 * (compute units) * 544 words, which holds scratch
  *               that every call writes before it reads it.
  *               Calls that share one workspace must be stream-ordered.
  * rows == 0 launches nothing and returns DSEL_OK.

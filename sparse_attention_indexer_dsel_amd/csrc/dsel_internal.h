@@ -38,8 +38,13 @@ inline int last_pass_bins(int dtype) { return dtype == 0 ? 32 : 1024; }
 // every call and every slot layout, and is never cleared: a reader uses
 // only words the header says were written by this call.  The row slots
 // (counters, histograms) follow it.
+// Area layout (words): the 16 counts at bin boundaries (the 128-byte line
+// every reader fetches first), the header, then the 512 counts; padded to
+// whole 128-byte lines.
 constexpr int kOneKeys = 512;
-constexpr int kOneWords = 1 + kOneKeys;
+constexpr int kOneHdr = 16;
+constexpr int kOneFine = 32;
+constexpr int kOneWords = kOneFine + kOneKeys;
 constexpr int kOneMaxSplit = 64;
 constexpr int kOneWgPerCu = 8;
 inline int64_t one_region_words(int cus) { return (int64_t)kOneWgPerCu * cus * kOneWords; }

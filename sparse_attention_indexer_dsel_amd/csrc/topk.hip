@@ -1274,6 +1274,7 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
                                   uint32_t *err) {
     static_assert(K::PACK && K::SH1 == 5, "one exchange: 16-bit keys, 32 keys per first-digit bin");
     static_assert(kOneKeys == 2 * NT, "two fine bins per thread");
+    static_assert(kOneHdr == kOneKeys / 32 && kOneFine > kOneHdr, "area: boundary counts, header, counts");
     constexpr int NBIN = kOneKeys / 32;  // first-digit bins a chunk's region may span
     const int t = tid();
     const int lane = t & 63;
@@ -1318,8 +1319,10 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
         const int top = kOneKeys - 2 * t;
         const uint32_t h1 = fh[top - 1], h0 = fh[top - 2];
         const uint32_t incl = block_scan(h1 + h0, L.red).incl;
-        if (incl - h0) st_agent(mine + 1 + (top - 1), incl - h0);
-        if (incl) st_agent(mine + 1 + (top - 2), incl);
+        if (incl - h0) st_agent(mine + kOneFine + (top - 1), incl - h0);
+        if (incl) st_agent(mine + kOneFine + (top - 2), incl);
+        // and the counts at bin boundaries (key 32 j) side by side
+        if (incl && ((top - 2) & 31) == 0) st_agent(mine + ((top - 2) >> 5), incl);
         // words [0, nz) hold nonzero counts: nz = highest nonzero key + 1
         const uint32_t last = h1 ? (uint32_t)top : (h0 ? (uint32_t)top - 1u : 0u);
         const uint32_t wm = wave_max_u32(last);
@@ -1329,7 +1332,8 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
         for (int w = 0; w < NWAVE; ++w) nz = max(nz, L.red[w]);
     }
     if (t == 0)
-        st_agent(mine, bc | (full << 16) | (ok << 17) | (blk_nan ? 1u << 18 : 0u) | (nz << 20));
+        st_agent(mine + kOneHdr,
+                 bc | (full << 16) | (ok << 17) | (blk_nan ? 1u << 18 : 0u) | (nz << 20));
     row_rendezvous(slot, (uint32_t)G, err);
 
     // ---- every chunk's header and counts at its bin boundaries -------------
@@ -1345,7 +1349,7 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
             const int i = q * NT + t;
             const int ii = i < total ? i : 0;
             const int cc = ii / PER, j = ii % PER;
-            v[q] = ld_agent(area + (int64_t)cc * kOneWords + (j == NBIN ? 0 : 1 + 32 * j));
+            v[q] = ld_agent(area + (int64_t)cc * kOneWords + j);  // j == NBIN: the header
         }
 #pragma unroll
         for (int q = 0; q < R1; ++q) {
@@ -1423,7 +1427,7 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
         for (int q = 0; q < R2; ++q) {
             const int i = q * NT + t;
             const int ii = i < total ? i : 0;
-            v[q] = ld_agent(area + (int64_t)(ii / PER) * kOneWords + 1 +
+            v[q] = ld_agent(area + (int64_t)(ii / PER) * kOneWords + kOneFine +
                             (idx[q] < nzv[q] ? idx[q] : 0u));
         }
         __syncthreads();  // every wave is done with the headers and boundary counts

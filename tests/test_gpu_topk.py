@@ -65,10 +65,10 @@ class one_exchange:
 def assert_workspaces_clean(dsel):
     """Every workspace is back in the state the next call needs: word 0 (error
     bits) clear and every word past the exchange region (the 64-word header,
-    then 8 * CUs * 513 words of per-workgroup scratch) zero."""
+    then 8 * CUs * 544 words of per-workgroup scratch) zero."""
     torch.cuda.synchronize()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    region = (64 + 8 * cus * 513) * 4
+    region = (64 + 8 * cus * 544) * 4
     for ws in dsel._WORKSPACES.values():
         assert int(ws[:4].count_nonzero()) == 0, "an error bit is set (a rendezvous timed out)"
         assert int(ws[region:].count_nonzero()) == 0, "row slots must be zero after a call"
@@ -347,7 +347,7 @@ def test_exchange_region_garbage(dsel, orc):
     x2 = W.random_rows(141, 5, 70000, W.BF16, "normal")
     re2 = torch.tensor([70000, 65000, 30001, 9000, 0], dtype=torch.int32)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    region = (64 + 8 * cus * 513) * 4
+    region = (64 + 8 * cus * 544) * 4
     gen = torch.Generator(device="cuda").manual_seed(7)
     for rep in range(3):
         check_case(dsel, orc, f"garbage{rep}/cfg2", case.x, case.k, case.row_end,
