@@ -92,11 +92,21 @@ def gather_algorithmic_bytes(n_positions: int, dim: int, elt: int, pos_elt: int,
 # HBM traffic from rocprofv3 counters
 # ---------------------------------------------------------------------------
 
-def kernel_source_hash() -> str:
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace: what the compiler sees."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the kernel sources' code (comments and whitespace ignored), so
+    that stored counter figures stay valid across comment edits only."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+    for f in sources or KERNEL_SOURCES:
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

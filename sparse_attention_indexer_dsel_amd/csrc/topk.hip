@@ -34,12 +34,16 @@
 //     per-wave LDS histogram and wave scans only, so no row waits on a
 //     workgroup barrier and four rows run side by side per workgroup;
 //   * rows longer than one workgroup holds (16384 columns) are split over G
-//     workgroups, each holding one chunk: their histograms meet in a per-row
-//     workspace slot (device-scope relaxed atomics and a rendezvous per
-//     radix pass); each workgroup lists its own candidates; the last pass
-//     also carries each workgroup's counts, which give every workgroup the
-//     ranks of the chunks before its own, and each writes its part of the
-//     row's output;
+//     workgroups, each holding one chunk.  bf16 rows first try the one
+//     exchange: each workgroup lists its keys from the floor of its own
+//     top-k bin (the row's k-th largest key cannot lie below it), publishes
+//     their suffix counts, and one rendezvous gives every workgroup the exact
+//     threshold and its starting ranks.  Otherwise (and for fp32) the
+//     histograms meet in a per-row workspace slot (device-scope relaxed
+//     atomics and a rendezvous per radix pass); each workgroup lists its own
+//     candidates; the last pass also carries each workgroup's counts, which
+//     give every workgroup the ranks of the chunks before its own.  Either
+//     way each workgroup writes its part of the row's output;
 //   * if a candidate list would not fit (massive ties at the threshold), the
 //     radix select finishes over the range re-read from cache (slower, same
 //     result).
