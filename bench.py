@@ -7,7 +7,10 @@
 Prints ONE JSON line.  The headline workload is the 4 x 204800 bf16 top-k
 (k = 1024, ascending int32 indices plus values); a step is one top-k call
 over one batch.  ``per_config`` adds the same measurement for the five named
-workloads (top-k and, where they have one, the gather).
+workloads (top-k and, where they have one, the gather), and for two of them
+(the 4 x 204800 headline and the 128 x 129280 sampling rows) the top-k with
+the selection ordered by value (``topk_by_value``: the select, then the
+bitonic value-order pass).
 
 Timing protocol
   * inputs are generated on the host from fixed seeds and copied to HBM
@@ -63,6 +66,9 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_indexer_dsel_amd", "csrc", f)
                   for f in ("topk.hip", "dsel_internal.h", "api.hip")]
 METRIC = "top-k rows/s and achieved HBM GB/s (% of peak) per config; gather GB/s"
+# workloads also timed with the selection ordered by value (the sampling
+# workload, where that order is the natural one, and the headline)
+VALUE_ORDER_CONFIGS = (2, 4)
 
 
 def output_convention_gbps(out_bytes: float, seconds: float) -> float:
@@ -205,8 +211,9 @@ def _copies_for(nbytes: int, cap: int = 4096) -> int:
 class TopkBench:
     """Device-resident inputs (rotating copies) and a reusable top-k call."""
 
-    def __init__(self, dsel, torch, case, stream):
+    def __init__(self, dsel, torch, case, stream, by_value=False):
         self.dsel, self.torch, self.case, self.stream = dsel, torch, case, stream
+        self.by_value = by_value
         x = case.x
         self.in_bytes = x.numel() * x.element_size()
         self.ncopy = _copies_for(self.in_bytes)
@@ -221,7 +228,8 @@ class TopkBench:
         c = self.case
         return self.dsel.topk(self.xs[i % self.ncopy], c.k, end=self.row_end,
                               sorted_index=c.sorted_index, indices_type=c.indices_type,
-                              return_value=c.return_value, stream=self.stream)
+                              return_value=c.return_value, by_value=self.by_value,
+                              stream=self.stream)
 
     def algorithmic_bytes(self) -> int:
         c = self.case
@@ -265,8 +273,10 @@ def graph_time(torch, stream, fn, steps: int, warmup: int, reps: int = 1):
     return best, best_ev
 
 
-def measure_topk(dsel, torch, case, stream, steps, warmup):
-    tb = TopkBench(dsel, torch, case, stream)
+def measure_topk(dsel, torch, case, stream, steps, warmup, by_value=False):
+    """One top-k call per step (with by_value, the select and then the
+    value-order pass: kernel_us covers both)."""
+    tb = TopkBench(dsel, torch, case, stream, by_value)
     t_step, t_kern = graph_time(torch, stream, tb.call, steps, warmup, reps=3)
     nbytes = tb.algorithmic_bytes()
     rows = case.x.shape[0]
@@ -447,6 +457,8 @@ def main(argv=None):
         for i in sorted(W.CONFIGS):
             c = case if i == cfg_id else W.make_config(i)
             entry = {"topk": measure_topk(dsel, torch, c, stream, 20, 3)}
+            if i in VALUE_ORDER_CONFIGS:
+                entry["topk_by_value"] = measure_topk(dsel, torch, c, stream, 20, 3, by_value=True)
             if c.keys:
                 entry["gather"] = measure_gather(dsel, torch, c, stream, 10, 2)
             per[c.name] = entry

@@ -68,14 +68,18 @@ int dsel_stride_requirement(int64_t *in_align_bytes, int64_t *out_align_bytes);
  *     out_val[i, 0:c) = bit copies of x at those columns (NaN payloads kept)
  *     out_val[i, c:k) = -inf
  *     nan_flag[i]     = (n > k) && some x[i, 0:n) is NaN
- * The selected columns always come out ascending, so `sorted_index` costs
- * nothing and both settings give the same bytes.
+ * The selected columns always come out ascending, so `sorted_index` 0 and 1
+ * cost nothing and give the same bytes.  `sorted_index` 2 orders each row's
+ * c selected entries by value instead: largest first, equal values by
+ * ascending column, NaN above every value, -0 equal to +0 (the tutorial's
+ * end-bound example and its tip on ordering "by index or by value"); a
+ * bitonic pass in LDS runs after the select, so this order costs time.
  *
  * x             [rows, cols] bf16 or f32 (`dtype`), last dim contiguous,
  *               row stride `x_row_stride` elements (>= cols).
  * k             1..4096, else DSEL_ERR_K.
  * row_end       int32 [rows] or NULL (all rows full length).
- * sorted_index  0/1 (see above).
+ * sorted_index  0, 1 or 2 (see above), else DSEL_ERR_ARG.
  * indices_type  DSEL_I32 or DSEL_I64.
  * return_value  0/1; when 0, out_val is ignored and may be NULL.
  * out_idx       caller-owned [rows, >= k] of the index dtype, row stride

@@ -67,6 +67,9 @@ class Oracle:
              ) -> Tuple[Optional[np.ndarray], np.ndarray, np.ndarray]:
         """x: 2-D uint16 (bf16 bits) or float32, last dim contiguous.
 
+        sorted_index: False/0 (any order; here the value order), True/1
+        (ascending index) or 2 (by value: largest first, equal values by
+        ascending index).
         Returns (values or None, indices [rows, k], nan_flag uint8 [rows]).
         Values come back in the input's storage type (uint16 bits for bf16).
         """
@@ -94,7 +97,7 @@ class Oracle:
         st = self.lib.oracle_topk(
             x.ctypes.data if rows else None, dt, rows, cols, max(stride, cols), k,
             re.ctypes.data if re is not None else None,
-            int(bool(sorted_index)), it, int(bool(return_value)),
+            int(sorted_index), it, int(bool(return_value)),
             idx.ctypes.data, k, vals.ctypes.data if vals is not None else None, k,
             flag.ctypes.data, nt)
         if st != 0:

@@ -10,6 +10,10 @@
  *   - section "Ukusebenzisa i-TopK Okuyisisekelo": input (rows, cols), last
  *     dim contiguous, row stride given; values keep the input dtype; indices
  *     are int32 or int64; with sorted_index each row's indices ascend.
+ *   - section "Ukusebenzisa i-end" example and tip 3 of "Ukusebenza
+ *     namathiphu athuthukile": a selection may also be ordered by value.
+ *     sorted_index = 2 asks for that order: largest value first, equal
+ *     values by ascending index, which is the ranking order itself.
  *   - section "Ukusebenza Ngemigqa Enobude Obuhlukahlukene": a per-row
  *     exclusive end; a row shorter than k is padded with the OOB fill values.
  *   - section "Ukuphathwa kwe-NaN": NaN checking is always on, and rows whose
@@ -172,7 +176,11 @@ static void *topk_rows(void *arg) {
         qsort(ent, (size_t)n, sizeof(or_entry), cmp_entry);
         for (int64_t s = 0; s < c; ++s) sel[s] = ent[s].idx;
 #if ORACLE_MUTANT != 8
-        if (J->sorted_index) qsort(sel, (size_t)c, sizeof(int64_t), cmp_idx);
+        if (J->sorted_index == 1) qsort(sel, (size_t)c, sizeof(int64_t), cmp_idx);
+#endif
+#if ORACLE_MUTANT == 13
+        if (J->sorted_index == 2) /* planted: value order reversed */
+            for (int64_t a = 0, b = c - 1; a < b; ++a, --b) { int64_t t = sel[a]; sel[a] = sel[b]; sel[b] = t; }
 #endif
         unsigned char *orow = J->out_idx + (size_t)(i * J->idx_row_stride) * (J->indices_type == OR_I32 ? 4 : 8);
         for (int64_t s = 0; s < J->k; ++s) {
@@ -210,6 +218,7 @@ int oracle_topk(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_
     if (rows < 0 || cols < 0 || k < 1 || k > 4096) return -2;
     if (dtype != OR_BF16 && dtype != OR_F32) return -1;
     if (indices_type != OR_I32 && indices_type != OR_I64) return -1;
+    if (sorted_index < 0 || sorted_index > 2) return -1;
     if (rows == 0) return 0;
     if (!x || !out_idx || (return_value && !out_val)) return -1;
     if (x_row_stride < cols || idx_row_stride < k || (return_value && val_row_stride < k)) return -1;

@@ -125,11 +125,11 @@ def _row_stride(t: torch.Tensor) -> int:
     return -(-max(int(t.shape[1]), 1) // per) * per
 
 
-def _topk_call(x, k, end, sorted_index, itype, return_value, idx, val, flag, ws_ptr, ws_bytes, sptr):
+def _topk_call(x, k, end, order, itype, return_value, idx, val, flag, ws_ptr, ws_bytes, sptr):
     return _lib.dsel_topk(
         x.data_ptr(), _dtype_code(x.dtype), x.shape[0], x.shape[1], _row_stride(x),
         int(k), end.data_ptr() if end is not None else None,
-        int(bool(sorted_index)), _index_code(itype), int(bool(return_value)),
+        int(order), _index_code(itype), int(bool(return_value)),
         idx.data_ptr(), _row_stride(idx),
         val.data_ptr() if val is not None else None, _row_stride(val) if val is not None else 0,
         flag.data_ptr(), ws_ptr, ctypes.byref(ws_bytes), sptr)
@@ -147,7 +147,7 @@ def _check_input(x: torch.Tensor) -> None:
 def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
          sorted_index: bool = False, sorted: Optional[bool] = None,
          indices_type: torch.dtype = torch.int32, return_value: bool = True,
-         output_idx: Optional[torch.Tensor] = None, stream=None
+         output_idx: Optional[torch.Tensor] = None, by_value: bool = False, stream=None
          ) -> Tuple[Optional[torch.Tensor], torch.Tensor, torch.Tensor]:
     """Row-wise top-k of ``x`` [rows, cols] (bf16 or fp32), 1 <= topk <= 4096.
 
@@ -158,10 +158,14 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
     ``end`` (int32 [rows]) is each row's exclusive end.  ``sorted`` is
     accepted as another name for ``sorted_index``.  ``output_idx`` is a
     caller-owned [rows, >= topk] index buffer with an aligned row stride.
+    ``by_value=True`` orders each row's selection by value instead (largest
+    first, equal values by ascending column; NaN first, -0 equal to +0);
+    it takes precedence over ``sorted_index``.
     """
     _check_input(x)
     if sorted is not None:
         sorted_index = bool(sorted)
+    order = 2 if by_value else int(bool(sorted_index))
     rows = x.shape[0]
     dev = x.device
     if end is not None:
@@ -183,11 +187,11 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
     with torch.cuda.device(dev):
         sptr = _stream_ptr(dev, stream)
         nb = ctypes.c_size_t(0)
-        _check(_topk_call(x, topk, end, sorted_index, indices_type, return_value, idx, val, flag,
+        _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
                           None, nb, sptr), "dsel_topk (size query)")
         ws = _workspace(dev, sptr, nb.value)
         nb = ctypes.c_size_t(ws.numel())
-        _check(_topk_call(x, topk, end, sorted_index, indices_type, return_value, idx, val, flag,
+        _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
                           ws.data_ptr(), nb, sptr), "dsel_topk")
     if output_idx is not None:
         idx = output_idx[:, :topk]

@@ -221,7 +221,9 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
                          int64_t idx_row_stride, void *out_val, int64_t val_row_stride,
                          uint8_t *nan_flag, void *workspace, size_t *workspace_bytes,
                          void *stream) {
-    (void)sorted_index;  // output is ascending by construction
+    // sorted_index 0 and 1: the output is ascending by construction; 2: a
+    // value-order pass follows the select
+    if (sorted_index < 0 || sorted_index > 2) return DSEL_ERR_ARG;
     if (dtype != DSEL_BF16 && dtype != DSEL_F32) return DSEL_ERR_ARG;
     if (indices_type != DSEL_I32 && indices_type != DSEL_I64) return DSEL_ERR_ARG;
     if (rows < 0 || cols < 1) return DSEL_ERR_ARG;
@@ -282,6 +284,15 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
         if (grid > INT32_MAX) return DSEL_ERR_ARG;
         if (launch_topk(dtype, pl.ept, pl.kind, a, (unsigned)grid, s) != hipSuccess)
             return DSEL_ERR_DEVICE;
+    }
+    if (sorted_index == 2) {
+        // one workgroup per row, in launches of at most 2^30 rows
+        constexpr int64_t kMaxGrid = (int64_t)1 << 30;
+        for (int64_t r0 = 0; r0 < rows; r0 += kMaxGrid) {
+            a.row0 = r0;
+            const int64_t nr = (rows - r0) < kMaxGrid ? (rows - r0) : kMaxGrid;
+            if (launch_value_sort(dtype, a, (unsigned)nr, s) != hipSuccess) return DSEL_ERR_DEVICE;
+        }
     }
     return DSEL_OK;
 }

@@ -98,6 +98,8 @@ inline int topk_vec(int dtype) { return dtype == 0 ? 8 : 4; }
 size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind);
 hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned grid,
                        hipStream_t stream);
+// Value order of the top-k outputs of rows [a.row0, a.row0 + grid), in place.
+hipError_t launch_value_sort(int dtype, const TopkArgs &a, unsigned grid, hipStream_t stream);
 
 struct GatherArgs {
     const char *key;

@@ -2115,6 +2115,103 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Value order (sorted_index = 2): each row's selection, largest value first,
+// equal values by ascending column.  One workgroup per row sorts the row's
+// c = min(k, n) (key, column) pairs in LDS with a bitonic network over
+// 64-bit words key << 32 | ~column, descending; the padding slots stay.  Runs
+// after the top-k on the same stream, in place on its outputs.
+// ---------------------------------------------------------------------------
+
+// Order-preserving key of one value's bits (NaN on top, -0 with +0), the
+// element form of the key words above.
+template <class K>
+__device__ __forceinline__ uint32_t key_of_bits(uint32_t bits) {
+    if constexpr (K::PACK) {
+        const uint32_t mag = bits & 0x7FFFu;
+        if (mag > 0x7F80u) return 0xFFFFu;
+        return (bits & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
+    } else {
+        const uint32_t mag = bits & 0x7FFFFFFFu;
+        if (mag > 0x7F800000u) return 0xFFFFFFFFu;
+        return (bits & 0x80000000u) ? 0x80000000u - mag : 0x80000000u + mag;
+    }
+}
+
+constexpr int SORT_NT = 1024;  // threads of a value-order workgroup (1..2 pairs each per step)
+
+template <class K>
+__global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) {
+    using raw_t = typename K::raw_t;
+    extern __shared__ __attribute__((aligned(16))) uint64_t s_pair[];  // P words
+    const int64_t row = a.row0 + blockIdx.x;
+    if (row >= a.rows) return;
+    const int t = (int)threadIdx.x;
+    const int64_t n = valid_length(a, row);
+    const uint32_t c = (uint32_t)(n < a.k ? n : a.k);
+    if (c <= 1) return;
+    uint32_t P = 2;
+    while (P < c) P <<= 1;
+    const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
+    const RowOut o = row_out<K>(a, row);
+    for (uint32_t j = (uint32_t)t; j < P; j += SORT_NT) {
+        uint64_t w = 0;  // below every pair: sorts to the tail
+        if (j < c) {
+            const uint32_t col = o.idx64 ? (uint32_t)reinterpret_cast<const int64_t *>(o.idx)[j]
+                                         : (uint32_t)reinterpret_cast<const int32_t *>(o.idx)[j];
+            const uint32_t bits = o.val ? (uint32_t)reinterpret_cast<const raw_t *>(o.val)[j]
+                                        : (uint32_t)xr[col];
+            w = ((uint64_t)key_of_bits<K>(bits) << 32) | (uint32_t)~col;
+        }
+        s_pair[j] = w;
+    }
+    // bitonic network: blocks of `size` merge descending where (lo & size)
+    // is clear, ascending where set; the last merge is descending throughout.
+    // A step of stride < blk pairs elements inside one aligned block of blk,
+    // so wave w runs those steps on block w alone, ordered by wave syncs;
+    // only the steps of larger strides take workgroup barriers.
+    auto step = [&](uint32_t lo, uint32_t stride, uint32_t size) {
+        const uint32_t hi = lo + stride;
+        const uint64_t x = s_pair[lo], y = s_pair[hi];
+        const bool desc = (lo & size) == 0;
+        if ((x < y) == desc) {
+            s_pair[lo] = y;
+            s_pair[hi] = x;
+        }
+    };
+    // elements per wave-local block: one block per wave (at most 256
+    // elements, at least 2)
+    constexpr uint32_t NW = SORT_NT / 64;
+    uint32_t blk = P / NW;
+    blk = blk > 256u ? 256u : (blk < 2u ? 2u : blk);
+    const uint32_t lane = (uint32_t)t & 63u, w = (uint32_t)t >> 6;
+    for (uint32_t size = 2; size <= P; size <<= 1) {
+        uint32_t stride = size >> 1;
+        for (; stride >= blk; stride >>= 1) {
+            __syncthreads();
+            for (uint32_t i = (uint32_t)t; i < P / 2; i += SORT_NT)
+                step(((i & ~(stride - 1)) << 1) | (i & (stride - 1)), stride, size);
+        }
+        __syncthreads();
+        if (w * blk < P) {
+            const uint32_t base = w * blk;
+            for (; stride > 0; stride >>= 1) {
+                for (uint32_t i = lane; i < blk / 2; i += 64)
+                    step(base + (((i & ~(stride - 1)) << 1) | (i & (stride - 1))), stride, size);
+                wave_sync();
+            }
+        }
+    }
+    __syncthreads();
+    for (uint32_t j = (uint32_t)t; j < c; j += SORT_NT) {
+        const uint64_t w = s_pair[j];
+        const uint32_t col = ~(uint32_t)w, key = (uint32_t)(w >> 32);
+        store_index(o, j, col);
+        if (o.val)
+            store_value<K>(o, j, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
+    }
+}
+
 template <class K, int EPT, bool SPLIT>
 const void *kptr() {
     if constexpr (SPLIT)
@@ -2180,6 +2277,21 @@ hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned
     void *args[] = {&copy};
     return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, topk_dyn_lds(dtype, a.cap, ept, kind),
                            stream);
+}
+
+// Bitonic LDS words of a value-order launch: the next power of two >= k.
+static size_t value_sort_lds(int64_t k) {
+    size_t P = 2;
+    while ((int64_t)P < k) P <<= 1;
+    return P * sizeof(uint64_t);
+}
+
+hipError_t launch_value_sort(int dtype, const TopkArgs &a, unsigned grid, hipStream_t stream) {
+    const void *fn = dtype == 0 ? reinterpret_cast<const void *>(&sort_rows_by_value<Bf16Key>)
+                                : reinterpret_cast<const void *>(&sort_rows_by_value<F32Key>);
+    TopkArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel(fn, dim3(grid), dim3(SORT_NT), args, value_sort_lds(a.k), stream);
 }
 
 }  // namespace dsel

@@ -269,6 +269,50 @@ def pin_numpy_stable_argsort(orc, seed=2):
                         assert got.tolist() == sorted(want.tolist())
 
 
+def _ranks_before(a_val, a_idx, b_val, b_idx) -> bool:
+    """(a_val, a_idx) comes before (b_val, b_idx) in value order: NaN above
+    everything, NaNs equal, -0 equal to +0, equal values by ascending index."""
+    an, bn = bool(np.isnan(a_val)), bool(np.isnan(b_val))
+    if an != bn:
+        return an
+    if not an and a_val != b_val:
+        return a_val > b_val
+    return a_idx < b_idx
+
+
+def pin_value_order(orc, seed=9):
+    """sorted_index=2: rows without NaN equal numpy's stable argsort of -x
+    position by position; every row (NaN, +-0, ties included) is in value
+    order with ties by ascending index; the set matches the unsorted call."""
+    rng = np.random.default_rng(seed)
+    for dtype in ("bf16", "f32"):
+        base = rng.integers(-20, 20, size=(5, 1000)).astype(np.float32) * 0.5
+        base[base == 0.0] = -0.0
+        base[:, ::7] = 0.0
+        x = bf16_bits(torch.from_numpy(base).to(torch.bfloat16)).copy() if dtype == "bf16" else base
+        vals = decode(x)
+        for k in (1, 10, 333, 1000, 1200):
+            _, idx, _ = orc.topk(x, k, sorted_index=2)
+            for i in range(x.shape[0]):
+                c = min(k, 1000)
+                want = np.argsort(-vals[i], kind="stable")[:c]
+                assert idx[i, :c].astype(np.int64).tolist() == want.tolist()
+                assert (idx[i, c:] == -1).all()
+        xs = _tiny_rows(rng, 12, 40, dtype)
+        vs = decode(xs)
+        row_end = rng.integers(0, 45, size=12).astype(np.int32)
+        for k in (1, 3, 17, 40, 50):
+            v, idx, _ = orc.topk(xs, k, row_end=row_end, sorted_index=2)
+            _, idx0, _ = orc.topk(xs, k, row_end=row_end, sorted_index=0)
+            for i in range(xs.shape[0]):
+                n = valid_len(row_end, i, 40)
+                sel = check_row_contract(vs[i], raw_bits(xs[i]), n, k, idx[i], raw_bits(v[i]),
+                                         False, dtype == "bf16")
+                assert sorted(sel) == sorted(int(t) for t in idx0[i, :min(k, n)])
+                for a, b in zip(sel, sel[1:]):
+                    assert _ranks_before(vs[i][a], a, vs[i][b], b), (dtype, k, i, a, b)
+
+
 def pin_torch_topk_distinct(orc, seed=3):
     """Rows of distinct values: the set and values equal torch.topk's."""
     g = torch.Generator().manual_seed(seed)
@@ -443,6 +487,7 @@ ALL_PINS = [
     pin_bruteforce_tiny,
     pin_pairwise,
     pin_numpy_stable_argsort,
+    pin_value_order,
     pin_torch_topk_distinct,
     pin_closed_forms,
     pin_nan_flag_rule,

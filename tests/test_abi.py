@@ -75,6 +75,8 @@ def test_topk_host_checks(lib):
     assert _topk(lib, k=4097) == -2
     assert _topk(lib, dtype=7) == -1
     assert _topk(lib, itype=3) == -1
+    assert _topk(lib, sorted_index=3) == -1   # 0/1: ascending columns, 2: by value
+    assert _topk(lib, sorted_index=-1) == -1
     assert _topk(lib, cols=0) == -1
     assert _topk(lib, rows=-1) == -1
     assert _topk(lib, x=None) == -1

@@ -338,6 +338,59 @@ def test_workload_split_path_cfg1(dsel, orc):
         check_case(dsel, orc, f"cfg1/G{G}", case.x, case.k, None, False, torch.int32, True, G)
 
 
+def check_value_order(dsel, orc, name, x, k, row_end=None, indices_type=torch.int32,
+                      return_value=True, G=None):
+    """by_value=True against the oracle's value order, position by position."""
+    say(f"[topk by value] {name} shape={tuple(x.shape)} k={k} G={G} idx={indices_type} "
+        f"val={return_value}")
+    xd = to_device(x)
+    re = row_end.cuda() if row_end is not None else None
+    with blocks_per_row(G):
+        v, i, f = dsel.topk(xd, k, end=re, indices_type=indices_type, return_value=return_value,
+                            by_value=True)
+    torch.cuda.synchronize()
+    got = (gpu_bits(v) if v is not None else None, i.cpu().numpy(), f.cpu().numpy())
+    want = oracle_topk(orc, x, k, row_end, 2, indices_type, return_value)
+    n = valid_lengths(x.shape[0], x.shape[1], row_end)
+    compare_topk(got, want, n, k, True, name)  # positional
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c[0])
+def test_value_order_small(dsel, orc, case):
+    """Value order (sorted_index 2) over every small distribution: ties,
+    all-equal rows, +-0, +-inf, denormals and NaN payloads, k >= cols."""
+    name, rows, cols, dt, dist, k = case
+    x = W.random_rows(zlib.crc32(name.encode()) & 0xFFFF, rows, cols, dt, dist)
+    for ret, itype in ((True, torch.int32), (False, torch.int64)):
+        check_value_order(dsel, orc, f"{name}/val{int(ret)}", x, k, None, itype, ret)
+
+
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_value_order_paths(dsel, orc, dt):
+    """Value order after every select path: one wave per row, one workgroup
+    per row, split rows (one exchange and multi-pass), with ragged row
+    ends, NaN rows and k up to 4096."""
+    x = W.random_rows(151, 6, 50000, dt, "normal")
+    W.plant_nans(x, 152, 2)
+    re = torch.tensor([50000, 49999, 30000, 4097, 1500, 0], dtype=torch.int32)
+    for k in (1, 100, 1024, 4096):
+        check_value_order(dsel, orc, f"split/{dt}/k{k}", x, k, re)
+    xw = W.random_rows(153, 9, 16000, dt, "special")
+    rw = torch.tensor([16000, 9000, 2048, 2000, 700, 300, 1, 0, 12345], dtype=torch.int32)
+    for k in (5, 512, 2000):
+        check_value_order(dsel, orc, f"whole/{dt}/k{k}", xw, k, rw, torch.int64)
+    xs = W.random_rows(154, 13, 1900, dt, "ties")
+    check_value_order(dsel, orc, f"wave/{dt}", xs, 333, None, torch.int32, False)
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_value_order_workloads(dsel, orc, cfg):
+    """The 4 x 204800 bf16 and 128 x 129280 fp32 (sampling) workloads ordered by value."""
+    case = W.make_config(cfg)
+    check_value_order(dsel, orc, f"{case.name}/by_value", case.x, case.k, case.row_end,
+                      case.indices_type, case.return_value)
+
+
 def test_exchange_region_garbage(dsel, orc):
     """The exchange region may hold anything between calls: with random bits
     written over it (headers and counts included), the one-exchange select

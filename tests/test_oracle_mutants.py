@@ -23,6 +23,7 @@ MUTANTS = {
     10: "gather position off by one",
     11: "ascending instead of descending",
     12: "input row stride ignored",
+    13: "value order reversed",
 }
 
 
