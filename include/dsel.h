@@ -110,6 +110,25 @@ int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_ro
               void *workspace, size_t *workspace_bytes,
               void *stream);
 
+/* dsel_topk with the out-of-range fills given (DeepSelect tutorial, section
+ * "Ukusebenza Ngemigqa Enobude Obuhlukahlukene": slots past a row's valid
+ * length hold `idx_oob_fill_value` and `value_oob_fill_value`).  Same
+ * arguments, then:
+ * idx_fill        index written to slots [c, k) of a row (c = min(k, n));
+ *                 must fit the index dtype (int32 range for DSEL_I32), else
+ *                 DSEL_ERR_ARG.
+ * val_fill_bits   raw bits of the value written there (bf16: <= 0xFFFF, else
+ *                 DSEL_ERR_ARG).
+ * dsel_topk is dsel_topk_ex with idx_fill -1 and val_fill_bits of -inf. */
+int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
+                 int64_t k, const int32_t *row_end,
+                 int sorted_index, int indices_type, int return_value,
+                 void *out_idx, int64_t idx_row_stride,
+                 void *out_val, int64_t val_row_stride,
+                 uint8_t *nan_flag,
+                 void *workspace, size_t *workspace_bytes,
+                 void *stream, int64_t idx_fill, uint32_t val_fill_bits);
+
 /*
  * Gather of key rows at selected positions, batch offset folded in.
  *

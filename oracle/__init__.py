@@ -55,7 +55,7 @@ class Oracle:
         i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         self.lib.oracle_topk.restype = i32
         self.lib.oracle_topk.argtypes = [vp, i32, i64, i64, i64, i64, vp, i32, i32, i32,
-                                         vp, i64, vp, i64, vp, i32]
+                                         vp, i64, vp, i64, vp, i32, i64, ctypes.c_uint32]
         self.lib.oracle_gather.restype = i32
         self.lib.oracle_gather.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i32, i64,
                                            i64, i64, vp]
@@ -63,13 +63,16 @@ class Oracle:
     # -- top-k -------------------------------------------------------------
     def topk(self, x: np.ndarray, k: int, row_end: Optional[np.ndarray] = None,
              sorted_index: bool = False, indices_type=np.int32, return_value: bool = True,
-             threads: Optional[int] = None
+             threads: Optional[int] = None, idx_fill: int = -1,
+             val_fill_bits: Optional[int] = None
              ) -> Tuple[Optional[np.ndarray], np.ndarray, np.ndarray]:
         """x: 2-D uint16 (bf16 bits) or float32, last dim contiguous.
 
         sorted_index: False/0 (any order; here the value order), True/1
         (ascending index) or 2 (by value: largest first, equal values by
         ascending index).
+        idx_fill / val_fill_bits: index and raw value bits of the slots past
+        a short row's length (default -1 and -inf).
         Returns (values or None, indices [rows, k], nan_flag uint8 [rows]).
         Values come back in the input's storage type (uint16 bits for bf16).
         """
@@ -99,7 +102,8 @@ class Oracle:
             re.ctypes.data if re is not None else None,
             int(sorted_index), it, int(bool(return_value)),
             idx.ctypes.data, k, vals.ctypes.data if vals is not None else None, k,
-            flag.ctypes.data, nt)
+            flag.ctypes.data, nt, int(idx_fill),
+            (0xFF80 if dt == OR_BF16 else 0xFF800000) if val_fill_bits is None else int(val_fill_bits))
         if st != 0:
             raise RuntimeError(f"oracle_topk failed: {st}")
         return vals, idx, flag

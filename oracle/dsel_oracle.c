@@ -24,7 +24,9 @@
  *     (the lower index wins);
  *   - every NaN ranks above +inf and all NaNs are equal to each other;
  *     -0 equals +0; denormals are ordinary values;
- *   - fills are index -1 and value -inf;
+ *   - fills (section "Ukusebenza Ngemigqa Enobude Obuhlukahlukene" names
+ *     them, gives no values) default to index -1 and value -inf; a call may
+ *     give others;
  *   - a row's valid length is clamp(end, 0, cols); the NaN check is reported
  *     as a per-row flag instead of a device trap.
  *
@@ -113,6 +115,8 @@ typedef struct {
     int64_t rows, cols, x_row_stride, k;
     const int32_t *row_end;
     int sorted_index, indices_type, return_value;
+    int64_t idx_fill;
+    uint32_t val_fill;
     unsigned char *out_idx;
     int64_t idx_row_stride;
     unsigned char *out_val;
@@ -131,13 +135,12 @@ static void put_index(unsigned char *row, int indices_type, int64_t slot, int64_
     }
 }
 
-static void put_neg_inf(unsigned char *row, int dtype, int64_t slot) {
+static void put_fill(unsigned char *row, int dtype, int64_t slot, uint32_t bits) {
     if (dtype == OR_BF16) {
-        uint16_t h = 0xFF80u;
+        uint16_t h = (uint16_t)bits;
         memcpy(row + 2 * slot, &h, 2);
     } else {
-        uint32_t w = 0xFF800000u;
-        memcpy(row + 4 * slot, &w, 4);
+        memcpy(row + 4 * slot, &bits, 4);
     }
 }
 
@@ -187,7 +190,7 @@ static void *topk_rows(void *arg) {
 #if ORACLE_MUTANT == 6
             put_index(orow, J->indices_type, s, s < c ? sel[s] : 0); /* planted: pad with 0 */
 #else
-            put_index(orow, J->indices_type, s, s < c ? sel[s] : -1);
+            put_index(orow, J->indices_type, s, s < c ? sel[s] : J->idx_fill);
 #endif
         }
         if (J->return_value) {
@@ -200,7 +203,7 @@ static void *topk_rows(void *arg) {
 #endif
                     memcpy(vrow + esz * s, row + esz * src, (size_t)esz); /* bit copy */
                 } else {
-                    put_neg_inf(vrow, J->dtype, s);
+                    put_fill(vrow, J->dtype, s, J->val_fill);
                 }
             }
         }
@@ -210,11 +213,14 @@ static void *topk_rows(void *arg) {
     return NULL;
 }
 
-/* Returns 0 on success, negative on bad arguments or allocation failure. */
+/* Returns 0 on success, negative on bad arguments or allocation failure.
+ * idx_fill / val_fill_bits: the index and value bits of slots past a short
+ * row's length (the defaults are -1 and -inf). */
 int oracle_topk(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
                 int64_t k, const int32_t *row_end, int sorted_index, int indices_type,
                 int return_value, void *out_idx, int64_t idx_row_stride, void *out_val,
-                int64_t val_row_stride, uint8_t *nan_flag, int nthreads) {
+                int64_t val_row_stride, uint8_t *nan_flag, int nthreads, int64_t idx_fill,
+                uint32_t val_fill_bits) {
     if (rows < 0 || cols < 0 || k < 1 || k > 4096) return -2;
     if (dtype != OR_BF16 && dtype != OR_F32) return -1;
     if (indices_type != OR_I32 && indices_type != OR_I64) return -1;
@@ -236,6 +242,7 @@ int oracle_topk(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_
         J->x = (const unsigned char *)x; J->dtype = dtype; J->rows = rows; J->cols = cols;
         J->x_row_stride = x_row_stride; J->k = k; J->row_end = row_end;
         J->sorted_index = sorted_index; J->indices_type = indices_type; J->return_value = return_value;
+        J->idx_fill = idx_fill; J->val_fill = val_fill_bits;
         J->out_idx = (unsigned char *)out_idx; J->idx_row_stride = idx_row_stride;
         J->out_val = (unsigned char *)out_val; J->val_row_stride = val_row_stride;
         J->nan_flag = nan_flag;

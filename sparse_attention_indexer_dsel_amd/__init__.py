@@ -52,6 +52,9 @@ def _load() -> ctypes.CDLL:
     lib.dsel_topk.restype = i32
     lib.dsel_topk.argtypes = [vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, i64, vp, i64,
                               vp, vp, szp, vp]
+    lib.dsel_topk_ex.restype = i32
+    lib.dsel_topk_ex.argtypes = [vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, i64, vp,
+                                 i64, vp, vp, szp, vp, i64, ctypes.c_uint32]
     lib.dsel_gather_rows.restype = i32
     lib.dsel_gather_rows.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i32, i64, i64, i64,
                                      vp, vp]
@@ -125,14 +128,24 @@ def _row_stride(t: torch.Tensor) -> int:
     return -(-max(int(t.shape[1]), 1) // per) * per
 
 
-def _topk_call(x, k, end, order, itype, return_value, idx, val, flag, ws_ptr, ws_bytes, sptr):
-    return _lib.dsel_topk(
+def _fill_bits(value, dtype: torch.dtype) -> int:
+    """Raw bits of `value` in the value dtype (None: -inf)."""
+    v = float("-inf") if value is None else float(value)
+    t = torch.tensor([v], dtype=dtype)
+    return int(t.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).item()) & (
+        0xFFFF if dtype == torch.bfloat16 else 0xFFFFFFFF)
+
+
+def _topk_call(x, k, end, order, itype, return_value, idx, val, flag, ws_ptr, ws_bytes, sptr,
+               idx_fill=-1, val_fill=None):
+    return _lib.dsel_topk_ex(
         x.data_ptr(), _dtype_code(x.dtype), x.shape[0], x.shape[1], _row_stride(x),
         int(k), end.data_ptr() if end is not None else None,
         int(order), _index_code(itype), int(bool(return_value)),
         idx.data_ptr(), _row_stride(idx),
         val.data_ptr() if val is not None else None, _row_stride(val) if val is not None else 0,
-        flag.data_ptr(), ws_ptr, ctypes.byref(ws_bytes), sptr)
+        flag.data_ptr(), ws_ptr, ctypes.byref(ws_bytes), sptr, int(idx_fill),
+        _fill_bits(val_fill, x.dtype))
 
 
 def _check_input(x: torch.Tensor) -> None:
@@ -147,7 +160,9 @@ def _check_input(x: torch.Tensor) -> None:
 def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
          sorted_index: bool = False, sorted: Optional[bool] = None,
          indices_type: torch.dtype = torch.int32, return_value: bool = True,
-         output_idx: Optional[torch.Tensor] = None, by_value: bool = False, stream=None
+         output_idx: Optional[torch.Tensor] = None, by_value: bool = False,
+         idx_oob_fill_value: int = -1, value_oob_fill_value: Optional[float] = None,
+         abort_when_nan_found: bool = False, stream=None
          ) -> Tuple[Optional[torch.Tensor], torch.Tensor, torch.Tensor]:
     """Row-wise top-k of ``x`` [rows, cols] (bf16 or fp32), 1 <= topk <= 4096.
 
@@ -160,7 +175,11 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
     caller-owned [rows, >= topk] index buffer with an aligned row stride.
     ``by_value=True`` orders each row's selection by value instead (largest
     first, equal values by ascending column; NaN first, -0 equal to +0);
-    it takes precedence over ``sorted_index``.
+    it takes precedence over ``sorted_index``.  ``idx_oob_fill_value`` and
+    ``value_oob_fill_value`` (default -1 and -inf) fill the slots past a
+    short row's length.  ``abort_when_nan_found=True`` raises
+    FloatingPointError when a row longer than ``topk`` holds a NaN (this
+    waits for the call to finish); by default the flag is only returned.
     """
     _check_input(x)
     if sorted is not None:
@@ -188,13 +207,18 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
         sptr = _stream_ptr(dev, stream)
         nb = ctypes.c_size_t(0)
         _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
-                          None, nb, sptr), "dsel_topk (size query)")
+                          None, nb, sptr, idx_oob_fill_value, value_oob_fill_value),
+               "dsel_topk (size query)")
         ws = _workspace(dev, sptr, nb.value)
         nb = ctypes.c_size_t(ws.numel())
         _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
-                          ws.data_ptr(), nb, sptr), "dsel_topk")
+                          ws.data_ptr(), nb, sptr, idx_oob_fill_value, value_oob_fill_value),
+               "dsel_topk")
     if output_idx is not None:
         idx = output_idx[:, :topk]
+    if abort_when_nan_found and bool(flag.any()):
+        rows_hit = torch.nonzero(flag).flatten()[:8].tolist()
+        raise FloatingPointError(f"NaN in rows longer than topk (first rows: {rows_hit})")
     return val, idx, flag
 
 

@@ -221,11 +221,26 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
                          int64_t idx_row_stride, void *out_val, int64_t val_row_stride,
                          uint8_t *nan_flag, void *workspace, size_t *workspace_bytes,
                          void *stream) {
+    return dsel_topk_ex(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index,
+                        indices_type, return_value, out_idx, idx_row_stride, out_val,
+                        val_row_stride, nan_flag, workspace, workspace_bytes, stream, -1,
+                        dtype == DSEL_BF16 ? 0xFF80u : 0xFF800000u);
+}
+
+extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols,
+                            int64_t x_row_stride, int64_t k, const int32_t *row_end,
+                            int sorted_index, int indices_type, int return_value, void *out_idx,
+                            int64_t idx_row_stride, void *out_val, int64_t val_row_stride,
+                            uint8_t *nan_flag, void *workspace, size_t *workspace_bytes,
+                            void *stream, int64_t idx_fill, uint32_t val_fill_bits) {
     // sorted_index 0 and 1: the output is ascending by construction; 2: a
     // value-order pass follows the select
     if (sorted_index < 0 || sorted_index > 2) return DSEL_ERR_ARG;
     if (dtype != DSEL_BF16 && dtype != DSEL_F32) return DSEL_ERR_ARG;
     if (indices_type != DSEL_I32 && indices_type != DSEL_I64) return DSEL_ERR_ARG;
+    if (indices_type == DSEL_I32 && (idx_fill < INT32_MIN || idx_fill > INT32_MAX))
+        return DSEL_ERR_ARG;
+    if (dtype == DSEL_BF16 && val_fill_bits > 0xFFFFu) return DSEL_ERR_ARG;
     if (rows < 0 || cols < 1) return DSEL_ERR_ARG;
     if (k < 1 || k > 4096) return DSEL_ERR_K;
     if (!workspace_bytes) return DSEL_ERR_ARG;
@@ -276,6 +291,8 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
     a.idx64 = indices_type == DSEL_I64;
     a.ret_val = return_value ? 1 : 0;
     a.one = pl.one ? 1 : 0;
+    a.idx_fill = idx_fill;
+    a.val_fill = val_fill_bits;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     for (int64_t r0 = 0; r0 < rows; r0 += pl.rows_per_launch) {
         const int64_t nr = (rows - r0) < pl.rows_per_launch ? (rows - r0) : pl.rows_per_launch;

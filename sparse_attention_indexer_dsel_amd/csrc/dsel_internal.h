@@ -82,6 +82,8 @@ struct TopkArgs {
     int idx64;
     int ret_val;
     int one;                 // split bf16 rows: try the one-exchange select first
+    int64_t idx_fill;        // index of the slots past a short row's length
+    uint32_t val_fill;       // value bits of those slots
 };
 
 // Top-k kernel kinds: one workgroup per row, G workgroups per row, one wave

@@ -359,7 +359,8 @@ __device__ __forceinline__ void emit(const RowOut &o, uint32_t pos, uint32_t col
         store_value<K>(o, pos, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
 }
 
-// Rows with n <= k: columns 0..n-1 in order, then padding.  Workgroup c of G
+// Rows with n <= k: columns 0..n-1 in order, then padding (the fill index
+// and fill value bits the call gives).  Workgroup c of G
 // writes slots [c*S, (c+1)*S) with S = ceil(k / G); `me` of `nthr` threads
 // (a workgroup's, or one wave's lanes) share them.
 template <class K>
@@ -372,27 +373,30 @@ __device__ __forceinline__ void write_short_row(const TopkArgs &a, int64_t row, 
     if (!a.idx64 && !a.ret_val && (a.idx_stride & 3) == 0 && (s0 & 3) == 0) {
         // index-only int32: four slots per 16-byte store
         int32_t *o = reinterpret_cast<int32_t *>(a.out_idx) + row * a.idx_stride;
+        const int fill = (int)a.idx_fill;
         const int nv = (s1 - s0) >> 2;
         for (int v = me; v < nv; v += nthr) {
             const int s = s0 + 4 * v;
             int4 q;
-            q.x = s < n ? s : -1;
-            q.y = s + 1 < n ? s + 1 : -1;
-            q.z = s + 2 < n ? s + 2 : -1;
-            q.w = s + 3 < n ? s + 3 : -1;
+            q.x = s < n ? s : fill;
+            q.y = s + 1 < n ? s + 1 : fill;
+            q.z = s + 2 < n ? s + 2 : fill;
+            q.w = s + 3 < n ? s + 3 : fill;
             *reinterpret_cast<int4 *>(o + s) = q;
         }
-        for (int s = s0 + 4 * nv + me; s < s1; s += nthr) o[s] = s < n ? s : -1;
+        for (int s = s0 + 4 * nv + me; s < s1; s += nthr) o[s] = s < n ? s : fill;
     } else {
         for (int s = s0 + me; s < s1; s += nthr) {
             const bool in = s < n;
             if (a.idx64)
-                reinterpret_cast<int64_t *>(a.out_idx)[row * a.idx_stride + s] = in ? (int64_t)s : -1;
+                reinterpret_cast<int64_t *>(a.out_idx)[row * a.idx_stride + s] =
+                    in ? (int64_t)s : a.idx_fill;
             else
-                reinterpret_cast<int32_t *>(a.out_idx)[row * a.idx_stride + s] = in ? s : -1;
+                reinterpret_cast<int32_t *>(a.out_idx)[row * a.idx_stride + s] =
+                    in ? s : (int32_t)a.idx_fill;
             if (a.ret_val)
                 reinterpret_cast<typename K::raw_t *>(a.out_val)[row * a.val_stride + s] =
-                    in ? xr[s] : (typename K::raw_t)K::NEG_INF;
+                    in ? xr[s] : (typename K::raw_t)a.val_fill;
         }
     }
     if (c == 0 && me == 0 && a.nan_flag) a.nan_flag[row] = 0;

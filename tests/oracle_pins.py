@@ -313,6 +313,25 @@ def pin_value_order(orc, seed=9):
                     assert _ranks_before(vs[i][a], a, vs[i][b], b), (dtype, k, i, a, b)
 
 
+def pin_custom_fills(orc, seed=10):
+    """Rows shorter than k: slots [n, k) hold the given fill index and the
+    given fill value bits, and slots [0, n) are the row's columns in order
+    (the closed form of a short row), whatever the fills."""
+    rng = np.random.default_rng(seed)
+    for dtype, bits in (("bf16", 0x7FC0), ("f32", 0x3F800000)):
+        x = _tiny_rows(rng, 6, 30, dtype)
+        row_end = np.array([0, 1, 7, 19, 30, 29], dtype=np.int32)
+        for itype, fill in ((np.int32, -7), (np.int64, 2 ** 40)):
+            v, idx, _ = orc.topk(x, 32, row_end=row_end, sorted_index=True, indices_type=itype,
+                                 idx_fill=fill, val_fill_bits=bits)
+            for i in range(6):
+                n = int(row_end[i])
+                assert idx[i, :n].tolist() == list(range(n))
+                assert (idx[i, n:] == fill).all()
+                assert (raw_bits(v[i])[:n] == raw_bits(x[i])[:n]).all()
+                assert (raw_bits(v[i])[n:] == bits).all()
+
+
 def pin_torch_topk_distinct(orc, seed=3):
     """Rows of distinct values: the set and values equal torch.topk's."""
     g = torch.Generator().manual_seed(seed)
@@ -488,6 +507,7 @@ ALL_PINS = [
     pin_pairwise,
     pin_numpy_stable_argsort,
     pin_value_order,
+    pin_custom_fills,
     pin_torch_topk_distinct,
     pin_closed_forms,
     pin_nan_flag_rule,

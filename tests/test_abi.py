@@ -34,8 +34,9 @@ def declared():
     return sorted(set(re.findall(r"\bint\s+(dsel_\w+)\s*\(", text)))
 
 
-def test_header_declares_the_three_calls():
-    assert declared() == ["dsel_gather_rows", "dsel_stride_requirement", "dsel_topk"]
+def test_header_declares_the_calls():
+    assert declared() == ["dsel_gather_rows", "dsel_stride_requirement", "dsel_topk",
+                          "dsel_topk_ex"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -111,3 +112,23 @@ def test_gather_host_checks(lib):
     assert call(krs=129) == -3
     assert call(out=24) == -3
     assert call(R=0) == 0             # empty: nothing launched
+
+
+def _topk_ex(lib, idx_fill, val_bits, dtype=0, itype=0):
+    nb = ctypes.c_size_t(0)
+    f = lib.dsel_topk_ex
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_uint32]
+    return f(16, dtype, 4, 64, 64, 8, None, 0, itype, 0, 16, 16, None, 0, None, None,
+             ctypes.byref(nb), None, idx_fill, val_bits)
+
+
+def test_topk_ex_fill_checks(lib):
+    """Fills that do not fit the output types are refused before any launch."""
+    assert _topk_ex(lib, 2 ** 31, 0xFF80) == -1               # int32 index fill out of range
+    assert _topk_ex(lib, -(2 ** 31) - 1, 0xFF80) == -1
+    assert _topk_ex(lib, -1, 0x1FF80) == -1                    # bf16 fill wider than 16 bits

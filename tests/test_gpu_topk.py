@@ -391,6 +391,49 @@ def test_value_order_workloads(dsel, orc, cfg):
                       case.indices_type, case.return_value)
 
 
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_custom_fills(dsel, orc, dt):
+    """idx_oob_fill_value / value_oob_fill_value on short rows of every select
+    path (one wave, one workgroup, split rows), both index types, values on
+    and off, in ascending and value order."""
+    fill_val = 2.5
+    bits = 0x4020 if dt == W.BF16 else 0x40200000
+    for cols, G in ((1500, None), (9000, None), (40000, 5)):
+        x = W.random_rows(161 + cols, 5, cols, dt, "normal")
+        re = torch.tensor([cols, 0, 3, 700, cols - 1], dtype=torch.int32)
+        for k, itype, fill, ret, order in ((1000, torch.int32, -5, True, 1),
+                                           (2048, torch.int64, 2 ** 40, False, 0),
+                                           (777, torch.int32, 123456, True, 2)):
+            xd = to_device(x)
+            with blocks_per_row(G):
+                v, i, f = dsel.topk(xd, k, end=re.cuda(), sorted_index=order == 1,
+                                    by_value=order == 2, indices_type=itype, return_value=ret,
+                                    idx_oob_fill_value=fill, value_oob_fill_value=fill_val)
+            torch.cuda.synchronize()
+            got = (gpu_bits(v) if v is not None else None, i.cpu().numpy(), f.cpu().numpy())
+            xh = x.view(torch.int16).numpy().view(np.uint16) if dt == W.BF16 else x.numpy()
+            want = orc.topk(xh, k, row_end=re.numpy(), sorted_index=order, indices_type=np.dtype(
+                np.int32 if itype == torch.int32 else np.int64), return_value=ret,
+                idx_fill=fill, val_fill_bits=bits)
+            n = valid_lengths(5, cols, re)
+            compare_topk(got, want, n, k, order != 0, f"fills/{dt}/{cols}/k{k}")
+            assert (got[1][1] == fill).all(), "an empty row is all fill"
+
+
+def test_abort_when_nan_found(dsel):
+    """abort_when_nan_found=True raises for a NaN in a row longer than k, and
+    not for a NaN in a row of length <= k (which is never checked)."""
+    x = torch.randn(3, 5000).to(torch.bfloat16)
+    x[2, 10] = float("nan")
+    re = torch.tensor([5000, 5000, 100], dtype=torch.int32)
+    dsel.topk(x.cuda(), 200, end=re.cuda(), abort_when_nan_found=True)  # row 2: n <= k
+    x[1, 4000] = float("nan")
+    with pytest.raises(FloatingPointError):
+        dsel.topk(x.cuda(), 200, end=re.cuda(), abort_when_nan_found=True)
+    _, _, f = dsel.topk(x.cuda(), 200, end=re.cuda())
+    assert f.cpu().tolist() == [0, 1, 0]
+
+
 def test_exchange_region_garbage(dsel, orc):
     """The exchange region may hold anything between calls: with random bits
     written over it (headers and counts included), the one-exchange select
