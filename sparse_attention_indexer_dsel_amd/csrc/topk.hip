@@ -6,8 +6,9 @@
 // row the c = min(k, n) largest entries of the valid prefix x[0:n), n the
 // clamped per-row exclusive end; equal values keep column order, NaN ranks
 // above +inf, -0 equals +0; the selected columns are written in ascending
-// order, short rows padded with -1 / -inf; a per-row flag reports NaN in rows
-// longer than k.
+// order (or, on request, by value), short rows padded with the fill index
+// and value (-1 / -inf unless the call gives others); a per-row flag reports
+// NaN in rows longer than k.
 //
 // How (this file's design, not the pages'):
 //   * a key is the value's bits mapped to an unsigned integer whose order is
@@ -46,7 +47,10 @@
 //     way each workgroup writes its part of the row's output;
 //   * if a candidate list would not fit (massive ties at the threshold), the
 //     radix select finishes over the range re-read from cache (slower, same
-//     result).
+//     result);
+//   * value order (sorted_index 2) is a separate pass after the select: one
+//     workgroup per row sorts its (key, column) pairs with a bitonic network
+//     in LDS, largest value first, equal values by ascending column.
 #include "dsel_internal.h"
 
 namespace dsel {
