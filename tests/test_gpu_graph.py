@@ -29,21 +29,24 @@ def test_graph_replays_match_eager():
         ev, ei, ef = dsel.topk(x, 1024, sorted_index=True, stream=s)
         _, ei2, ef2 = dsel.topk(xs, 100, end=re, return_value=False, stream=s)
         eg = dsel.gather_rows(key, ei2.view(3, 100, 100), stream=s)
+        evv, eiv, _ = dsel.topk(xs, 700, end=re, by_value=True, stream=s)   # value order
     s.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         gv, gi, gf = dsel.topk(x, 1024, sorted_index=True, stream=s)
         _, gi2, gf2 = dsel.topk(xs, 100, end=re, return_value=False, stream=s)
         gg = dsel.gather_rows(key, gi2.view(3, 100, 100), stream=s)
+        gvv, giv, _ = dsel.topk(xs, 700, end=re, by_value=True, stream=s)
     for rep in range(4):
         say(f"[graph] replay {rep}")
-        for t in (gv, gi, gf, gi2, gf2, gg):
+        for t in (gv, gi, gf, gi2, gf2, gg, gvv, giv):
             t.fill_(-7)
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(gi, ei) and torch.equal(gv.view(torch.int16), ev.view(torch.int16))
         assert torch.equal(gf, ef) and torch.equal(gi2, ei2) and torch.equal(gf2, ef2)
         assert torch.equal(gg.view(torch.int16), eg.view(torch.int16))
+        assert torch.equal(giv, eiv) and torch.equal(gvv.view(torch.int32), evv.view(torch.int32))
         # eager work between replays on the same workspace
         dsel.topk(x, 512, stream=s)
         s.synchronize()
