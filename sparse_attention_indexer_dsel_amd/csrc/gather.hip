@@ -15,7 +15,7 @@
 namespace dsel {
 namespace {
 
-constexpr int GT = 256;        // threads per workgroup
+constexpr int GT = 512;        // threads per workgroup (measured: 256 and 1024 were slower)
 constexpr int UNROLL = 16;     // independent 16-byte copies in flight per thread
 constexpr int POS_CHUNK = 1024;  // positions staged in LDS at a time
 
