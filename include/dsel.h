@@ -64,9 +64,10 @@ int dsel_stride_requirement(int64_t *in_align_bytes, int64_t *out_align_bytes);
  * x[i, 0:n) under: NaN above +inf (all NaNs equal), -0 == +0, and among equal
  * values the lower column first.  Then
  *     out_idx[i, 0:c) = the selected columns in ascending column order
- *     out_idx[i, c:k) = -1
+ *                       (by value with sorted_index 2, below)
+ *     out_idx[i, c:k) = -1 (dsel_topk_ex: the given fill index)
  *     out_val[i, 0:c) = bit copies of x at those columns (NaN payloads kept)
- *     out_val[i, c:k) = -inf
+ *     out_val[i, c:k) = -inf (dsel_topk_ex: the given fill value bits)
  *     nan_flag[i]     = (n > k) && some x[i, 0:n) is NaN
  * The selected columns always come out ascending, so `sorted_index` 0 and 1
  * cost nothing and give the same bytes.  `sorted_index` 2 orders each row's
