@@ -434,6 +434,55 @@ def test_abort_when_nan_found(dsel):
     assert f.cpu().tolist() == [0, 1, 0]
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_sweep(dsel, orc, seed):
+    """Seeded random configurations against the oracle: rows 1..9, columns
+    1..70000, k 1..4096, both dtypes, every distribution, forced workgroups
+    per row (split paths), the one exchange on or off, all three orders,
+    both index types, values on or off, ragged and empty row ends, fills."""
+    rng = np.random.default_rng(1000 + seed)
+    dists = ["normal", "ties", "equal", "ascending", "descending", "narrow", "special"]
+    for case in range(10):
+        rows = int(rng.integers(1, 10))
+        cols = int(rng.choice([int(rng.integers(1, 2100)), int(rng.integers(2100, 16400)),
+                               int(rng.integers(16400, 70000))]))
+        k = int(min(4096, max(1, rng.integers(1, 2 * cols + 2))))
+        dt = W.BF16 if rng.random() < 0.6 else W.F32
+        dist = dists[int(rng.integers(0, len(dists)))]
+        x = W.random_rows(int(rng.integers(0, 1 << 16)), rows, cols, dt, dist)
+        if rng.random() < 0.3:
+            W.plant_nans(x, int(rng.integers(0, 1 << 16)), 1)
+        re = None
+        if rng.random() < 0.6:
+            re = torch.from_numpy(rng.integers(-3, cols + 4, size=rows).astype(np.int32))
+        G = None
+        if cols > 2048 and rng.random() < 0.6:
+            G = int(rng.integers(2, 65))
+        one = [None, False][int(rng.integers(0, 2))]
+        order = int(rng.integers(0, 3))
+        itype = torch.int32 if rng.random() < 0.6 else torch.int64
+        ret = bool(rng.random() < 0.7)
+        fill = int(rng.integers(-9, 9))
+        name = (f"sweep{seed}.{case}: {rows}x{cols} {dt} {dist} k={k} G={G} one={one} "
+                f"order={order} {itype} val={ret} re={re is not None} fill={fill}")
+        say("[topk] " + name)
+        xd = to_device(x)
+        with blocks_per_row(G), one_exchange(one):
+            v, i, f = dsel.topk(xd, k, end=re.cuda() if re is not None else None,
+                                sorted_index=order == 1, by_value=order == 2,
+                                indices_type=itype, return_value=ret, idx_oob_fill_value=fill)
+        torch.cuda.synchronize()
+        got = (gpu_bits(v) if v is not None else None, i.cpu().numpy(), f.cpu().numpy())
+        xh = x.view(torch.int16).numpy().view(np.uint16) if dt == W.BF16 else x.numpy()
+        want = orc.topk(xh, k, row_end=re.numpy() if re is not None else None,
+                        sorted_index=order,
+                        indices_type=np.int32 if itype == torch.int32 else np.int64,
+                        return_value=ret, idx_fill=fill)
+        n = valid_lengths(rows, cols, re)
+        compare_topk(got, want, n, k, order != 0, name)
+    assert_workspaces_clean(dsel)
+
+
 def test_exchange_region_garbage(dsel, orc):
     """The exchange region may hold anything between calls: with random bits
     written over it (headers and counts included), the one-exchange select
