@@ -92,8 +92,10 @@ enum { kTopkWhole = 0, kTopkSplit = 1, kTopkWave = 2 };
 // Rows of at most this many columns take one wave each.
 constexpr int64_t kWaveCapacity = 64 * 32;
 
-// Kernel instance for (dtype, elements per thread, kind); nullptr if none.
-const void *topk_kernel_ptr(int dtype, int ept, int kind);
+// Kernel instance for (dtype, elements per thread, kind, values returned);
+// nullptr if none.  The two one-wave instances of a (dtype, ept) pair have
+// the same occupancy.
+const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val = 0);
 // Elements per 16-byte vector for a dtype.
 inline int topk_vec(int dtype) { return dtype == 0 ? 8 : 4; }
 // Dynamic LDS bytes of a top-k launch with candidate capacity `cap`.

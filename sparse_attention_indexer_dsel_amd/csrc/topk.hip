@@ -363,10 +363,105 @@ __device__ __forceinline__ void emit(const RowOut &o, uint32_t pos, uint32_t col
         store_value<K>(o, pos, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
 }
 
-// Rows with n <= k: columns 0..n-1 in order, then padding (the fill index
-// and fill value bits the call gives).  Workgroup c of G
-// writes slots [c*S, (c+1)*S) with S = ceil(k / G); `me` of `nthr` threads
-// (a workgroup's, or one wave's lanes) share them.
+// Range-checked view of one row's first `end` columns for raw buffer loads:
+// bytes at or past the (dword-rounded) end read as zero without touching
+// memory, so every 16-byte load is unconditional.  The rounding keeps a
+// partly valid dword whole; the element past the end is masked by the
+// caller before it is looked at.
+template <class K>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_view(const typename K::raw_t *xr, int64_t end) {
+    const int64_t bytes = end > 0 ? ((end * (int64_t)sizeof(typename K::raw_t) + 3) & ~(int64_t)3) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<typename K::raw_t *>(xr), (short)0,
+                                             (int)bytes, 0x00020000);
+}
+
+// 16 bytes of raw values at column p of a row view.
+template <class K>
+__device__ __forceinline__ uint4 load_vec(__amdgpu_buffer_rsrc_t view, int64_t p) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+        view, (unsigned)(p * (int64_t)sizeof(typename K::raw_t)), 0u, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Short rows (n <= k) hold columns 0..n-1 in order, then padding (the fill
+// index and fill value bits the call gives).
+//
+// The value slots [s0, s1) of a short row, `me` of `nthr` threads sharing
+// them: range-checked 16-byte loads over the aligned middle (an element-wise
+// load then store waits for every earlier store, since the vector memory
+// counter counts stores too), element-wise ends.
+template <class K>
+__device__ __forceinline__ void write_short_values(typename K::raw_t *ov, typename K::raw_t fill,
+                                                   int64_t n, int s0, int s1,
+                                                   const typename K::raw_t *xr, int me, int nthr) {
+    using raw_t = typename K::raw_t;
+    constexpr int VEC = K::VEC;  // elements per 16 bytes
+    const int vb = min(s1, (s0 + VEC - 1) / VEC * VEC);
+    const int ve = max(vb, s1 / VEC * VEC);
+    for (int s = s0 + me; s < vb; s += nthr) ov[s] = s < n ? xr[s] : fill;
+    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
+    for (int s = vb + VEC * me; s < ve; s += VEC * nthr) {
+        uint4 q = load_vec<K>(view, s);  // bytes past the row end read as zero
+        raw_t e[VEC];
+        __builtin_memcpy(e, &q, 16);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) e[i] = s + i < n ? e[i] : fill;
+        __builtin_memcpy(&q, e, 16);
+        *reinterpret_cast<uint4 *>(ov + s) = q;
+    }
+    for (int s = ve + me; s < s1; s += nthr) ov[s] = s < n ? xr[s] : fill;
+}
+
+// The index slots [s0, s1) of a short row (int32 in 16-byte stores) and its
+// NaN flag.
+__device__ __forceinline__ void write_short_idx(const TopkArgs &a, int64_t row, int64_t n, int c,
+                                                int s0, int s1, int me, int nthr) {
+    if (!a.idx64 && (s0 & 3) == 0) {
+        // int32: four slots per 16-byte store
+        int32_t *o = reinterpret_cast<int32_t *>(a.out_idx) + row * a.idx_stride;
+        const int fill = (int)a.idx_fill;
+        const int nv = (s1 - s0) >> 2;
+        for (int v = me; v < nv; v += nthr) {
+            const int s = s0 + 4 * v;
+            int4 q;
+            q.x = s < n ? s : fill;
+            q.y = s + 1 < n ? s + 1 : fill;
+            q.z = s + 2 < n ? s + 2 : fill;
+            q.w = s + 3 < n ? s + 3 : fill;
+            *reinterpret_cast<int4 *>(o + s) = q;
+        }
+        for (int s = s0 + 4 * nv + me; s < s1; s += nthr) o[s] = s < n ? s : fill;
+    } else {
+        for (int s = s0 + me; s < s1; s += nthr) {
+            if (a.idx64)
+                reinterpret_cast<int64_t *>(a.out_idx)[row * a.idx_stride + s] =
+                    s < n ? (int64_t)s : a.idx_fill;
+            else
+                reinterpret_cast<int32_t *>(a.out_idx)[row * a.idx_stride + s] =
+                    s < n ? s : (int32_t)a.idx_fill;
+        }
+    }
+    if (c == 0 && me == 0 && a.nan_flag) a.nan_flag[row] = 0;
+}
+
+// One wave's short-row values (slots [0, k)), kept out of line: inlined into
+// the one-wave kernel the copy would cost that kernel a wave per SIMD.
+template <class K>
+__device__ __attribute__((noinline)) void write_short_values_wave(typename K::raw_t *ov,
+                                                                  typename K::raw_t fill,
+                                                                  int64_t n, int k,
+                                                                  const typename K::raw_t *xr,
+                                                                  int lane) {
+    write_short_values<K>(ov, fill, n, 0, k, xr, lane, 64);
+}
+
+// A whole short row, index and value stores in one element-wise loop
+// (index-only int32 rows take 16-byte stores).  Workgroup c of G writes
+// slots [c*S, (c+1)*S) with S = ceil(k / G); `me` of `nthr` threads (a
+// workgroup's, or one wave's lanes) share them.  The whole-row and split
+// kernels and the index-only one-wave kernel keep this form: the two writers
+// above measured no faster there and moved those kernels' code enough to slow
+// their long rows by 1 to 4%.
 template <class K>
 __device__ __forceinline__ void write_short_row(const TopkArgs &a, int64_t row, int64_t n, int c, int G,
                                 const typename K::raw_t *xr, int me = tid(),
@@ -404,26 +499,6 @@ __device__ __forceinline__ void write_short_row(const TopkArgs &a, int64_t row, 
         }
     }
     if (c == 0 && me == 0 && a.nan_flag) a.nan_flag[row] = 0;
-}
-
-// Range-checked view of one row's first `end` columns for raw buffer loads:
-// bytes at or past the (dword-rounded) end read as zero without touching
-// memory, so every 16-byte load is unconditional.  The rounding keeps a
-// partly valid dword whole; the element past the end is masked by the
-// caller before it is looked at.
-template <class K>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_view(const typename K::raw_t *xr, int64_t end) {
-    const int64_t bytes = end > 0 ? ((end * (int64_t)sizeof(typename K::raw_t) + 3) & ~(int64_t)3) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<typename K::raw_t *>(xr), (short)0,
-                                             (int)bytes, 0x00020000);
-}
-
-// 16 bytes of raw values at column p of a row view.
-template <class K>
-__device__ __forceinline__ uint4 load_vec(__amdgpu_buffer_rsrc_t view, int64_t p) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-        view, (unsigned)(p * (int64_t)sizeof(typename K::raw_t)), 0u, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // Keys of one 16-byte vector; NaNs sent to the top key.  Returns true if the
@@ -2026,7 +2101,10 @@ __device__ __forceinline__ void wave_write_staged(const TopkArgs &a, int64_t row
 }
 
 // EPL = columns per lane (a multiple of VEC); rows of n <= k are padded.
-template <class K, int EPL>
+// RV: the instance for calls that return values (launched only with
+// a.ret_val set), whose short rows copy values out of line with 16-byte
+// loads; index-only calls take the other instance, which has no call.
+template <class K, int EPL, bool RV>
 __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
     using raw_t = typename K::raw_t;
     using D = WaveDigits<K>;
@@ -2045,7 +2123,13 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
         const int64_t n = valid_length(a, row);
         const raw_t *xr = x + row * a.x_stride;
         if (n <= a.k) {
-            write_short_row<K>(a, row, n, 0, 1, xr, lane, 64);
+            if constexpr (RV) {
+                write_short_idx(a, row, n, 0, 0, a.k, lane, 64);
+                write_short_values_wave<K>(reinterpret_cast<raw_t *>(a.out_val) + row * a.val_stride,
+                                           (raw_t)a.val_fill, n, a.k, xr, lane);
+            } else {
+                write_short_row<K>(a, row, n, 0, 1, xr, lane, 64);
+            }
             continue;
         }
         const int len = (int)n;
@@ -2244,20 +2328,23 @@ const void *pick(int ept) {
 
 }  // namespace
 
-template <class K>
+template <class K, bool RV>
 const void *pick_wave(int epl) {
     switch (epl) {
-        case 8: return reinterpret_cast<const void *>(&topk_rows_wave<K, 8>);
-        case 16: return reinterpret_cast<const void *>(&topk_rows_wave<K, 16>);
-        case 32: return reinterpret_cast<const void *>(&topk_rows_wave<K, 32>);
+        case 8: return reinterpret_cast<const void *>(&topk_rows_wave<K, 8, RV>);
+        case 16: return reinterpret_cast<const void *>(&topk_rows_wave<K, 16, RV>);
+        case 32: return reinterpret_cast<const void *>(&topk_rows_wave<K, 32, RV>);
         default: return nullptr;
     }
 }
 
 // ept = columns per thread of one workgroup's range (the whole row, or one
 // split chunk), or per lane of a wave's row (kTopkWave).
-const void *topk_kernel_ptr(int dtype, int ept, int kind) {
-    if (kind == kTopkWave) return dtype == 0 ? pick_wave<Bf16Key>(ept) : pick_wave<F32Key>(ept);
+const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val) {
+    if (kind == kTopkWave) {
+        if (ret_val) return dtype == 0 ? pick_wave<Bf16Key, true>(ept) : pick_wave<F32Key, true>(ept);
+        return dtype == 0 ? pick_wave<Bf16Key, false>(ept) : pick_wave<F32Key, false>(ept);
+    }
     const bool split = kind == kTopkSplit;
     if (dtype == 0) return split ? pick<Bf16Key, true>(ept) : pick<Bf16Key, false>(ept);
     return split ? pick<F32Key, true>(ept) : pick<F32Key, false>(ept);
@@ -2279,7 +2366,7 @@ size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind) {
 
 hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned grid,
                        hipStream_t stream) {
-    const void *fn = topk_kernel_ptr(dtype, ept, kind);
+    const void *fn = topk_kernel_ptr(dtype, ept, kind, a.ret_val);
     if (!fn) return hipErrorInvalidValue;
     TopkArgs copy = a;
     void *args[] = {&copy};
