@@ -2210,9 +2210,22 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
 // ---------------------------------------------------------------------------
 // Value order (sorted_index = 2): each row's selection, largest value first,
 // equal values by ascending column.  One workgroup per row sorts the row's
-// c = min(k, n) (key, column) pairs in LDS with a bitonic network over
-// 64-bit words key << 32 | ~column, descending; the padding slots stay.  Runs
+// c = min(k, n) (key, column) pairs in LDS; the padding slots stay.  Runs
 // after the top-k on the same stream, in place on its outputs.
+//
+// The select leaves every row in ascending column order, so a stable sort on
+// the key alone orders equal keys by column.  The sort is least significant
+// digit first over 8-bit digits of the inverted key (2 passes for bf16 keys,
+// 4 for fp32), each pass stable:
+//   * pair j of a pass sits in batch (w*B + b) of 64, wave w's batch b,
+//     lane j % 64, with B = ceil(c / 1024) batches per wave, so (w, b, lane)
+//     runs in pair order;
+//   * a wave ranks each batch's lanes among equal digits with eight ballots
+//     and keeps per-(digit, wave) running counts in LDS;
+//   * one exclusive scan of the counts in digit-major order gives every
+//     (digit, wave) its first slot; each pair goes to that slot plus its rank.
+// Four workgroup barriers per pass, against one per step of a bitonic network
+// (78 steps for 4096 pairs) that were each an LDS round trip.
 // ---------------------------------------------------------------------------
 
 // Order-preserving key of one value's bits (NaN on top, -0 with +0), the
@@ -2230,74 +2243,104 @@ __device__ __forceinline__ uint32_t key_of_bits(uint32_t bits) {
     }
 }
 
-constexpr int SORT_NT = 1024;  // threads of a value-order workgroup (1..2 pairs each per step)
+constexpr int SORT_NT = 1024;               // threads of a value-order workgroup
+constexpr int SORT_NW = SORT_NT / 64;       // its waves
+constexpr int SORT_CNT = 256 * SORT_NW;     // (digit, wave) counters, digit-major
+constexpr int SORT_MAXB = 4;                // batches per wave: k <= 4096
 
 template <class K>
 __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) {
     using raw_t = typename K::raw_t;
-    extern __shared__ __attribute__((aligned(16))) uint64_t s_pair[];  // P words
+    // LDS: k pair words (key << 32 | ~column), two arrays of 16-bit counters
+    // (a pass counts in one while the other is cleared), the wave totals
+    extern __shared__ __attribute__((aligned(16))) uint64_t s_pair[];
     const int64_t row = a.row0 + blockIdx.x;
     if (row >= a.rows) return;
     const int t = (int)threadIdx.x;
     const int64_t n = valid_length(a, row);
     const uint32_t c = (uint32_t)(n < a.k ? n : a.k);
     if (c <= 1) return;
-    uint32_t P = 2;
-    while (P < c) P <<= 1;
+    uint16_t *cnt_base = reinterpret_cast<uint16_t *>(s_pair + a.k);
+    uint32_t *wtot = reinterpret_cast<uint32_t *>(cnt_base + 2 * SORT_CNT);
     const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
     const RowOut o = row_out<K>(a, row);
-    for (uint32_t j = (uint32_t)t; j < P; j += SORT_NT) {
-        uint64_t w = 0;  // below every pair: sorts to the tail
-        if (j < c) {
-            const uint32_t col = o.idx64 ? (uint32_t)reinterpret_cast<const int64_t *>(o.idx)[j]
-                                         : (uint32_t)reinterpret_cast<const int32_t *>(o.idx)[j];
-            const uint32_t bits = o.val ? (uint32_t)reinterpret_cast<const raw_t *>(o.val)[j]
-                                        : (uint32_t)xr[col];
-            w = ((uint64_t)key_of_bits<K>(bits) << 32) | (uint32_t)~col;
-        }
-        s_pair[j] = w;
+    for (uint32_t j = (uint32_t)t; j < c; j += SORT_NT) {
+        const uint32_t col = o.idx64 ? (uint32_t)reinterpret_cast<const int64_t *>(o.idx)[j]
+                                     : (uint32_t)reinterpret_cast<const int32_t *>(o.idx)[j];
+        const uint32_t bits = o.val ? (uint32_t)reinterpret_cast<const raw_t *>(o.val)[j]
+                                    : (uint32_t)xr[col];
+        s_pair[j] = ((uint64_t)key_of_bits<K>(bits) << 32) | (uint32_t)~col;
     }
-    // bitonic network: blocks of `size` merge descending where (lo & size)
-    // is clear, ascending where set; the last merge is descending throughout.
-    // A step of stride < blk pairs elements inside one aligned block of blk,
-    // so wave w runs those steps on block w alone, ordered by wave syncs;
-    // only the steps of larger strides take workgroup barriers.
-    auto step = [&](uint32_t lo, uint32_t stride, uint32_t size) {
-        const uint32_t hi = lo + stride;
-        const uint64_t x = s_pair[lo], y = s_pair[hi];
-        const bool desc = (lo & size) == 0;
-        if ((x < y) == desc) {
-            s_pair[lo] = y;
-            s_pair[hi] = x;
-        }
-    };
-    // elements per wave-local block: one block per wave (at most 256
-    // elements, at least 2)
-    constexpr uint32_t NW = SORT_NT / 64;
-    uint32_t blk = P / NW;
-    blk = blk > 256u ? 256u : (blk < 2u ? 2u : blk);
+    for (int i = t; i < SORT_CNT; i += SORT_NT) cnt_base[i] = 0;
+    __syncthreads();
+
     const uint32_t lane = (uint32_t)t & 63u, w = (uint32_t)t >> 6;
-    for (uint32_t size = 2; size <= P; size <<= 1) {
-        uint32_t stride = size >> 1;
-        for (; stride >= blk; stride >>= 1) {
-            __syncthreads();
-            for (uint32_t i = (uint32_t)t; i < P / 2; i += SORT_NT)
-                step(((i & ~(stride - 1)) << 1) | (i & (stride - 1)), stride, size);
-        }
-        __syncthreads();
-        if (w * blk < P) {
-            const uint32_t base = w * blk;
-            for (; stride > 0; stride >>= 1) {
-                for (uint32_t i = lane; i < blk / 2; i += 64)
-                    step(base + (((i & ~(stride - 1)) << 1) | (i & (stride - 1))), stride, size);
+    const uint32_t B = (c + SORT_NT - 1) / SORT_NT;
+    const uint64_t below = (1ull << lane) - 1ull;
+    constexpr int PASSES = K::PACK ? 2 : 4;
+#pragma unroll 1
+    for (int pass = 0; pass < PASSES; ++pass) {
+        uint16_t *cnt = cnt_base + (pass & 1) * SORT_CNT;
+        uint16_t *nxt = cnt_base + ((pass + 1) & 1) * SORT_CNT;
+        const int sh = 8 * pass;
+        uint64_t el[SORT_MAXB];
+        uint32_t dg[SORT_MAXB], rk[SORT_MAXB];
+#pragma unroll
+        for (int b = 0; b < SORT_MAXB; ++b) {
+            el[b] = 0;
+            dg[b] = 0;
+            rk[b] = 0;
+            if ((uint32_t)b < B) {
+                const uint32_t j = ((w * B + (uint32_t)b) << 6) + lane;
+                const bool valid = j < c;
+                const uint64_t e = valid ? s_pair[j] : 0ull;
+                const uint32_t d = (~(uint32_t)(e >> 32) >> sh) & 0xFFu;
+                uint64_t peers = __ballot(valid);
+#pragma unroll
+                for (int bit = 0; bit < 8; ++bit) {
+                    const uint64_t m = __ballot((d >> bit) & 1u);
+                    peers &= ((d >> bit) & 1u) ? m : ~m;
+                }
+                uint32_t base = 0;
+                if (valid) base = cnt[d * SORT_NW + w];
+                wave_sync();  // every lane has read the count before its leader adds
+                if (valid && (uint32_t)__builtin_ctzll(peers) == lane)
+                    cnt[d * SORT_NW + w] = (uint16_t)(base + (uint32_t)__builtin_popcountll(peers));
                 wave_sync();
+                el[b] = e;
+                dg[b] = d;
+                rk[b] = base + (uint32_t)__builtin_popcountll(peers & below);
             }
         }
+        __syncthreads();
+        // exclusive scan of the counters, four per thread
+        const uint2 q = reinterpret_cast<const uint2 *>(cnt)[t];
+        const uint32_t c0 = q.x & 0xFFFFu, c1 = q.x >> 16, c2 = q.y & 0xFFFFu, c3 = q.y >> 16;
+        const uint32_t sum = c0 + c1 + c2 + c3;
+        uint32_t inc = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = __shfl_up(inc, off, 64);
+            if (lane >= (uint32_t)off) inc += v;
+        }
+        if (lane == 63) wtot[w] = inc;
+        for (int i = t; i < SORT_CNT; i += SORT_NT) nxt[i] = 0;  // the next pass's counters
+        __syncthreads();
+        uint32_t pre = inc - sum;
+        for (uint32_t v = 0; v < w; ++v) pre += wtot[v];
+        const uint32_t p1 = pre + c0, p2 = p1 + c1, p3 = p2 + c2;
+        reinterpret_cast<uint2 *>(cnt)[t] = make_uint2(pre | (p1 << 16), p2 | (p3 << 16));
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < SORT_MAXB; ++b) {
+            if ((uint32_t)b < B && ((w * B + (uint32_t)b) << 6) + lane < c)
+                s_pair[(uint32_t)cnt[dg[b] * SORT_NW + w] + rk[b]] = el[b];
+        }
+        __syncthreads();
     }
-    __syncthreads();
     for (uint32_t j = (uint32_t)t; j < c; j += SORT_NT) {
-        const uint64_t w = s_pair[j];
-        const uint32_t col = ~(uint32_t)w, key = (uint32_t)(w >> 32);
+        const uint64_t e = s_pair[j];
+        const uint32_t col = ~(uint32_t)e, key = (uint32_t)(e >> 32);
         store_index(o, j, col);
         if (o.val)
             store_value<K>(o, j, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
@@ -2374,14 +2417,14 @@ hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned
                            stream);
 }
 
-// Bitonic LDS words of a value-order launch: the next power of two >= k.
+// LDS bytes of a value-order launch: k pair words, two arrays of 16-bit
+// counters, the wave totals.
 static size_t value_sort_lds(int64_t k) {
-    size_t P = 2;
-    while ((int64_t)P < k) P <<= 1;
-    return P * sizeof(uint64_t);
+    return (size_t)k * sizeof(uint64_t) + 2 * SORT_CNT * sizeof(uint16_t) + SORT_NW * sizeof(uint32_t);
 }
 
 hipError_t launch_value_sort(int dtype, const TopkArgs &a, unsigned grid, hipStream_t stream) {
+    if (a.k < 1 || a.k > (int64_t)SORT_MAXB * SORT_NT) return hipErrorInvalidValue;
     const void *fn = dtype == 0 ? reinterpret_cast<const void *>(&sort_rows_by_value<Bf16Key>)
                                 : reinterpret_cast<const void *>(&sort_rows_by_value<F32Key>);
     TopkArgs copy = a;
