@@ -2215,8 +2215,10 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
 //
 // The select leaves every row in ascending column order, so a stable sort on
 // the key alone orders equal keys by column.  The sort is least significant
-// digit first over 8-bit digits of the inverted key (2 passes for bf16 keys,
-// 4 for fp32), each pass stable:
+// digit first over 8-bit digits of kmax - key, kmax the row's largest
+// selected key, each pass stable; only the digits that span kmax - kmin
+// needs get a pass (the selected keys all lie at or above the k-th largest,
+// so the span is narrow: one pass for most bf16 rows, none for equal keys):
 //   * pair j of a pass sits in batch (w*B + b) of 64, wave w's batch b,
 //     lane j % 64, with B = ceil(c / 1024) batches per wave, so (w, b, lane)
 //     runs in pair order;
@@ -2252,7 +2254,8 @@ template <class K>
 __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) {
     using raw_t = typename K::raw_t;
     // LDS: k pair words (key << 32 | ~column), two arrays of 16-bit counters
-    // (a pass counts in one while the other is cleared), the wave totals
+    // (a pass counts in one while the other is cleared), the wave totals, the
+    // waves' smallest and largest keys
     extern __shared__ __attribute__((aligned(16))) uint64_t s_pair[];
     const int64_t row = a.row0 + blockIdx.x;
     if (row >= a.rows) return;
@@ -2260,26 +2263,44 @@ __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) 
     const int64_t n = valid_length(a, row);
     const uint32_t c = (uint32_t)(n < a.k ? n : a.k);
     if (c <= 1) return;
-    uint16_t *cnt_base = reinterpret_cast<uint16_t *>(s_pair + a.k);
+    // (the pair words rounded up to an even count: what follows is 16-byte aligned)
+    uint16_t *cnt_base = reinterpret_cast<uint16_t *>(s_pair + ((a.k + 1) & ~(int64_t)1));
     uint32_t *wtot = reinterpret_cast<uint32_t *>(cnt_base + 2 * SORT_CNT);
+    uint32_t *wmin = wtot + SORT_NW, *wmax = wmin + SORT_NW;
     const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
     const RowOut o = row_out<K>(a, row);
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0;
     for (uint32_t j = (uint32_t)t; j < c; j += SORT_NT) {
         const uint32_t col = o.idx64 ? (uint32_t)reinterpret_cast<const int64_t *>(o.idx)[j]
                                      : (uint32_t)reinterpret_cast<const int32_t *>(o.idx)[j];
         const uint32_t bits = o.val ? (uint32_t)reinterpret_cast<const raw_t *>(o.val)[j]
                                     : (uint32_t)xr[col];
-        s_pair[j] = ((uint64_t)key_of_bits<K>(bits) << 32) | (uint32_t)~col;
+        const uint32_t key = key_of_bits<K>(bits);
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+        s_pair[j] = ((uint64_t)key << 32) | (uint32_t)~col;
     }
     for (int i = t; i < SORT_CNT; i += SORT_NT) cnt_base[i] = 0;
-    __syncthreads();
-
     const uint32_t lane = (uint32_t)t & 63u, w = (uint32_t)t >> 6;
+    kmin = ~wave_max_u32(~kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) {
+        wmin[w] = kmin;
+        wmax[w] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < SORT_NW; ++v) {
+        kmin = min(kmin, wmin[v]);
+        kmax = max(kmax, wmax[v]);
+    }
+    const uint32_t span = kmax - kmin;
+    const int passes = span == 0 ? 0 : (32 - __builtin_clz(span) + 7) / 8;
+
     const uint32_t B = (c + SORT_NT - 1) / SORT_NT;
     const uint64_t below = (1ull << lane) - 1ull;
-    constexpr int PASSES = K::PACK ? 2 : 4;
 #pragma unroll 1
-    for (int pass = 0; pass < PASSES; ++pass) {
+    for (int pass = 0; pass < passes; ++pass) {
         uint16_t *cnt = cnt_base + (pass & 1) * SORT_CNT;
         uint16_t *nxt = cnt_base + ((pass + 1) & 1) * SORT_CNT;
         const int sh = 8 * pass;
@@ -2294,7 +2315,7 @@ __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) 
                 const uint32_t j = ((w * B + (uint32_t)b) << 6) + lane;
                 const bool valid = j < c;
                 const uint64_t e = valid ? s_pair[j] : 0ull;
-                const uint32_t d = (~(uint32_t)(e >> 32) >> sh) & 0xFFu;
+                const uint32_t d = ((kmax - (uint32_t)(e >> 32)) >> sh) & 0xFFu;
                 uint64_t peers = __ballot(valid);
 #pragma unroll
                 for (int bit = 0; bit < 8; ++bit) {
@@ -2317,17 +2338,17 @@ __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) 
         const uint2 q = reinterpret_cast<const uint2 *>(cnt)[t];
         const uint32_t c0 = q.x & 0xFFFFu, c1 = q.x >> 16, c2 = q.y & 0xFFFFu, c3 = q.y >> 16;
         const uint32_t sum = c0 + c1 + c2 + c3;
-        uint32_t inc = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t v = __shfl_up(inc, off, 64);
-            if (lane >= (uint32_t)off) inc += v;
-        }
+        const uint32_t inc = wave_incl_scan(sum);
         if (lane == 63) wtot[w] = inc;
         for (int i = t; i < SORT_CNT; i += SORT_NT) nxt[i] = 0;  // the next pass's counters
         __syncthreads();
         uint32_t pre = inc - sum;
-        for (uint32_t v = 0; v < w; ++v) pre += wtot[v];
+#pragma unroll
+        for (int v = 0; v < SORT_NW; v += 4) {
+            const uint4 q4 = *reinterpret_cast<const uint4 *>(wtot + v);
+            pre += ((uint32_t)v < w ? q4.x : 0u) + ((uint32_t)v + 1 < w ? q4.y : 0u) +
+                   ((uint32_t)v + 2 < w ? q4.z : 0u) + ((uint32_t)v + 3 < w ? q4.w : 0u);
+        }
         const uint32_t p1 = pre + c0, p2 = p1 + c1, p3 = p2 + c2;
         reinterpret_cast<uint2 *>(cnt)[t] = make_uint2(pre | (p1 << 16), p2 | (p3 << 16));
         __syncthreads();
@@ -2417,10 +2438,11 @@ hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned
                            stream);
 }
 
-// LDS bytes of a value-order launch: k pair words, two arrays of 16-bit
-// counters, the wave totals.
+// LDS bytes of a value-order launch: k pair words (rounded up to even), two
+// arrays of 16-bit counters, the wave totals, minima and maxima.
 static size_t value_sort_lds(int64_t k) {
-    return (size_t)k * sizeof(uint64_t) + 2 * SORT_CNT * sizeof(uint16_t) + SORT_NW * sizeof(uint32_t);
+    return (size_t)((k + 1) & ~(int64_t)1) * sizeof(uint64_t) + 2 * SORT_CNT * sizeof(uint16_t) +
+           3 * SORT_NW * sizeof(uint32_t);
 }
 
 hipError_t launch_value_sort(int dtype, const TopkArgs &a, unsigned grid, hipStream_t stream) {
