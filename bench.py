@@ -10,7 +10,7 @@ over one batch.  ``per_config`` adds the same measurement for the five named
 workloads (top-k and, where they have one, the gather), and for two of them
 (the 4 x 204800 headline and the 128 x 129280 sampling rows) the top-k with
 the selection ordered by value (``topk_by_value``: the select, then the
-bitonic value-order pass).
+radix value-order sort).
 
 Timing protocol
   * inputs are generated on the host from fixed seeds and copied to HBM

@@ -74,7 +74,7 @@ int dsel_stride_requirement(int64_t *in_align_bytes, int64_t *out_align_bytes);
  * c selected entries by value instead: largest first, equal values by
  * ascending column, NaN above every value, -0 equal to +0 (the tutorial's
  * end-bound example and its tip on ordering "by index or by value"); a
- * bitonic pass in LDS runs after the select, so this order costs time.
+ * radix sort in LDS runs after the select, so this order costs time.
  *
  * x             [rows, cols] bf16 or f32 (`dtype`), last dim contiguous,
  *               row stride `x_row_stride` elements (>= cols).

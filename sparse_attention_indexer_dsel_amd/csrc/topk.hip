@@ -49,8 +49,8 @@
 //     radix select finishes over the range re-read from cache (slower, same
 //     result);
 //   * value order (sorted_index 2) is a separate pass after the select: one
-//     workgroup per row sorts its (key, column) pairs with a bitonic network
-//     in LDS, largest value first, equal values by ascending column.
+//     workgroup per row sorts its (key, column) pairs with a stable radix
+//     sort in LDS, largest value first, equal values by ascending column.
 #include "dsel_internal.h"
 
 namespace dsel {
@@ -2226,8 +2226,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
 //     and keeps per-(digit, wave) running counts in LDS;
 //   * one exclusive scan of the counts in digit-major order gives every
 //     (digit, wave) its first slot; each pair goes to that slot plus its rank.
-// Four workgroup barriers per pass, against one per step of a bitonic network
-// (78 steps for 4096 pairs) that were each an LDS round trip.
+// Four workgroup barriers per pass; a bitonic network over 4096 pairs takes
+// 78 steps, each a dependent LDS round trip.
 // ---------------------------------------------------------------------------
 
 // Order-preserving key of one value's bits (NaN on top, -0 with +0), the
