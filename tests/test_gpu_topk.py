@@ -383,6 +383,42 @@ def test_value_order_paths(dsel, orc, dt):
     check_value_order(dsel, orc, f"wave/{dt}", xs, 333, None, torch.int32, False)
 
 
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_value_order_key_spans(dsel, orc, dt):
+    """Value order where the selected keys span nothing (all equal), one
+    8-bit digit, just over one, several digits, the whole finite range and,
+    with a NaN among them, the whole key range: the sort runs as many digit
+    passes as the span needs, and equal keys stay in column order."""
+    rng = np.random.default_rng(0x5A17)
+    cols, k = 3072, 1000
+    if dt == W.BF16:
+        base, low, nan = 0x3F80, 0xBF80, 0x7FC0
+        spans = [0, 1, 255, 256, 257, 511, 512, 0x3FFF]
+    else:
+        base, low, nan = 0x3F800000, 0xBF800000, 0x7FC00000
+        spans = [0, 1, 255, 256, 65535, 65536, (1 << 24) - 1, 1 << 24, 0x3FFFFFFF]
+    rows = []
+    for span in spans:
+        r = np.full(cols, low, dtype=np.int64)
+        top = base + rng.integers(0, span + 1, size=k)
+        top[0], top[-1] = base, base + span
+        r[rng.permutation(cols)[:k]] = top
+        rows.append(r)
+    r = rows[-1].copy()
+    r[int(np.flatnonzero(r != low)[7])] = nan
+    rows.append(r)
+    arr = np.stack(rows)
+    if dt == W.BF16:
+        x = torch.from_numpy(arr.astype(np.uint16).view(np.int16)).view(torch.bfloat16)
+    else:
+        x = torch.from_numpy(arr.astype(np.uint32).view(np.int32)).view(torch.float32)
+    for ret, itype in ((True, torch.int32), (False, torch.int64)):
+        check_value_order(dsel, orc, f"spans/{dt}/val{int(ret)}", x, k, None, itype, ret)
+        check_value_order(dsel, orc, f"spans/{dt}/val{int(ret)}/short", x, k,
+                          torch.tensor([3072, 999, 1000, 2, 1, 0, 1500, 3000, 2048, 17][:len(rows)],
+                                       dtype=torch.int32), itype, ret)
+
+
 @pytest.mark.parametrize("cfg", [2, 4])
 def test_value_order_workloads(dsel, orc, cfg):
     """The 4 x 204800 bf16 and 128 x 129280 fp32 (sampling) workloads ordered by value."""
