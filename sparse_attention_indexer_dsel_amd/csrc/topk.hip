@@ -2215,15 +2215,17 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
 //
 // The select leaves every row in ascending column order, so a stable sort on
 // the key alone orders equal keys by column.  The sort is least significant
-// digit first over 8-bit digits of kmax - key, kmax the row's largest
+// digit first over 9-bit digits of kmax - key, kmax the row's largest
 // selected key, each pass stable; only the digits that span kmax - kmin
 // needs get a pass (the selected keys all lie at or above the k-th largest,
 // so the span is narrow: one pass for most bf16 rows, none for equal keys):
 //   * pair j of a pass sits in batch (w*B + b) of 64, wave w's batch b,
 //     lane j % 64, with B = ceil(c / 1024) batches per wave, so (w, b, lane)
 //     runs in pair order;
-//   * a wave ranks each batch's lanes among equal digits with eight ballots
-//     and keeps per-(digit, wave) running counts in LDS;
+//   * a wave ranks each batch's lanes among equal digits with nine ballots
+//     and keeps per-(digit, wave) running counts in 16-bit LDS counters,
+//     bit 15 marking a count of this pass (the scan rewrites every counter
+//     as a prefix with the bit clear, so no pass clears them);
 //   * one exclusive scan of the counts in digit-major order gives every
 //     (digit, wave) its first slot; each pair goes to that slot plus its rank.
 // Four workgroup barriers per pass; a bitonic network over 4096 pairs takes
@@ -2247,15 +2249,15 @@ __device__ __forceinline__ uint32_t key_of_bits(uint32_t bits) {
 
 constexpr int SORT_NT = 1024;               // threads of a value-order workgroup
 constexpr int SORT_NW = SORT_NT / 64;       // its waves
-constexpr int SORT_CNT = 256 * SORT_NW;     // (digit, wave) counters, digit-major
+constexpr int SORT_DB = 9;                  // digit bits
+constexpr int SORT_CNT = (1 << SORT_DB) * SORT_NW;  // (digit, wave) counters, digit-major
 constexpr int SORT_MAXB = 4;                // batches per wave: k <= 4096
 
 template <class K>
 __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) {
     using raw_t = typename K::raw_t;
-    // LDS: k pair words (key << 32 | ~column), two arrays of 16-bit counters
-    // (a pass counts in one while the other is cleared), the wave totals, the
-    // waves' smallest and largest keys
+    // LDS: k pair words (key << 32 | ~column), the 16-bit counters, the wave
+    // totals, the waves' smallest and largest keys
     extern __shared__ __attribute__((aligned(16))) uint64_t s_pair[];
     const int64_t row = a.row0 + blockIdx.x;
     if (row >= a.rows) return;
@@ -2265,7 +2267,8 @@ __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) 
     if (c <= 1) return;
     // (the pair words rounded up to an even count: what follows is 16-byte aligned)
     uint16_t *cnt_base = reinterpret_cast<uint16_t *>(s_pair + ((a.k + 1) & ~(int64_t)1));
-    uint32_t *wtot = reinterpret_cast<uint32_t *>(cnt_base + 2 * SORT_CNT);
+    uint16_t *cnt = cnt_base;
+    uint32_t *wtot = reinterpret_cast<uint32_t *>(cnt_base + SORT_CNT);
     uint32_t *wmin = wtot + SORT_NW, *wmax = wmin + SORT_NW;
     const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
     const RowOut o = row_out<K>(a, row);
@@ -2295,15 +2298,13 @@ __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) 
         kmax = max(kmax, wmax[v]);
     }
     const uint32_t span = kmax - kmin;
-    const int passes = span == 0 ? 0 : (32 - __builtin_clz(span) + 7) / 8;
+    const int passes = span == 0 ? 0 : (32 - __builtin_clz(span) + SORT_DB - 1) / SORT_DB;
 
     const uint32_t B = (c + SORT_NT - 1) / SORT_NT;
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll 1
     for (int pass = 0; pass < passes; ++pass) {
-        uint16_t *cnt = cnt_base + (pass & 1) * SORT_CNT;
-        uint16_t *nxt = cnt_base + ((pass + 1) & 1) * SORT_CNT;
-        const int sh = 8 * pass;
+        const int sh = SORT_DB * pass;
         uint64_t el[SORT_MAXB];
         uint32_t dg[SORT_MAXB], rk[SORT_MAXB];
 #pragma unroll
@@ -2315,18 +2316,22 @@ __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) 
                 const uint32_t j = ((w * B + (uint32_t)b) << 6) + lane;
                 const bool valid = j < c;
                 const uint64_t e = valid ? s_pair[j] : 0ull;
-                const uint32_t d = ((kmax - (uint32_t)(e >> 32)) >> sh) & 0xFFu;
+                const uint32_t d = ((kmax - (uint32_t)(e >> 32)) >> sh) & ((1u << SORT_DB) - 1u);
                 uint64_t peers = __ballot(valid);
 #pragma unroll
-                for (int bit = 0; bit < 8; ++bit) {
+                for (int bit = 0; bit < SORT_DB; ++bit) {
                     const uint64_t m = __ballot((d >> bit) & 1u);
                     peers &= ((d >> bit) & 1u) ? m : ~m;
                 }
                 uint32_t base = 0;
-                if (valid) base = cnt[d * SORT_NW + w];
+                if (valid) {
+                    const uint32_t raw = cnt[d * SORT_NW + w];
+                    base = (raw & 0x8000u) ? (raw & 0x7FFFu) : 0u;  // counted this pass, else 0
+                }
                 wave_sync();  // every lane has read the count before its leader adds
                 if (valid && (uint32_t)__builtin_ctzll(peers) == lane)
-                    cnt[d * SORT_NW + w] = (uint16_t)(base + (uint32_t)__builtin_popcountll(peers));
+                    cnt[d * SORT_NW + w] =
+                        (uint16_t)(0x8000u | (base + (uint32_t)__builtin_popcountll(peers)));
                 wave_sync();
                 el[b] = e;
                 dg[b] = d;
@@ -2334,13 +2339,23 @@ __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) 
             }
         }
         __syncthreads();
-        // exclusive scan of the counters, four per thread
-        const uint2 q = reinterpret_cast<const uint2 *>(cnt)[t];
-        const uint32_t c0 = q.x & 0xFFFFu, c1 = q.x >> 16, c2 = q.y & 0xFFFFu, c3 = q.y >> 16;
-        const uint32_t sum = c0 + c1 + c2 + c3;
+        // exclusive scan of the counters, eight per thread
+        static_assert(SORT_CNT == 8 * SORT_NT, "eight counters per thread");
+        const uint4 q = reinterpret_cast<const uint4 *>(cnt)[t];
+        uint32_t cv[8];
+        {
+            const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t raw = (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                cv[i] = (raw & 0x8000u) ? (raw & 0x7FFFu) : 0u;
+            }
+        }
+        uint32_t sum = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sum += cv[i];
         const uint32_t inc = wave_incl_scan(sum);
         if (lane == 63) wtot[w] = inc;
-        for (int i = t; i < SORT_CNT; i += SORT_NT) nxt[i] = 0;  // the next pass's counters
         __syncthreads();
         uint32_t pre = inc - sum;
 #pragma unroll
@@ -2349,8 +2364,14 @@ __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) 
             pre += ((uint32_t)v < w ? q4.x : 0u) + ((uint32_t)v + 1 < w ? q4.y : 0u) +
                    ((uint32_t)v + 2 < w ? q4.z : 0u) + ((uint32_t)v + 3 < w ? q4.w : 0u);
         }
-        const uint32_t p1 = pre + c0, p2 = p1 + c1, p3 = p2 + c2;
-        reinterpret_cast<uint2 *>(cnt)[t] = make_uint2(pre | (p1 << 16), p2 | (p3 << 16));
+        uint32_t pw[4];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            const uint32_t lo = pre, hi = pre + cv[i];
+            pw[i >> 1] = lo | (hi << 16);
+            pre = hi + cv[i + 1];
+        }
+        reinterpret_cast<uint4 *>(cnt)[t] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < SORT_MAXB; ++b) {
@@ -2438,10 +2459,10 @@ hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned
                            stream);
 }
 
-// LDS bytes of a value-order launch: k pair words (rounded up to even), two
-// arrays of 16-bit counters, the wave totals, minima and maxima.
+// LDS bytes of a value-order launch: k pair words (rounded up to even), the
+// 16-bit counters, the wave totals, minima and maxima.
 static size_t value_sort_lds(int64_t k) {
-    return (size_t)((k + 1) & ~(int64_t)1) * sizeof(uint64_t) + 2 * SORT_CNT * sizeof(uint16_t) +
+    return (size_t)((k + 1) & ~(int64_t)1) * sizeof(uint64_t) + SORT_CNT * sizeof(uint16_t) +
            3 * SORT_NW * sizeof(uint32_t);
 }
 
