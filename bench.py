@@ -10,7 +10,8 @@ over one batch.  ``per_config`` adds the same measurement for the five named
 workloads (top-k and, where they have one, the gather), and for two of them
 (the 4 x 204800 headline and the 128 x 129280 sampling rows) the top-k with
 the selection ordered by value (``topk_by_value``: the select, then the
-radix value-order sort).
+radix value-order sort).  The causal prefill rows are also timed with values
+returned (``topk_with_values``).
 
 Timing protocol
   * inputs are generated on the host from fixed seeds and copied to HBM
@@ -47,6 +48,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import hashlib
 import json
 import os
@@ -69,6 +71,10 @@ METRIC = "top-k rows/s and achieved HBM GB/s (% of peak) per config; gather GB/s
 # workloads also timed with the selection ordered by value (the sampling
 # workload, where that order is the natural one, and the headline)
 VALUE_ORDER_CONFIGS = (2, 4)
+# index-only workloads also timed with values returned (the causal prefill
+# rows: half of them are shorter than k, so this times the short-row value
+# copy)
+WITH_VALUES_CONFIGS = (3,)
 
 
 def output_convention_gbps(out_bytes: float, seconds: float) -> float:
@@ -459,6 +465,9 @@ def main(argv=None):
             entry = {"topk": measure_topk(dsel, torch, c, stream, 20, 3)}
             if i in VALUE_ORDER_CONFIGS:
                 entry["topk_by_value"] = measure_topk(dsel, torch, c, stream, 20, 3, by_value=True)
+            if i in WITH_VALUES_CONFIGS and not c.return_value:
+                entry["topk_with_values"] = measure_topk(
+                    dsel, torch, dataclasses.replace(c, return_value=True), stream, 20, 3)
             if c.keys:
                 entry["gather"] = measure_gather(dsel, torch, c, stream, 10, 2)
             per[c.name] = entry
