@@ -44,6 +44,7 @@ struct TopkPlan {
     int64_t slot0 = 0;
     size_t ws_bytes = 0;
     bool one = false;  // split bf16 rows try the one-exchange select
+    int per_cu = 0;    // one-wave rows: resident workgroups per CU the grid assumes
 };
 
 // Candidate-list capacity: k plus room for the boundary bin of the first
@@ -131,6 +132,7 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
                 topk_dyn_lds(dtype, 0, pl->ept, kTopkWave)) != hipSuccess ||
             per_cu <= 0)
             return DSEL_ERR_DEVICE;
+        pl->per_cu = per_cu;
         const int64_t slots = (int64_t)per_cu * cus;
         const int64_t wgs = cdiv(rows, kTopkThreads / 64);
         pl->rows_per_launch = rows;
@@ -293,6 +295,10 @@ extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols
     a.one = pl.one ? 1 : 0;
     a.idx_fill = idx_fill;
     a.val_fill = val_fill_bits;
+    // (only the values instance of the one-wave kernel reads a separate stage)
+    a.stage_words = pl.kind == kTopkWave && a.ret_val
+                        ? wave_stage_words(dtype, k, a.idx64 ? 8 : 4, a.ret_val, pl.per_cu)
+                        : 0u;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     for (int64_t r0 = 0; r0 < rows; r0 += pl.rows_per_launch) {
         const int64_t nr = (rows - r0) < pl.rows_per_launch ? (rows - r0) : pl.rows_per_launch;

@@ -84,6 +84,8 @@ struct TopkArgs {
     int one;                 // split bf16 rows: try the one-exchange select first
     int64_t idx_fill;        // index of the slots past a short row's length
     uint32_t val_fill;       // value bits of those slots
+    uint32_t stage_words;    // one-wave rows: LDS words per wave for the staged output
+                             // after the histograms (0: staged in the histogram's space)
 };
 
 // Top-k kernel kinds: one workgroup per row, G workgroups per row, one wave
@@ -98,8 +100,15 @@ constexpr int64_t kWaveCapacity = 64 * 32;
 const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val = 0);
 // Elements per 16-byte vector for a dtype.
 inline int topk_vec(int dtype) { return dtype == 0 ? 8 : 4; }
-// Dynamic LDS bytes of a top-k launch with candidate capacity `cap`.
+// Dynamic LDS bytes of a top-k launch with candidate capacity `cap` (for
+// one-wave rows: with each wave's histogram only).
 size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind);
+// One-wave rows: LDS words of a wave's histogram, and the LDS words per wave
+// of a separate stage for the row's output (k indices of idx_bytes each, and
+// k values when ret_val) when it does not fit the histogram's space and
+// `per_cu` workgroups with it still fit a compute unit; else 0.
+uint32_t wave_hist_words(int dtype);
+uint32_t wave_stage_words(int dtype, int64_t k, int idx_bytes, int ret_val, int per_cu);
 hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned grid,
                        hipStream_t stream);
 // Value order of the top-k outputs of rows [a.row0, a.row0 + grid), in place.

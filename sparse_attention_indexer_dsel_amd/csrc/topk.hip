@@ -2115,6 +2115,17 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
     // output descriptors are then scalar, not per-lane values
     const int lane = tid() & 63, wid = __builtin_amdgcn_readfirstlane(tid() >> 6);
     uint32_t *hist = s_dyn + wid * wave_lds_words<K>();
+    // the row's output is staged in the histogram's space, or, when a launch
+    // that returns values gives one, in a region of its own after the
+    // histograms (the index-only instance keeps every LDS offset constant)
+    char *stage = reinterpret_cast<char *>(hist);
+    uint32_t stage_cap = wave_lds_words<K>() * 4u;
+    if constexpr (RV) {
+        if (a.stage_words) {
+            stage = reinterpret_cast<char *>(s_dyn + NWAVE * wave_lds_words<K>() + wid * a.stage_words);
+            stage_cap = a.stage_words * 4u;
+        }
+    }
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
     const int64_t step = (int64_t)gridDim.x * NWAVE;
 
@@ -2193,9 +2204,9 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
         // (equal << 16 | above) counts gives each lane its ranks.  Values come
         // from the keys, so the stores wait for no load; +-0 / NaN keys get
         // their bits from the row in a second pass, run only if one was taken.
-        if (stage_bytes<K>(a) <= wave_lds_words<K>() * 4u) {
-            wave_sync();  // the histogram is dead: its space holds the row's slots
-            wave_write_staged<K, LPL>(a, row, kw, len, b, lane, xr, reinterpret_cast<char *>(hist));
+        if (stage_bytes<K>(a) <= stage_cap) {
+            wave_sync();  // the histogram is dead: its space may hold the row's slots
+            wave_write_staged<K, LPL>(a, row, kw, len, b, lane, xr, stage);
         } else {
             const RowViews o = row_views<K>(a, row);
             uint32_t amb = 0;
@@ -2449,14 +2460,31 @@ size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind) {
     return (size_t)(words > hist ? words : hist) * 4;
 }
 
+uint32_t wave_hist_words(int dtype) {
+    return dtype == 0 ? wave_lds_words<Bf16Key>() : wave_lds_words<F32Key>();
+}
+
+uint32_t wave_stage_words(int dtype, int64_t k, int idx_bytes, int ret_val, int per_cu) {
+    constexpr uint64_t kLdsPerCu = 160u * 1024u, kLdsPerWg = 64u * 1024u;
+    const uint32_t base = wave_hist_words(dtype);
+    const uint64_t stage = (((uint64_t)k * (uint64_t)idx_bytes + 15u) & ~(uint64_t)15u) +
+                           (ret_val ? (uint64_t)k * (dtype == 0 ? 2u : 4u) : 0u);
+    const uint64_t words = (stage + 15u) / 16u * 4u;  // whole 16-byte units: every stage stays aligned
+    if (words <= base) return 0;  // fits the histogram's space
+    const uint64_t wg = (uint64_t)NWAVE * (base + words) * 4u;
+    if (wg > kLdsPerWg || (uint64_t)(per_cu > 0 ? per_cu : 1) * wg > kLdsPerCu) return 0;
+    return (uint32_t)words;
+}
+
 hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned grid,
                        hipStream_t stream) {
     const void *fn = topk_kernel_ptr(dtype, ept, kind, a.ret_val);
     if (!fn) return hipErrorInvalidValue;
     TopkArgs copy = a;
+    size_t lds = topk_dyn_lds(dtype, a.cap, ept, kind);
+    if (kind == kTopkWave) lds = (size_t)NWAVE * (wave_hist_words(dtype) + copy.stage_words) * 4u;
     void *args[] = {&copy};
-    return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, topk_dyn_lds(dtype, a.cap, ept, kind),
-                           stream);
+    return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, lds, stream);
 }
 
 // LDS bytes of a value-order launch: k pair words (rounded up to even), the
