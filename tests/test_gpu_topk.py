@@ -427,6 +427,27 @@ def test_value_order_workloads(dsel, orc, cfg):
                       case.indices_type, case.return_value)
 
 
+@pytest.mark.parametrize("cols", [2048, 1536])
+def test_wave_rows_with_values_staged(dsel, orc, cols):
+    """One-wave bf16 rows with values whose k int32 indices and k values do
+    not fit a wave's histogram space (k > 725), so the values launch stages
+    them in an LDS region of its own: k not a multiple of 4 or 8, rows
+    longer and shorter than k, NaN rows, +-0 and infinities; ascending and
+    value order; int64 indices (whose stage does not fit) as a control."""
+    x = W.random_rows(0x57A6 + cols, 24, cols, W.BF16, "special")
+    W.plant_nans(x, 0x57A7 + cols, 3)
+    ends = [cols, cols - 1, cols - 7, 2000, 1800, 1500, 1200, 1100, 1025, 1024, 1023, 1001,
+            1000, 900, 727, 726, 725, 600, 100, 3, 1, 0, cols, cols - 33]
+    re = torch.tensor([min(e, cols) for e in ends], dtype=torch.int32)
+    for k in (726, 1001, 1024, 1500, 2000):
+        if k >= cols:
+            continue
+        check_case(dsel, orc, f"staged/{cols}/k{k}", x, k, re, False, torch.int32, True)
+        check_case(dsel, orc, f"staged/{cols}/k{k}/sorted", x, k, re, True, torch.int32, True)
+        check_value_order(dsel, orc, f"staged/{cols}/k{k}/by_value", x, k, re, torch.int32, True)
+    check_case(dsel, orc, f"staged/{cols}/k1001/i64", x, 1001, re, False, torch.int64, True)
+
+
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
 def test_custom_fills(dsel, orc, dt):
     """idx_oob_fill_value / value_oob_fill_value on short rows of every select
