@@ -28,7 +28,8 @@ enum {
     DSEL_ERR_K = -2,          /* k outside [1, 4096] */
     DSEL_ERR_ALIGN = -3,      /* pointer or row stride not a multiple of the alignment */
     DSEL_ERR_WORKSPACE = -4,  /* workspace smaller than the size query returned */
-    DSEL_ERR_DEVICE = -5      /* no usable device, or a launch failed */
+    DSEL_ERR_DEVICE = -5,     /* no usable device, or a launch failed */
+    DSEL_ERR_SPLIT = -6       /* dsel_topk_check: a split row's workgroups did not all meet */
 };
 
 enum { DSEL_BF16 = 0, DSEL_F32 = 1 };  /* value dtype (bf16 = upper half of binary32) */
@@ -95,10 +96,11 @@ int dsel_stride_requirement(int64_t *in_align_bytes, int64_t *out_align_bytes);
  *               size provided (DSEL_ERR_WORKSPACE if smaller than the query).
  *               The workspace must be zero-filled before its first use; every
  *               call leaves it zero-filled again, except (a) word 0, which
- *               holds sticky error bits (bit 0: a split-row rendezvous timed
- *               out), and (b) the exchange region that follows the 64-word
- *               header, 8 * (compute units) * 544 words, which holds scratch
- *               that every call writes before it reads it.
+ *               holds sticky error bits (bit 0: a split-row rendezvous gave
+ *               up; see dsel_topk_check, which reports and clears them), and
+ *               (b) the exchange region that follows the 64-word header,
+ *               8 * (compute units) * 544 words, which holds scratch that
+ *               every call writes before it reads it.
  *               Calls that share one workspace must be stream-ordered.
  * rows == 0 launches nothing and returns DSEL_OK.
  */
@@ -129,6 +131,27 @@ int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x
                  uint8_t *nan_flag,
                  void *workspace, size_t *workspace_bytes,
                  void *stream, int64_t idx_fill, uint32_t val_fill_bits);
+
+/*
+ * Error state of split rows on a workspace, and its reset.
+ *
+ * A row longer than one workgroup holds (16384 columns) is split over
+ * several workgroups that meet at rendezvous points in the workspace; the
+ * launch never asks for more workgroups than the GPU holds at once, but
+ * work from other streams or processes can keep some of them from starting.
+ * Every wait is bounded (about 0.1 s): a workgroup that gives up sets bit 0
+ * (1) of workspace word 0 and finishes, so the kernel always ends, but that
+ * call's split rows hold undefined output and the workspace is left in an
+ * undefined state.  dsel_topk_check reports and clears that state.
+ *
+ * workspace, workspace_bytes: the workspace and size given to dsel_topk.
+ * stream:     the stream of those calls; the call SYNCHRONISES it.
+ * error_bits: host pointer; receives word 0 (0 when no error).
+ * Returns DSEL_OK when no rendezvous gave up since the last check.  Else it
+ * zero-fills the whole workspace (so it is ready for the next call), writes
+ * the bits and returns DSEL_ERR_SPLIT.  NULL workspace: DSEL_OK.
+ */
+int dsel_topk_check(void *workspace, size_t workspace_bytes, void *stream, uint32_t *error_bits);
 
 /*
  * Gather of key rows at selected positions, batch offset folded in.

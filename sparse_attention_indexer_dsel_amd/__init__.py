@@ -23,16 +23,18 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["stride_requirement", "topk", "gather_rows", "DselError", "LIB_PATH"]
+__all__ = ["stride_requirement", "topk", "gather_rows", "check_workspaces", "DselError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsel.so")
 
-DSEL_OK, DSEL_ERR_ARG, DSEL_ERR_K, DSEL_ERR_ALIGN, DSEL_ERR_WORKSPACE, DSEL_ERR_DEVICE = \
-    0, -1, -2, -3, -4, -5
+DSEL_OK, DSEL_ERR_ARG, DSEL_ERR_K, DSEL_ERR_ALIGN, DSEL_ERR_WORKSPACE, DSEL_ERR_DEVICE, \
+    DSEL_ERR_SPLIT = 0, -1, -2, -3, -4, -5, -6
 DSEL_BF16, DSEL_F32 = 0, 1
 DSEL_I32, DSEL_I64 = 0, 1
 _NAMES = {DSEL_ERR_ARG: "DSEL_ERR_ARG", DSEL_ERR_K: "DSEL_ERR_K", DSEL_ERR_ALIGN: "DSEL_ERR_ALIGN",
-          DSEL_ERR_WORKSPACE: "DSEL_ERR_WORKSPACE", DSEL_ERR_DEVICE: "DSEL_ERR_DEVICE"}
+          DSEL_ERR_WORKSPACE: "DSEL_ERR_WORKSPACE", DSEL_ERR_DEVICE: "DSEL_ERR_DEVICE",
+          DSEL_ERR_SPLIT: "DSEL_ERR_SPLIT (a split row's workgroups did not all meet; "
+                          "its output is undefined and the workspace was reset)"}
 
 
 class DselError(RuntimeError):
@@ -55,6 +57,8 @@ def _load() -> ctypes.CDLL:
     lib.dsel_topk_ex.restype = i32
     lib.dsel_topk_ex.argtypes = [vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, i64, vp,
                                  i64, vp, vp, szp, vp, i64, ctypes.c_uint32]
+    lib.dsel_topk_check.restype = i32
+    lib.dsel_topk_check.argtypes = [vp, ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_uint32)]
     lib.dsel_gather_rows.restype = i32
     lib.dsel_gather_rows.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i32, i64, i64, i64,
                                      vp, vp]
@@ -92,11 +96,6 @@ def _index_code(dt: torch.dtype) -> int:
     raise TypeError(f"unsupported index dtype {dt} (int32 or int64)")
 
 
-def _stream_ptr(device: torch.device, stream) -> int:
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return int(s.cuda_stream)
-
-
 def _aligned_empty(rows: int, k: int, dtype: torch.dtype, device) -> torch.Tensor:
     """[rows, k] view of a buffer whose row stride is aligned to the output alignment."""
     _, out_align = stride_requirement()
@@ -105,18 +104,41 @@ def _aligned_empty(rows: int, k: int, dtype: torch.dtype, device) -> torch.Tenso
     return torch.empty(rows, stride, dtype=dtype, device=device)[:, :k]
 
 
+# Zero-initialised scratch per (device, stream), for split rows; the library
+# leaves it zeroed after every call.  A bigger one replaces it when a call
+# needs more, but every buffer ever handed out stays alive in _RETIRED: a
+# HIP graph captured with an older one keeps using its address on replay.
 _WORKSPACES = {}
+_RETIRED = []
 
 
 def _workspace(device: torch.device, stream_ptr: int, nbytes: int) -> torch.Tensor:
-    """Zero-initialised scratch kept per (device, stream); the library leaves it zeroed."""
+    """The (device, stream)'s workspace of at least nbytes, zero-filled on
+    the current stream (the caller makes that the stream the kernels run on)."""
     key = (device.index, stream_ptr)
     ws = _WORKSPACES.get(key)
     need = max(int(nbytes), 256)
     if ws is None or ws.numel() < need:
+        if ws is not None:
+            _RETIRED.append(ws)
         ws = torch.zeros(need, dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
+
+
+def check_workspaces() -> None:
+    """Raise DselError(DSEL_ERR_SPLIT) if a split-row rendezvous gave up on any
+    workspace since the last check (that call's split rows hold undefined
+    output; the workspace is reset).  Synchronises each workspace's stream."""
+    for (dev, sptr), ws in list(_WORKSPACES.items()):
+        _check_one(ws, sptr)
+
+
+def _check_one(ws: torch.Tensor, sptr: int) -> None:
+    bits = ctypes.c_uint32(0)
+    with torch.cuda.device(ws.device):
+        _check(_lib.dsel_topk_check(ws.data_ptr(), ws.numel(), sptr, ctypes.byref(bits)),
+               f"dsel_topk (error bits {bits.value:#x})")
 
 
 def _row_stride(t: torch.Tensor) -> int:
@@ -162,7 +184,7 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
          indices_type: torch.dtype = torch.int32, return_value: bool = True,
          output_idx: Optional[torch.Tensor] = None, by_value: bool = False,
          idx_oob_fill_value: int = -1, value_oob_fill_value: Optional[float] = None,
-         abort_when_nan_found: bool = False, stream=None
+         abort_when_nan_found: bool = False, check: bool = False, stream=None
          ) -> Tuple[Optional[torch.Tensor], torch.Tensor, torch.Tensor]:
     """Row-wise top-k of ``x`` [rows, cols] (bf16 or fp32), 1 <= topk <= 4096.
 
@@ -180,6 +202,12 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
     short row's length.  ``abort_when_nan_found=True`` raises
     FloatingPointError when a row longer than ``topk`` holds a NaN (this
     waits for the call to finish); by default the flag is only returned.
+    ``check=True`` waits for the call and raises DselError (DSEL_ERR_SPLIT)
+    if the workgroups of a split row (rows over 16384 columns) could not all
+    run at once, so that its output is undefined; see ``check_workspaces``.
+    With ``stream`` given, the outputs and workspace are allocated and zeroed
+    on that stream and the kernels run there; ordering against other streams
+    (the producer of ``x``, the consumers of the outputs) is the caller's.
     """
     _check_input(x)
     if sorted is not None:
@@ -198,22 +226,26 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
             raise ValueError("output_idx must be [rows, >= topk]")
         if output_idx.shape[1] > 1 and output_idx.stride(1) != 1:
             raise ValueError("output_idx's last dim must be contiguous")
-        idx = output_idx
-    else:
-        idx = _aligned_empty(rows, topk, indices_type, dev)
-    val = _aligned_empty(rows, topk, x.dtype, dev) if return_value else None
-    flag = torch.empty(rows, dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        sptr = _stream_ptr(dev, stream)
-        nb = ctypes.c_size_t(0)
-        _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
-                          None, nb, sptr, idx_oob_fill_value, value_oob_fill_value),
-               "dsel_topk (size query)")
-        ws = _workspace(dev, sptr, nb.value)
-        nb = ctypes.c_size_t(ws.numel())
-        _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
-                          ws.data_ptr(), nb, sptr, idx_oob_fill_value, value_oob_fill_value),
-               "dsel_topk")
+        s = torch.cuda.current_stream(dev) if stream is None else stream
+        with torch.cuda.stream(s):
+            # allocated (and the workspace zeroed) on the stream the kernels run on
+            idx = output_idx if output_idx is not None else _aligned_empty(rows, topk,
+                                                                          indices_type, dev)
+            val = _aligned_empty(rows, topk, x.dtype, dev) if return_value else None
+            flag = torch.empty(rows, dtype=torch.uint8, device=dev)
+            sptr = int(s.cuda_stream)
+            nb = ctypes.c_size_t(0)
+            _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
+                              None, nb, sptr, idx_oob_fill_value, value_oob_fill_value),
+                   "dsel_topk (size query)")
+            ws = _workspace(dev, sptr, nb.value)
+            nb = ctypes.c_size_t(ws.numel())
+            _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
+                              ws.data_ptr(), nb, sptr, idx_oob_fill_value, value_oob_fill_value),
+                   "dsel_topk")
+            if check:
+                _check_one(ws, sptr)
     if output_idx is not None:
         idx = output_idx[:, :topk]
     if abort_when_nan_found and bool(flag.any()):
@@ -246,12 +278,15 @@ def gather_rows(key: torch.Tensor, pos: torch.Tensor, *, out: Optional[torch.Ten
         raise ValueError("pos batch stride must equal R * row stride")
     if key.device != pos.device or not key.is_cuda:
         raise ValueError("key and pos must be GPU tensors on one device")
-    if out is None:
-        out = torch.empty(B, R, P, D, dtype=key.dtype, device=key.device)
-    elif out.shape != (B, R, P, D) or not out.is_contiguous() or out.dtype != key.dtype:
+    if out is not None and (out.shape != (B, R, P, D) or not out.is_contiguous()
+                            or out.dtype != key.dtype):
         raise ValueError("out must be a contiguous [B, R, P, D] tensor of key's dtype")
     with torch.cuda.device(key.device):
-        sptr = _stream_ptr(key.device, stream)
+        s = torch.cuda.current_stream(key.device) if stream is None else stream
+        with torch.cuda.stream(s):
+            if out is None:
+                out = torch.empty(B, R, P, D, dtype=key.dtype, device=key.device)
+        sptr = int(s.cuda_stream)
         _check(_lib.dsel_gather_rows(
             key.data_ptr(), _dtype_code(key.dtype), B, L, D,
             key.stride(0), key.stride(1), pos.data_ptr(), _index_code(pos.dtype), R, P, prs,

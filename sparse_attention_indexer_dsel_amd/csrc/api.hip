@@ -29,6 +29,16 @@ int cu_count() {
 
 bool aligned_ptr(const void *p) { return ((uintptr_t)p % kAlign) == 0; }
 
+// Polls of a split-row rendezvous before it gives up.  DSEL_SPIN_LIMIT
+// overrides it (tests force a rendezvous to give up from the host).
+uint32_t spin_limit() {
+    if (const char *env = std::getenv("DSEL_SPIN_LIMIT")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v >= 1) return (uint32_t)(v < (long)kSpinLimit ? v : (long)kSpinLimit);
+    }
+    return kSpinLimit;
+}
+
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct TopkPlan {
@@ -105,7 +115,7 @@ int choose_G(int64_t rows, int64_t cols, int cus) {
     return (int)G;
 }
 
-int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
+int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, TopkPlan *pl) {
     const int cus = cu_count();
     if (cus <= 0) return DSEL_ERR_DEVICE;
     const int vec = topk_vec(dtype);
@@ -127,8 +137,9 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, TopkPlan *pl) {
         pl->chunk = cols;
         pl->cap = 0;
         int per_cu = 0;
+        // (the instance the call launches: the values instance may differ)
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, topk_kernel_ptr(dtype, pl->ept, kTopkWave), kTopkThreads,
+                &per_cu, topk_kernel_ptr(dtype, pl->ept, kTopkWave, ret_val), kTopkThreads,
                 topk_dyn_lds(dtype, 0, pl->ept, kTopkWave)) != hipSuccess ||
             per_cu <= 0)
             return DSEL_ERR_DEVICE;
@@ -263,7 +274,7 @@ extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols
         return DSEL_ERR_ALIGN;
 
     TopkPlan pl;
-    const int st = plan_topk(dtype, rows, cols, k, &pl);
+    const int st = plan_topk(dtype, rows, cols, k, return_value ? 1 : 0, &pl);
     if (st != DSEL_OK) return st;
     if (!workspace) {
         *workspace_bytes = pl.ws_bytes;
@@ -295,6 +306,7 @@ extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols
     a.one = pl.one ? 1 : 0;
     a.idx_fill = idx_fill;
     a.val_fill = val_fill_bits;
+    a.spin_limit = spin_limit();
     // (only the values instance of the one-wave kernel reads a separate stage)
     a.stage_words = pl.kind == kTopkWave && a.ret_val
                         ? wave_stage_words(dtype, k, a.idx64 ? 8 : 4, a.ret_val, pl.per_cu)
@@ -318,6 +330,29 @@ extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols
         }
     }
     return DSEL_OK;
+}
+
+extern "C" int dsel_topk_check(void *workspace, size_t workspace_bytes, void *stream,
+                               uint32_t *error_bits) {
+    if (!error_bits) return DSEL_ERR_ARG;
+    *error_bits = 0;
+    if (!workspace || workspace_bytes < sizeof(uint32_t)) return DSEL_OK;  // nothing split ran on it
+    if (!aligned_ptr(workspace)) return DSEL_ERR_ALIGN;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint32_t bits = 0;
+    if (hipMemcpyAsync(&bits, workspace, sizeof(bits), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return DSEL_ERR_DEVICE;
+    if (!bits) return DSEL_OK;
+    // a rendezvous gave up: the workgroups of a row did not all meet, so
+    // counters and histograms may be left non-zero; zero the whole
+    // workspace (the exchange region needs no clearing, but costs nothing)
+    if (launch_zero_words(reinterpret_cast<uint32_t *>(workspace),
+                          (int64_t)(workspace_bytes / sizeof(uint32_t)), s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return DSEL_ERR_DEVICE;
+    *error_bits = bits;
+    return DSEL_ERR_SPLIT;
 }
 
 extern "C" int dsel_gather_rows(const void *key, int dtype, int64_t batch, int64_t len,

@@ -86,7 +86,15 @@ struct TopkArgs {
     uint32_t val_fill;       // value bits of those slots
     uint32_t stage_words;    // one-wave rows: LDS words per wave for the staged output
                              // after the histograms (0: staged in the histogram's space)
+    uint32_t spin_limit;     // split rows: polls of a rendezvous before it gives up
 };
+
+// Polls of a split-row rendezvous before it gives up and records an error
+// (about 0.1 s at the s_sleep granularity).
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Sticky error bits in workspace word 0.
+constexpr uint32_t kErrRendezvous = 1u;  // a split row's workgroups did not all meet
 
 // Top-k kernel kinds: one workgroup per row, G workgroups per row, one wave
 // per row.
@@ -126,5 +134,9 @@ struct GatherArgs {
 };
 
 hipError_t launch_gather(int pos64, const GatherArgs &a, hipStream_t stream);
+
+// Zero `words` 32-bit words at `p` (a fill kernel: no memset node in a
+// captured graph).
+hipError_t launch_zero_words(uint32_t *p, int64_t words, hipStream_t stream);
 
 }  // namespace dsel

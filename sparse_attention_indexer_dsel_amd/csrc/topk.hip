@@ -58,7 +58,6 @@ namespace {
 
 constexpr int NT = kTopkThreads;
 constexpr int NWAVE = NT / 64;
-constexpr uint32_t kSpinLimit = 1u << 22;
 
 // Hide a value from the optimiser so a comparison repeated after a
 // workgroup scan is recomputed instead of keeping one lane mask per element
@@ -249,9 +248,19 @@ __device__ __forceinline__ void drain_memory() { __builtin_amdgcn_s_waitcnt(0); 
 
 // Rendezvous of the G workgroups of one row.  `ctr` counts arrivals over the
 // whole launch; the m-th rendezvous completes at m*G.  The wait is bounded:
-// past the spin limit the workgroup records an error bit and goes on, so
-// every wave always exits.
-__device__ void row_rendezvous(uint32_t *ctr, uint32_t target, uint32_t *err) {
+// past `limit` polls the workgroup records kErrRendezvous in workspace word
+// 0 (`err`) and goes on, so every wave always exits; the row's output is
+// then undefined and the host learns of it from dsel_topk_check.
+//
+// Ordering: a workgroup's data for its peers is written with agent-scope
+// atomic stores or adds (they bypass the compute unit's L1 and land in L2,
+// the agent's point of coherence); the s_waitcnt(0) before the arrival add
+// waits until every one of them is acknowledged, so they are visible in L2
+// before the arrival is.  A peer that has seen the target count reads with
+// agent-scope atomic loads, which also go to L2 and so never return a stale
+// L1 line.  No cache-wide release or acquire fence is needed (on gfx950 an
+// agent-scope fence writes back and invalidates the whole L2 per workgroup).
+__device__ void row_rendezvous(uint32_t *ctr, uint32_t target, uint32_t *err, uint32_t limit) {
     drain_memory();
     __syncthreads();
     if (tid() == 0) {
@@ -259,8 +268,9 @@ __device__ void row_rendezvous(uint32_t *ctr, uint32_t target, uint32_t *err) {
         uint32_t spins = 0;
         while (ld_agent(ctr) < target) {
             __builtin_amdgcn_s_sleep(1);
-            if (++spins > kSpinLimit) {
-                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (++spins > limit) {
+                __hip_atomic_fetch_or(err, kErrRendezvous, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
@@ -1421,7 +1431,7 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
     if (t == 0)
         st_agent(mine + kOneHdr,
                  bc | (full << 16) | (ok << 17) | (blk_nan ? 1u << 18 : 0u) | (nz << 20));
-    row_rendezvous(slot, (uint32_t)G, err);
+    row_rendezvous(slot, (uint32_t)G, err, a.spin_limit);
 
     // ---- every chunk's header and counts at its bin boundaries -------------
     uint32_t *s_hdr = L.hist + kOneKeys;       // [64]
@@ -1507,7 +1517,7 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
             const int ii = i < total ? i : 0;
             const uint32_t hh = s_hdr[ii / PER];
             idx[q] = 32u * (B - (hh & 0x7FFu)) + (uint32_t)(ii % PER);
-            nzv[q] = (hh >> 20) & 0x3FFu;
+            nzv[q] = min((hh >> 20) & 0x3FFu, (uint32_t)kOneKeys);  // (a header is never past it)
         }
         uint32_t v[R2];
 #pragma unroll
@@ -1531,7 +1541,10 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
 #pragma unroll 8
         for (int cc = 0; cc < G; ++cc) gf += L.hist[cc * 33 + lane];
     }
-    const uint32_t js = (uint32_t)__popcll(__ballot(lane <= 32 && gf >= k)) - 1u;  // <= 31
+    // (js >= 0 whenever the rendezvous completed; the guard keeps every LDS
+    // index in range after one that gave up)
+    const uint32_t nge = (uint32_t)__popcll(__ballot(lane <= 32 && gf >= k));
+    const uint32_t js = nge ? min(nge - 1u, 31u) : 0u;
     const uint32_t above = (uint32_t)__shfl((int)gf, (int)js + 1);
     // keys above / at T in the chunks before this one: lane = chunk
     const uint32_t s1 = lane < c ? L.hist[lane * 33 + js + 1] : 0u;
@@ -1656,7 +1669,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
 
     // ---- merge the histograms of the row's workgroups ----------------------
     merge_histogram(L.hist, ghist, kBins);
-    row_rendezvous(slot, (++nren) * (uint32_t)G, err);
+    row_rendezvous(slot, (++nren) * (uint32_t)G, err, a.spin_limit);
     fetch_histogram(ghist, L.hist, kBins);
     __syncthreads();
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
@@ -1712,7 +1725,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
             }
             uint32_t *g = ghist + pass * kBins;
             merge_histogram(L.hist, g, nb);
-            row_rendezvous(slot, (++nren) * (uint32_t)G, err);
+            row_rendezvous(slot, (++nren) * (uint32_t)G, err, a.spin_limit);
             fetch_histogram(g, L.hist, nb);
             __syncthreads();
             const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
@@ -1741,7 +1754,7 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
             st_agent(gcnt + 2 * c + 0, mine & 0xFFFFu);
             st_agent(gcnt + 2 * c + 1, mine >> 16);
         }
-        row_rendezvous(slot, (++nren) * (uint32_t)G, err);
+        row_rendezvous(slot, (++nren) * (uint32_t)G, err, a.spin_limit);
         for (int i = t; i < c; i += NT) {
             gg += ld_agent(gcnt + 2 * i + 0);
             qq += ld_agent(gcnt + 2 * i + 1);
@@ -2219,6 +2232,453 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 rows of at most 2048 columns: one wave per row on packed 16-bit keys.
+//
+// A row's keys stay packed two per VGPR (element 2q in the low half of word
+// q of a load) from the transform to the write, so the transform, the NaN
+// probe and the value rebuild are packed 16-bit operations.  Each load is
+// turned into keys and histogrammed (10-bit first digit, 1024 bins) as soon
+// as it arrives.  The digit search reads the histogram 16 bins per lane,
+// finds the lane holding the k-th key with one wave scan, then resolves the
+// bin inside that lane's 16 with one 16-lane scan (no serial walk).  A
+// second pass over the 6 low bits (64 bins) of the boundary bin's keys
+// gives the exact threshold key T and the number of T-keys to take.
+//
+// The selection is then a per-element predicate, key > T' (or, when equal
+// keys at T are only partly taken, key > T or key == T at a column at or
+// before the cut: the column of the last T-key taken, found once per row
+// with per-load wave scans), so the write needs one comparison per element:
+// per load, a wave scan of the lanes' counts gives each lane its first slot
+// in column order.  The slots are filled in LDS and copied out with
+// contiguous 16-byte stores (or stored straight to the row when the stage
+// does not fit).
+// ---------------------------------------------------------------------------
+constexpr int W16_BINS = 1024;                    // first digit: key >> 6
+constexpr uint32_t W16_WORDS = W16_BINS + 64;     // bins, then one spare bin per lane
+
+// Keys of two bf16 values: 0x8000 + magnitude (positive), 0x8000 -
+// magnitude (negative): x ^ (s | 0x8000) - s per half, s the sign spread
+// over the half.
+__device__ __forceinline__ uint32_t bf16_key2(uint32_t x) {
+    const u16x2 s = __builtin_bit_cast(u16x2, __builtin_bit_cast(s16x2, as_u16x2(x)) >> (short)15);
+    const uint32_t t = x ^ (as_u32(s) | 0x80008000u);
+    return as_u32(as_u16x2(t) - s);
+}
+
+// The values of two keys (the inverse map; key 0x8000 gives +0 and the NaN
+// key 0xFFFF gives 0xFFFF, so those two keys' bits come from the row).
+__device__ __forceinline__ uint32_t bf16_val2(uint32_t key) {
+    const u16x2 s = __builtin_bit_cast(
+        u16x2, __builtin_bit_cast(s16x2, as_u16x2(key ^ 0x80008000u)) >> (short)15);
+    return as_u32(as_u16x2(key) + s) ^ (as_u32(s) | 0x80008000u);
+}
+
+__device__ __forceinline__ bool K16ambiguous(uint32_t key) { return key == 0x8000u || key == 0xFFFFu; }
+
+// Packed 16-bit max / min.
+__device__ __forceinline__ uint32_t pk_max16(uint32_t a, uint32_t b) {
+    return as_u32(__builtin_elementwise_max(as_u16x2(a), as_u16x2(b)));
+}
+__device__ __forceinline__ uint32_t pk_min16(uint32_t a, uint32_t b) {
+    return as_u32(__builtin_elementwise_min(as_u16x2(a), as_u16x2(b)));
+}
+
+// Word with the halves at and past `valid` (0..2 in this word) cleared.
+__device__ __forceinline__ uint32_t keep_halves(uint32_t w, int valid) {
+    return valid >= 2 ? w : (valid == 1 ? (w & 0xFFFFu) : 0u);
+}
+
+// Inclusive prefix sum within each 16-lane row of the wave.
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    return x;
+}
+
+__device__ __forceinline__ uint32_t rdlane(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// The bin of a 1024-bin histogram holding the need-th largest key (bins
+// counted from the top; the histogram holds at least `need` keys).
+__device__ __forceinline__ Digit w16_find1024(const uint32_t *hist, uint32_t need, int lane) {
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + (W16_BINS - 16) - 16 * lane);
+    const uint4 a0 = h4[0], a1 = h4[1], a2 = h4[2], a3 = h4[3];
+    const uint32_t local = (a0.x + a0.y + a0.z + a0.w) + (a1.x + a1.y + a1.z + a1.w) +
+                           (a2.x + a2.y + a2.z + a2.w) + (a3.x + a3.y + a3.z + a3.w);
+    const uint32_t incl = wave_incl_scan(local);
+    const int L = (int)__builtin_ctzll(__ballot(incl >= need));
+    const uint32_t above = rdlane(incl - local, L);
+    // lane i of each row of 16 takes bin 1023 - 16 L - i (descending)
+    const int bin = (W16_BINS - 1) - 16 * L - (lane & 15);
+    const uint32_t h = hist[bin];
+    const uint32_t cum = above + row16_incl_scan(h);
+    const int L2 = (int)__builtin_ctzll(__ballot(lane < 16 && cum >= need));
+    return Digit{rdlane((uint32_t)bin, L2), rdlane(cum - h, L2), rdlane(h, L2)};
+}
+
+// The same for a 64-bin histogram.
+__device__ __forceinline__ Digit w16_find64(const uint32_t *hist, uint32_t need, int lane) {
+    const uint32_t h = hist[63 - lane];
+    const uint32_t incl = wave_incl_scan(h);
+    const int L = (int)__builtin_ctzll(__ballot(incl >= need));
+    return Digit{(uint32_t)(63 - L), rdlane(incl - h, L), rdlane(h, L)};
+}
+
+// One wave's selection written in column order.  take(key, col) decides an
+// element; emit(pos, col, key_half, val_half) stores a taken one.  (The
+// direct-store and value fix-up paths.)
+template <int LPL, class Take, class Emit>
+__device__ __forceinline__ void w16_write(const uint32_t (&kw)[LPL * 4], int any, int lane,
+                                          Take take, Emit emit) {
+    uint32_t run = 0;
+#pragma unroll
+    for (int j = 0; j < LPL; ++j) {
+        if (j >= any) break;
+        const uint32_t c0 = (uint32_t)(j * 64 + lane) * 8u;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = opaque(kw[4 * j + q]);
+            cnt += take(w & 0xFFFFu, c0 + 2 * q) ? 1u : 0u;
+            cnt += take(w >> 16, c0 + 2 * q + 1) ? 1u : 0u;
+        }
+        const uint32_t incl = wave_incl_scan(cnt);
+        uint32_t pos = run + incl - cnt;
+        run += rdlane(incl, 63);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = opaque(kw[4 * j + q]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t key = h ? (w >> 16) : (w & 0xFFFFu);
+                const uint32_t col = c0 + 2 * q + h;
+                if (take(key, col)) {
+                    emit(pos, col, key);
+                    ++pos;
+                }
+            }
+        }
+    }
+}
+
+// The staged form: every element stores, a taken one at its slot of the
+// stage (index, and with RVAL the rebuilt value at voff), the others to a
+// per-lane dummy word (no branches and no exec-mask changes per element).
+// CUT: equal keys at T are only partly taken (those at columns <= cut).
+template <int LPL, bool CUT, bool I64, bool RVAL>
+__device__ __forceinline__ void w16_stage(const uint32_t (&kw)[LPL * 4], int any, int lane,
+                                          uint32_t T, uint32_t cut, char *stage, uint32_t voff,
+                                          char *dummy, uint32_t &amb) {
+    auto take = [&](uint32_t key, uint32_t col) {
+        return CUT ? (key > T || (key == T && col <= cut)) : key > T;
+    };
+    uint32_t run = 0;
+#pragma unroll
+    for (int j = 0; j < LPL; ++j) {
+        if (j >= any) break;
+        const uint32_t c0 = (uint32_t)(j * 64 + lane) * 8u;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = kw[4 * j + q];
+            cnt += take(w & 0xFFFFu, c0 + 2 * q) ? 1u : 0u;
+            cnt += take(w >> 16, c0 + 2 * q + 1) ? 1u : 0u;
+        }
+        const uint32_t incl = wave_incl_scan(cnt);
+        uint32_t pos = run + incl - cnt;
+        run += rdlane(incl, 63);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = opaque(kw[4 * j + q]);
+            const uint32_t vw = RVAL ? bf16_val2(w) : 0u;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t key = h ? (w >> 16) : (w & 0xFFFFu);
+                const uint32_t col = c0 + 2 * q + h;
+                const bool t = take(key, col);
+                if constexpr (I64) {
+                    char *p = t ? stage + pos * 8u : dummy;
+                    *reinterpret_cast<uint64_t *>(p) = (uint64_t)col;
+                } else {
+                    char *p = t ? stage + pos * 4u : dummy;
+                    *reinterpret_cast<uint32_t *>(p) = col;
+                }
+                if constexpr (RVAL) {
+                    char *p = t ? stage + voff + pos * 2u : dummy;
+                    *reinterpret_cast<uint16_t *>(p) = (uint16_t)(h ? (vw >> 16) : vw);
+                    amb |= (t && K16ambiguous(key)) ? 1u : 0u;
+                }
+                pos += t ? 1u : 0u;
+            }
+        }
+    }
+}
+
+template <int LPL, bool RV>
+__global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
+    using K = Bf16Key;
+    constexpr int SPAN = 64 * 8;  // columns per load over the wave
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // one region per wave
+    const int wid = __builtin_amdgcn_readfirstlane(tid() >> 6);
+    uint32_t *hist = s_dyn + wid * W16_WORDS;
+    char *stage = reinterpret_cast<char *>(hist);
+    uint32_t stage_cap = W16_WORDS * 4u;
+    if constexpr (RV) {
+        if (a.stage_words) {
+            stage = reinterpret_cast<char *>(s_dyn + NWAVE * W16_WORDS + wid * a.stage_words);
+            stage_cap = a.stage_words * 4u;
+        }
+    }
+    const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x);
+    const int64_t step = (int64_t)gridDim.x * NWAVE;
+
+#pragma unroll 1
+    for (int64_t row = a.row0 + (int64_t)blockIdx.x * NWAVE + wid; row < a.rows; row += step) {
+        // the lane index again, opaque: the per-lane column numbers derived
+        // from it must not be hoisted out of the row loop into VGPRs
+        const int lane = tid() & 63;
+        const int64_t n = valid_length(a, row);
+        const uint16_t *xr = x + row * a.x_stride;
+        if (n <= a.k) {
+            if constexpr (RV) {
+                write_short_idx(a, row, n, 0, 0, a.k, lane, 64);
+                write_short_values_wave<K>(reinterpret_cast<uint16_t *>(a.out_val) + row * a.val_stride,
+                                           (uint16_t)a.val_fill, n, a.k, xr, lane);
+            } else {
+                write_short_row<K>(a, row, n, 0, 1, xr, lane, 64);
+            }
+            continue;
+        }
+        const int len = (int)n;
+        const int full = len / SPAN, any = (len + SPAN - 1) / SPAN;  // uniform
+        uint4 v[LPL];
+        {
+            const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
+#pragma unroll
+            for (int j = 0; j < LPL; ++j)
+                if (j < any) v[j] = load_vec<K>(view, (int64_t)(j * 64 + lane) * 8);
+        }
+        wave_sync();  // the previous row's reads of this wave's LDS are done
+        {
+            uint4 *h4 = reinterpret_cast<uint4 *>(hist);
+#pragma unroll
+            for (int i = 0; i < W16_BINS / 256; ++i) h4[lane + 64 * i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        wave_sync();
+
+        // keys and the first-digit histogram, one load at a time as it arrives
+        uint32_t kw[LPL * 4];
+        uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+        const uint32_t spare = (uint32_t)W16_BINS + (uint32_t)lane;
+#pragma unroll
+        for (int j = 0; j < LPL; ++j) {
+            if (j >= any) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) kw[4 * j + q] = 0u;
+                continue;
+            }
+            uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            if (j < full) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t kk = bf16_key2(w[q]);
+                    kmax = pk_max16(kmax, kk);
+                    kmin = pk_min16(kmin, kk);
+                    kw[4 * j + q] = kk;
+                    atomicAdd(&hist[(kk >> 6) & 0x3FFu], 1u);
+                    atomicAdd(&hist[kk >> 22], 1u);
+                }
+            } else {
+                // the row ends in this load: halves at or past it get key 0
+                // (raw bits cleared first, so they are never probed)
+                int valid = len - (j * 64 + lane) * 8;
+                valid = valid < 0 ? 0 : (valid > 8 ? 8 : valid);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t kk = bf16_key2(keep_halves(w[q], valid - 2 * q));
+                    kmax = pk_max16(kmax, kk);
+                    kmin = pk_min16(kmin, kk);
+                    const uint32_t kz = keep_halves(kk, valid - 2 * q);
+                    kw[4 * j + q] = kz;
+                    const uint32_t lo = kz & 0xFFFFu, hi = kz >> 16;
+                    atomicAdd(&hist[lo ? (lo >> 6) : spare], 1u);
+                    atomicAdd(&hist[hi ? (hi >> 6) : spare], 1u);
+                }
+            }
+        }
+        // a NaN key lies above +inf's (0xFF80) or below -inf's (0x0080)
+        const bool row_nan =
+            __ballot(max(kmax & 0xFFFFu, kmax >> 16) > 0xFF80u || min(kmin & 0xFFFFu, kmin >> 16) < 0x0080u) != 0ull;
+        if (row_nan) {
+            // rare: every NaN to the top key, and the histogram again
+            wave_sync();
+            {
+                uint4 *h4 = reinterpret_cast<uint4 *>(hist);
+#pragma unroll
+                for (int i = 0; i < W16_BINS / 256; ++i) h4[lane + 64 * i] = make_uint4(0u, 0u, 0u, 0u);
+            }
+            wave_sync();
+#pragma unroll
+            for (int j = 0; j < LPL; ++j) {
+                if (j >= any) break;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t kz = K::fix_nan_word(kw[4 * j + q]);
+                    kw[4 * j + q] = kz;
+                    const uint32_t lo = kz & 0xFFFFu, hi = kz >> 16;
+                    atomicAdd(&hist[lo ? (lo >> 6) : spare], 1u);
+                    atomicAdd(&hist[hi ? (hi >> 6) : spare], 1u);
+                }
+            }
+        }
+        wave_sync();
+        const uint32_t k = (uint32_t)a.k;
+        const Digit d1 = w16_find1024(hist, k, lane);
+        // every valid key is at least -inf's 0x0080, so the boundary bin is
+        // >= 2 and no empty slot (key 0) is ever counted in it
+        uint32_t T, cut = 0xFFFFFFFFu;  // take: key > T, or key == T at a column <= cut
+        const uint32_t need1 = k - d1.above;
+        if (d1.cnt == need1) {
+            T = (d1.v << 6) - 1u;  // the boundary bin is taken whole
+        } else {
+            wave_sync();
+            hist[lane] = 0u;
+            wave_sync();
+            // every element adds: the boundary bin's keys to their low 6
+            // bits' bin, the others to this lane's spare bin (no branches)
+            const uint32_t spare2 = 64u + (uint32_t)lane;
+#pragma unroll
+            for (int j = 0; j < LPL; ++j) {
+                if (j >= any) break;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = kw[4 * j + q];
+                    const uint32_t lo = w & 0xFFFFu, hi = w >> 16;
+                    atomicAdd(&hist[(lo >> 6) == d1.v ? (lo & 63u) : spare2], 1u);
+                    atomicAdd(&hist[(hi >> 6) == d1.v ? (hi & 63u) : spare2], 1u);
+                }
+            }
+            wave_sync();
+            const Digit d2 = w16_find64(hist, need1, lane);
+            const uint32_t needT = need1 - d2.above;  // T-keys to take, 1..d2.cnt
+            T = (d1.v << 6) | d2.v;
+            if (needT == d2.cnt) {
+                T -= 1u;  // every T-key is taken
+            } else {
+                // the column of the needT-th T-key in column order
+                uint32_t rem = needT;
+#pragma unroll
+                for (int j = 0; j < LPL; ++j) {
+                    if (j >= any) break;
+                    uint32_t c = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t w = kw[4 * j + q];
+                        c += ((w & 0xFFFFu) == T) ? 1u : 0u;
+                        c += ((w >> 16) == T) ? 1u : 0u;
+                    }
+                    const uint32_t incl = wave_incl_scan(c);
+                    const uint32_t tot = rdlane(incl, 63);
+                    if (rem <= tot) {
+                        const int L = (int)__builtin_ctzll(__ballot(incl >= rem));
+                        uint32_t r = rem - rdlane(incl - c, L);
+                        uint32_t col = 0;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t w = kw[4 * j + q];
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const bool eq = (h ? (w >> 16) : (w & 0xFFFFu)) == T;
+                                if (eq && r == 1u) col = (uint32_t)(j * 64 + lane) * 8u + 2 * q + h;
+                                r -= eq ? 1u : 0u;
+                            }
+                        }
+                        cut = rdlane(col, L);
+                        break;
+                    }
+                    rem -= tot;
+                }
+            }
+        }
+
+        // the write
+        const bool rv = RV && a.ret_val;  // (the values instance is launched only with values)
+        const uint32_t idx_bytes = a.idx64 ? 8u : 4u;
+        const uint32_t voff = ((uint32_t)a.k * idx_bytes + 15u) & ~15u;
+        const uint32_t sbytes = voff + (rv ? (uint32_t)a.k * 2u : 0u);
+        // staged when the slots fit the stage; in the histogram's space they
+        // must leave its last 256 bytes (the spare bins) to the dummy stores
+        const bool staged = sbytes <= (RV && a.stage_words ? stage_cap : (uint32_t)W16_BINS * 4u);
+        uint32_t amb = 0;
+        if (staged) {
+            wave_sync();  // the histogram is dead: its space may hold the row's slots
+            char *dummy = reinterpret_cast<char *>(hist + W16_BINS + (lane & ~1));
+            const bool c = cut != 0xFFFFFFFFu;
+            if (rv) {
+                if constexpr (RV) {
+                    if (a.idx64) {
+                        if (c) w16_stage<LPL, true, true, true>(kw, any, lane, T, cut, stage, voff, dummy, amb);
+                        else   w16_stage<LPL, false, true, true>(kw, any, lane, T, cut, stage, voff, dummy, amb);
+                    } else {
+                        if (c) w16_stage<LPL, true, false, true>(kw, any, lane, T, cut, stage, voff, dummy, amb);
+                        else   w16_stage<LPL, false, false, true>(kw, any, lane, T, cut, stage, voff, dummy, amb);
+                    }
+                }
+            } else if (a.idx64) {
+                if (c) w16_stage<LPL, true, true, false>(kw, any, lane, T, cut, stage, voff, dummy, amb);
+                else   w16_stage<LPL, false, true, false>(kw, any, lane, T, cut, stage, voff, dummy, amb);
+            } else {
+                if (c) w16_stage<LPL, true, false, false>(kw, any, lane, T, cut, stage, voff, dummy, amb);
+                else   w16_stage<LPL, false, false, false>(kw, any, lane, T, cut, stage, voff, dummy, amb);
+            }
+        } else {
+            const RowViews o = row_views<K>(a, row);
+            auto direct = [&](auto take) {
+                w16_write<LPL>(kw, any, lane, take, [&](uint32_t pos, uint32_t col, uint32_t key) {
+                    view_store<K>(o, true, pos, col, bf16_val2(key) & 0xFFFFu);
+                    amb |= K::ambiguous(key) ? 1u : 0u;
+                });
+            };
+            if (cut == 0xFFFFFFFFu)
+                direct([&](uint32_t key, uint32_t) { return key > T; });
+            else
+                direct([&](uint32_t key, uint32_t col) { return key > T || (key == T && col <= cut); });
+        }
+        // +-0 and NaN keys: the value bits come from the row (the rebuilt
+        // bits of the same slot are overwritten)
+        if (rv && __ballot(amb != 0u)) {
+            const RowViews o = row_views<K>(a, row);
+            auto fix = [&](auto take) {
+                w16_write<LPL>(kw, any, lane, take, [&](uint32_t pos, uint32_t col, uint32_t key) {
+                    if (!K::ambiguous(key)) return;
+                    if (staged)
+                        reinterpret_cast<uint16_t *>(stage + voff)[pos] = xr[col];
+                    else
+                        view_store_value<K>(o, true, pos, (uint32_t)xr[col]);
+                });
+            };
+            if (cut == 0xFFFFFFFFu)
+                fix([&](uint32_t key, uint32_t) { return key > T; });
+            else
+                fix([&](uint32_t key, uint32_t col) { return key > T || (key == T && col <= cut); });
+        }
+        if (staged) {
+            wave_sync();
+            wave_copy_out(stage, reinterpret_cast<char *>(a.out_idx) + row * a.idx_stride * (int64_t)idx_bytes,
+                          (uint32_t)a.k * idx_bytes, lane);
+            if (rv)
+                wave_copy_out(stage + voff,
+                              reinterpret_cast<char *>(a.out_val) + row * a.val_stride * 2,
+                              (uint32_t)a.k * 2u, lane);
+        }
+        if (lane == 0 && a.nan_flag) a.nan_flag[row] = row_nan ? 1u : 0u;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Value order (sorted_index = 2): each row's selection, largest value first,
 // equal values by ascending column.  One workgroup per row sorts the row's
 // c = min(k, n) (key, column) pairs in LDS; the padding slots stay.  Runs
@@ -2426,6 +2886,14 @@ const void *pick(int ept) {
 
 template <class K, bool RV>
 const void *pick_wave(int epl) {
+    if constexpr (sizeof(typename K::raw_t) == 2) {
+        switch (epl) {
+            case 8: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<1, RV>);
+            case 16: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<2, RV>);
+            case 32: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<4, RV>);
+            default: return nullptr;
+        }
+    }
     switch (epl) {
         case 8: return reinterpret_cast<const void *>(&topk_rows_wave<K, 8, RV>);
         case 16: return reinterpret_cast<const void *>(&topk_rows_wave<K, 16, RV>);
@@ -2492,6 +2960,22 @@ hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned
 static size_t value_sort_lds(int64_t k) {
     return (size_t)((k + 1) & ~(int64_t)1) * sizeof(uint64_t) + SORT_CNT * sizeof(uint16_t) +
            3 * SORT_NW * sizeof(uint32_t);
+}
+
+namespace {
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, int64_t words) {
+    const int64_t step = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += step) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_zero_words(uint32_t *p, int64_t words, hipStream_t stream) {
+    if (words <= 0) return hipSuccess;
+    const int64_t blocks = (words + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 4096 ? blocks : 4096);
+    void *args[] = {&p, &words};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&zero_words_kernel), dim3(grid),
+                           dim3(256), args, 0, stream);
 }
 
 hipError_t launch_value_sort(int dtype, const TopkArgs &a, unsigned grid, hipStream_t stream) {

@@ -36,7 +36,7 @@ def declared():
 
 def test_header_declares_the_calls():
     assert declared() == ["dsel_gather_rows", "dsel_stride_requirement", "dsel_topk",
-                          "dsel_topk_ex"]
+                          "dsel_topk_check", "dsel_topk_ex"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -132,3 +132,18 @@ def test_topk_ex_fill_checks(lib):
     assert _topk_ex(lib, 2 ** 31, 0xFF80) == -1               # int32 index fill out of range
     assert _topk_ex(lib, -(2 ** 31) - 1, 0xFF80) == -1
     assert _topk_ex(lib, -1, 0x1FF80) == -1                    # bf16 fill wider than 16 bits
+
+
+def test_topk_check_host_checks(lib):
+    """dsel_topk_check: a NULL error-bits pointer is refused; a NULL or
+    too-small workspace had no split rows run on it (nothing to report);
+    a misaligned one is refused.  None of these touch a device."""
+    f = lib.dsel_topk_check
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32)]
+    bits = ctypes.c_uint32(7)
+    assert f(16, 1024, None, None) == -1
+    assert f(None, 1024, None, ctypes.byref(bits)) == 0 and bits.value == 0
+    bits.value = 7
+    assert f(16, 2, None, ctypes.byref(bits)) == 0 and bits.value == 0
+    assert f(20, 1024, None, ctypes.byref(bits)) == -3
