@@ -144,14 +144,41 @@ int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x
  * call's split rows hold undefined output and the workspace is left in an
  * undefined state.  dsel_topk_check reports and clears that state.
  *
- * workspace, workspace_bytes: the workspace and size given to dsel_topk.
+ * workspace, workspace_bytes: the workspace and size given to dsel_topk;
+ *            NULL: the scratch of dsel_topk_noalloc on the current device
+ *            (DSEL_OK at once if that entry point never ran on it).
  * stream:     the stream of those calls; the call SYNCHRONISES it.
  * error_bits: host pointer; receives word 0 (0 when no error).
  * Returns DSEL_OK when no rendezvous gave up since the last check.  Else it
  * zero-fills the whole workspace (so it is ready for the next call), writes
- * the bits and returns DSEL_ERR_SPLIT.  NULL workspace: DSEL_OK.
+ * the bits and returns DSEL_ERR_SPLIT.
  */
 int dsel_topk_check(void *workspace, size_t workspace_bytes, void *stream, uint32_t *error_bits);
+
+/*
+ * dsel_topk_ex for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments as dsel_topk_ex without the workspace: split rows (rows
+ * over 16384 columns) use a scratch array of the library instead, 32 MiB of
+ * device memory that every GPU the library runs on holds from its first
+ * call until the process ends.  The first call on a device looks the array
+ * up and zero-fills it (on `stream`; waited for unless `stream` is being
+ * captured); every call leaves it ready for the next.  The call allocates
+ * and frees nothing.  A call whose rows need more scratch than the array
+ * holds is split into several launches; a single row that needs more
+ * returns DSEL_ERR_WORKSPACE before anything is launched.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (other streams, other threads) race and must not be made;
+ * order them on one stream.  Split-row errors are read and cleared with
+ * dsel_topk_check(NULL, 0, stream, &bits).
+ */
+int dsel_topk_noalloc(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
+                      int64_t k, const int32_t *row_end,
+                      int sorted_index, int indices_type, int return_value,
+                      void *out_idx, int64_t idx_row_stride,
+                      void *out_val, int64_t val_row_stride,
+                      uint8_t *nan_flag, void *stream, int64_t idx_fill, uint32_t val_fill_bits);
 
 /*
  * Gather of key rows at selected positions, batch offset folded in.

@@ -2,6 +2,7 @@
 // sizing and launches on the caller's stream.  No allocation, no sync.
 #include <atomic>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/dsel.h"
 #include "dsel_internal.h"
@@ -115,7 +116,10 @@ int choose_G(int64_t rows, int64_t cols, int cus) {
     return (int)G;
 }
 
-int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, TopkPlan *pl) {
+// max_ws_words > 0 caps the split layout (rows per launch) to that many
+// workspace words (the entry point that allocates nothing).
+int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, int64_t max_ws_words,
+              TopkPlan *pl) {
     const int cus = cu_count();
     if (cus <= 0) return DSEL_ERR_DEVICE;
     const int vec = topk_vec(dtype);
@@ -199,6 +203,13 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, Top
     if (G > capacity) return DSEL_ERR_ARG;  // row longer than the GPU holds on chip
     int64_t rpl = capacity / G;
     if (rpl > rows) rpl = rows;
+    const int64_t slot0 = kHeaderWords + one_region_words(cus);
+    const int64_t sw = slot_words(G, dtype);
+    if (max_ws_words > 0) {
+        const int64_t fit = max_ws_words > slot0 ? (max_ws_words - slot0) / sw : 0;
+        if (fit < 1) return DSEL_ERR_WORKSPACE;
+        if (rpl > fit) rpl = fit;
+    }
     pl->kind = kTopkSplit;
     pl->split = true;
     pl->G = G;
@@ -210,8 +221,8 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, Top
     // the exchange region is part of every split layout (so no slot of any
     // layout ever overlaps it) and holds one area per resident workgroup
     pl->one = one && rpl * G <= (int64_t)kOneWgPerCu * cus;
-    pl->slot_words = slot_words(G, dtype);
-    pl->slot0 = kHeaderWords + one_region_words(cus);
+    pl->slot_words = sw;
+    pl->slot0 = slot0;
     pl->ws_bytes = (size_t)(pl->slot0 + rpl * pl->slot_words) * sizeof(uint32_t);
     return DSEL_OK;
 }
@@ -240,12 +251,15 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
                         dtype == DSEL_BF16 ? 0xFF80u : 0xFF800000u);
 }
 
-extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols,
-                            int64_t x_row_stride, int64_t k, const int32_t *row_end,
-                            int sorted_index, int indices_type, int return_value, void *out_idx,
-                            int64_t idx_row_stride, void *out_val, int64_t val_row_stride,
-                            uint8_t *nan_flag, void *workspace, size_t *workspace_bytes,
-                            void *stream, int64_t idx_fill, uint32_t val_fill_bits) {
+namespace {
+
+// dsel_topk_ex, with the split layout capped at max_ws_words (0: no cap).
+int topk_entry(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
+               int64_t k, const int32_t *row_end, int sorted_index, int indices_type,
+               int return_value, void *out_idx, int64_t idx_row_stride, void *out_val,
+               int64_t val_row_stride, uint8_t *nan_flag, void *workspace,
+               size_t *workspace_bytes, void *stream, int64_t idx_fill, uint32_t val_fill_bits,
+               int64_t max_ws_words) {
     // sorted_index 0 and 1: the output is ascending by construction; 2: a
     // value-order pass follows the select
     if (sorted_index < 0 || sorted_index > 2) return DSEL_ERR_ARG;
@@ -274,7 +288,7 @@ extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols
         return DSEL_ERR_ALIGN;
 
     TopkPlan pl;
-    const int st = plan_topk(dtype, rows, cols, k, return_value ? 1 : 0, &pl);
+    const int st = plan_topk(dtype, rows, cols, k, return_value ? 1 : 0, max_ws_words, &pl);
     if (st != DSEL_OK) return st;
     if (!workspace) {
         *workspace_bytes = pl.ws_bytes;
@@ -332,11 +346,100 @@ extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols
     return DSEL_OK;
 }
 
+// ---- the scratch of dsel_topk_noalloc ----------------------------------
+// Split rows need device scratch (rendezvous counters, histograms, the
+// exchange region).  dsel_topk_noalloc takes it from this array instead of
+// a caller's workspace: each GPU the library runs on holds its own copy for
+// the life of the process.  In host code `scratch` names a host-side stand-in
+// only; the device address comes from hipGetSymbolAddress, once per device.
+constexpr int64_t kScratchWords = (int64_t)8 << 20;  // 32 MiB
+__device__ __align__(256) uint32_t scratch[kScratchWords];
+
+std::mutex g_scratch_mu;
+uint32_t *g_scratch[kMaxDevices];
+std::atomic<bool> g_scratch_any{false};
+
+// The current device's address of `scratch`, zero-filled on first use (on
+// `s`, waited for unless `s` is being captured: then the fill is part of the
+// graph), or nullptr on failure.
+uint32_t *device_scratch(hipStream_t s) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev]) return g_scratch[dev];
+    uint32_t *ptr = nullptr;
+    if (hipGetSymbolAddress(reinterpret_cast<void **>(&ptr), HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+        return nullptr;
+    if (launch_zero_words(ptr, kScratchWords, s) != hipSuccess) return nullptr;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) return nullptr;
+    if (cap == hipStreamCaptureStatusNone && hipStreamSynchronize(s) != hipSuccess) return nullptr;
+    g_scratch[dev] = ptr;
+    g_scratch_any.store(true);
+    return ptr;
+}
+
+// The scratch of the current device if dsel_topk_noalloc has set it up there.
+uint32_t *known_scratch() {
+    if (!g_scratch_any.load()) return nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" int dsel_topk_noalloc(const void *x, int dtype, int64_t rows, int64_t cols,
+                                 int64_t x_row_stride, int64_t k, const int32_t *row_end,
+                                 int sorted_index, int indices_type, int return_value,
+                                 void *out_idx, int64_t idx_row_stride, void *out_val,
+                                 int64_t val_row_stride, uint8_t *nan_flag, void *stream,
+                                 int64_t idx_fill, uint32_t val_fill_bits) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    size_t bytes = (size_t)kScratchWords * sizeof(uint32_t);
+    // argument checks and the plan first (nothing launched on an error)
+    size_t need = 0;
+    int st = topk_entry(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index,
+                        indices_type, return_value, out_idx, idx_row_stride, out_val,
+                        val_row_stride, nan_flag, nullptr, &need, stream, idx_fill,
+                        val_fill_bits, kScratchWords);
+    if (st != DSEL_OK || rows == 0) return st;
+    uint32_t *ws = nullptr;
+    if (need > 0) {  // split rows: the scratch
+        ws = device_scratch(s);
+        if (!ws) return DSEL_ERR_DEVICE;
+    }
+    // (a plan without split rows uses no workspace: any non-null pointer
+    // with a size of 0 passes the workspace checks)
+    return topk_entry(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index, indices_type,
+                      return_value, out_idx, idx_row_stride, out_val, val_row_stride, nan_flag,
+                      ws ? ws : reinterpret_cast<uint32_t *>(out_idx), ws ? &bytes : &need,
+                      stream, idx_fill, val_fill_bits, kScratchWords);
+}
+
+extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols,
+                            int64_t x_row_stride, int64_t k, const int32_t *row_end,
+                            int sorted_index, int indices_type, int return_value, void *out_idx,
+                            int64_t idx_row_stride, void *out_val, int64_t val_row_stride,
+                            uint8_t *nan_flag, void *workspace, size_t *workspace_bytes,
+                            void *stream, int64_t idx_fill, uint32_t val_fill_bits) {
+    return topk_entry(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index, indices_type,
+                      return_value, out_idx, idx_row_stride, out_val, val_row_stride, nan_flag,
+                      workspace, workspace_bytes, stream, idx_fill, val_fill_bits, 0);
+}
+
 extern "C" int dsel_topk_check(void *workspace, size_t workspace_bytes, void *stream,
                                uint32_t *error_bits) {
     if (!error_bits) return DSEL_ERR_ARG;
     *error_bits = 0;
-    if (!workspace || workspace_bytes < sizeof(uint32_t)) return DSEL_OK;  // nothing split ran on it
+    if (!workspace) {
+        // the scratch of dsel_topk_noalloc on the current device, if set up
+        workspace = known_scratch();
+        workspace_bytes = (size_t)kScratchWords * sizeof(uint32_t);
+        if (!workspace) return DSEL_OK;
+    }
+    if (workspace_bytes < sizeof(uint32_t)) return DSEL_OK;  // nothing split ran on it
     if (!aligned_ptr(workspace)) return DSEL_ERR_ALIGN;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     uint32_t bits = 0;

@@ -36,7 +36,7 @@ def declared():
 
 def test_header_declares_the_calls():
     assert declared() == ["dsel_gather_rows", "dsel_stride_requirement", "dsel_topk",
-                          "dsel_topk_check", "dsel_topk_ex"]
+                          "dsel_topk_check", "dsel_topk_ex", "dsel_topk_noalloc"]
 
 
 def test_every_declared_symbol_is_exported(lib):
