@@ -184,33 +184,47 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, int
     // workgroup lists every key from the floor of its own top-k bin, about k
     // plus one bin, so its list needs the whole-row capacity.
     // DSEL_SPLIT_ONE_EXCHANGE=0 turns it off (tests of the multi-pass path).
-    bool one = dtype == DSEL_BF16 && G <= kOneMaxSplit && ept <= kOneMaxEpt;
+    // (fp32 rows: the window exchange, under the same switch)
+    bool one = G <= kOneMaxSplit && (dtype != DSEL_BF16 || ept <= kOneMaxEpt);
     if (const char *env = std::getenv("DSEL_SPLIT_ONE_EXCHANGE"))
         if (std::strtol(env, nullptr, 10) == 0) one = false;
-    if (one) {
+    if (one && dtype == DSEL_BF16) {
         const int64_t own = candidate_cap(k, chunk);
         if (own > cap) cap = own;
     }
     // every workgroup of a row must be resident at once: size launches by
-    // the number of workgroups the GPU holds
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, topk_kernel_ptr(dtype, ept, kTopkSplit),
-                                                     kTopkThreads, topk_dyn_lds(dtype, cap, ept, kTopkSplit)) !=
-            hipSuccess ||
-        per_cu <= 0)
-        return DSEL_ERR_DEVICE;
-    const int64_t capacity = (int64_t)per_cu * cus;
-    if (G > capacity) return DSEL_ERR_ARG;  // row longer than the GPU holds on chip
-    int64_t rpl = capacity / G;
-    if (rpl > rows) rpl = rows;
+    // the number of workgroups the GPU holds.  fp32 rows take the window
+    // exchange's kernel when its areas fit the exchange region, else the
+    // multi-pass kernel.
     const int64_t slot0 = kHeaderWords + one_region_words(cus);
     const int64_t sw = slot_words(G, dtype);
-    if (max_ws_words > 0) {
-        const int64_t fit = max_ws_words > slot0 ? (max_ws_words - slot0) / sw : 0;
-        if (fit < 1) return DSEL_ERR_WORKSPACE;
-        if (rpl > fit) rpl = fit;
+    int kind = (dtype == DSEL_F32 && one) ? kTopkSplitWx : kTopkSplit;
+    int64_t rpl = 0;
+    for (;;) {
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, topk_kernel_ptr(dtype, ept, kind),
+                                                         kTopkThreads,
+                                                         topk_dyn_lds(dtype, cap, ept, kind)) !=
+                hipSuccess ||
+            per_cu <= 0)
+            return DSEL_ERR_DEVICE;
+        const int64_t capacity = (int64_t)per_cu * cus;
+        if (G > capacity) return DSEL_ERR_ARG;  // row longer than the GPU holds on chip
+        rpl = capacity / G;
+        if (rpl > rows) rpl = rows;
+        if (max_ws_words > 0) {
+            const int64_t fit = max_ws_words > slot0 ? (max_ws_words - slot0) / sw : 0;
+            if (fit < 1) return DSEL_ERR_WORKSPACE;
+            if (rpl > fit) rpl = fit;
+        }
+        if (kind == kTopkSplitWx && rpl * G * kWxWords > one_region_words(cus)) {
+            kind = kTopkSplit;  // the areas do not fit: plan the multi-pass kernel
+            one = false;
+            continue;
+        }
+        break;
     }
-    pl->kind = kTopkSplit;
+    pl->kind = kind;
     pl->split = true;
     pl->G = G;
     pl->ept = ept;
@@ -220,7 +234,7 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, int
     pl->grid = rpl * G;
     // the exchange region is part of every split layout (so no slot of any
     // layout ever overlaps it) and holds one area per resident workgroup
-    pl->one = one && rpl * G <= (int64_t)kOneWgPerCu * cus;
+    pl->one = one && rpl * G * (dtype == DSEL_BF16 ? kOneWords : kWxWords) <= one_region_words(cus);
     pl->slot_words = sw;
     pl->slot0 = slot0;
     pl->ws_bytes = (size_t)(pl->slot0 + rpl * pl->slot_words) * sizeof(uint32_t);

@@ -52,6 +52,19 @@ inline int64_t one_region_words(int cus) { return (int64_t)kOneWgPerCu * cus * k
 // exchange's registers).
 constexpr int kOneMaxEpt = 64;
 
+// Window exchange of split fp32 rows (at most kOneMaxSplit workgroups per
+// row, one rendezvous): each workgroup's area in the same exchange region
+// holds a header and the keys of a three-bin window of a 12-bit first digit
+// around its estimate of the row's boundary bin, grouped by bin.  Like the
+// bf16 areas it is never cleared: a reader uses only words the header says
+// this call wrote.  A launch uses it only when its workgroups' areas fit the
+// region.
+constexpr int kWxBins = 4096;              // first digit: key >> 20
+constexpr int kWxHdr = 16;                 // header words
+constexpr int kWxKeys = 1024;              // window keys one workgroup may publish
+constexpr int kWxWords = kWxHdr + kWxKeys;
+constexpr int kWxGather = 2048;            // boundary-bin keys of a row a workgroup may gather
+
 // Per-row workspace slot (32-bit words): counters, one histogram per radix
 // pass, per-workgroup counts, and each workgroup's suffix counts over the
 // last pass's bins.
@@ -97,8 +110,8 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr uint32_t kErrRendezvous = 1u;  // a split row's workgroups did not all meet
 
 // Top-k kernel kinds: one workgroup per row, G workgroups per row, one wave
-// per row.
-enum { kTopkWhole = 0, kTopkSplit = 1, kTopkWave = 2 };
+// per row, G workgroups per fp32 row through the window exchange.
+enum { kTopkWhole = 0, kTopkSplit = 1, kTopkWave = 2, kTopkSplitWx = 3 };
 // Rows of at most this many columns take one wave each.
 constexpr int64_t kWaveCapacity = 64 * 32;
 

@@ -165,6 +165,19 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
+// Inclusive prefix sum within each 16-lane row of the wave.
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    return x;
+}
+
+__device__ __forceinline__ uint32_t rdlane(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
 // Lanes below this one whose bit is set in a wave mask.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -230,6 +243,69 @@ __device__ Digit find_digit(const uint32_t *hist, int nb, uint32_t need, uint32_
     const Digit d{s_out[0], s_out[1], s_out[2]};
     __syncthreads();
     return d;
+}
+
+// find_digit for histograms of at least NT bins (nb = NT * bpt, bpt <= 16,
+// a multiple of 4): each thread sums its bpt bins with 16-byte reads, one
+// workgroup scan finds the thread holding the need-th largest element, and
+// every wave then resolves the bin among that thread's bpt bins with one
+// 16-lane scan (no serial walk).
+__device__ Digit find_digit_fast(const uint32_t *hist, int nb, uint32_t need, uint32_t *s_red,
+                                 uint32_t *s_out) {
+    const int t = tid();
+    const int lane = t & 63;
+    const int bpt = nb / NT;
+    const int top = nb - t * bpt;  // exclusive upper bin of this thread
+    uint32_t local = 0;
+    for (int i = 0; i < bpt; i += 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(hist + top - bpt + i);
+        local += (q.x + q.y) + (q.z + q.w);
+    }
+    const uint32_t incl = block_scan(local, s_red).incl;
+    const uint32_t excl = incl - local;
+    if (excl < need && need <= incl) {
+        s_out[0] = (uint32_t)t;
+        s_out[1] = excl;
+    }
+    __syncthreads();
+    const int T = (int)s_out[0];
+    const uint32_t ex = s_out[1];
+    const int topT = nb - T * bpt;
+    const int bin = topT - 1 - (lane & 15);  // descending over the thread's bins
+    const uint32_t h = (lane & 15) < bpt ? hist[bin] : 0u;
+    const uint32_t cum = ex + row16_incl_scan(h);
+    const int L = (int)__builtin_ctzll(__ballot(lane < bpt && cum >= need));
+    const Digit d{rdlane((uint32_t)bin, L), rdlane(cum - h, L), rdlane(h, L)};
+    __syncthreads();  // s_out may be rewritten by the next search
+    return d;
+}
+
+// Order this wave's LDS accesses (one wave's LDS operations execute in
+// order; this keeps the compiler from moving them across phases).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave's search of a 1024-bin histogram for the bin holding the need-th
+// largest key (bins counted from the top; the histogram holds at least
+// `need` keys): 16 bins per lane with 16-byte reads, one wave scan for the
+// lane, one 16-lane scan for the bin (no serial walk).
+__device__ __forceinline__ Digit wave_find1024(const uint32_t *hist, uint32_t need, int lane) {
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + (1024 - 16) - 16 * lane);
+    const uint4 a0 = h4[0], a1 = h4[1], a2 = h4[2], a3 = h4[3];
+    const uint32_t local = (a0.x + a0.y + a0.z + a0.w) + (a1.x + a1.y + a1.z + a1.w) +
+                           (a2.x + a2.y + a2.z + a2.w) + (a3.x + a3.y + a3.z + a3.w);
+    const uint32_t incl = wave_incl_scan(local);
+    const int L = (int)__builtin_ctzll(__ballot(incl >= need));
+    const uint32_t above = rdlane(incl - local, L);
+    // lane i of each row of 16 takes bin 1023 - 16 L - i (descending)
+    const int bin = (1024 - 1) - 16 * L - (lane & 15);
+    const uint32_t h = hist[bin];
+    const uint32_t cum = above + row16_incl_scan(h);
+    const int L2 = (int)__builtin_ctzll(__ballot(lane < 16 && cum >= need));
+    return Digit{rdlane((uint32_t)bin, L2), rdlane(cum - h, L2), rdlane(h, L2)};
 }
 
 // Cross-workgroup data moves only through device-scope relaxed atomics (no
@@ -971,7 +1047,8 @@ __device__ __forceinline__ void view_store(const RowViews &v, bool take, uint32_
 // then 16-bit values), each thread puts its entries there by rank and the
 // run is copied out with consecutive stores (a list holds many more entries
 // than it selects, so stores straight from the list would scatter a few
-// lanes over many store instructions).
+// lanes over many store instructions).  The stage takes kStageSlots column
+// words then kStageSlots keys (16 or 32 bits).
 constexpr uint32_t kStageSlots = 1024;
 
 template <class K>
@@ -979,7 +1056,7 @@ __device__ __forceinline__ void write_exact(const TopkArgs &a, int64_t row, List
                                             uint32_t T, uint32_t need, uint32_t gt0, uint32_t eq0,
                                             uint32_t col0, uint32_t *s_red, uint32_t *stage,
                                             const typename K::raw_t *xr) {
-    static_assert(sizeof(typename K::raw_t) == 2, "staged values are 16-bit");
+    using skey_t = typename K::raw_t;  // a key has the width of its value
     constexpr int U = 4;
     const RowOut o = row_out<K>(a, row);
     const RowViews v = row_views<K>(a, row);
@@ -1013,7 +1090,7 @@ __device__ __forceinline__ void write_exact(const TopkArgs &a, int64_t row, List
         // columns and keys by rank; no global access in this loop (a load
         // here would make each iteration wait for every outstanding one)
         uint32_t *s_col = stage;
-        uint16_t *s_key = reinterpret_cast<uint16_t *>(stage + kStageSlots);
+        skey_t *s_key = reinterpret_cast<skey_t *>(stage + kStageSlots);
         for (uint32_t i = i0; i < i0 + E; i += U) {
             uint2 e[U];
 #pragma unroll
@@ -1024,7 +1101,7 @@ __device__ __forceinline__ void write_exact(const TopkArgs &a, int64_t row, List
                 const uint32_t pos = gt ? gb + min(qb, need) : gb + qb;
                 if (gt || (eq && qb < need)) {
                     s_col[pos - p0] = e[u].y + col0;
-                    s_key[pos - p0] = (uint16_t)e[u].x;
+                    s_key[pos - p0] = (skey_t)e[u].x;
                 }
                 gb += gt ? 1u : 0u;
                 qb += eq ? 1u : 0u;
@@ -1116,6 +1193,22 @@ __device__ void refine_histogram_stream(__amdgpu_buffer_rsrc_t view, int64_t bas
                 const uint32_t key = K::elem(w4[q], h);
                 if (key && (key >> s) == P) atomicAdd(&hist[(key >> sh) & dmask], 1u);
             }
+    }
+}
+
+// First-digit histogram of the range's keys re-read from cache (columns at
+// or past len go to this lane's spare bin).
+template <class K>
+__device__ void first_digit_histogram_stream(__amdgpu_buffer_rsrc_t view, int64_t base, int len,
+                                             uint32_t *hist) {
+    const int loads = (len + NT * K::VEC - 1) / (NT * K::VEC);
+    const uint32_t spare = kBins + (uint32_t)(tid() & 63);
+#pragma unroll 1
+    for (int j = 0; j < loads; ++j) {
+        uint32_t w4[4];
+        reload_keys<K>(view, base, len, j, w4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hist_add_masked<K>(hist, w4[q], spare);
     }
 }
 
@@ -1559,6 +1652,486 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
 }
 
 // ---------------------------------------------------------------------------
+// Window exchange of a split fp32 row (G <= kOneMaxSplit workgroups, one
+// rendezvous).
+//
+// Chunk c estimates the row's boundary bin (12-bit first digit) from its
+// own keys: the bin b_c of its q_c-th largest key, q_c = ceil(k len_c / n),
+// the row's selected share of its own keys.  It lists its keys from bin
+// b_c - 1 up (column order, LDS), publishes the keys of the window
+// [b_c - 1, b_c + 1] grouped by bin, their counts, and its count above the
+// window.  After one rendezvous every workgroup reads the G headers.  For a
+// bin B inside every non-empty chunk's window the row's count of keys at or
+// above B is known exactly (above-window counts plus window counts from B
+// up), so the boundary bin B1 (the highest bin whose count reaches k) is
+// found when it lies in all windows.  The keys of bin B1 of every chunk are
+// gathered into LDS; the (k - count above B1)-th largest of them is the
+// row's k-th largest key T (two local radix passes over the low 20 bits).
+// The chunks' counts above and at T follow, and each workgroup writes its
+// part of the output from its list as in the bf16 exchange.
+//
+// The exchange holds when every chunk's list and window fit, the windows of
+// the non-empty chunks meet and hold the boundary, and the row's keys in B1
+// fit the gather buffer.  Otherwise (skewed or short chunks, heavy ties) the
+// row runs the multi-pass select; every workgroup reads the same headers,
+// so the choice is uniform over the row.
+//
+// Area of a workgroup: word 0 = lo | hi << 12 | ok << 24 | empty << 25 |
+// nan << 26 (the window bins [lo, hi]), word 1 = keys above the window,
+// words 2..4 = keys in bins lo, lo+1, lo+2, then the window keys from word
+// kWxHdr, bin by bin.
+// LDS after the rendezvous (the histogram's space): gathered keys [0, 2048),
+// the local radix histogram [2048, 3072), per-chunk words [3072, 3397) (five
+// arrays of G + 1 <= 65: segment starts, offsets, counts above B1, above T,
+// at T), headers [3584, 3904).
+// ---------------------------------------------------------------------------
+struct WxResult {
+    bool ok, nan;
+    uint32_t T, need, gt0, eq0, run;
+};
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return ~wave_max_u32(~x); }
+
+template <class K, int LOADS>
+__device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, int G, int len, int64_t n,
+                                    uint32_t (&kw)[LOADS * 4], bool blk_nan, const TopkLds &L,
+                                    List ent, uint32_t cap, uint32_t *area, uint32_t *slot,
+                                    uint32_t *err) {
+    static_assert(!K::PACK, "window exchange: 32-bit keys");
+    constexpr int SH = 20;                 // 12-bit first digit
+    constexpr uint32_t GAT = 0, SEL = 2048, CHK = 3072, HDR = 3584;
+    const int t = tid();
+    const int lane = t & 63;
+    const uint32_t k = (uint32_t)a.k;
+    WxResult r{};
+
+    // ---- this chunk: window, counts, list -----------------------------------
+    uint32_t wlo = 0, whi = 0, above = 0, cw0 = 0, cw1 = 0, cw2 = 0, ok = 1, run = 0;
+    const bool empty = len <= 0;
+    if (!empty) {
+        uint64_t q = ((uint64_t)k * (uint64_t)len + (uint64_t)n - 1) / (uint64_t)n;
+        q = q < 1 ? 1 : (q > (uint64_t)len ? (uint64_t)len : q);
+        const Digit d = find_digit_fast(L.hist, kWxBins, (uint32_t)q, L.red, L.out);
+        wlo = d.v > 0 ? d.v - 1 : 0;
+        whi = d.v < (uint32_t)kWxBins - 1 ? d.v + 1 : d.v;
+        above = d.above - (whi > d.v ? L.hist[whi] : 0u);
+        cw0 = L.hist[wlo];
+        cw1 = wlo + 1 <= whi ? L.hist[wlo + 1] : 0u;
+        cw2 = wlo + 2 <= whi ? L.hist[wlo + 2] : 0u;
+        ok = (cw0 + cw1 + cw2 < (uint32_t)kWxKeys) ? 1u : 0u;  // each count then fits 10 bits
+        __syncthreads();  // every thread has read the histogram
+        const uint32_t T1 = max(wlo << SH, 1u);
+        run = compact_candidates<K, LOADS, true>(kw, len, T1, L.wtot, L.base, ent, cap);
+        if (run > cap) ok = 0;  // uniform
+    }
+    uint32_t *mine = area + (int64_t)c * kWxWords;
+    if (ok && !empty) {
+        // the window keys, bin by bin: thread t owns list entries [t E, t E + E)
+        const uint32_t E = (run + NT - 1) / NT;
+        const uint32_t i0 = (uint32_t)t * E, i1 = min(run, i0 + E);
+        uint32_t m = 0;
+        for (uint32_t i = i0; i < i1; ++i) {
+            const uint32_t w = (list_key<K>(ent, i) >> SH) - wlo;
+            m += w == 0 ? 1u : (w == 1 ? (1u << 10) : (w == 2 ? (1u << 20) : 0u));
+        }
+        const uint32_t ex = block_scan(m, L.red).incl - m;
+        uint32_t o0 = ex & 0x3FFu, o1 = cw0 + ((ex >> 10) & 0x3FFu), o2 = cw0 + cw1 + (ex >> 20);
+        uint32_t *dst = mine + kWxHdr;
+        for (uint32_t i = i0; i < i1; ++i) {
+            const uint32_t key = list_key<K>(ent, i);
+            const uint32_t w = (key >> SH) - wlo;
+            if (w == 0) st_agent(dst + o0++, key);
+            else if (w == 1) st_agent(dst + o1++, key);
+            else if (w == 2) st_agent(dst + o2++, key);
+        }
+    }
+    if (t == 0) {
+        st_agent(mine + 0, wlo | (whi << 12) | (ok << 24) | (empty ? 1u << 25 : 0u) |
+                               (blk_nan ? 1u << 26 : 0u));
+        st_agent(mine + 1, above);
+        st_agent(mine + 2, cw0);
+        st_agent(mine + 3, cw1);
+        st_agent(mine + 4, cw2);
+    }
+    row_rendezvous(slot, (uint32_t)G, err, a.spin_limit);
+
+    // ---- every chunk's header ---------------------------------------------
+    uint32_t *hdr = L.hist + HDR;
+    for (int i = t; i < G * 5; i += NT) hdr[i] = ld_agent(area + (int64_t)(i / 5) * kWxWords + i % 5);
+    __syncthreads();
+    // every wave decides on its own (lane = chunk; no barrier to share it)
+    const bool in = lane < G;
+    const uint32_t h0 = in ? hdr[lane * 5] : (1u << 25);
+    const uint32_t clo = h0 & 0xFFFu, chi = (h0 >> 12) & 0xFFFu;
+    const bool cok = (h0 >> 24) & 1u, cempty = (h0 >> 25) & 1u;
+    const uint32_t cab = in ? hdr[lane * 5 + 1] : 0u;
+    const uint32_t cc0 = in ? hdr[lane * 5 + 2] : 0u, cc1 = in ? hdr[lane * 5 + 3] : 0u,
+                   cc2 = in ? hdr[lane * 5 + 4] : 0u;
+    const bool live = in && !cempty;
+    r.nan = __ballot(in && ((h0 >> 26) & 1u)) != 0ull;
+    // a header this call wrote always passes these checks; they keep every
+    // read below inside its area should a rendezvous have given up
+    const bool sane = clo <= chi && chi - clo <= 2u && cc0 < (uint32_t)kWxKeys &&
+                      cc1 < (uint32_t)kWxKeys && cc2 < (uint32_t)kWxKeys &&
+                      cc0 + cc1 + cc2 < (uint32_t)kWxKeys;
+    const bool all_ok = __ballot(live && !(cok && sane)) == 0ull;
+    const bool any_live = __ballot(live) != 0ull;
+    const uint32_t maxlo = wave_max_u32(live ? clo : 0u);
+    const uint32_t minhi = wave_min_u32(live ? chi : 0xFFFFFFFFu);
+    // this chunk's keys at or above bin B (B within its window, or one past it)
+    auto at_or_above = [&](uint32_t B) -> uint32_t {
+        if (!live) return 0u;
+        uint32_t v = cab;
+        v += clo >= B ? cc0 : 0u;
+        v += clo + 1 <= chi && clo + 1 >= B ? cc1 : 0u;
+        v += clo + 2 <= chi && clo + 2 >= B ? cc2 : 0u;
+        return v;
+    };
+    bool good = all_ok && any_live && maxlo <= minhi;
+    uint32_t B1 = 0;
+    if (good) {
+        good = wave_sum(at_or_above(minhi + 1)) < k && wave_sum(at_or_above(maxlo)) >= k;
+        if (good) {
+            B1 = maxlo;
+            for (uint32_t B = minhi; B > maxlo; --B)
+                if (wave_sum(at_or_above(B)) >= k) {
+                    B1 = B;
+                    break;
+                }
+        }
+    }
+    uint32_t M = 0;
+    if (good) {
+        const uint32_t w1 = B1 - clo;  // bin B1 in this lane's window (live lanes)
+        const uint32_t mc = !live ? 0u : (w1 == 0 ? cc0 : (w1 == 1 ? cc1 : cc2));
+        const uint32_t boff = w1 == 0 ? 0u : (w1 == 1 ? cc0 : cc0 + cc1);
+        const uint32_t ac = at_or_above(B1 + 1);
+        const uint32_t incl = wave_incl_scan(mc);
+        M = rdlane(incl, 63);
+        good = M <= (uint32_t)kWxGather;
+        if (good && t < 64) {  // wave 0 keeps the per-chunk words
+            uint32_t *chk = L.hist + CHK;
+            if (in) {
+                chk[lane] = incl - mc;      // segment start of this chunk's keys in B1
+                chk[65 + lane] = boff;      // their offset in its area
+                chk[130 + lane] = ac;       // its keys above bin B1
+            }
+            if (lane == 0) chk[G] = M;
+        }
+    }
+    if (!good) {
+        r.ok = false;
+        __syncthreads();  // the caller reuses the histogram's space
+        return r;
+    }
+    const uint32_t R1 = wave_sum(at_or_above(B1 + 1));
+    const uint32_t need1 = k - R1;  // keys to take from bin B1, 1..M
+    __syncthreads();
+
+    // ---- gather bin B1's keys of every chunk: NT / G threads per chunk ------
+    {
+        const uint32_t *chk = L.hist + CHK;
+        const int tpc = NT / G;
+        const int cc = t / tpc, r0 = t % tpc;
+        if (cc < G) {
+            const uint32_t seg = chk[cc], m = chk[cc + 1] - seg;
+            const uint32_t *src = area + (int64_t)cc * kWxWords + kWxHdr + chk[65 + cc];
+#pragma unroll 1
+            for (uint32_t i = (uint32_t)r0; i < m; i += 4u * (uint32_t)tpc) {
+                uint32_t v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t ii = i + (uint32_t)(u * tpc);
+                    v[u] = ld_agent(src + (ii < m ? ii : 0u));
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t ii = i + (uint32_t)(u * tpc);
+                    if (ii < m) L.hist[GAT + seg + ii] = v[u];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // ---- the (need1)-th largest of them, by wave 0 alone (no workgroup
+    // barrier): digits (key >> 10) & 1023, then key & 1023
+    uint32_t *sel = L.hist + SEL;
+    if (t < 64) {
+        auto zero_sel = [&]() {
+            uint4 *s4 = reinterpret_cast<uint4 *>(sel);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s4[lane + 64 * i] = make_uint4(0u, 0u, 0u, 0u);
+        };
+        zero_sel();
+        wave_sync();
+        for (uint32_t i = (uint32_t)lane; i < M; i += 64) atomicAdd(&sel[(L.hist[GAT + i] >> 10) & 1023u], 1u);
+        wave_sync();
+        const Digit dA = wave_find1024(sel, need1, lane);
+        const uint32_t needA = need1 - dA.above;
+        uint32_t T, needT;
+        if (dA.cnt == needA) {
+            T = ((B1 << SH) | (dA.v << 10)) - 1u;  // the digit's bin is taken whole
+            needT = 0;
+        } else {
+            wave_sync();
+            zero_sel();
+            wave_sync();
+            for (uint32_t i = (uint32_t)lane; i < M; i += 64) {
+                const uint32_t key = L.hist[GAT + i];
+                if (((key >> 10) & 1023u) == dA.v) atomicAdd(&sel[key & 1023u], 1u);
+            }
+            wave_sync();
+            const Digit dB = wave_find1024(sel, needA, lane);
+            T = (B1 << SH) | (dA.v << 10) | dB.v;
+            needT = needA - dB.above;
+        }
+        if (lane == 0) {
+            L.out[4] = T;
+            L.out[5] = needT;
+        }
+    }
+    __syncthreads();
+    const uint32_t T = L.out[4], needT = L.out[5];
+    // ---- per chunk: its keys of B1 above / at T (wave w: chunks w, w + 4, ...)
+    {
+        uint32_t *chk = L.hist + CHK;
+        for (int cc = t >> 6; cc < G; cc += NWAVE) {
+            const uint32_t s0 = chk[cc], s1 = chk[cc + 1];
+            uint32_t g = 0, qn = 0;
+            for (uint32_t i = s0 + (uint32_t)lane; i < s1; i += 64) {
+                const uint32_t key = L.hist[GAT + i];
+                g += key > T ? 1u : 0u;
+                qn += key == T ? 1u : 0u;
+            }
+            g = wave_sum(g);
+            qn = wave_sum(qn);
+            if (lane == 0) {
+                chk[195 + cc] = g;
+                chk[260 + cc] = qn;
+            }
+        }
+    }
+    __syncthreads();
+    {
+        const uint32_t *chk = L.hist + CHK;
+        const bool before = lane < c;
+        r.gt0 = wave_sum(before ? chk[130 + lane] + chk[195 + lane] : 0u);
+        r.eq0 = wave_sum(before ? chk[260 + lane] : 0u);
+    }
+    r.T = T;
+    r.need = needT;
+    r.run = run;
+    r.ok = true;
+    __syncthreads();  // the gathered keys are read; the caller may reuse the space
+    return r;
+}
+
+// Keys of a workgroup's loads (coalesced layout), each load turned into keys
+// and, with_hist, histogrammed (12-bit first digit) as soon as it arrives.
+// Columns at or past len get key 0 (the spare bin of this lane).  Returns
+// whether this thread saw a NaN.
+template <class K, int LOADS>
+__device__ __forceinline__ uint32_t keys_hist12(const uint4 (&v)[LOADS], int len,
+                                                uint32_t (&kw)[LOADS * 4], uint32_t *hist,
+                                                bool with_hist) {
+    constexpr int VEC = K::VEC, EPW = K::EPW, SPAN = NT * VEC;
+    const int me = tid();
+    const int full = len / SPAN, any = (len + SPAN - 1) / SPAN;
+    const uint32_t spare = (uint32_t)kWxBins + (uint32_t)(me & 63);
+    uint32_t nan = 0;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        if (j >= any) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) kw[4 * j + q] = 0u;
+            continue;
+        }
+        uint4 x = v[j];
+        int valid = VEC;
+        if (j >= full) {
+            valid = len - (j * NT + me) * VEC;
+            valid = valid < 0 ? 0 : (valid > VEC ? VEC : valid);
+            x.x = K::keep_raw(x.x, valid);
+            x.y = K::keep_raw(x.y, valid - EPW);
+            x.z = K::keep_raw(x.z, valid - 2 * EPW);
+            x.w = K::keep_raw(x.w, valid - 3 * EPW);
+        }
+        nan |= keys_of<K>(x, &kw[4 * j]) ? 1u : 0u;
+        if (j >= full) clear_tail<K>(&kw[4 * j], valid);
+        if (with_hist) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t key = kw[4 * j + q];
+                atomicAdd(&hist[(j < full || key) ? (key >> 20) : spare], 1u);
+            }
+        }
+    }
+    return nan;
+}
+
+// The multi-pass select of a split row, from each workgroup's first-digit
+// histogram in LDS (hist): the histograms meet in the row's workspace slot,
+// one rendezvous per radix pass (nren rendezvous of this launch are already
+// behind the row), each workgroup writes its own part.  STREAM: the
+// workgroup does not hold its keys (the fallback of the fp32 window
+// exchange, whose registers are reused), so its passes and its write re-read
+// its range from cache.
+template <class K, int LOADS, bool STREAM>
+__device__ __forceinline__ void split_multipass(const TopkArgs &a, int64_t row, int64_t n, int c,
+                                                int G, int len, int64_t lo,
+                                                uint32_t (&kw)[LOADS * 4], const TopkLds &L,
+                                                List ent, uint32_t cap,
+                                                __amdgpu_buffer_rsrc_t view, uint32_t *slot,
+                                                uint32_t *err, uint32_t nren,
+                                                const typename K::raw_t *xr) {
+    const int t = tid();
+    uint32_t *ghist = slot + kSlotHeadWords;
+    uint32_t *gcnt = ghist + kMaxPasses * kBins;
+    constexpr int LASTB = 1 << K::digit_last();  // bins of the last pass
+    uint32_t *pub = gcnt + 4 * G;                // G x (LASTB + 1) suffix counts
+    // ---- merge the histograms of the row's workgroups ----------------------
+    merge_histogram(L.hist, ghist, kBins);
+    row_rendezvous(slot, (++nren) * (uint32_t)G, err, a.spin_limit);
+    fetch_histogram(ghist, L.hist, kBins);
+    __syncthreads();
+    const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
+
+    // ---- the rest of the radix select, one rendezvous per pass.  Each
+    // workgroup histograms its own keys at the boundary: straight from VGPRs
+    // when it holds a few keys per thread and candidates are dense, else from
+    // an LDS list of its candidates (key >= T1), else (its candidates do not
+    // fit the list: massive ties, or a row whose largest values crowd into
+    // one chunk) from its range re-read from cache.  All three take part in
+    // the same rendezvous.  In the last pass each workgroup also publishes its
+    // suffix counts, so the counts of the chunks before it come with that
+    // pass's rendezvous.
+    Bound b{d1.v, K::SH1, (uint32_t)a.k - d1.above};
+    // dense: at least a quarter of the row are candidates (uniform over it)
+    const bool regs = !STREAM && LOADS <= 2 && 4 * (int64_t)(d1.above + d1.cnt) >= n;
+    uint32_t run = 0;
+    bool listed = false;
+    if constexpr (!STREAM) {
+        if (!regs) {
+            run = compact_candidates<K, LOADS, true>(kw, len, d1.v << K::SH1, L.wtot, L.base, ent,
+                                                     cap);
+            listed = run <= cap;  // uniform over the workgroup
+        }
+    }
+    // this workgroup's (equal << 16 | above) counts at a bound
+    auto local_counts = [&](Bound bb) -> uint32_t {
+        if constexpr (!STREAM) {
+            if (regs) return block_scan(counts_regs<K, LOADS>(kw, bb), L.red).total;
+        }
+        if (listed) return list_counts<K>(ent, run, bb, L.red);
+        return block_scan(range_counts<K>(view, lo, len, bb), L.red).total;
+    };
+    bool folded = false;  // the last pass published this workgroup's counts
+    auto local_histogram = [&](uint32_t P, int s, int sh, uint32_t dmask) {
+        if constexpr (!STREAM) {
+            if (regs) {
+                refine_histogram_regs<K, LOADS>(kw, P, s, sh, dmask, L.hist);
+                return;
+            }
+        }
+        if (listed)
+            list_refine_histogram<K>(ent, run, P, s, sh, dmask, L.hist);
+        else
+            refine_histogram_stream<K>(view, lo, len, P, s, sh, dmask, L.hist);
+    };
+    if (d1.cnt != b.need) {
+#pragma unroll 1
+        for (int pass = 1; pass < K::NPASS; ++pass) {
+            const int d = K::digit(pass);
+            const int sh = b.s - d;
+            const int nb = 1 << d;
+            for (int i = t; i < nb; i += NT) L.hist[i] = 0;
+            __syncthreads();
+            local_histogram(b.P, b.s, sh, (1u << d) - 1u);
+            __syncthreads();
+            if (pass == K::NPASS - 1) {
+                publish_suffix(L.hist, nb, local_counts(b) & 0xFFFFu,
+                               pub + (int64_t)c * (LASTB + 1), L.red);
+                folded = true;
+            }
+            uint32_t *g = ghist + pass * kBins;
+            merge_histogram(L.hist, g, nb);
+            row_rendezvous(slot, (++nren) * (uint32_t)G, err, a.spin_limit);
+            fetch_histogram(g, L.hist, nb);
+            __syncthreads();
+            const Digit dg = find_digit(L.hist, nb, b.need, L.red, L.out);
+            b.need -= dg.above;
+            b.P = (b.P << d) | dg.v;
+            b.s = sh;
+            if (dg.cnt == b.need) break;  // the boundary bin is taken whole
+        }
+    }
+    // ---- the taken-above and equal counts of the chunks before this one:
+    // from the last pass's suffix counts, or (the selection ended at an
+    // earlier digit) one more exchange.  Each workgroup then writes its own
+    // part of the row's output.
+    uint32_t gg = 0, qq = 0;
+    if (folded) {
+        const uint32_t v = b.P & (uint32_t)(LASTB - 1);
+        for (int i = t; i < c; i += NT) {
+            const uint32_t *w = pub + (int64_t)i * (LASTB + 1) + v;
+            const uint32_t at = ld_agent(w), above = ld_agent(w + 1);
+            gg += above;
+            qq += at - above;
+        }
+    } else {
+        const uint32_t mine = local_counts(b);
+        if (t == 0) {
+            st_agent(gcnt + 2 * c + 0, mine & 0xFFFFu);
+            st_agent(gcnt + 2 * c + 1, mine >> 16);
+        }
+        row_rendezvous(slot, (++nren) * (uint32_t)G, err, a.spin_limit);
+        for (int i = t; i < c; i += NT) {
+            gg += ld_agent(gcnt + 2 * i + 0);
+            qq += ld_agent(gcnt + 2 * i + 1);
+        }
+    }
+    const uint32_t gt0 = block_scan(gg, L.red).total;
+    const uint32_t eq0 = block_scan(qq, L.red).total;
+    if constexpr (!STREAM) {
+        if (regs) write_from_regs<K, LOADS>(a, row, kw, len, b, gt0, eq0, view, lo, L.red, xr);
+    }
+    if (regs)
+        ;
+    else if (listed)
+        write_from_list<K>(a, row, ent, run, b, L.red, xr, gt0, eq0, (uint32_t)lo);
+    else
+        write_from_stream<K>(a, row, view, lo, len, b, gt0, eq0, L.red, xr);
+    // every workgroup's NaN bit was in before the first rendezvous
+    if (c == 0 && t == 0 && a.nan_flag) a.nan_flag[row] = ld_agent(slot + 2) ? 1u : 0u;
+
+    // Leave the slot zeroed for the next call (whose slot layout may differ).
+    // The histograms of all passes but the last were read before the last
+    // rendezvous, so each workgroup clears a share of them now; the last
+    // workgroup out, once every workgroup has read what it needs, clears the
+    // last pass's histogram, the counts and the counters.  The stores
+    // complete before the launch does.
+    constexpr int HW = (K::NPASS - 1) * kBins;
+    const int per = (HW + G - 1) / G;
+    const int z0 = c * per, z1 = min(HW, z0 + per);
+    for (int i = z0 + t; i < z1; i += NT) st_agent(ghist + i, 0u);
+    __syncthreads();
+    if (t == 0) L.out[3] = (add_agent(slot + 1, 1u) == (uint32_t)G - 1u) ? 1u : 0u;
+    __syncthreads();
+    if (L.out[3]) {
+        for (int i = t; i < LASTB; i += NT) st_agent(ghist + HW + i, 0u);
+        if (folded)
+            for (int i = t; i < G * (LASTB + 1); i += NT) st_agent(pub + i, 0u);
+        else
+            for (int i = t; i < 2 * G; i += NT) st_agent(gcnt + i, 0u);
+        if (t == 0) {
+            st_agent(slot + 0, 0u);
+            st_agent(slot + 1, 0u);
+            st_agent(slot + 2, 0u);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Split rows: G workgroups per row, workgroup c owning columns
 // [c*chunk, (c+1)*chunk) of the valid prefix, held in VGPRs.
 // ---------------------------------------------------------------------------
@@ -1798,6 +2371,159 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     }
 }
 
+// fp32 key of one value: 0x80000000 + magnitude (positive), 0x80000000 -
+// magnitude (negative), so -0 and +0 meet: (x ^ (s | 0x80000000)) - s with
+// s the sign spread over the word.  A NaN lands above +inf's key
+// (0xFF800000) or below -inf's (0x00800000) and is moved to the top apart.
+__device__ __forceinline__ uint32_t f32_key(uint32_t x) {
+    const uint32_t s = (uint32_t)((int32_t)x >> 31);
+    return (x ^ (s | 0x80000000u)) - s;
+}
+
+// The window exchange's first pass: each 16-byte load turned into four keys
+// and histogrammed (12-bit first digit) as soon as it arrives, with a
+// running max / min of the keys as the NaN probe.  Columns at or past len
+// get key 0 (and this lane's spare bin).  If this thread saw a NaN (rare),
+// returns true with the NaN keys NOT yet moved to the top: the caller fixes
+// them and rebuilds the histogram.
+template <int LOADS>
+__device__ __forceinline__ bool f32_keys_hist12(const uint4 (&v)[LOADS], int len,
+                                                uint32_t (&kw)[LOADS * 4], uint32_t *hist) {
+    constexpr int VEC = 4, SPAN = NT * VEC;
+    const int me = tid();
+    const int full = len / SPAN, any = (len + SPAN - 1) / SPAN;
+    const uint32_t spare = (uint32_t)kWxBins + (uint32_t)(me & 63);
+    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        if (j >= any) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) kw[4 * j + q] = 0u;
+            continue;
+        }
+        uint32_t x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        if (j < full) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) kw[4 * j + q] = f32_key(x[q]);
+            kmax = max(kmax, max(max(kw[4 * j], kw[4 * j + 1]), max(kw[4 * j + 2], kw[4 * j + 3])));
+            kmin = min(kmin, min(min(kw[4 * j], kw[4 * j + 1]), min(kw[4 * j + 2], kw[4 * j + 3])));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) atomicAdd(&hist[kw[4 * j + q] >> 20], 1u);
+        } else {
+            int valid = len - (j * NT + me) * VEC;
+            valid = valid < 0 ? 0 : (valid > VEC ? VEC : valid);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t kk = f32_key(q < valid ? x[q] : 0u);  // raw 0: a harmless key
+                kmax = max(kmax, kk);
+                kmin = min(kmin, kk);
+                kw[4 * j + q] = q < valid ? kk : 0u;
+                atomicAdd(&hist[q < valid ? (kk >> 20) : spare], 1u);
+            }
+        }
+    }
+    return kmax > 0xFF800000u || kmin < 0x00800000u;
+}
+
+// ---------------------------------------------------------------------------
+// Split fp32 rows through the window exchange: one rendezvous per row.  The
+// rare rows it does not hold for take the multi-pass select on keys re-read
+// from cache, so no key stays in VGPRs past the exchange's list.  Same grid,
+// workspace layout and output contract as topk_rows_split; the candidate
+// list lies past the 12-bit histogram.
+// ---------------------------------------------------------------------------
+template <int EPT>
+__global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
+    using K = F32Key;
+    using raw_t = typename K::raw_t;
+    constexpr int VEC = K::VEC;
+    constexpr int LOADS = EPT / VEC;
+    static_assert(EPT % VEC == 0, "EPT must be a multiple of the vector width");
+
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // histogram, candidate list
+    __shared__ TopkShared<LOADS> S;
+    const TopkLds L{s_dyn, S.wtot, S.base, S.red, S.out};
+
+    const int t = tid();
+    const int G = a.G;
+    const int c = (int)(blockIdx.x % (unsigned)G);
+    const int64_t lrow = (int64_t)(blockIdx.x / (unsigned)G);
+    const int64_t row = a.row0 + lrow;
+    if (row >= a.rows) return;  // uniform over the row's workgroups
+
+    const int64_t n = valid_length(a, row);
+    const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
+    if (n <= a.k) {
+        write_short_row<K>(a, row, n, c, G, xr);
+        return;
+    }
+    const uint32_t cap = (uint32_t)a.cap;
+    const List ent = list_of<K>(s_dyn + (kWxBins + 64));
+    uint32_t *slot = a.ws + a.slot0 + lrow * a.slot_words;
+    uint32_t *err = a.ws;
+    uint32_t *area = a.ws + kHeaderWords + lrow * G * kWxWords;
+
+    const int64_t lo = (int64_t)c * a.chunk;
+    const int64_t hi = min(lo + a.chunk, n);
+    const int len = hi > lo ? (int)(hi - lo) : 0;
+    uint32_t kw[LOADS * 4];
+    uint32_t nan;
+    {
+        const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
+        uint4 v[LOADS];
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) v[j] = load_vec<K>(view, lo + (int64_t)(j * NT + t) * VEC);
+        for (int b = t; b < kWxBins + 64; b += NT) L.hist[b] = 0;
+        __syncthreads();
+        // the 12-bit histogram, filled load by load as the data arrives
+        nan = f32_keys_hist12<LOADS>(v, len, kw, L.hist) ? 1u : 0u;
+    }
+    const bool blk_nan = __syncthreads_or((int)nan) != 0;
+    if (blk_nan) {
+        // rare: every NaN key to the top, and the histogram again
+        for (int b = t; b < kWxBins + 64; b += NT) L.hist[b] = 0;
+        __syncthreads();
+        const uint32_t spare = (uint32_t)kWxBins + (uint32_t)(t & 63);
+#pragma unroll
+        for (int w = 0; w < LOADS * 4; ++w) {
+            const uint32_t key = K::fix_nan_word(kw[w]);
+            kw[w] = key;
+            atomicAdd(&L.hist[key ? (key >> 20) : spare], 1u);
+        }
+        __syncthreads();
+    }
+    const WxResult r = window_exchange<K, LOADS>(a, c, G, len, n, kw, blk_nan, L, ent, cap, area,
+                                                 slot, err);
+    if (r.ok) {
+        // every read of the row's shared words is done: depart now, so the
+        // returning atomic overlaps the write
+        uint32_t dep = 0;
+        if (t == 0) dep = add_agent(slot + 1 + opaque(0u), 1u);
+        write_exact<K>(a, row, ent, r.run, r.T, r.need, r.gt0, r.eq0, (uint32_t)lo, L.red, L.hist, xr);
+        if (t == 0) {
+            if (c == 0 && a.nan_flag) a.nan_flag[row] = r.nan ? 1u : 0u;
+            L.out[3] = dep == (uint32_t)G - 1u ? 1u : 0u;
+        }
+        __syncthreads();
+        if (L.out[3] && t == 0) {  // last out: the counters back to zero
+            st_agent(slot + 0, 0u);
+            st_agent(slot + 1, 0u);
+        }
+        return;
+    }
+    // the exchange does not hold: the multi-pass select with the row's NaN
+    // bit, from an 11-bit histogram of the keys re-read from cache
+    if (blk_nan && t == 0)
+        __hip_atomic_fetch_or(slot + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
+    for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
+    __syncthreads();
+    first_digit_histogram_stream<K>(view, lo, len, L.hist);
+    __syncthreads();
+    split_multipass<K, LOADS, true>(a, row, n, c, G, len, lo, kw, L, ent, cap, view, slot, err, 1u,
+                                    xr);
+}
+
 // ---------------------------------------------------------------------------
 // Whole rows: one workgroup per row.
 // ---------------------------------------------------------------------------
@@ -1917,14 +2643,6 @@ struct WaveDigits<F32Key> {
 template <class K>
 __host__ __device__ constexpr uint32_t wave_lds_words() {
     return (uint32_t)WaveDigits<K>::HB + 64;
-}
-
-// Order this wave's LDS accesses (one wave's LDS operations execute in
-// order; this keeps the compiler from moving them across phases).
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // find_digit for one wave: lane l sums the bins [nb - (l+1)*bpt, nb - l*bpt)
@@ -2288,35 +3006,9 @@ __device__ __forceinline__ uint32_t keep_halves(uint32_t w, int valid) {
     return valid >= 2 ? w : (valid == 1 ? (w & 0xFFFFu) : 0u);
 }
 
-// Inclusive prefix sum within each 16-lane row of the wave.
-__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t x) {
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
-    return x;
-}
-
-__device__ __forceinline__ uint32_t rdlane(uint32_t v, int l) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
-}
-
-// The bin of a 1024-bin histogram holding the need-th largest key (bins
-// counted from the top; the histogram holds at least `need` keys).
+// The bin of a 1024-bin histogram holding the need-th largest key.
 __device__ __forceinline__ Digit w16_find1024(const uint32_t *hist, uint32_t need, int lane) {
-    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + (W16_BINS - 16) - 16 * lane);
-    const uint4 a0 = h4[0], a1 = h4[1], a2 = h4[2], a3 = h4[3];
-    const uint32_t local = (a0.x + a0.y + a0.z + a0.w) + (a1.x + a1.y + a1.z + a1.w) +
-                           (a2.x + a2.y + a2.z + a2.w) + (a3.x + a3.y + a3.z + a3.w);
-    const uint32_t incl = wave_incl_scan(local);
-    const int L = (int)__builtin_ctzll(__ballot(incl >= need));
-    const uint32_t above = rdlane(incl - local, L);
-    // lane i of each row of 16 takes bin 1023 - 16 L - i (descending)
-    const int bin = (W16_BINS - 1) - 16 * L - (lane & 15);
-    const uint32_t h = hist[bin];
-    const uint32_t cum = above + row16_incl_scan(h);
-    const int L2 = (int)__builtin_ctzll(__ballot(lane < 16 && cum >= need));
-    return Digit{rdlane((uint32_t)bin, L2), rdlane(cum - h, L2), rdlane(h, L2)};
+    return wave_find1024(hist, need, lane);
 }
 
 // The same for a 64-bin histogram.
@@ -2905,6 +3597,17 @@ const void *pick_wave(int epl) {
 // ept = columns per thread of one workgroup's range (the whole row, or one
 // split chunk), or per lane of a wave's row (kTopkWave).
 const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val) {
+    if (kind == kTopkSplitWx) {
+        if (dtype != 1) return nullptr;
+        switch (ept) {
+            case 8: return reinterpret_cast<const void *>(&topk_rows_wx<8>);
+            case 16: return reinterpret_cast<const void *>(&topk_rows_wx<16>);
+            case 32: return reinterpret_cast<const void *>(&topk_rows_wx<32>);
+            case 64: return reinterpret_cast<const void *>(&topk_rows_wx<64>);
+            case 128: return reinterpret_cast<const void *>(&topk_rows_wx<128>);
+            default: return nullptr;
+        }
+    }
     if (kind == kTopkWave) {
         if (ret_val) return dtype == 0 ? pick_wave<Bf16Key, true>(ept) : pick_wave<F32Key, true>(ept);
         return dtype == 0 ? pick_wave<Bf16Key, false>(ept) : pick_wave<F32Key, false>(ept);
@@ -2921,7 +3624,8 @@ size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind) {
     if (kind == kTopkWave)
         return (size_t)NWAVE * (dtype == 0 ? wave_lds_words<Bf16Key>() : wave_lds_words<F32Key>()) * 4;
     const uint64_t hist = (uint64_t)(kBins + 64);
-    const uint64_t base = kind == kTopkSplit ? split_list_base()
+    const uint64_t base = kind == kTopkSplitWx ? (uint64_t)(kWxBins + 64)
+                          : kind == kTopkSplit ? split_list_base()
                           : dtype == 0      ? list_base<Bf16Key>()
                                             : list_base<F32Key>();
     const uint64_t words = base + (dtype == 0 ? 1u : 2u) * (uint64_t)(cap + 64);
