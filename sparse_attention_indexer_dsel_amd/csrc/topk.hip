@@ -308,6 +308,44 @@ __device__ __forceinline__ Digit wave_find1024(const uint32_t *hist, uint32_t ne
     return Digit{rdlane((uint32_t)bin, L2), rdlane(cum - h, L2), rdlane(h, L2)};
 }
 
+// Workgroup search of a 4096-bin histogram for the bin holding the need-th
+// largest key, with bank-conflict-free reads: thread t reads the 16 bytes at
+// bins 1024 i + 4 t (i < 4; consecutive lanes, consecutive 16 bytes), each
+// quad of lanes sums its 16-bin group (DPP), the 256 group sums go through
+// LDS (s_grp, 256 words), one workgroup scan over the groups from the top
+// finds the group, and one 16-lane scan of its bins finds the bin.
+__device__ Digit find_digit_4096(const uint32_t *hist, uint32_t need, uint32_t *s_grp,
+                                 uint32_t *s_red, uint32_t *s_out) {
+    const int t = tid();
+    const int lane = t & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(hist + 1024 * i + 4 * t);
+        uint32_t v = (q.x + q.y) + (q.z + q.w);
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+        if ((t & 3) == 0) s_grp[64 * i + (t >> 2)] = v;  // group (1024 i + 4 t) / 16
+    }
+    __syncthreads();
+    const uint32_t local = s_grp[255 - t];  // thread t: group 255 - t (from the top)
+    const uint32_t incl = block_scan(local, s_red).incl;
+    const uint32_t excl = incl - local;
+    if (excl < need && need <= incl) {
+        s_out[0] = (uint32_t)t;
+        s_out[1] = excl;
+    }
+    __syncthreads();
+    const int g = 255 - (int)s_out[0];
+    const uint32_t ex = s_out[1];
+    const int bin = 16 * g + 15 - (lane & 15);  // descending over the group's bins
+    const uint32_t h = hist[bin];
+    const uint32_t cum = ex + row16_incl_scan(h);
+    const int L = (int)__builtin_ctzll(__ballot(lane < 16 && cum >= need));
+    const Digit d{rdlane((uint32_t)bin, L), rdlane(cum - h, L), rdlane(h, L)};
+    __syncthreads();  // s_out and s_grp may be rewritten by the next search
+    return d;
+}
+
 // Cross-workgroup data moves only through device-scope relaxed atomics (no
 // cache-wide fences); ordering comes from waiting for this workgroup's
 // outstanding memory operations before it signals.
@@ -1711,7 +1749,7 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     if (!empty) {
         uint64_t q = ((uint64_t)k * (uint64_t)len + (uint64_t)n - 1) / (uint64_t)n;
         q = q < 1 ? 1 : (q > (uint64_t)len ? (uint64_t)len : q);
-        const Digit d = find_digit_fast(L.hist, kWxBins, (uint32_t)q, L.red, L.out);
+        const Digit d = find_digit_4096(L.hist, (uint32_t)q, ent.w + 2 * (cap + 64), L.red, L.out);
         wlo = d.v > 0 ? d.v - 1 : 0;
         whi = d.v < (uint32_t)kWxBins - 1 ? d.v + 1 : d.v;
         above = d.above - (whi > d.v ? L.hist[whi] : 0u);
@@ -1853,45 +1891,31 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         }
     }
     __syncthreads();
-    // ---- the (need1)-th largest of them, by wave 0 alone (no workgroup
-    // barrier): digits (key >> 10) & 1023, then key & 1023
+    // ---- the (need1)-th largest of them: digits (key >> 10) & 1023, then
+    // key & 1023, over the workgroup
     uint32_t *sel = L.hist + SEL;
-    if (t < 64) {
-        auto zero_sel = [&]() {
-            uint4 *s4 = reinterpret_cast<uint4 *>(sel);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s4[lane + 64 * i] = make_uint4(0u, 0u, 0u, 0u);
-        };
-        zero_sel();
-        wave_sync();
-        for (uint32_t i = (uint32_t)lane; i < M; i += 64) atomicAdd(&sel[(L.hist[GAT + i] >> 10) & 1023u], 1u);
-        wave_sync();
-        const Digit dA = wave_find1024(sel, need1, lane);
-        const uint32_t needA = need1 - dA.above;
-        uint32_t T, needT;
-        if (dA.cnt == needA) {
-            T = ((B1 << SH) | (dA.v << 10)) - 1u;  // the digit's bin is taken whole
-            needT = 0;
-        } else {
-            wave_sync();
-            zero_sel();
-            wave_sync();
-            for (uint32_t i = (uint32_t)lane; i < M; i += 64) {
-                const uint32_t key = L.hist[GAT + i];
-                if (((key >> 10) & 1023u) == dA.v) atomicAdd(&sel[key & 1023u], 1u);
-            }
-            wave_sync();
-            const Digit dB = wave_find1024(sel, needA, lane);
-            T = (B1 << SH) | (dA.v << 10) | dB.v;
-            needT = needA - dB.above;
-        }
-        if (lane == 0) {
-            L.out[4] = T;
-            L.out[5] = needT;
-        }
-    }
+    for (int i = t; i < 1024; i += NT) sel[i] = 0;
     __syncthreads();
-    const uint32_t T = L.out[4], needT = L.out[5];
+    for (uint32_t i = (uint32_t)t; i < M; i += NT) atomicAdd(&sel[(L.hist[GAT + i] >> 10) & 1023u], 1u);
+    __syncthreads();
+    const Digit dA = find_digit_fast(sel, 1024, need1, L.red, L.out);
+    const uint32_t needA = need1 - dA.above;
+    uint32_t T, needT;
+    if (dA.cnt == needA) {
+        T = ((B1 << SH) | (dA.v << 10)) - 1u;  // the digit's bin is taken whole
+        needT = 0;
+    } else {
+        for (int i = t; i < 1024; i += NT) sel[i] = 0;
+        __syncthreads();
+        for (uint32_t i = (uint32_t)t; i < M; i += NT) {
+            const uint32_t key = L.hist[GAT + i];
+            if (((key >> 10) & 1023u) == dA.v) atomicAdd(&sel[key & 1023u], 1u);
+        }
+        __syncthreads();
+        const Digit dB = find_digit_fast(sel, 1024, needA, L.red, L.out);
+        T = (B1 << SH) | (dA.v << 10) | dB.v;
+        needT = needA - dB.above;
+    }
     // ---- per chunk: its keys of B1 above / at T (wave w: chunks w, w + 4, ...)
     {
         uint32_t *chk = L.hist + CHK;
@@ -3624,8 +3648,9 @@ size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind) {
     if (kind == kTopkWave)
         return (size_t)NWAVE * (dtype == 0 ? wave_lds_words<Bf16Key>() : wave_lds_words<F32Key>()) * 4;
     const uint64_t hist = (uint64_t)(kBins + 64);
-    const uint64_t base = kind == kTopkSplitWx ? (uint64_t)(kWxBins + 64)
-                          : kind == kTopkSplit ? split_list_base()
+    if (kind == kTopkSplitWx)  // the histogram, the list with a spare entry per lane, group sums
+        return (size_t)(kWxBins + 64 + 2 * ((uint64_t)cap + 64) + 256) * 4;
+    const uint64_t base = kind == kTopkSplit ? split_list_base()
                           : dtype == 0      ? list_base<Bf16Key>()
                                             : list_base<F32Key>();
     const uint64_t words = base + (dtype == 0 ? 1u : 2u) * (uint64_t)(cap + 64);
