@@ -1,29 +1,35 @@
 """Benchmark of the selection step (row-wise top-k, then key gather) on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2]
-                    [--no-per-config] [--no-cpu-baseline] [--copy-calibration]
-    python bench.py --traffic-from FETCH.csv WRITE.csv   # no GPU: writes profiles/traffic.json
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg4]
+                    [--no-per-config] [--no-cpu-baseline] [--no-floors]
+    python bench.py --profile-run cfgN      # a few calls of one workload, for counter runs
+    python bench.py --traffic-from DIR      # no GPU: counter files -> profiles/traffic.json
 
-Prints ONE JSON line.  The headline workload is the 4 x 204800 bf16 top-k
-(k = 1024, ascending int32 indices plus values); a step is one top-k call
-over one batch.  ``per_config`` adds the same measurement for the five named
-workloads (top-k and, where they have one, the gather), and for two of them
-(the 4 x 204800 headline and the 128 x 129280 sampling rows) the top-k with
-the selection ordered by value (``topk_by_value``: the select, then the
-radix value-order sort).  The causal prefill rows are also timed with values
-returned (``topk_with_values``).
+Prints ONE JSON line.  The headline workload is the sampling top-k (128 x
+129280 fp32, k = 4096, int64 indices plus values): the largest top-k of the
+five named workloads, the one whose HBM roofline a single call can reach (the
+4 x 8192 and 4 x 204800 top-k move 0.07 and 1.7 MB, below what any launch
+can stream in its floor time).  A step is one top-k call over the whole
+batch.  ``per_config`` carries the same measurement, with its own roofline
+block, for all five workloads (top-k and, where they have one, the gather),
+plus the top-k with the selection ordered by value for the 4 x 204800 and
+sampling rows and the causal prefill rows with values returned.
 
 Timing protocol
   * inputs are generated on the host from fixed seeds and copied to HBM
     before timing; each step reads a different copy of the input, and the
     copies together exceed twice the 256 MB Infinity Cache, so top-k reads
-    come from HBM rather than from cache;
+    come from HBM rather than from cache (warm, back-to-back throughput);
   * the K timed steps are captured once in a HIP graph and replayed, so the
     timed region holds no Python launch overhead; the region is bracketed
     by torch.cuda.synchronize() on both sides and wall-clock timed;
   * a HIP event pair on the kernels' stream brackets the same replay: each
-    step is one top-k kernel, so events / K is that kernel's mean duration
-    back to back (the roofline figure), comparable with rocprofv3's.
+    step is one top-k kernel (two with value order), so events / K is that
+    kernel's mean duration back to back (the roofline figure), comparable
+    with rocprofv3's kernel trace;
+  * ``floors`` gives the launch floor (a graph of empty-work kernels, per
+    launch) and streaming read, write and copy rates of plain device
+    kernels over 1 GiB, for scale.
 
 Byte accounting (algorithmic bytes: what the method must move)
   top-k  = sum over rows of the valid-prefix read (a row of valid length
@@ -36,19 +42,27 @@ The gather is also reported in the pages' convention (gathered output bytes
 over time; MindSpore hyper-parallel PR #1094, mechanism check).
 
 HBM traffic (roofline "traffic")
-  Two rocprofv3 counter runs of this script with --copy-calibration give
-  FETCH_SIZE and WRITE_SIZE per dispatch for the dominant top-k kernel and
-  for a plain streaming copy of known size (torch.neg, 256 MiB in, 256 MiB
-  out).  --traffic-from turns them into bytes per launch (counter value x
-  known copy bytes / copy counter value) and stores them in
-  profiles/traffic.json with a hash of the kernel sources; the bench reports
-  them only while that hash still matches, and null otherwise.
+  Two rocprofv3 counter runs per workload of ``--profile-run cfgN`` give
+  FETCH_SIZE and WRITE_SIZE per dispatch for its top-k and gather kernels
+  and for a plain streaming copy of known size (torch.neg, 256 MiB in,
+  256 MiB out).  ``--traffic-from`` turns them into bytes per launch
+  (counter value x known copy bytes / copy counter value) and stores them
+  in profiles/traffic.json with a hash of the kernel sources; the bench
+  reports them only while that hash still matches, and null otherwise.
+
+CPU baseline
+  The oracle (plain C, one row at a time) timed on the host's cores for
+  every workload's top-k, once with a thread per core (rows split over the
+  threads) and once on one thread, and on the gathers; each leg runs a
+  bounded number of repetitions.  ``cores`` is the host's core count; each
+  entry states the threads it used.
 """
 from __future__ import annotations
 
 import argparse
 import csv
 import dataclasses
+import glob
 import hashlib
 import json
 import os
@@ -66,10 +80,11 @@ MALL_BYTES = 256 << 20
 COPY_CAL_BYTES = 256 << 20
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_indexer_dsel_amd", "csrc", f)
-                  for f in ("topk.hip", "dsel_internal.h", "api.hip")]
+                  for f in ("topk.hip", "gather.hip", "dsel_internal.h", "api.hip")]
 METRIC = "top-k rows/s and achieved HBM GB/s (% of peak) per config; gather GB/s"
+HEADLINE = 4
 # workloads also timed with the selection ordered by value (the sampling
-# workload, where that order is the natural one, and the headline)
+# workload, where that order is the natural one, and the 4 x 204800 rows)
 VALUE_ORDER_CONFIGS = (2, 4)
 # index-only workloads also timed with values returned (the causal prefill
 # rows: half of them are shorter than k, so this times the short-row value
@@ -98,6 +113,13 @@ def topk_algorithmic_bytes(n_valid: np.ndarray, k: int, elt: int, idx_elt: int,
 def gather_algorithmic_bytes(n_positions: int, dim: int, elt: int, pos_elt: int,
                              distinct_rows: int) -> int:
     return n_positions * dim * elt + n_positions * pos_elt + distinct_rows * dim * elt
+
+
+def roofline(alg_bytes: int, kernel_s: float, kernel: str, traffic=None) -> dict:
+    achieved = alg_bytes / kernel_s / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "kernel": kernel,
+            "kernel_us": kernel_s * 1e6, "algorithmic_bytes_per_launch": alg_bytes}
 
 
 # ---------------------------------------------------------------------------
@@ -152,37 +174,47 @@ def _counter_means(path: str, counter: str):
     return {name: (float(np.mean(v)), len(v)) for name, v in out.items()}
 
 
-def traffic_from(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC_JSON) -> dict:
-    """Per-launch HBM bytes of the top-k kernel, scaled by the copy kernel's
-    reading of the same counters (counter x known bytes / copy counter)."""
-    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
-    write = _counter_means(write_csv, "WRITE_SIZE")
+def _find_csv(d: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return hits[0]
 
-    def pick(table, pat):
-        names = [n for n in table if pat in n]
-        if not names:
-            raise SystemExit(f"no kernel matching {pat!r} in the counter file")
-        return max(names, key=lambda n: table[n][1])
 
-    copy_f, copy_w = pick(fetch, "neg"), pick(write, "neg")
-    tk_f, tk_w = pick(fetch, "topk_rows"), pick(write, "topk_rows")
-    f_fac = COPY_CAL_BYTES / fetch[copy_f][0]
-    w_fac = COPY_CAL_BYTES / write[copy_w][0]
-    rec = {
-        "kernel": tk_f,
-        "source_hash": kernel_source_hash(),
-        "fetch_counter_per_launch": fetch[tk_f][0],
-        "write_counter_per_launch": write[tk_w][0],
-        "launches_sampled": [fetch[tk_f][1], write[tk_w][1]],
-        "copy_fetch_counter": fetch[copy_f][0],
-        "copy_write_counter": write[copy_w][0],
-        "copy_bytes": COPY_CAL_BYTES,
-        "fetch_factor": f_fac,
-        "write_factor": w_fac,
-        "fetch_bytes": fetch[tk_f][0] * f_fac,
-        "write_bytes": write[tk_w][0] * w_fac,
-    }
-    rec["traffic_bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+def traffic_from(root: str, out_path: str = TRAFFIC_JSON) -> dict:
+    """Per-launch HBM bytes of each workload's top-k and gather kernels from
+    counter runs under `root` (fetch_cfgN/ and write_cfgN/ directories, one
+    --profile-run each), scaled by the copy kernel's reading of the same
+    counters (counter x known bytes / copy counter)."""
+    rec = {"source_hash": kernel_source_hash(), "copy_bytes": COPY_CAL_BYTES, "configs": {}}
+    specs = [f"cfg{c}" for c in range(1, 6)] + [f"cfg{c}v" for c in VALUE_ORDER_CONFIGS]
+    for spec in specs:
+        fd, wd = os.path.join(root, f"fetch_{spec}"), os.path.join(root, f"write_{spec}")
+        if not (os.path.isdir(fd) and os.path.isdir(wd)):
+            continue
+        fetch = _counter_means(_find_csv(fd), "FETCH_SIZE")
+        write = _counter_means(_find_csv(wd), "WRITE_SIZE")
+
+        def pick(table, pat):
+            names = [n for n in table if pat in n]
+            return max(names, key=lambda n: table[n][1]) if names else None
+
+        cf, cw = pick(fetch, "neg"), pick(write, "neg")
+        if cf is None or cw is None:
+            raise SystemExit(f"no copy-calibration kernel in the {spec} counter files")
+        f_fac, w_fac = COPY_CAL_BYTES / fetch[cf][0], COPY_CAL_BYTES / write[cw][0]
+        entry = rec["configs"].setdefault(spec.rstrip("v"), {})
+        entry["fetch_factor" + ("_by_value_run" if spec.endswith("v") else "")] = f_fac
+        entry["write_factor" + ("_by_value_run" if spec.endswith("v") else "")] = w_fac
+        roles = (("value_order", "sort_rows_by_value"),) if spec.endswith("v") else \
+            (("topk", "topk_rows"), ("gather", "gather_rows"))
+        for role, pat in roles:
+            kf, kw = pick(fetch, pat), pick(write, pat)
+            if kf is None or kw is None:
+                continue
+            fb, wb = fetch[kf][0] * f_fac, write[kw][0] * w_fac
+            entry[role] = {"kernel": kf, "fetch_bytes": fb, "write_bytes": wb,
+                           "traffic_bytes": fb + wb, "dispatches": [fetch[kf][1], write[kw][1]]}
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
@@ -197,6 +229,13 @@ def load_traffic():
     except (OSError, ValueError):
         return None
     return rec if rec.get("source_hash") == kernel_source_hash() else None
+
+
+def traffic_for(traffic, cfg_name: str, role: str):
+    if not traffic:
+        return None
+    e = traffic.get("configs", {}).get(cfg_name, {}).get(role)
+    return e["traffic_bytes"] if e else None
 
 
 # ---------------------------------------------------------------------------
@@ -246,10 +285,10 @@ class TopkBench:
 
 
 def graph_time(torch, stream, fn, steps: int, warmup: int, reps: int = 1):
-    """Capture `steps` calls of fn(i) (one kernel each) in one HIP graph and
-    replay it; return (wall seconds per call, event seconds per call).  The
-    event pair brackets the replay on the stream the kernels run on, so the
-    second figure is the kernels' mean duration back to back."""
+    """Capture `steps` calls of fn(i) in one HIP graph and replay it; return
+    (wall seconds per call, event seconds per call).  The event pair brackets
+    the replay on the stream the kernels run on, so the second figure is the
+    kernels' mean duration back to back."""
     with torch.cuda.stream(stream):
         for i in range(max(warmup, 1)):
             fn(i)
@@ -279,10 +318,15 @@ def graph_time(torch, stream, fn, steps: int, warmup: int, reps: int = 1):
     return best, best_ev
 
 
-def measure_topk(dsel, torch, case, stream, steps, warmup, by_value=False):
+def topk_kernel_name(case, by_value=False) -> str:
+    return "dsel_topk" + (" + value order" if by_value else "") + f" ({case.name})"
+
+
+def measure_topk(dsel, torch, case, stream, steps, warmup, by_value=False, traffic=None):
     """One top-k call per step (with by_value, the select and then the
     value-order pass: kernel_us covers both)."""
     tb = TopkBench(dsel, torch, case, stream, by_value)
+    steps = min(max(steps, tb.ncopy), 256)  # every input copy read once per replay
     t_step, t_kern = graph_time(torch, stream, tb.call, steps, warmup, reps=3)
     nbytes = tb.algorithmic_bytes()
     rows = case.x.shape[0]
@@ -294,22 +338,25 @@ def measure_topk(dsel, torch, case, stream, steps, warmup, by_value=False):
         "gbps": nbytes / t_step / 1e9,
         "pct_peak": 100.0 * nbytes / t_step / 1e9 / HBM_PEAK_GBPS,
         "input_copies": tb.ncopy,
+        "steps": steps,
+        "roofline": roofline(nbytes, t_kern, topk_kernel_name(case, by_value), traffic),
     }
     del tb
     torch.cuda.empty_cache()
     return res
 
 
-def measure_gather(dsel, torch, case, stream, steps, warmup):
+def measure_gather(dsel, torch, case, stream, steps, warmup, traffic=None):
     """Gather(s) of the case's keys at the top-k positions (one call per key)."""
     dev = torch.device("cuda")
-    _, idx, _ = dsel.topk(case.x.to(dev), case.k, end=case.row_end.to(dev) if case.row_end is not None else None,
+    _, idx, _ = dsel.topk(case.x.to(dev), case.k,
+                          end=case.row_end.to(dev) if case.row_end is not None else None,
                           indices_type=case.indices_type, return_value=False)
     B = case.gather_batch
     R = case.x.shape[0] // B
     pos = idx.contiguous().view(B, R, case.k)
     out = []
-    for ki, key in enumerate(case.keys):
+    for key in case.keys:
         kd = key.to(dev)
         D = key.shape[2]
         dst = torch.empty(B, R, case.k, D, dtype=key.dtype, device=dev)
@@ -333,33 +380,190 @@ def measure_gather(dsel, torch, case, stream, steps, warmup):
             "gbps": alg / t / 1e9,
             "pct_peak": 100.0 * alg / t / 1e9 / HBM_PEAK_GBPS,
             "output_convention_gbps": output_convention_gbps(out_bytes, t),
+            "roofline": roofline(alg, tk, f"dsel_gather_rows ({case.name})", traffic),
         })
         del dst, kd
     torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(case, budget_s: float = 10.0):
-    """The oracle on the host cores, repeated over the same workload for ~budget_s."""
+def _event_time(torch, stream, fn, reps: int = 5) -> float:
+    """Best event-timed duration of fn() on `stream`, seconds (eager)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        fn()
+    stream.synchronize()
+    best = None
+    for _ in range(reps):
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        stream.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None else min(best, t)
+    return best
+
+
+def measure_floors(torch, stream) -> dict:
+    """Launch floor and plain streaming rates of device kernels over 1 GiB
+    (torch's own kernels: a reduction for read, a fill for write, a copy)."""
+    dev = torch.device("cuda")
+    tiny = torch.zeros(1, device=dev)
+    _, launch = graph_time(torch, stream, lambda i: tiny.add_(1.0), 200, 5, reps=3)
+    n = (1 << 30) // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    acc = torch.zeros((), dtype=torch.float32, device=dev)
+    t_read = _event_time(torch, stream, lambda: torch.sum(a, 0, dtype=torch.float32, out=acc))
+    t_write = _event_time(torch, stream, lambda: b.fill_(1.0))
+    h = n // 2
+    t_copy = _event_time(torch, stream, lambda: b[:h].copy_(a[h:]))
+    res = {"launch_us": launch * 1e6,
+           "read_gbps": (1 << 30) / t_read / 1e9,
+           "write_gbps": (1 << 30) / t_write / 1e9,
+           "copy_gbps": (1 << 30) / t_copy / 1e9,  # 512 MiB read + 512 MiB written
+           "how": "launch: a graph of 200 one-element adds, event time per launch; "
+                  "read 1 GiB (torch.sum), write 1 GiB (fill_), copy 512 MiB -> 512 MiB, "
+                  "best of 5 event-timed eager calls"}
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle)
+# ---------------------------------------------------------------------------
+
+def _host_x(case):
+    import torch
+    x = case.x
+    return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
+
+
+def _time_reps(fn, budget_s: float, max_reps: int):
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or reps >= max_reps:
+            return reps, dt
+
+
+def cpu_baseline(cases, headline, budget_s: float = 2.0) -> dict:
+    """The oracle on the host cores: every workload's top-k with a thread per
+    core and with one thread, and the gathers."""
     import torch
     import oracle
     orc = oracle.Oracle()
-    x = case.x
-    xh = x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
-    it = np.int32 if str(case.indices_type).endswith("int32") else np.int64
-    re = case.row_end.numpy() if case.row_end is not None else None
-    threads = min(oracle.host_threads(), x.shape[0])
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        orc.topk(xh, case.k, row_end=re, sorted_index=case.sorted_index, indices_type=it,
-                 return_value=case.return_value, threads=threads)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": reps * x.shape[0] / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full passes of the {case.name} top-k ({x.shape[0]} rows x "
-                      f"{x.shape[1]}) in {dt:.1f} s, {threads} threads"}
+    cores = oracle.host_threads()
+    per = {}
+    for c in cases:
+        xh = _host_x(c)
+        it = np.int32 if c.indices_type == torch.int32 else np.int64
+        re = c.row_end.numpy() if c.row_end is not None else None
+        rows = c.x.shape[0]
+        entry = {}
+        for label, threads in (("all_cores", min(cores, rows)), ("one_thread", 1)):
+            def run(threads=threads):
+                orc.topk(xh, c.k, row_end=re, sorted_index=c.sorted_index, indices_type=it,
+                         return_value=c.return_value, threads=threads)
+            reps, dt = _time_reps(run, budget_s, 1000)
+            entry[label] = {"rows_per_s": reps * rows / dt, "s_per_call": dt / reps,
+                            "threads": threads, "calls": reps}
+        if c.keys:
+            _, idx, _ = orc.topk(xh, c.k, row_end=re, sorted_index=c.sorted_index,
+                                 indices_type=it, return_value=False)
+            B = c.gather_batch
+            pos = idx.reshape(B, rows // B, c.k)
+            g = []
+            for key in c.keys:
+                kh = key.view(torch.int16).numpy().view(np.uint16)
+                reps, dt = _time_reps(lambda kh=kh: orc.gather(kh, pos), budget_s, 100)
+                out_bytes = pos.size * key.shape[2] * key.element_size()
+                g.append({"key": "contiguous" if key.is_contiguous() else "strided view",
+                          "s_per_call": dt / reps, "output_convention_gbps": out_bytes * reps / dt / 1e9,
+                          "threads": 1, "calls": reps})
+            entry["gather"] = g
+        per[c.name] = entry
+    h = per[headline.name]["all_cores"]
+    return {"value": h["rows_per_s"], "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "threads": h["threads"],
+            "sample": f"{h['calls']} full calls of the {headline.name} top-k "
+                      f"({headline.x.shape[0]} rows x {headline.x.shape[1]}) on {h['threads']} "
+                      f"threads (rows split over threads; the host has {cores} cores); every "
+                      f"workload on all cores and on one thread, and the gathers, in per_config",
+            "per_config": per}
+
+
+# ---------------------------------------------------------------------------
+
+def profile_run(spec: str) -> int:
+    """A few calls of one workload's top-k and gathers, plus the counter
+    calibration copy: the program the counter runs profile.  ``cfgN`` runs
+    the workload as named; ``cfgNv`` runs its top-k ordered by value (the
+    select, then the value-order pass) and no gather."""
+    import torch
+    import workloads as W
+    import sparse_attention_indexer_dsel_amd as dsel
+    by_value = spec.endswith("v")
+    cfg_id = int(spec.replace("cfg", "").rstrip("v"))
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    copy_calibration(torch, stream)
+    case = W.make_config(cfg_id)
+    dev = torch.device("cuda")
+    x = case.x.to(dev)
+    re = case.row_end.to(dev) if case.row_end is not None else None
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            _, idx, _ = dsel.topk(x, case.k, end=re, sorted_index=case.sorted_index,
+                                  indices_type=case.indices_type, return_value=case.return_value,
+                                  by_value=by_value, stream=stream)
+        if case.keys and not by_value:
+            B = case.gather_batch
+            pos = idx.contiguous().view(B, case.x.shape[0] // B, case.k)
+            for key in case.keys:
+                kd = key.to(dev)
+                for _ in range(3):
+                    dsel.gather_rows(kd, pos, stream=stream)
+    stream.synchronize()
+    print(f"profile run of {case.name}{' by value' if by_value else ''} done", flush=True)
+    return 0
+
+
+# One SQ counter pass (8 SQ counters and GRBM_GUI_ACTIVE, the most one run
+# can hold): instruction counts, and rocprofv3's derived occupancy, LDS
+# bank-conflict and VALU-busy figures for gfx950 (their inputs are
+# SQ_WAVE_CYCLES, SQ_LDS_BANK_CONFLICT, SQ_ACTIVE_INST_VALU and
+# GRBM_GUI_ACTIVE).
+SQ_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_ACTIVE_INST_LDS "
+               "SQ_LDS_BANK_CONFLICT OccupancyPercent LDSBankConflict VALUBusy")
+
+
+def counters_from(d: str) -> str:
+    """Markdown table of per-dispatch means per library kernel from one
+    rocprofv3 run with SQ_COUNTERS, plus bank-conflict cycles per LDS
+    instruction cycle."""
+    path = _find_csv(d)
+    names = SQ_COUNTERS.split()
+    table = {}
+    for c in names:
+        for kern, (mean, cnt) in _counter_means(path, c).items():
+            table.setdefault(kern, {})[c] = (mean, cnt)
+    lines = ["| kernel | dispatches | " + " | ".join(names) + " | conflict cycles / LDS cycles |",
+             "|---" * (len(names) + 3) + "|"]
+    for kern, row in sorted(table.items()):
+        if not any(p in kern for p in ("dsel", "topk", "gather", "sort_rows")):
+            continue
+        get = lambda c: row.get(c, (float("nan"), 0))[0]
+        lds = get("SQ_ACTIVE_INST_LDS")
+        ratio = get("SQ_LDS_BANK_CONFLICT") / lds if lds else float("nan")
+        short = kern.split("(dsel::")[0].replace("dsel::", "").replace("(anonymous namespace)::", "")
+        lines.append(f"| `{short}` | {max(v[1] for v in row.values())} | " +
+                     " | ".join(f"{get(c):.4g}" for c in names) + f" | {ratio:.3f} |")
+    return "\n".join(lines)
 
 
 def main(argv=None):
@@ -367,21 +571,29 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="cfg2")
+    ap.add_argument("--workload", default=f"cfg{HEADLINE}")
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run the plain copy kernel the traffic counters are scaled by")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="no GPU: turn two rocprofv3 counter files into profiles/traffic.json")
+    ap.add_argument("--no-floors", action="store_true")
+    ap.add_argument("--profile-run", metavar="CFG",
+                    help="a few calls of one workload (cfgN, or cfgNv ordered by value) for counter runs")
+    ap.add_argument("--counters-from", metavar="DIR",
+                    help="no GPU: per-kernel table of an SQ counter run")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="no GPU: turn per-workload counter runs into profiles/traffic.json")
     args = ap.parse_args(argv)
     if args.traffic_from:
-        print(json.dumps(traffic_from(*args.traffic_from)))
+        print(json.dumps(traffic_from(args.traffic_from)))
+        return 0
+    if args.counters_from:
+        print(counters_from(args.counters_from))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU (run with --gpus 1): the selection step shards by "
               "rows with no exchange, so N GPUs run N independent row slices", file=sys.stderr)
         return 2
+    if args.profile_run:
+        return profile_run(args.profile_run)
 
     import torch
     import workloads as W
@@ -392,8 +604,7 @@ def main(argv=None):
     stream = torch.cuda.Stream()
     cfg_id = int(args.workload.replace("cfg", ""))
     case = W.make_config(cfg_id)
-    if args.copy_calibration:
-        copy_calibration(torch, stream)
+    traffic = load_traffic()
 
     # ---- headline: K steps of the workload's top-k -------------------------
     tb = TopkBench(dsel, torch, case, stream)
@@ -424,8 +635,7 @@ def main(argv=None):
     t_step = elapsed / args.steps
     nbytes = tb.algorithmic_bytes()
     rows = case.x.shape[0]
-    achieved = nbytes / t_kern / 1e9
-    traffic = load_traffic() if cfg_id == 2 else None
+    dt_name = "bf16" if case.x.dtype == torch.bfloat16 else "f32"
     del tb
     torch.cuda.empty_cache()
 
@@ -440,42 +650,46 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if case.x.dtype == torch.bfloat16 else "f32",
+        "dtype": dt_name,
         "data": "synthetic (seeded host generator; no datasets or weights)",
-        "config": {"workload": f"{case.name}: top-k {rows}x{case.x.shape[1]} "
-                               f"{'bf16' if case.x.dtype == torch.bfloat16 else 'fp32'}, "
+        "config": {"workload": f"{case.name}: top-k {rows}x{case.x.shape[1]} {dt_name}, "
                                f"k={case.k}, sorted_index={case.sorted_index}, "
                                f"{str(case.indices_type).split('.')[-1]} indices, "
                                f"values={case.return_value}",
                    "global_batch": rows, "seq_len": int(case.x.shape[1]), "parallelism": "none"},
         "gbps": nbytes / t_step / 1e9,
         "pct_peak": 100.0 * nbytes / t_step / 1e9 / HBM_PEAK_GBPS,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic["traffic_bytes"] if traffic else None,
-                     "kernel": traffic["kernel"] if traffic else "dsel_topk (one kernel per call)",
-                     "kernel_us": t_kern * 1e6,
-                     "algorithmic_bytes_per_launch": nbytes},
+        "roofline": roofline(nbytes, t_kern, topk_kernel_name(case),
+                             traffic_for(traffic, case.name, "topk")),
+        "timing": "warm back-to-back graph replay over rotating input copies (> 2x the "
+                  "Infinity Cache), events on the kernels' stream",
     }
 
+    cases = [case if i == cfg_id else W.make_config(i) for i in sorted(W.CONFIGS)]
+    if not args.no_floors:
+        line["floors"] = measure_floors(torch, stream)
+        print(f"# floors: {json.dumps(line['floors'])}", file=sys.stderr, flush=True)
     if not args.no_per_config:
         per = {}
-        for i in sorted(W.CONFIGS):
-            c = case if i == cfg_id else W.make_config(i)
-            entry = {"topk": measure_topk(dsel, torch, c, stream, 20, 3)}
-            if i in VALUE_ORDER_CONFIGS:
+        for c in cases:
+            entry = {"topk": measure_topk(dsel, torch, c, stream, 20, 3,
+                                          traffic=traffic_for(traffic, c.name, "topk"))}
+            if c.x.shape[0] and c.name == case.name:
+                entry["topk"]["headline"] = True
+            if int(c.name[3:]) in VALUE_ORDER_CONFIGS:
                 entry["topk_by_value"] = measure_topk(dsel, torch, c, stream, 20, 3, by_value=True)
-            if i in WITH_VALUES_CONFIGS and not c.return_value:
+            if int(c.name[3:]) in WITH_VALUES_CONFIGS and not c.return_value:
                 entry["topk_with_values"] = measure_topk(
                     dsel, torch, dataclasses.replace(c, return_value=True), stream, 20, 3)
             if c.keys:
-                entry["gather"] = measure_gather(dsel, torch, c, stream, 10, 2)
+                entry["gather"] = measure_gather(dsel, torch, c, stream, 10, 2,
+                                                 traffic=traffic_for(traffic, c.name, "gather"))
             per[c.name] = entry
             print(f"# {c.name}: {json.dumps(entry)}", file=sys.stderr, flush=True)
         line["per_config"] = per
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case)
+        line["cpu_baseline"] = cpu_baseline(cases, case)
 
     print(json.dumps(line), flush=True)
     return 0
