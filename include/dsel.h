@@ -36,6 +36,24 @@ enum { DSEL_BF16 = 0, DSEL_F32 = 1 };  /* value dtype (bf16 = upper half of bina
 enum { DSEL_I32 = 0, DSEL_I64 = 1 };   /* index dtype */
 
 /*
+ * Order in which a launch's workers take rows (dsel_topk_ex, dsel_topk_noalloc).
+ * It changes timing only: every row's output is the same bytes in any order.
+ *
+ * PaddleFleet PR #1762, Description: under a causal mask the cost of a query
+ * row grows with its position, and the dual-chunk split evens it out by
+ * pairing chunk g with its mirror 2G-1-g.  Here the workers (one wave or one
+ * workgroup per row) take rows 0, R-1, 1, R-2, 2, ... in launch order, so the
+ * workers that start first hold rows from both ends of a ramp of row lengths
+ * and the long rows no longer all start last.  Rows split over several
+ * workgroups (over 16384 columns) always take the natural order.
+ *   DSEL_ROWS_AUTO        dual chunk when row_end is given, else natural
+ *   DSEL_ROWS_NATURAL     rows 0, 1, 2, ... in launch order
+ *   DSEL_ROWS_DUAL_CHUNK  rows 0, R-1, 1, R-2, ...
+ * Anything else: DSEL_ERR_ARG.
+ */
+enum { DSEL_ROWS_AUTO = 0, DSEL_ROWS_NATURAL = 1, DSEL_ROWS_DUAL_CHUNK = 2 };
+
+/*
  * Byte alignment the library needs of row strides and base pointers.
  *
  * DeepSelect tutorial ("Sheshisa Imisebenzi ye-PyTorch TopK nge-DeepSelect"),
@@ -115,14 +133,16 @@ int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_ro
 
 /* dsel_topk with the out-of-range fills given (DeepSelect tutorial, section
  * "Ukusebenza Ngemigqa Enobude Obuhlukahlukene": slots past a row's valid
- * length hold `idx_oob_fill_value` and `value_oob_fill_value`).  Same
- * arguments, then:
+ * length hold `idx_oob_fill_value` and `value_oob_fill_value`) and the row
+ * order chosen.  Same arguments, then:
  * idx_fill        index written to slots [c, k) of a row (c = min(k, n));
  *                 must fit the index dtype (int32 range for DSEL_I32), else
  *                 DSEL_ERR_ARG.
  * val_fill_bits   raw bits of the value written there (bf16: <= 0xFFFF, else
  *                 DSEL_ERR_ARG).
- * dsel_topk is dsel_topk_ex with idx_fill -1 and val_fill_bits of -inf. */
+ * row_order       DSEL_ROWS_AUTO, DSEL_ROWS_NATURAL or DSEL_ROWS_DUAL_CHUNK.
+ * dsel_topk is dsel_topk_ex with idx_fill -1, val_fill_bits of -inf and
+ * DSEL_ROWS_AUTO. */
 int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
                  int64_t k, const int32_t *row_end,
                  int sorted_index, int indices_type, int return_value,
@@ -130,7 +150,7 @@ int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x
                  void *out_val, int64_t val_row_stride,
                  uint8_t *nan_flag,
                  void *workspace, size_t *workspace_bytes,
-                 void *stream, int64_t idx_fill, uint32_t val_fill_bits);
+                 void *stream, int64_t idx_fill, uint32_t val_fill_bits, int row_order);
 
 /*
  * Error state of split rows on a workspace, and its reset.
@@ -178,7 +198,8 @@ int dsel_topk_noalloc(const void *x, int dtype, int64_t rows, int64_t cols, int6
                       int sorted_index, int indices_type, int return_value,
                       void *out_idx, int64_t idx_row_stride,
                       void *out_val, int64_t val_row_stride,
-                      uint8_t *nan_flag, void *stream, int64_t idx_fill, uint32_t val_fill_bits);
+                      uint8_t *nan_flag, void *stream, int64_t idx_fill, uint32_t val_fill_bits,
+                      int row_order);
 
 /*
  * Gather of key rows at selected positions, batch offset folded in.

@@ -31,6 +31,9 @@ DSEL_OK, DSEL_ERR_ARG, DSEL_ERR_K, DSEL_ERR_ALIGN, DSEL_ERR_WORKSPACE, DSEL_ERR_
     DSEL_ERR_SPLIT = 0, -1, -2, -3, -4, -5, -6
 DSEL_BF16, DSEL_F32 = 0, 1
 DSEL_I32, DSEL_I64 = 0, 1
+DSEL_ROWS_AUTO, DSEL_ROWS_NATURAL, DSEL_ROWS_DUAL_CHUNK = 0, 1, 2
+_ROW_ORDERS = {None: DSEL_ROWS_AUTO, "auto": DSEL_ROWS_AUTO, "natural": DSEL_ROWS_NATURAL,
+               "dual_chunk": DSEL_ROWS_DUAL_CHUNK}
 _NAMES = {DSEL_ERR_ARG: "DSEL_ERR_ARG", DSEL_ERR_K: "DSEL_ERR_K", DSEL_ERR_ALIGN: "DSEL_ERR_ALIGN",
           DSEL_ERR_WORKSPACE: "DSEL_ERR_WORKSPACE", DSEL_ERR_DEVICE: "DSEL_ERR_DEVICE",
           DSEL_ERR_SPLIT: "DSEL_ERR_SPLIT (a split row's workgroups did not all meet; "
@@ -56,7 +59,7 @@ def _load() -> ctypes.CDLL:
                               vp, vp, szp, vp]
     lib.dsel_topk_ex.restype = i32
     lib.dsel_topk_ex.argtypes = [vp, i32, i64, i64, i64, i64, vp, i32, i32, i32, vp, i64, vp,
-                                 i64, vp, vp, szp, vp, i64, ctypes.c_uint32]
+                                 i64, vp, vp, szp, vp, i64, ctypes.c_uint32, i32]
     lib.dsel_topk_check.restype = i32
     lib.dsel_topk_check.argtypes = [vp, ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_uint32)]
     lib.dsel_gather_rows.restype = i32
@@ -159,7 +162,7 @@ def _fill_bits(value, dtype: torch.dtype) -> int:
 
 
 def _topk_call(x, k, end, order, itype, return_value, idx, val, flag, ws_ptr, ws_bytes, sptr,
-               idx_fill=-1, val_fill=None):
+               idx_fill=-1, val_fill=None, row_order=0):
     return _lib.dsel_topk_ex(
         x.data_ptr(), _dtype_code(x.dtype), x.shape[0], x.shape[1], _row_stride(x),
         int(k), end.data_ptr() if end is not None else None,
@@ -167,7 +170,7 @@ def _topk_call(x, k, end, order, itype, return_value, idx, val, flag, ws_ptr, ws
         idx.data_ptr(), _row_stride(idx),
         val.data_ptr() if val is not None else None, _row_stride(val) if val is not None else 0,
         flag.data_ptr(), ws_ptr, ctypes.byref(ws_bytes), sptr, int(idx_fill),
-        _fill_bits(val_fill, x.dtype))
+        _fill_bits(val_fill, x.dtype), int(row_order))
 
 
 def _check_input(x: torch.Tensor) -> None:
@@ -184,7 +187,8 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
          indices_type: torch.dtype = torch.int32, return_value: bool = True,
          output_idx: Optional[torch.Tensor] = None, by_value: bool = False,
          idx_oob_fill_value: int = -1, value_oob_fill_value: Optional[float] = None,
-         abort_when_nan_found: bool = False, check: bool = False, stream=None
+         abort_when_nan_found: bool = False, check: bool = False, stream=None,
+         row_order: Optional[str] = None
          ) -> Tuple[Optional[torch.Tensor], torch.Tensor, torch.Tensor]:
     """Row-wise top-k of ``x`` [rows, cols] (bf16 or fp32), 1 <= topk <= 4096.
 
@@ -208,8 +212,14 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
     With ``stream`` given, the outputs and workspace are allocated and zeroed
     on that stream and the kernels run there; ordering against other streams
     (the producer of ``x``, the consumers of the outputs) is the caller's.
+    ``row_order`` ("natural", "dual_chunk", or None/"auto": dual chunk when
+    ``end`` is given) is the order in which the workers take rows; it
+    changes timing only, never the output.
     """
     _check_input(x)
+    if row_order not in _ROW_ORDERS:
+        raise ValueError(f"row_order must be one of {sorted(k for k in _ROW_ORDERS if k)} or None")
+    ro = _ROW_ORDERS[row_order]
     if sorted is not None:
         sorted_index = bool(sorted)
     order = 2 if by_value else int(bool(sorted_index))
@@ -237,12 +247,12 @@ def topk(x: torch.Tensor, topk: int, *, end: Optional[torch.Tensor] = None,
             sptr = int(s.cuda_stream)
             nb = ctypes.c_size_t(0)
             _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
-                              None, nb, sptr, idx_oob_fill_value, value_oob_fill_value),
+                              None, nb, sptr, idx_oob_fill_value, value_oob_fill_value, ro),
                    "dsel_topk (size query)")
             ws = _workspace(dev, sptr, nb.value)
             nb = ctypes.c_size_t(ws.numel())
             _check(_topk_call(x, topk, end, order, indices_type, return_value, idx, val, flag,
-                              ws.data_ptr(), nb, sptr, idx_oob_fill_value, value_oob_fill_value),
+                              ws.data_ptr(), nb, sptr, idx_oob_fill_value, value_oob_fill_value, ro),
                    "dsel_topk")
             if check:
                 _check_one(ws, sptr)

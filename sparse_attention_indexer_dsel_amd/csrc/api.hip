@@ -262,7 +262,7 @@ extern "C" int dsel_topk(const void *x, int dtype, int64_t rows, int64_t cols,
     return dsel_topk_ex(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index,
                         indices_type, return_value, out_idx, idx_row_stride, out_val,
                         val_row_stride, nan_flag, workspace, workspace_bytes, stream, -1,
-                        dtype == DSEL_BF16 ? 0xFF80u : 0xFF800000u);
+                        dtype == DSEL_BF16 ? 0xFF80u : 0xFF800000u, DSEL_ROWS_AUTO);
 }
 
 namespace {
@@ -273,7 +273,7 @@ int topk_entry(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_r
                int return_value, void *out_idx, int64_t idx_row_stride, void *out_val,
                int64_t val_row_stride, uint8_t *nan_flag, void *workspace,
                size_t *workspace_bytes, void *stream, int64_t idx_fill, uint32_t val_fill_bits,
-               int64_t max_ws_words) {
+               int row_order, int64_t max_ws_words) {
     // sorted_index 0 and 1: the output is ascending by construction; 2: a
     // value-order pass follows the select
     if (sorted_index < 0 || sorted_index > 2) return DSEL_ERR_ARG;
@@ -282,6 +282,7 @@ int topk_entry(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_r
     if (indices_type == DSEL_I32 && (idx_fill < INT32_MIN || idx_fill > INT32_MAX))
         return DSEL_ERR_ARG;
     if (dtype == DSEL_BF16 && val_fill_bits > 0xFFFFu) return DSEL_ERR_ARG;
+    if (row_order < DSEL_ROWS_AUTO || row_order > DSEL_ROWS_DUAL_CHUNK) return DSEL_ERR_ARG;
     if (rows < 0 || cols < 1) return DSEL_ERR_ARG;
     if (k < 1 || k > 4096) return DSEL_ERR_K;
     if (!workspace_bytes) return DSEL_ERR_ARG;
@@ -335,6 +336,10 @@ int topk_entry(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_r
     a.idx_fill = idx_fill;
     a.val_fill = val_fill_bits;
     a.spin_limit = spin_limit();
+    // rows of ragged length take the dual-chunk order unless told otherwise
+    a.row_order = row_order == DSEL_ROWS_DUAL_CHUNK || (row_order == DSEL_ROWS_AUTO && row_end)
+                      ? kRowsDualChunk
+                      : kRowsNatural;
     // (only the values instance of the one-wave kernel reads a separate stage)
     a.stage_words = pl.kind == kTopkWave && a.ret_val
                         ? wave_stage_words(dtype, k, a.idx64 ? 8 : 4, a.ret_val, pl.per_cu)
@@ -409,7 +414,7 @@ extern "C" int dsel_topk_noalloc(const void *x, int dtype, int64_t rows, int64_t
                                  int sorted_index, int indices_type, int return_value,
                                  void *out_idx, int64_t idx_row_stride, void *out_val,
                                  int64_t val_row_stride, uint8_t *nan_flag, void *stream,
-                                 int64_t idx_fill, uint32_t val_fill_bits) {
+                                 int64_t idx_fill, uint32_t val_fill_bits, int row_order) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     size_t bytes = (size_t)kScratchWords * sizeof(uint32_t);
     // argument checks and the plan first (nothing launched on an error)
@@ -417,7 +422,7 @@ extern "C" int dsel_topk_noalloc(const void *x, int dtype, int64_t rows, int64_t
     int st = topk_entry(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index,
                         indices_type, return_value, out_idx, idx_row_stride, out_val,
                         val_row_stride, nan_flag, nullptr, &need, stream, idx_fill,
-                        val_fill_bits, kScratchWords);
+                        val_fill_bits, row_order, kScratchWords);
     if (st != DSEL_OK || rows == 0) return st;
     uint32_t *ws = nullptr;
     if (need > 0) {  // split rows: the scratch
@@ -429,7 +434,7 @@ extern "C" int dsel_topk_noalloc(const void *x, int dtype, int64_t rows, int64_t
     return topk_entry(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index, indices_type,
                       return_value, out_idx, idx_row_stride, out_val, val_row_stride, nan_flag,
                       ws ? ws : reinterpret_cast<uint32_t *>(out_idx), ws ? &bytes : &need,
-                      stream, idx_fill, val_fill_bits, kScratchWords);
+                      stream, idx_fill, val_fill_bits, row_order, kScratchWords);
 }
 
 extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols,
@@ -437,10 +442,11 @@ extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols
                             int sorted_index, int indices_type, int return_value, void *out_idx,
                             int64_t idx_row_stride, void *out_val, int64_t val_row_stride,
                             uint8_t *nan_flag, void *workspace, size_t *workspace_bytes,
-                            void *stream, int64_t idx_fill, uint32_t val_fill_bits) {
+                            void *stream, int64_t idx_fill, uint32_t val_fill_bits,
+                            int row_order) {
     return topk_entry(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index, indices_type,
                       return_value, out_idx, idx_row_stride, out_val, val_row_stride, nan_flag,
-                      workspace, workspace_bytes, stream, idx_fill, val_fill_bits, 0);
+                      workspace, workspace_bytes, stream, idx_fill, val_fill_bits, row_order, 0);
 }
 
 extern "C" int dsel_topk_check(void *workspace, size_t workspace_bytes, void *stream,

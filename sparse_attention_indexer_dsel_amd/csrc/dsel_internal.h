@@ -100,7 +100,21 @@ struct TopkArgs {
     uint32_t stage_words;    // one-wave rows: LDS words per wave for the staged output
                              // after the histograms (0: staged in the histogram's space)
     uint32_t spin_limit;     // split rows: polls of a rendezvous before it gives up
+    int row_order;           // kRowsNatural or kRowsDualChunk (rows of one workgroup or wave)
 };
+
+// Order in which the workgroups (one-wave rows: the waves) of a launch take
+// rows.  Dual chunk (PaddleFleet PR #1762, Description: the dual-chunk
+// causal split): the t-th taker gets row t/2 for even t and row R-1-t/2 for
+// odd t, so neighbouring takers pair a row from the front with its mirror
+// from the back, and takers started early hold rows from both ends of a
+// causal (or anti-causal) ramp of lengths.  A permutation of [0, R): the
+// outputs are the same bytes in either order.
+enum { kRowsNatural = 0, kRowsDualChunk = 1 };
+
+__host__ __device__ inline int64_t taker_row(int order, int64_t t, int64_t R) {
+    return order == kRowsDualChunk ? ((t & 1) ? R - 1 - (t >> 1) : (t >> 1)) : t;
+}
 
 // Polls of a split-row rendezvous before it gives up and records an error
 // (about 0.1 s at the s_sleep granularity).

@@ -2625,8 +2625,10 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     const List ent = list_of<K>(s_dyn + list_base<K>());
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
 
+    const int64_t R = a.rows - a.row0;
 #pragma unroll 1
-    for (int64_t row = a.row0 + blockIdx.x; row < a.rows; row += gridDim.x) {
+    for (int64_t t = blockIdx.x; t < R; t += gridDim.x) {
+        const int64_t row = a.row0 + taker_row(a.row_order, t, R);
         const int64_t n = valid_length(a, row);
         const raw_t *xr = x + row * a.x_stride;
         if (n <= a.k) {
@@ -2884,8 +2886,10 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
     const raw_t *x = reinterpret_cast<const raw_t *>(a.x);
     const int64_t step = (int64_t)gridDim.x * NWAVE;
 
+    const int64_t R = a.rows - a.row0;
 #pragma unroll 1
-    for (int64_t row = a.row0 + (int64_t)blockIdx.x * NWAVE + wid; row < a.rows; row += step) {
+    for (int64_t t = (int64_t)blockIdx.x * NWAVE + wid; t < R; t += step) {
+        const int64_t row = a.row0 + taker_row(a.row_order, t, R);
         const int64_t n = valid_length(a, row);
         const raw_t *xr = x + row * a.x_stride;
         if (n <= a.k) {
@@ -3084,7 +3088,7 @@ __device__ __forceinline__ void w16_write(const uint32_t (&kw)[LPL * 4], int any
 // stage (index, and with RVAL the rebuilt value at voff), the others to a
 // per-lane dummy word (no branches and no exec-mask changes per element).
 // CUT: equal keys at T are only partly taken (those at columns <= cut).
-template <int LPL, bool CUT, bool I64, bool RVAL>
+template <int LPL, bool CUT, bool I64, bool RVAL, bool IDX = true>
 __device__ __forceinline__ void w16_stage(const uint32_t (&kw)[LPL * 4], int any, int lane,
                                           uint32_t T, uint32_t cut, char *stage, uint32_t voff,
                                           char *dummy, uint32_t &amb) {
@@ -3115,10 +3119,10 @@ __device__ __forceinline__ void w16_stage(const uint32_t (&kw)[LPL * 4], int any
                 const uint32_t key = h ? (w >> 16) : (w & 0xFFFFu);
                 const uint32_t col = c0 + 2 * q + h;
                 const bool t = take(key, col);
-                if constexpr (I64) {
+                if constexpr (IDX && I64) {
                     char *p = t ? stage + pos * 8u : dummy;
                     *reinterpret_cast<uint64_t *>(p) = (uint64_t)col;
-                } else {
+                } else if constexpr (IDX) {
                     char *p = t ? stage + pos * 4u : dummy;
                     *reinterpret_cast<uint32_t *>(p) = col;
                 }
@@ -3151,13 +3155,16 @@ __global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
     const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x);
     const int64_t step = (int64_t)gridDim.x * NWAVE;
 
+    const int64_t R = a.rows - a.row0;
+
 #pragma unroll 1
-    for (int64_t row = a.row0 + (int64_t)blockIdx.x * NWAVE + wid; row < a.rows; row += step) {
+    for (int64_t t = (int64_t)blockIdx.x * NWAVE + wid; t < R; t += step) {
+        const int64_t row = a.row0 + taker_row(a.row_order, t, R);
         // the lane index again, opaque: the per-lane column numbers derived
         // from it must not be hoisted out of the row loop into VGPRs
         const int lane = tid() & 63;
-        const int64_t n = valid_length(a, row);
         const uint16_t *xr = x + row * a.x_stride;
+        const int64_t n = valid_length(a, row);
         if (n <= a.k) {
             if constexpr (RV) {
                 write_short_idx(a, row, n, 0, 0, a.k, lane, 64);
@@ -3323,15 +3330,43 @@ __global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
         // the write
         const bool rv = RV && a.ret_val;  // (the values instance is launched only with values)
         const uint32_t idx_bytes = a.idx64 ? 8u : 4u;
-        const uint32_t voff = ((uint32_t)a.k * idx_bytes + 15u) & ~15u;
-        const uint32_t sbytes = voff + (rv ? (uint32_t)a.k * 2u : 0u);
+        const uint32_t ibytes = (uint32_t)a.k * idx_bytes;
         // staged when the slots fit the stage; in the histogram's space they
-        // must leave its last 256 bytes (the spare bins) to the dummy stores
-        const bool staged = sbytes <= (RV && a.stage_words ? stage_cap : (uint32_t)W16_BINS * 4u);
+        // must leave its last 256 bytes (the spare bins) to the dummy stores.
+        // Without a stage of its own, a row with values stages its indices
+        // and then its values there, one after the other ("two").
+        bool staged, two = false;
+        uint32_t voff;
+        if (RV && a.stage_words) {
+            voff = (ibytes + 15u) & ~15u;
+            staged = voff + (rv ? (uint32_t)a.k * 2u : 0u) <= stage_cap;
+        } else {
+            staged = ibytes <= (uint32_t)W16_BINS * 4u && (!rv || (uint32_t)a.k * 2u <= (uint32_t)W16_BINS * 4u);
+            two = rv && staged;
+            voff = two ? 0u : (ibytes + 15u) & ~15u;
+        }
         uint32_t amb = 0;
-        if (staged) {
+        char *const dummy = reinterpret_cast<char *>(hist + W16_BINS + (lane & ~1));
+        if (two) {
+            if constexpr (RV) {
+                wave_sync();  // the histogram is dead: its space holds the indices
+                const bool c = cut != 0xFFFFFFFFu;
+                if (a.idx64) {
+                    if (c) w16_stage<LPL, true, true, false>(kw, any, lane, T, cut, stage, 0u, dummy, amb);
+                    else   w16_stage<LPL, false, true, false>(kw, any, lane, T, cut, stage, 0u, dummy, amb);
+                } else {
+                    if (c) w16_stage<LPL, true, false, false>(kw, any, lane, T, cut, stage, 0u, dummy, amb);
+                    else   w16_stage<LPL, false, false, false>(kw, any, lane, T, cut, stage, 0u, dummy, amb);
+                }
+                wave_sync();
+                wave_copy_out(stage, reinterpret_cast<char *>(a.out_idx) + row * a.idx_stride * (int64_t)idx_bytes,
+                              ibytes, lane);
+                wave_sync();  // the indices are read out: the values take their place
+                if (c) w16_stage<LPL, true, false, true, false>(kw, any, lane, T, cut, stage, 0u, dummy, amb);
+                else   w16_stage<LPL, false, false, true, false>(kw, any, lane, T, cut, stage, 0u, dummy, amb);
+            }
+        } else if (staged) {
             wave_sync();  // the histogram is dead: its space may hold the row's slots
-            char *dummy = reinterpret_cast<char *>(hist + W16_BINS + (lane & ~1));
             const bool c = cut != 0xFFFFFFFFu;
             if (rv) {
                 if constexpr (RV) {
@@ -3383,8 +3418,9 @@ __global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
         }
         if (staged) {
             wave_sync();
-            wave_copy_out(stage, reinterpret_cast<char *>(a.out_idx) + row * a.idx_stride * (int64_t)idx_bytes,
-                          (uint32_t)a.k * idx_bytes, lane);
+            if (!two)
+                wave_copy_out(stage, reinterpret_cast<char *>(a.out_idx) + row * a.idx_stride * (int64_t)idx_bytes,
+                              ibytes, lane);
             if (rv)
                 wave_copy_out(stage + voff,
                               reinterpret_cast<char *>(a.out_val) + row * a.val_stride * 2,
@@ -3664,6 +3700,11 @@ uint32_t wave_hist_words(int dtype) {
 uint32_t wave_stage_words(int dtype, int64_t k, int idx_bytes, int ret_val, int per_cu) {
     constexpr uint64_t kLdsPerCu = 160u * 1024u, kLdsPerWg = 64u * 1024u;
     const uint32_t base = wave_hist_words(dtype);
+    // bf16 rows stage indices and values one after the other in the
+    // histogram's first W16_BINS words when each fits there
+    if (dtype == 0 && (uint64_t)k * (uint64_t)idx_bytes <= (uint64_t)W16_BINS * 4u &&
+        (!ret_val || (uint64_t)k * 2u <= (uint64_t)W16_BINS * 4u))
+        return 0;
     const uint64_t stage = (((uint64_t)k * (uint64_t)idx_bytes + 15u) & ~(uint64_t)15u) +
                            (ret_val ? (uint64_t)k * (dtype == 0 ? 2u : 4u) : 0u);
     const uint64_t words = (stage + 15u) / 16u * 4u;  // whole 16-byte units: every stage stays aligned

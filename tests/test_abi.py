@@ -114,7 +114,7 @@ def test_gather_host_checks(lib):
     assert call(R=0) == 0             # empty: nothing launched
 
 
-def _topk_ex(lib, idx_fill, val_bits, dtype=0, itype=0):
+def _topk_ex(lib, idx_fill, val_bits, dtype=0, itype=0, row_order=0):
     nb = ctypes.c_size_t(0)
     f = lib.dsel_topk_ex
     f.restype = ctypes.c_int
@@ -122,9 +122,9 @@ def _topk_ex(lib, idx_fill, val_bits, dtype=0, itype=0):
                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p,
-                  ctypes.c_int64, ctypes.c_uint32]
+                  ctypes.c_int64, ctypes.c_uint32, ctypes.c_int]
     return f(16, dtype, 4, 64, 64, 8, None, 0, itype, 0, 16, 16, None, 0, None, None,
-             ctypes.byref(nb), None, idx_fill, val_bits)
+             ctypes.byref(nb), None, idx_fill, val_bits, row_order)
 
 
 def test_topk_ex_fill_checks(lib):
@@ -132,6 +132,8 @@ def test_topk_ex_fill_checks(lib):
     assert _topk_ex(lib, 2 ** 31, 0xFF80) == -1               # int32 index fill out of range
     assert _topk_ex(lib, -(2 ** 31) - 1, 0xFF80) == -1
     assert _topk_ex(lib, -1, 0x1FF80) == -1                    # bf16 fill wider than 16 bits
+    assert _topk_ex(lib, -1, 0xFF80, row_order=3) == -1        # no such row order
+    assert _topk_ex(lib, -1, 0xFF80, row_order=-1) == -1
 
 
 def test_topk_check_host_checks(lib):

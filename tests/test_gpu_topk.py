@@ -74,21 +74,23 @@ def assert_workspaces_clean(dsel):
         assert int(ws[region:].count_nonzero()) == 0, "row slots must be zero after a call"
 
 
-def run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value, output_idx=None):
+def run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value, output_idx=None,
+            row_order=None):
     xd = to_device(x)
     re = row_end.cuda() if row_end is not None else None
     v, i, f = dsel.topk(xd, k, end=re, sorted_index=sorted_index, indices_type=indices_type,
-                        return_value=return_value, output_idx=output_idx)
+                        return_value=return_value, output_idx=output_idx, row_order=row_order)
     torch.cuda.synchronize()
     return (gpu_bits(v) if v is not None else None, i.cpu().numpy(), f.cpu().numpy())
 
 
 def check_case(dsel, orc, name, x, k, row_end=None, sorted_index=False,
-               indices_type=torch.int32, return_value=True, G=None, one=None):
+               indices_type=torch.int32, return_value=True, G=None, one=None, row_order=None):
     say(f"[topk] {name} shape={tuple(x.shape)} stride={x.stride()} k={k} G={G} one={one} "
-        f"sorted={sorted_index} idx={indices_type} val={return_value}")
+        f"sorted={sorted_index} idx={indices_type} val={return_value} order={row_order}")
     with blocks_per_row(G), one_exchange(one):
-        got = run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value)
+        got = run_gpu(dsel, x, k, row_end, sorted_index, indices_type, return_value,
+                      row_order=row_order)
     want = oracle_topk(orc, x, k, row_end, sorted_index, indices_type, return_value)
     n = valid_lengths(x.shape[0], x.shape[1], row_end)
     compare_topk(got, want, n, k, sorted_index, name)
@@ -429,23 +431,42 @@ def test_value_order_workloads(dsel, orc, cfg):
 
 @pytest.mark.parametrize("cols", [2048, 1536])
 def test_wave_rows_with_values_staged(dsel, orc, cols):
-    """One-wave bf16 rows with values whose k int32 indices and k values do
-    not fit a wave's histogram space (k > 725), so the values launch stages
-    them in an LDS region of its own: k not a multiple of 4 or 8, rows
-    longer and shorter than k, NaN rows, +-0 and infinities; ascending and
-    value order; int64 indices (whose stage does not fit) as a control."""
+    """One-wave bf16 rows with values, every way the output is staged in
+    LDS: k int32 indices (up to k = 1024) or int64 indices (up to 512) fit
+    the wave's histogram space, then the k values take their place there
+    (k = 300, 512, 726, 1001, 1024); larger k take an LDS region of their own
+    (1500, 2000; int64 at 1001).  k not a multiple of 4 or 8, rows longer
+    and shorter than k, NaN rows, +-0 and infinities; ascending and value
+    order."""
     x = W.random_rows(0x57A6 + cols, 24, cols, W.BF16, "special")
     W.plant_nans(x, 0x57A7 + cols, 3)
     ends = [cols, cols - 1, cols - 7, 2000, 1800, 1500, 1200, 1100, 1025, 1024, 1023, 1001,
             1000, 900, 727, 726, 725, 600, 100, 3, 1, 0, cols, cols - 33]
     re = torch.tensor([min(e, cols) for e in ends], dtype=torch.int32)
-    for k in (726, 1001, 1024, 1500, 2000):
+    for k in (300, 512, 726, 1001, 1024, 1500, 2000):
         if k >= cols:
             continue
         check_case(dsel, orc, f"staged/{cols}/k{k}", x, k, re, False, torch.int32, True)
         check_case(dsel, orc, f"staged/{cols}/k{k}/sorted", x, k, re, True, torch.int32, True)
         check_value_order(dsel, orc, f"staged/{cols}/k{k}/by_value", x, k, re, torch.int32, True)
-    check_case(dsel, orc, f"staged/{cols}/k1001/i64", x, 1001, re, False, torch.int64, True)
+    for k in (300, 512, 1001):
+        check_case(dsel, orc, f"staged/{cols}/k{k}/i64", x, k, re, False, torch.int64, True)
+
+
+@pytest.mark.parametrize("order", ["natural", "dual_chunk", None])
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_row_orders(dsel, orc, dt, order):
+    """Every row order gives the oracle's output: one-wave rows (2048 and
+    700 columns) and whole rows (9000 columns) under causal row ends, odd
+    and even row counts, a single row, and rows without row ends."""
+    shapes = ((257, 2048, 700), (256, 2048, 1024), (64, 700, 100), (33, 9000, 512), (1, 1000, 10))
+    for i, (rows, cols, k) in enumerate(shapes):
+        x = W.random_rows(0x0D0 + i, rows, cols, dt, "normal")
+        re = ((torch.arange(rows, dtype=torch.int64) + 1) * cols // rows).to(torch.int32)
+        check_case(dsel, orc, f"order/{order}/{rows}x{cols}", x, k, re, False, torch.int32, True,
+                   row_order=order)
+        check_case(dsel, orc, f"order/{order}/{rows}x{cols}/full", x, k, None, False, torch.int64,
+                   False, row_order=order)
 
 
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])

@@ -30,7 +30,7 @@ def dsel():
     f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
-                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32]
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int]
     return d
 
 
@@ -59,14 +59,14 @@ def _run_both(dsel, x, k, row_end, order, itype, ret, fill=-1):
     nb = ctypes.c_size_t(0)
     args = (x.data_ptr(), dt, rows, cols, x.stride(0), k, re, order, it, int(ret),
             a[0].data_ptr(), a[3], a[1].data_ptr(), a[4], a[2].data_ptr())
-    assert dsel._lib.dsel_topk_ex(*args, None, ctypes.byref(nb), sp, fill, fill_bits) == 0
+    assert dsel._lib.dsel_topk_ex(*args, None, ctypes.byref(nb), sp, fill, fill_bits, 0) == 0
     ws = torch.zeros(max(nb.value, 256), dtype=torch.uint8, device="cuda")
     nb = ctypes.c_size_t(ws.numel())
-    assert dsel._lib.dsel_topk_ex(*args, ws.data_ptr(), ctypes.byref(nb), sp, fill, fill_bits) == 0
+    assert dsel._lib.dsel_topk_ex(*args, ws.data_ptr(), ctypes.byref(nb), sp, fill, fill_bits, 0) == 0
     # the entry point that allocates nothing
     st = dsel._lib.dsel_topk_noalloc(x.data_ptr(), dt, rows, cols, x.stride(0), k, re, order, it,
                                      int(ret), b[0].data_ptr(), b[3], b[1].data_ptr(), b[4],
-                                     b[2].data_ptr(), sp, fill, fill_bits)
+                                     b[2].data_ptr(), sp, fill, fill_bits, 0)
     assert st == 0, st
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]), "indices differ"
