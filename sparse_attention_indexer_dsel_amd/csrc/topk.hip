@@ -1689,6 +1689,25 @@ __device__ OneResult one_exchange(const TopkArgs &a, int c, int G, int len,
     return r;
 }
 
+// The window exchange places a chunk's window from one load in kWxSample:
+// only those loads' keys go into the 12-bit histogram (a quarter of the LDS
+// atomics of a full one).  Every count the exchange relies on comes from the
+// chunk's exact list of candidates.
+constexpr int kWxSample = 4;
+
+// Columns of a chunk of len columns that the sampled loads cover.
+template <int LOADS>
+__device__ __forceinline__ uint32_t wx_sample_len(int len) {
+    constexpr int SPAN = NT * 4;
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < LOADS; j += kWxSample) {
+        const int r = len - j * SPAN;
+        s += r <= 0 ? 0u : (r >= SPAN ? (uint32_t)SPAN : (uint32_t)r);
+    }
+    return s;
+}
+
 // ---------------------------------------------------------------------------
 // Window exchange of a split fp32 row (G <= kOneMaxSplit workgroups, one
 // rendezvous).
@@ -1747,20 +1766,36 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     uint32_t wlo = 0, whi = 0, above = 0, cw0 = 0, cw1 = 0, cw2 = 0, ok = 1, run = 0;
     const bool empty = len <= 0;
     if (!empty) {
+        // q: the chunk's share of k; qs: the same share of the sample
         uint64_t q = ((uint64_t)k * (uint64_t)len + (uint64_t)n - 1) / (uint64_t)n;
         q = q < 1 ? 1 : (q > (uint64_t)len ? (uint64_t)len : q);
-        const Digit d = find_digit_4096(L.hist, (uint32_t)q, ent.w + 2 * (cap + 64), L.red, L.out);
+        const uint32_t slen = wx_sample_len<LOADS>(len);
+        uint64_t qs = (q * slen + (uint64_t)len - 1) / (uint64_t)len;
+        qs = qs < 1 ? 1 : (qs > slen ? slen : qs);
+        const Digit d = find_digit_4096(L.hist, (uint32_t)qs, ent.w + 2 * (cap + 64), L.red, L.out);
         wlo = d.v > 0 ? d.v - 1 : 0;
         whi = d.v < (uint32_t)kWxBins - 1 ? d.v + 1 : d.v;
-        above = d.above - (whi > d.v ? L.hist[whi] : 0u);
-        cw0 = L.hist[wlo];
-        cw1 = wlo + 1 <= whi ? L.hist[wlo + 1] : 0u;
-        cw2 = wlo + 2 <= whi ? L.hist[wlo + 2] : 0u;
-        ok = (cw0 + cw1 + cw2 < (uint32_t)kWxKeys) ? 1u : 0u;  // each count then fits 10 bits
-        __syncthreads();  // every thread has read the histogram
         const uint32_t T1 = max(wlo << SH, 1u);
         run = compact_candidates<K, LOADS, true>(kw, len, T1, L.wtot, L.base, ent, cap);
-        if (run > cap) ok = 0;  // uniform
+        if (run > cap) {
+            ok = 0;  // uniform
+        } else {
+            // the window's counts from the list (it holds every key of bin
+            // wlo and up: the rest lie above the window)
+            const uint32_t nwin = whi - wlo + 1u;
+            uint32_t c01 = 0, c2 = 0;
+            for (uint32_t i = (uint32_t)t; i < run; i += NT) {
+                const uint32_t w = (list_key<K>(ent, i) >> SH) - wlo;
+                c01 += w == 0 ? 1u : (w == 1 && nwin > 1 ? 0x10000u : 0u);
+                c2 += w == 2 && nwin > 2 ? 1u : 0u;
+            }
+            c01 = block_scan(c01, L.red).total;
+            cw2 = block_scan(c2, L.red).total;
+            cw0 = c01 & 0xFFFFu;
+            cw1 = c01 >> 16;
+            above = run - cw0 - cw1 - cw2;
+            ok = (cw0 + cw1 + cw2 < (uint32_t)kWxKeys) ? 1u : 0u;  // each count then fits 10 bits
+        }
     }
     uint32_t *mine = area + (int64_t)c * kWxWords;
     if (ok && !empty) {
@@ -1768,9 +1803,10 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         const uint32_t E = (run + NT - 1) / NT;
         const uint32_t i0 = (uint32_t)t * E, i1 = min(run, i0 + E);
         uint32_t m = 0;
+        const uint32_t nwin = whi - wlo + 1u;
         for (uint32_t i = i0; i < i1; ++i) {
             const uint32_t w = (list_key<K>(ent, i) >> SH) - wlo;
-            m += w == 0 ? 1u : (w == 1 ? (1u << 10) : (w == 2 ? (1u << 20) : 0u));
+            m += w >= nwin ? 0u : (w == 0 ? 1u : (w == 1 ? (1u << 10) : (1u << 20)));
         }
         const uint32_t ex = block_scan(m, L.red).incl - m;
         uint32_t o0 = ex & 0x3FFu, o1 = cw0 + ((ex >> 10) & 0x3FFu), o2 = cw0 + cw1 + (ex >> 20);
@@ -1778,9 +1814,10 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         for (uint32_t i = i0; i < i1; ++i) {
             const uint32_t key = list_key<K>(ent, i);
             const uint32_t w = (key >> SH) - wlo;
+            if (w >= nwin) continue;
             if (w == 0) st_agent(dst + o0++, key);
             else if (w == 1) st_agent(dst + o1++, key);
-            else if (w == 2) st_agent(dst + o2++, key);
+            else st_agent(dst + o2++, key);
         }
     }
     if (t == 0) {
@@ -2405,8 +2442,8 @@ __device__ __forceinline__ uint32_t f32_key(uint32_t x) {
 }
 
 // The window exchange's first pass: each 16-byte load turned into four keys
-// and histogrammed (12-bit first digit) as soon as it arrives, with a
-// running max / min of the keys as the NaN probe.  Columns at or past len
+// as soon as it arrives, and one load in kWxSample histogrammed (12-bit
+// first digit), with a running max / min of the keys as the NaN probe.  Columns at or past len
 // get key 0 (and this lane's spare bin).  If this thread saw a NaN (rare),
 // returns true with the NaN keys NOT yet moved to the top: the caller fixes
 // them and rebuilds the histogram.
@@ -2431,8 +2468,10 @@ __device__ __forceinline__ bool f32_keys_hist12(const uint4 (&v)[LOADS], int len
             for (int q = 0; q < 4; ++q) kw[4 * j + q] = f32_key(x[q]);
             kmax = max(kmax, max(max(kw[4 * j], kw[4 * j + 1]), max(kw[4 * j + 2], kw[4 * j + 3])));
             kmin = min(kmin, min(min(kw[4 * j], kw[4 * j + 1]), min(kw[4 * j + 2], kw[4 * j + 3])));
+            if (j % kWxSample == 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) atomicAdd(&hist[kw[4 * j + q] >> 20], 1u);
+                for (int q = 0; q < 4; ++q) atomicAdd(&hist[kw[4 * j + q] >> 20], 1u);
+            }
         } else {
             int valid = len - (j * NT + me) * VEC;
             valid = valid < 0 ? 0 : (valid > VEC ? VEC : valid);
@@ -2442,7 +2481,7 @@ __device__ __forceinline__ bool f32_keys_hist12(const uint4 (&v)[LOADS], int len
                 kmax = max(kmax, kk);
                 kmin = min(kmin, kk);
                 kw[4 * j + q] = q < valid ? kk : 0u;
-                atomicAdd(&hist[q < valid ? (kk >> 20) : spare], 1u);
+                if (j % kWxSample == 0) atomicAdd(&hist[q < valid ? (kk >> 20) : spare], 1u);
             }
         }
     }
@@ -2512,7 +2551,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
         for (int w = 0; w < LOADS * 4; ++w) {
             const uint32_t key = K::fix_nan_word(kw[w]);
             kw[w] = key;
-            atomicAdd(&L.hist[key ? (key >> 20) : spare], 1u);
+            if ((w / 4) % kWxSample == 0) atomicAdd(&L.hist[key ? (key >> 20) : spare], 1u);
         }
         __syncthreads();
     }
