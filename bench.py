@@ -405,6 +405,57 @@ def _event_time(torch, stream, fn, reps: int = 5) -> float:
     return best
 
 
+def measure_fused(dsel, torch, case, stream, steps, warmup) -> dict:
+    """The top-k and the gather of the workload's keys as one call
+    (dsel_topk_gather) against the two-call chain (the top-k, then one
+    gather launch per key), outputs reused across steps, inputs rotated."""
+    tb = TopkBench(dsel, torch, case, stream)
+    dev = torch.device("cuda")
+    rows = case.x.shape[0]
+    B = case.gather_batch
+    R = rows // B
+    keys = [k.to(dev) for k in case.keys]
+    idx = torch.empty(rows, -(-case.k // 4) * 4, dtype=case.indices_type, device=dev)
+    outs = [torch.empty(rows, case.k, k.shape[2], dtype=k.dtype, device=dev) for k in keys]
+    gouts = [o.view(B, R, case.k, -1) for o in outs]
+
+    def fused(i):
+        dsel.topk_gather(tb.xs[i % tb.ncopy], case.k, keys, rows_per_batch=R, end=tb.row_end,
+                         indices_type=case.indices_type, stream=stream, out=outs, output_idx=idx)
+
+    def chain(i):
+        dsel.topk(tb.xs[i % tb.ncopy], case.k, end=tb.row_end, indices_type=case.indices_type,
+                  return_value=False, stream=stream, output_idx=idx)
+        pos = idx[:, :case.k].view(B, R, case.k)
+        for k, o in zip(keys, gouts):
+            dsel.gather_rows(k, pos, out=o, stream=stream)
+
+    steps = min(max(steps, 2), 32)
+    t_f, k_f = graph_time(torch, stream, fused, steps, warmup, reps=3)
+    t_c, k_c = graph_time(torch, stream, chain, steps, warmup, reps=3)
+    n = _valid_lengths(case)
+    isz = 4 if case.indices_type == torch.int32 else 8
+    read = int(np.where(n > case.k, n, 0).sum()) * case.x.element_size() + 4 * rows
+    written = rows * case.k * isz + rows
+    # gathered rows written, and each key row the positions can reach read
+    # once (rows below the longest valid length, per batch)
+    gbytes = sum(rows * case.k * k.shape[2] * k.element_size() for k in case.keys)
+    gbytes += sum(int(min(k.shape[1], n.max())) * k.shape[2] * k.element_size() * B
+                  for k in case.keys)
+    alg = read + written + gbytes
+    res = {"fused_us": t_f * 1e6, "fused_kernel_us": k_f * 1e6,
+           "chain_us": t_c * 1e6, "chain_kernels_us": k_c * 1e6,
+           "fused_vs_chain": t_c / t_f,
+           "algorithmic_bytes": alg,
+           "roofline": roofline(alg, k_f, f"dsel_topk_gather ({case.name})"),
+           "how": "one dsel_topk_gather call (select and gather in the select's kernel) "
+                  "against dsel_topk then one dsel_gather_rows per key, same outputs, "
+                  "graph replay, inputs rotated"}
+    del tb, keys, outs, idx
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_floors(torch, stream) -> dict:
     """Launch floor and plain streaming rates of device kernels over 1 GiB
     (torch's own kernels: a reduction for read, a fill for write, a copy)."""
@@ -684,6 +735,7 @@ def main(argv=None):
             if c.keys:
                 entry["gather"] = measure_gather(dsel, torch, c, stream, 10, 2,
                                                  traffic=traffic_for(traffic, c.name, "gather"))
+                entry["topk_gather"] = measure_fused(dsel, torch, c, stream, 10, 2)
             per[c.name] = entry
             print(f"# {c.name}: {json.dumps(entry)}", file=sys.stderr, flush=True)
         line["per_config"] = per

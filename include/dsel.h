@@ -231,6 +231,58 @@ int dsel_gather_rows(const void *key, int dtype, int64_t batch, int64_t len, int
                      int64_t pos_row_stride,
                      void *out, void *stream);
 
+/*
+ * Top-k with the gather of keys at the selected positions, in one call.
+ *
+ * MindSpore hyper-parallel PR #1094: its candidate chain selects each query
+ * row's top positions, sorts them, masks the invalid ones and gathers the
+ * compressed keys there (key[batch_ids, safe_positions]); the English
+ * description and the section on the fix make the gather one index_select
+ * over batch-offset positions.  This entry point runs the chain's tail for a
+ * batch of rows: the top-k of dsel_topk (index fill -1, no values, row order
+ * DSEL_ROWS_AUTO), then for each key g
+ *     out_g[r, j, :] = key_g[r / rows_per_batch, p, :],  p = out_idx[r, j],
+ * where a position outside [0, len_g) (the -1 of a short row's padding) is
+ * clamped into it (DSEL_PAD_CLAMP: the "safe" positions, as dsel_gather_rows)
+ * or gives a row of zeros (DSEL_PAD_ZERO: the masked fill).  For one-wave
+ * bf16 rows (at most 2048 columns) and whole rows (at most 16384 columns)
+ * the select's own workers copy each row's keys as soon as it is selected:
+ * one launch, and the positions are never read back from HBM.  Other rows
+ * (split rows, fp32 rows of at most 2048 columns, sorted_index 2) run the
+ * select, then one gather launch per key.
+ *
+ * Top-k arguments as dsel_topk (return_value 0); sorted_index 0, 1 or 2 (the
+ * slots are gathered in the order the indices come out).
+ * rows_per_batch  query rows per batch: rows must be a multiple; row r
+ *                 belongs to batch r / rows_per_batch.
+ * keys, n_keys    host array of 1..4 key descriptors (DselGatherKey): key
+ *                 [batch, len, dim] of DSEL_BF16 or DSEL_F32 elements, last
+ *                 dim contiguous, element strides batch_stride and
+ *                 row_stride; out contiguous [rows, k, dim].  key, out,
+ *                 dim * elt and the strides * elt must be multiples of 16
+ *                 (else DSEL_ERR_ALIGN).
+ * pad             DSEL_PAD_CLAMP or DSEL_PAD_ZERO.
+ * workspace       as dsel_topk (NULL: size query, nothing launched).
+ * Returns DSEL_ERR_ARG for a bad key descriptor, n_keys, pad or
+ * rows_per_batch, else what dsel_topk returns for the same top-k.
+ */
+enum { DSEL_PAD_CLAMP = 0, DSEL_PAD_ZERO = 1 };
+
+typedef struct DselGatherKey {
+    const void *key;
+    int dtype;              /* DSEL_BF16 or DSEL_F32 */
+    int64_t len, dim;       /* rows per batch, elements per row */
+    int64_t batch_stride;   /* elements between batches */
+    int64_t row_stride;     /* elements between rows */
+    void *out;              /* contiguous [rows, k, dim] */
+} DselGatherKey;
+
+int dsel_topk_gather(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
+                     int64_t k, const int32_t *row_end, int sorted_index, int indices_type,
+                     void *out_idx, int64_t idx_row_stride, uint8_t *nan_flag,
+                     int64_t rows_per_batch, const DselGatherKey *keys, int n_keys, int pad,
+                     void *workspace, size_t *workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,7 +58,7 @@ class Oracle:
                                          vp, i64, vp, i64, vp, i32, i64, ctypes.c_uint32]
         self.lib.oracle_gather.restype = i32
         self.lib.oracle_gather.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i32, i64,
-                                           i64, i64, vp]
+                                           i64, i64, vp, i32]
 
     # -- top-k -------------------------------------------------------------
     def topk(self, x: np.ndarray, k: int, row_end: Optional[np.ndarray] = None,
@@ -109,8 +109,14 @@ class Oracle:
         return vals, idx, flag
 
     # -- gather --------------------------------------------------------------
-    def gather(self, key: np.ndarray, pos: np.ndarray) -> np.ndarray:
-        """key: [B, L, D] (any strides, last dim contiguous); pos: [B, R, P] int32/int64."""
+    def gather(self, key: np.ndarray, pos: np.ndarray, pad: str = "clamp") -> np.ndarray:
+        """key: [B, L, D] (any strides, last dim contiguous); pos: [B, R, P] int32/int64.
+
+        pad "clamp": positions clamped into [0, L-1] (the "safe" positions);
+        "zero": a position outside [0, L) gives a row of zeros (the masked fill).
+        """
+        if pad not in ("clamp", "zero"):
+            raise ValueError(pad)
         if key.ndim != 3 or key.strides[2] != key.itemsize:
             raise ValueError("key must be [B, L, D] with a contiguous last dim")
         if key.itemsize not in (2, 4):
@@ -126,7 +132,8 @@ class Oracle:
         out = np.empty((B, R, P, D), dtype=key.dtype)
         st = self.lib.oracle_gather(
             key.ctypes.data, key.itemsize, B, L, D, key.strides[0] // key.itemsize,
-            key.strides[1] // key.itemsize, pos.ctypes.data, pt, R, P, P, out.ctypes.data)
+            key.strides[1] // key.itemsize, pos.ctypes.data, pt, R, P, P, out.ctypes.data,
+            1 if pad == "zero" else 0)
         if st != 0:
             raise RuntimeError(f"oracle_gather failed: {st}")
         return out

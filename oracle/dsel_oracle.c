@@ -262,6 +262,9 @@ int oracle_topk(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_
 
 /*
  * out[b, r, j, :] = key[b, clamp(pos[b, r, j], 0, len-1), :]
+ * (MindSpore hyper-parallel PR #1094: key[batch_ids, safe_positions]); with
+ * pad_zero, a position outside [0, len) gives a row of zeros instead (the
+ * MaskedFill step of the same page's candidate chain).
  * key is addressed through element strides (batch, row); its last dim is
  * contiguous.  pos is [batch, rows_per_batch, per_row] with row stride
  * pos_row_stride (elements) and batch stride rows_per_batch*pos_row_stride.
@@ -270,7 +273,7 @@ int oracle_topk(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_
 int oracle_gather(const void *key, int elt_size, int64_t batch, int64_t len, int64_t dim,
                   int64_t key_batch_stride, int64_t key_row_stride, const void *pos,
                   int pos_type, int64_t rows_per_batch, int64_t per_row,
-                  int64_t pos_row_stride, void *out) {
+                  int64_t pos_row_stride, void *out, int pad_zero) {
     if (batch < 0 || len < 1 || dim < 1 || rows_per_batch < 0 || per_row < 0) return -1;
     if (elt_size != 2 && elt_size != 4) return -1;
     if (pos_type != OR_I32 && pos_type != OR_I64) return -1;
@@ -292,6 +295,17 @@ int oracle_gather(const void *key, int elt_size, int64_t batch, int64_t len, int
 #if ORACLE_MUTANT == 10
                 p += 1; /* planted: position off by one */
 #endif
+                unsigned char *dst0 = O + (((size_t)(b * rows_per_batch + r) * (size_t)per_row + (size_t)j) * row_bytes);
+#if ORACLE_MUTANT == 14
+                int inside = p >= 0 && p <= len; /* planted: the masked fill lets position len through */
+#else
+                int inside = p >= 0 && p < len;
+#endif
+                if (pad_zero && !inside) {
+                    /* the masked fill: a position outside the key gives a row of zeros */
+                    memset(dst0, 0, row_bytes);
+                    continue;
+                }
                 if (p < 0) p = 0;
                 if (p > len - 1) p = len - 1;
 #if ORACLE_MUTANT == 9

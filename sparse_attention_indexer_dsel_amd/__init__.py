@@ -13,7 +13,9 @@ contiguous and whose row stride is a multiple of ``stride_requirement()[0]``
 bytes; the outputs' row strides are aligned to ``stride_requirement()[1]``
 bytes, so they may be non-contiguous views.  The gather follows MindSpore
 hyper-parallel PR #1094: ``gather_rows(key, pos)`` equals
-``key[batch_ids, pos.clamp(0, L-1)]``.
+``key[batch_ids, pos.clamp(0, L-1)]``, and ``topk_gather`` runs that
+page's chain tail (top-k, then the gather of one or more keys at the selected
+positions, clamped or zero-filled) in one call.
 """
 from __future__ import annotations
 
@@ -23,7 +25,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["stride_requirement", "topk", "gather_rows", "check_workspaces", "DselError", "LIB_PATH"]
+__all__ = ["stride_requirement", "topk", "gather_rows", "topk_gather", "check_workspaces",
+           "DselError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsel.so")
 
@@ -62,6 +65,9 @@ def _load() -> ctypes.CDLL:
                                  i64, vp, vp, szp, vp, i64, ctypes.c_uint32, i32]
     lib.dsel_topk_check.restype = i32
     lib.dsel_topk_check.argtypes = [vp, ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_uint32)]
+    lib.dsel_topk_gather.restype = i32
+    lib.dsel_topk_gather.argtypes = [vp, i32, i64, i64, i64, i64, vp, i32, i32, vp, i64, vp, i64,
+                                     vp, i32, i32, vp, szp, vp]
     lib.dsel_gather_rows.restype = i32
     lib.dsel_gather_rows.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i32, i64, i64, i64,
                                      vp, vp]
@@ -302,3 +308,95 @@ def gather_rows(key: torch.Tensor, pos: torch.Tensor, *, out: Optional[torch.Ten
             key.stride(0), key.stride(1), pos.data_ptr(), _index_code(pos.dtype), R, P, prs,
             out.data_ptr(), sptr), "dsel_gather_rows")
     return out
+
+
+class _GatherKey(ctypes.Structure):
+    """DselGatherKey of dsel.h."""
+    _fields_ = [("key", ctypes.c_void_p), ("dtype", ctypes.c_int), ("len", ctypes.c_int64),
+                ("dim", ctypes.c_int64), ("batch_stride", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64), ("out", ctypes.c_void_p)]
+
+
+_PADS = {"clamp": 0, "zero": 1}
+
+
+def topk_gather(x: torch.Tensor, topk: int, keys, *, rows_per_batch: int,
+                end: Optional[torch.Tensor] = None, sorted_index: bool = False,
+                by_value: bool = False, indices_type: torch.dtype = torch.int32,
+                pad: str = "clamp", check: bool = False, stream=None, out=None,
+                output_idx: Optional[torch.Tensor] = None):
+    """Row-wise top-k of ``x`` and the gather of each key at the selected
+    positions, in one call (dsel_topk_gather).
+
+    ``keys``: a list of 1..4 tensors [B, L, D] (bf16/fp32, last dim
+    contiguous, any batch and row strides) with B = rows / rows_per_batch.
+    Returns ``(indices, nan_flag, outs)``: indices and flag as ``topk`` (no
+    values), and for each key a contiguous [rows, topk, D] tensor with
+    ``outs[g][r, j] = keys[g][r // rows_per_batch, p]``, p = indices[r, j];
+    a position outside [0, L) (a short row's -1 padding) is clamped into it
+    (``pad="clamp"``) or gives a zero row (``pad="zero"``).  ``out`` (a list
+    of contiguous [rows, topk, D] tensors, one per key) and ``output_idx``
+    (as in ``topk``) take caller-owned outputs.
+    """
+    _check_input(x)
+    if pad not in _PADS:
+        raise ValueError("pad must be 'clamp' or 'zero'")
+    keys = list(keys)
+    if not 1 <= len(keys) <= 4:
+        raise ValueError("between one and four keys")
+    rows = x.shape[0]
+    dev = x.device
+    if rows_per_batch < 1 or rows % rows_per_batch:
+        raise ValueError("rows must be a multiple of rows_per_batch")
+    B = rows // rows_per_batch
+    for kt in keys:
+        if kt.dim() != 3 or kt.shape[0] != B or kt.device != dev:
+            raise ValueError("each key must be [rows // rows_per_batch, L, D] on x's device")
+        if kt.shape[2] > 1 and kt.stride(2) != 1:
+            raise ValueError("a key's last dim must be contiguous")
+    if end is not None:
+        if end.dtype != torch.int32 or end.shape != (rows,) or end.device != dev:
+            raise ValueError("end must be an int32 [rows] tensor on x's device")
+        end = end.contiguous()
+    order = 2 if by_value else int(bool(sorted_index))
+    with torch.cuda.device(dev):
+        s = torch.cuda.current_stream(dev) if stream is None else stream
+        with torch.cuda.stream(s):
+            if output_idx is not None:
+                if (output_idx.dtype != indices_type or output_idx.dim() != 2
+                        or output_idx.shape[0] != rows or output_idx.shape[1] < topk
+                        or (output_idx.shape[1] > 1 and output_idx.stride(1) != 1)):
+                    raise ValueError("output_idx must be [rows, >= topk] of indices_type")
+                idx = output_idx
+            else:
+                idx = _aligned_empty(rows, topk, indices_type, dev)
+            flag = torch.empty(rows, dtype=torch.uint8, device=dev)
+            if out is not None:
+                outs = list(out)
+                if len(outs) != len(keys) or any(
+                        o.shape != (rows, topk, kt.shape[2]) or o.dtype != kt.dtype
+                        or not o.is_contiguous() for o, kt in zip(outs, keys)):
+                    raise ValueError("out must hold a contiguous [rows, topk, D] tensor per key")
+            else:
+                outs = [torch.empty(rows, topk, kt.shape[2], dtype=kt.dtype, device=dev)
+                        for kt in keys]
+            desc = (_GatherKey * len(keys))(*[
+                _GatherKey(kt.data_ptr(), _dtype_code(kt.dtype), kt.shape[1], kt.shape[2],
+                           kt.stride(0), kt.stride(1), o.data_ptr()) for kt, o in zip(keys, outs)])
+            sptr = int(s.cuda_stream)
+
+            def call(ws_ptr, nb):
+                return _lib.dsel_topk_gather(
+                    x.data_ptr(), _dtype_code(x.dtype), rows, x.shape[1], _row_stride(x), int(topk),
+                    end.data_ptr() if end is not None else None, order, _index_code(indices_type),
+                    idx.data_ptr(), _row_stride(idx), flag.data_ptr(), int(rows_per_batch), desc,
+                    len(keys), _PADS[pad], ws_ptr, ctypes.byref(nb), sptr)
+
+            nb = ctypes.c_size_t(0)
+            _check(call(None, nb), "dsel_topk_gather (size query)")
+            ws = _workspace(dev, sptr, nb.value)
+            nb = ctypes.c_size_t(ws.numel())
+            _check(call(ws.data_ptr(), nb), "dsel_topk_gather")
+            if check:
+                _check_one(ws, sptr)
+    return idx[:, :topk], flag, outs

@@ -56,6 +56,7 @@ struct TopkPlan {
     size_t ws_bytes = 0;
     bool one = false;  // split bf16 rows try the one-exchange select
     int per_cu = 0;    // one-wave rows: resident workgroups per CU the grid assumes
+    bool fused = false;  // a gather was asked for and the plan's kernel fuses it
 };
 
 // Candidate-list capacity: k plus room for the boundary bin of the first
@@ -118,8 +119,10 @@ int choose_G(int64_t rows, int64_t cols, int cus) {
 
 // max_ws_words > 0 caps the split layout (rows per launch) to that many
 // workspace words (the entry point that allocates nothing).
+// gather: plan for the fused gather's kernel where the row kind has one
+// (one-wave bf16 rows, whole rows); pl->fused says whether it does.
 int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, int64_t max_ws_words,
-              TopkPlan *pl) {
+              TopkPlan *pl, bool gather = false) {
     const int cus = cu_count();
     if (cus <= 0) return DSEL_ERR_DEVICE;
     const int vec = topk_vec(dtype);
@@ -141,10 +144,11 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, int
         pl->chunk = cols;
         pl->cap = 0;
         int per_cu = 0;
+        pl->fused = gather && dtype == DSEL_BF16 && !ret_val;
         // (the instance the call launches: the values instance may differ)
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, topk_kernel_ptr(dtype, pl->ept, kTopkWave, ret_val), kTopkThreads,
-                topk_dyn_lds(dtype, 0, pl->ept, kTopkWave)) != hipSuccess ||
+                &per_cu, topk_kernel_ptr(dtype, pl->ept, kTopkWave, ret_val, pl->fused ? 1 : 0),
+                kTopkThreads, topk_dyn_lds(dtype, 0, pl->ept, kTopkWave)) != hipSuccess ||
             per_cu <= 0)
             return DSEL_ERR_DEVICE;
         pl->per_cu = per_cu;
@@ -165,10 +169,12 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, int
         if (!pl->ept) return DSEL_ERR_ARG;
         pl->chunk = cols;
         pl->cap = candidate_cap(k, cols);
+        pl->fused = gather && !ret_val;
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, topk_kernel_ptr(dtype, pl->ept, kTopkWhole), kTopkThreads,
-                topk_dyn_lds(dtype, pl->cap, pl->ept, kTopkWhole)) != hipSuccess ||
+                &per_cu, topk_kernel_ptr(dtype, pl->ept, kTopkWhole, 0, pl->fused ? 1 : 0),
+                kTopkThreads,
+                topk_dyn_lds(dtype, pl->cap, pl->ept, kTopkWhole, pl->fused ? k : 0)) != hipSuccess ||
             per_cu <= 0)
             return DSEL_ERR_DEVICE;
         const int64_t slots = (int64_t)per_cu * cus;
@@ -273,7 +279,7 @@ int topk_entry(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_r
                int return_value, void *out_idx, int64_t idx_row_stride, void *out_val,
                int64_t val_row_stride, uint8_t *nan_flag, void *workspace,
                size_t *workspace_bytes, void *stream, int64_t idx_fill, uint32_t val_fill_bits,
-               int row_order, int64_t max_ws_words) {
+               int row_order, int64_t max_ws_words, const FusedGather *fg = nullptr) {
     // sorted_index 0 and 1: the output is ascending by construction; 2: a
     // value-order pass follows the select
     if (sorted_index < 0 || sorted_index > 2) return DSEL_ERR_ARG;
@@ -303,7 +309,9 @@ int topk_entry(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_r
         return DSEL_ERR_ALIGN;
 
     TopkPlan pl;
-    const int st = plan_topk(dtype, rows, cols, k, return_value ? 1 : 0, max_ws_words, &pl);
+    // (value order sorts after the select: its gather runs after the sort)
+    const int st = plan_topk(dtype, rows, cols, k, return_value ? 1 : 0, max_ws_words, &pl,
+                             fg != nullptr && sorted_index != 2);
     if (st != DSEL_OK) return st;
     if (!workspace) {
         *workspace_bytes = pl.ws_bytes;
@@ -344,6 +352,7 @@ int topk_entry(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_r
     a.stage_words = pl.kind == kTopkWave && a.ret_val
                         ? wave_stage_words(dtype, k, a.idx64 ? 8 : 4, a.ret_val, pl.per_cu)
                         : 0u;
+    if (fg && pl.fused) a.fg = *fg;  // the select's kernel also gathers
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     for (int64_t r0 = 0; r0 < rows; r0 += pl.rows_per_launch) {
         const int64_t nr = (rows - r0) < pl.rows_per_launch ? (rows - r0) : pl.rows_per_launch;
@@ -360,6 +369,28 @@ int topk_entry(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_r
             a.row0 = r0;
             const int64_t nr = (rows - r0) < kMaxGrid ? (rows - r0) : kMaxGrid;
             if (launch_value_sort(dtype, a, (unsigned)nr, s) != hipSuccess) return DSEL_ERR_DEVICE;
+        }
+    }
+    if (fg && !pl.fused) {
+        // rows whose kernel does not fuse the gather: the gather kernel on
+        // the indices just written, one launch per key
+        for (int g = 0; g < fg->n; ++g) {
+            const GatherKeyArgs &kg = fg->k[g];
+            GatherArgs ga{};
+            ga.key = kg.key;
+            ga.out = kg.out;
+            ga.pos = out_idx;
+            ga.batch = rows / fg->rows_per_batch;
+            ga.len = kg.len;
+            ga.R = fg->rows_per_batch;
+            ga.P = k;
+            ga.key_batch_bytes = kg.batch_bytes;
+            ga.key_row_bytes = kg.row_bytes;
+            ga.pos_row_stride = idx_row_stride;
+            ga.row_vecs = kg.vecs;
+            ga.row_vecs_log2 = kg.vecs_log2;
+            ga.pad_zero = fg->pad_zero;
+            if (launch_gather(indices_type == DSEL_I64, ga, s) != hipSuccess) return DSEL_ERR_DEVICE;
         }
     }
     return DSEL_OK;
@@ -447,6 +478,50 @@ extern "C" int dsel_topk_ex(const void *x, int dtype, int64_t rows, int64_t cols
     return topk_entry(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index, indices_type,
                       return_value, out_idx, idx_row_stride, out_val, val_row_stride, nan_flag,
                       workspace, workspace_bytes, stream, idx_fill, val_fill_bits, row_order, 0);
+}
+
+extern "C" int dsel_topk_gather(const void *x, int dtype, int64_t rows, int64_t cols,
+                                int64_t x_row_stride, int64_t k, const int32_t *row_end,
+                                int sorted_index, int indices_type, void *out_idx,
+                                int64_t idx_row_stride, uint8_t *nan_flag, int64_t rows_per_batch,
+                                const DselGatherKey *keys, int n_keys, int pad, void *workspace,
+                                size_t *workspace_bytes, void *stream) {
+    if (!keys || n_keys < 1 || n_keys > kMaxGatherKeys) return DSEL_ERR_ARG;
+    if (pad != DSEL_PAD_CLAMP && pad != DSEL_PAD_ZERO) return DSEL_ERR_ARG;
+    if (rows_per_batch < 1 || rows < 0 || rows % rows_per_batch != 0) return DSEL_ERR_ARG;
+    FusedGather fg{};
+    fg.n = n_keys;
+    fg.pad_zero = pad == DSEL_PAD_ZERO ? 1 : 0;
+    fg.rows_per_batch = rows_per_batch;
+    for (int g = 0; g < n_keys; ++g) {
+        const DselGatherKey &d = keys[g];
+        if (d.dtype != DSEL_BF16 && d.dtype != DSEL_F32) return DSEL_ERR_ARG;
+        if (d.len < 1 || d.dim < 1 || d.batch_stride < 0 || d.row_stride < 0) return DSEL_ERR_ARG;
+        if (rows > 0 && (!d.key || !d.out)) return DSEL_ERR_ARG;
+        const int64_t esz = d.dtype == DSEL_BF16 ? 2 : 4;
+        if (!aligned_ptr(d.key) || !aligned_ptr(d.out) || (d.dim * esz) % kAlign ||
+            (d.batch_stride * esz) % kAlign || (d.row_stride * esz) % kAlign)
+            return DSEL_ERR_ALIGN;
+        const int64_t rv = d.dim * esz / 16;
+        if (rv > (1 << 20)) return DSEL_ERR_ARG;
+        GatherKeyArgs &kg = fg.k[g];
+        kg.key = reinterpret_cast<const char *>(d.key);
+        kg.out = reinterpret_cast<char *>(d.out);
+        kg.batch_bytes = d.batch_stride * esz;
+        kg.row_bytes = d.row_stride * esz;
+        kg.len = d.len;
+        kg.vecs = (int)rv;
+        kg.vecs_log2 = -1;
+        if ((rv & (rv - 1)) == 0) {
+            int l = 0;
+            while ((1LL << l) < rv) ++l;
+            kg.vecs_log2 = l;
+        }
+    }
+    return topk_entry(x, dtype, rows, cols, x_row_stride, k, row_end, sorted_index, indices_type,
+                      0, out_idx, idx_row_stride, nullptr, 0, nan_flag, workspace, workspace_bytes,
+                      stream, -1, dtype == DSEL_BF16 ? 0xFF80u : 0xFF800000u, DSEL_ROWS_AUTO, 0,
+                      &fg);
 }
 
 extern "C" int dsel_topk_check(void *workspace, size_t workspace_bytes, void *stream,

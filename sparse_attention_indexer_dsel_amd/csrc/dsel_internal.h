@@ -73,6 +73,26 @@ inline int64_t slot_words(int G, int dtype) {
            (int64_t)G * (last_pass_bins(dtype) + 1);
 }
 
+// Gather of key rows fused into the top-k (dsel_topk_gather): after a row's
+// select, the workers that selected it copy out_g[row, j, :] = key_g[b, p, :]
+// for its k slots (b = row / rows_per_batch, p the slot's position).
+constexpr int kMaxGatherKeys = 4;
+struct GatherKeyArgs {
+    const char *key;
+    char *out;                 // contiguous [rows, k, row bytes]
+    int64_t batch_bytes;       // key strides in bytes
+    int64_t row_bytes;
+    int64_t len;               // key rows per batch
+    int vecs;                  // 16-byte vectors per key row
+    int vecs_log2;             // log2(vecs) when a power of two, else -1
+};
+struct FusedGather {
+    int n;                     // keys (0: no gather)
+    int pad_zero;              // positions outside [0, len): zero rows (else clamped)
+    int64_t rows_per_batch;
+    GatherKeyArgs k[kMaxGatherKeys];
+};
+
 struct TopkArgs {
     const void *x;
     int64_t rows;
@@ -101,6 +121,7 @@ struct TopkArgs {
                              // after the histograms (0: staged in the histogram's space)
     uint32_t spin_limit;     // split rows: polls of a rendezvous before it gives up
     int row_order;           // kRowsNatural or kRowsDualChunk (rows of one workgroup or wave)
+    FusedGather fg;          // the fused gather's keys (instances that gather only)
 };
 
 // Order in which the workgroups (one-wave rows: the waves) of a launch take
@@ -129,15 +150,16 @@ enum { kTopkWhole = 0, kTopkSplit = 1, kTopkWave = 2, kTopkSplitWx = 3 };
 // Rows of at most this many columns take one wave each.
 constexpr int64_t kWaveCapacity = 64 * 32;
 
-// Kernel instance for (dtype, elements per thread, kind, values returned);
-// nullptr if none.  The two one-wave instances of a (dtype, ept) pair have
+// Kernel instance for (dtype, elements per thread, kind, values returned,
+// gather fused: one-wave bf16 rows and whole rows only); nullptr if none.  The two one-wave instances of a (dtype, ept) pair have
 // the same occupancy.
-const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val = 0);
+const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val = 0, int gather = 0);
 // Elements per 16-byte vector for a dtype.
 inline int topk_vec(int dtype) { return dtype == 0 ? 8 : 4; }
 // Dynamic LDS bytes of a top-k launch with candidate capacity `cap` (for
-// one-wave rows: with each wave's histogram only).
-size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind);
+// one-wave rows: with each wave's histogram only; gather_k > 0: whole rows
+// that fuse the gather also stage that many positions).
+size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind, int64_t gather_k = 0);
 // One-wave rows: LDS words of a wave's histogram, and the LDS words per wave
 // of a separate stage for the row's output (k indices of idx_bytes each, and
 // k values when ret_val) when it does not fit the histogram's space and
@@ -158,6 +180,7 @@ struct GatherArgs {
     int64_t pos_row_stride;  // elements
     int row_vecs;            // 16-byte vectors per key row
     int row_vecs_log2;       // log2(row_vecs) when a power of two, else -1
+    int pad_zero;            // positions outside [0, len): zero rows (else clamped)
 };
 
 hipError_t launch_gather(int pos64, const GatherArgs &a, hipStream_t stream);

@@ -4,7 +4,9 @@
 // the fix): the two-tensor form key[batch_ids, positions] becomes a single
 // index_select of D-vectors over the flattened key at b*len + position; the
 // result is the same bits.  Positions are clamped into [0, len-1], the
-// "safe" positions its call sites pass.
+// "safe" positions its call sites pass; with pad_zero (the chain's masked
+// fill, for the fused entry point's unfused rows) a position outside
+// [0, len-1] gives a zero row instead.
 //
 // Layout here: one workgroup per (batch, query-row) pair walks that row's
 // positions (staged in LDS); 16-byte vector copies, cached loads from the
@@ -39,8 +41,9 @@ __global__ __launch_bounds__(GT) void gather_rows_kernel(const GatherArgs a) {
             for (int j = threadIdx.x; j < cnt; j += GT) {
                 int64_t p = POS64 ? reinterpret_cast<const int64_t *>(a.pos)[prow + p0 + j]
                                   : (int64_t)reinterpret_cast<const int32_t *>(a.pos)[prow + p0 + j];
+                const bool in = p >= 0 && p < a.len;
                 p = p < 0 ? 0 : (p >= a.len ? a.len - 1 : p);
-                s_off[j] = p * a.key_row_bytes;
+                s_off[j] = (a.pad_zero && !in) ? -1 : p * a.key_row_bytes;  // -1: a zero row
             }
             __syncthreads();
             const int64_t total = (int64_t)cnt * a.row_vecs;
@@ -53,7 +56,9 @@ __global__ __launch_bounds__(GT) void gather_rows_kernel(const GatherArgs a) {
                     const int64_t i = i0u < total ? i0u : total - 1;
                     const int64_t j = POW2 ? (i >> a.row_vecs_log2) : (i / a.row_vecs);
                     const int64_t vi = i - j * a.row_vecs;
-                    v[u] = *reinterpret_cast<const u32x4 *>(kb + s_off[j] + vi * 16);
+                    const int64_t off = s_off[j];
+                    v[u] = off < 0 ? u32x4{0u, 0u, 0u, 0u}
+                                   : *reinterpret_cast<const u32x4 *>(kb + off + vi * 16);
                 }
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u) {

@@ -86,7 +86,6 @@ struct Bf16Key {
     static constexpr int NPASS = 2;
     static constexpr int SH1 = 5;  // first digit = key >> 5 (11 bits)
     static constexpr bool PACK = true;  // list entry = key << 16 | column
-    static constexpr uint32_t NEG_INF = 0xFF80u;
     __device__ static int digit(int pass) { return pass == 0 ? 11 : 5; }
     static constexpr int digit_last() { return 5; }
     // offset binary of both halves: 0x8000 +/- magnitude (packed int16 ops);
@@ -130,7 +129,6 @@ struct F32Key {
     static constexpr int NPASS = 3;
     static constexpr int SH1 = 21;
     static constexpr bool PACK = false;  // list entry = (key, column) in two arrays
-    static constexpr uint32_t NEG_INF = 0xFF800000u;
     __device__ static int digit(int pass) { return pass == 2 ? 10 : 11; }
     static constexpr int digit_last() { return 10; }
     __device__ static uint32_t keyword(uint32_t w, uint32_t &magmax) {
@@ -2588,6 +2586,58 @@ __global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The gather fused into the select (dsel_topk_gather).  MindSpore hyper-
+// parallel PR #1094 (English description and the section on the fix): the
+// candidate chain selects each query row's top positions and then gathers
+// the compressed keys at them (key[batch_ids, positions], made one
+// index_select over batch-offset positions by the fix).  Here the workers
+// that selected a row copy its gathered rows right away:
+//     out_g[row, j, :] = key_g[row / rows_per_batch, p_j, :]   for j < k,
+// p_j the row's j-th selected position (a short row's padding slots carry
+// -1).  A position outside [0, len) is clamped into it, or (pad_zero, the
+// chain's masked fill) gives a zero row.  NTH threads (me = 0 .. NTH-1)
+// share the row's 16-byte vectors, U loads in flight per thread; the output
+// is written once and not re-read, so its stores are non-temporal.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int NTH, class Pos>
+__device__ __forceinline__ void gather_tail(const TopkArgs &a, int64_t row, int me, Pos pos) {
+    constexpr int U = 8;
+    const int64_t b = row / a.fg.rows_per_batch;
+    const uint32_t k = (uint32_t)a.k;
+#pragma unroll 1
+    for (int g = 0; g < a.fg.n; ++g) {  // uniform
+        const GatherKeyArgs &kg = a.fg.k[g];
+        const char *kb = kg.key + b * kg.batch_bytes;
+        u32x4 *ob = reinterpret_cast<u32x4 *>(kg.out) + row * (int64_t)k * kg.vecs;
+        const uint32_t total = k * (uint32_t)kg.vecs;
+        const int l2 = kg.vecs_log2;
+#pragma unroll 1
+        for (uint32_t i0 = (uint32_t)me; i0 < total; i0 += (uint32_t)(NTH * U)) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = min(i0 + (uint32_t)(u * NTH), total - 1u);
+                const uint32_t j = l2 >= 0 ? i >> l2 : i / (uint32_t)kg.vecs;
+                const uint32_t vi = i - j * (uint32_t)kg.vecs;
+                const int64_t p = pos(j);
+                const bool in = p >= 0 && p < kg.len;
+                const int64_t pc = in ? p : (p < 0 ? 0 : kg.len - 1);
+                v[u] = (a.fg.pad_zero && !in)
+                           ? u32x4{0u, 0u, 0u, 0u}
+                           : *reinterpret_cast<const u32x4 *>(kb + pc * kg.row_bytes + (int64_t)vi * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = i0 + (uint32_t)(u * NTH);
+                if (i < total) __builtin_nontemporal_store(v[u], ob + i);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Whole rows: one workgroup per row.
 // ---------------------------------------------------------------------------
 
@@ -2653,7 +2703,7 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
 // workgroup reaches it; other workgroups on the compute unit hide their
 // latency.  Holding only one row in VGPRs keeps more workgroups resident,
 // which pays more than double-buffering the next row's loads.
-template <class K, int EPT>
+template <class K, int EPT, bool GATHER = false>
 __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     using raw_t = typename K::raw_t;
     constexpr int LOADS = EPT / K::VEC;
@@ -2676,6 +2726,17 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
             uint4 v[LOADS];
             load_row<K, LOADS>(xr, n, v);
             select_row<K, LOADS>(a, row, n, v, L, ent);
+        }
+        if constexpr (GATHER) {
+            // the row's positions, as this workgroup wrote them, into LDS
+            // (the select's space is free; it holds at least k words)
+            __syncthreads();
+            int32_t *s_pos = reinterpret_cast<int32_t *>(s_dyn);
+            const uint32_t *ib = reinterpret_cast<const uint32_t *>(a.out_idx) +
+                                 row * a.idx_stride * (a.idx64 ? 2 : 1);
+            for (int j = tid(); j < a.k; j += NT) s_pos[j] = (int32_t)ld_agent(ib + (a.idx64 ? 2 * j : j));
+            __syncthreads();
+            gather_tail<NT>(a, row, tid(), [&](uint32_t j) -> int64_t { return s_pos[j]; });
         }
         __syncthreads();  // LDS is reused by the next row
     }
@@ -3176,7 +3237,7 @@ __device__ __forceinline__ void w16_stage(const uint32_t (&kw)[LPL * 4], int any
     }
 }
 
-template <int LPL, bool RV>
+template <int LPL, bool RV, bool GATHER = false>
 __global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
     using K = Bf16Key;
     constexpr int SPAN = 64 * 8;  // columns per load over the wave
@@ -3212,6 +3273,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
             } else {
                 write_short_row<K>(a, row, n, 0, 1, xr, lane, 64);
             }
+            if constexpr (GATHER)
+                gather_tail<64>(a, row, lane, [&](uint32_t j) -> int64_t { return (int64_t)j < n ? (int64_t)j : -1; });
             continue;
         }
         const int len = (int)n;
@@ -3466,6 +3529,18 @@ __global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
                               (uint32_t)a.k * 2u, lane);
         }
         if (lane == 0 && a.nan_flag) a.nan_flag[row] = row_nan ? 1u : 0u;
+        if constexpr (GATHER) {
+            // the row's positions: the stage (low words of int64 slots), or
+            // the index row this wave just wrote
+            const int32_t *sp = reinterpret_cast<const int32_t *>(stage);
+            const uint32_t *ib = reinterpret_cast<const uint32_t *>(a.out_idx) +
+                                 row * a.idx_stride * (a.idx64 ? 2 : 1);
+            if (!staged) __builtin_amdgcn_s_waitcnt(0);  // the index stores are done
+            const int sh = a.idx64 ? 1 : 0;
+            gather_tail<64>(a, row, lane, [&](uint32_t j) -> int64_t {
+                return staged ? sp[j << sh] : (int32_t)ld_agent(ib + (j << sh));
+            });
+        }
     }
 }
 
@@ -3651,23 +3726,24 @@ __global__ __launch_bounds__(SORT_NT) void sort_rows_by_value(const TopkArgs a) 
     }
 }
 
-template <class K, int EPT, bool SPLIT>
+template <class K, int EPT, bool SPLIT, bool GATHER>
 const void *kptr() {
     if constexpr (SPLIT)
         return reinterpret_cast<const void *>(&topk_rows_split<K, EPT>);
     else
-        return reinterpret_cast<const void *>(&topk_rows_whole<K, EPT>);
+        return reinterpret_cast<const void *>(&topk_rows_whole<K, EPT, GATHER>);
 }
 
-template <class K, bool SPLIT>
+template <class K, bool SPLIT, bool GATHER = false>
 const void *pick(int ept) {
+    static_assert(!(SPLIT && GATHER), "split rows do not fuse the gather");
     switch (ept) {
-        case 8: return kptr<K, 8, SPLIT>();
-        case 16: return kptr<K, 16, SPLIT>();
-        case 32: return kptr<K, 32, SPLIT>();
-        case 64: return kptr<K, 64, SPLIT>();
+        case 8: return kptr<K, 8, SPLIT, GATHER>();
+        case 16: return kptr<K, 16, SPLIT, GATHER>();
+        case 32: return kptr<K, 32, SPLIT, GATHER>();
+        case 64: return kptr<K, 64, SPLIT, GATHER>();
         case 128:
-            if constexpr (SPLIT) return kptr<K, 128, true>();
+            if constexpr (SPLIT) return kptr<K, 128, true, false>();
             return nullptr;
         default: return nullptr;
     }
@@ -3675,16 +3751,17 @@ const void *pick(int ept) {
 
 }  // namespace
 
-template <class K, bool RV>
+template <class K, bool RV, bool GATHER = false>
 const void *pick_wave(int epl) {
     if constexpr (sizeof(typename K::raw_t) == 2) {
         switch (epl) {
-            case 8: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<1, RV>);
-            case 16: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<2, RV>);
-            case 32: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<4, RV>);
+            case 8: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<1, RV, GATHER>);
+            case 16: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<2, RV, GATHER>);
+            case 32: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<4, RV, GATHER>);
             default: return nullptr;
         }
     }
+    if constexpr (GATHER) return nullptr;  // fp32 one-wave rows do not fuse the gather
     switch (epl) {
         case 8: return reinterpret_cast<const void *>(&topk_rows_wave<K, 8, RV>);
         case 16: return reinterpret_cast<const void *>(&topk_rows_wave<K, 16, RV>);
@@ -3695,7 +3772,14 @@ const void *pick_wave(int epl) {
 
 // ept = columns per thread of one workgroup's range (the whole row, or one
 // split chunk), or per lane of a wave's row (kTopkWave).
-const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val) {
+const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val, int gather) {
+    if (gather) {
+        if (ret_val) return nullptr;  // the fused gather returns no values
+        if (kind == kTopkWave) return dtype == 0 ? pick_wave<Bf16Key, false, true>(ept) : nullptr;
+        if (kind == kTopkWhole)
+            return dtype == 0 ? pick<Bf16Key, false, true>(ept) : pick<F32Key, false, true>(ept);
+        return nullptr;
+    }
     if (kind == kTopkSplitWx) {
         if (dtype != 1) return nullptr;
         switch (ept) {
@@ -3718,8 +3802,12 @@ const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val) {
 
 // The histogram, and the candidate list: cap entries plus one spare per
 // lane (one word per bf16 entry, two per fp32 entry), from list_base.
-size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind) {
+size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind, int64_t gather_k) {
     (void)ept;
+    if (kind == kTopkWhole && gather_k > 0) {  // the fused gather stages k positions
+        const size_t sel = topk_dyn_lds(dtype, cap, ept, kind, 0);
+        return sel > (size_t)gather_k * 4u ? sel : (size_t)gather_k * 4u;
+    }
     if (kind == kTopkWave)
         return (size_t)NWAVE * (dtype == 0 ? wave_lds_words<Bf16Key>() : wave_lds_words<F32Key>()) * 4;
     const uint64_t hist = (uint64_t)(kBins + 64);
@@ -3755,10 +3843,11 @@ uint32_t wave_stage_words(int dtype, int64_t k, int idx_bytes, int ret_val, int 
 
 hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned grid,
                        hipStream_t stream) {
-    const void *fn = topk_kernel_ptr(dtype, ept, kind, a.ret_val);
+    const int gather = a.fg.n > 0 ? 1 : 0;
+    const void *fn = topk_kernel_ptr(dtype, ept, kind, a.ret_val, gather);
     if (!fn) return hipErrorInvalidValue;
     TopkArgs copy = a;
-    size_t lds = topk_dyn_lds(dtype, a.cap, ept, kind);
+    size_t lds = topk_dyn_lds(dtype, a.cap, ept, kind, gather ? a.k : 0);
     if (kind == kTopkWave) lds = (size_t)NWAVE * (wave_hist_words(dtype) + copy.stage_words) * 4u;
     void *args[] = {&copy};
     return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, lds, stream);

@@ -502,6 +502,31 @@ def pin_gather_noncontiguous_and_repeats(orc, seed=8):
                 assert np.array_equal(out[b, r, j], want[b, int(pos[b, r, j])])
 
 
+def pin_gather_masked_fill(orc, seed=11):
+    """The masked fill: rows at positions inside [0, L) equal the clamped
+    gather's, every other row is zero; by brute force over a tiny key whose
+    rows are all non-zero, with positions -3 .. L + 2 (L itself included)."""
+    g = torch.Generator().manual_seed(seed)
+    for dtype in (torch.bfloat16, torch.float32):
+        B, L, D, R = 2, 6, 8, 3
+        key = (torch.rand(B, L, D, generator=g) + 0.5).to(dtype)   # no zero element
+        pos = torch.arange(-3, L + 3, dtype=torch.int32).repeat(B, R, 1)
+        P = pos.shape[2]
+        got = orc.gather(_np_key(key), pos.numpy(), pad="zero")
+        kz = _np_key(key)
+        for b in range(B):
+            for r in range(R):
+                for j in range(P):
+                    p = int(pos[b, r, j])
+                    if 0 <= p < L:
+                        assert np.array_equal(got[b, r, j], kz[b, p])
+                    else:
+                        assert not got[b, r, j].any()
+        clamp = orc.gather(_np_key(key), pos.numpy())
+        inside = ((pos >= 0) & (pos < L)).numpy()
+        assert np.array_equal(got[inside], clamp[inside])
+
+
 ALL_PINS = [
     pin_bruteforce_tiny,
     pin_pairwise,
@@ -516,4 +541,5 @@ ALL_PINS = [
     pin_gather_library,
     pin_gather_batches_do_not_mix,
     pin_gather_noncontiguous_and_repeats,
+    pin_gather_masked_fill,
 ]

@@ -36,7 +36,8 @@ def declared():
 
 def test_header_declares_the_calls():
     assert declared() == ["dsel_gather_rows", "dsel_stride_requirement", "dsel_topk",
-                          "dsel_topk_check", "dsel_topk_ex", "dsel_topk_noalloc"]
+                          "dsel_topk_check", "dsel_topk_ex", "dsel_topk_gather",
+                          "dsel_topk_noalloc"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -149,3 +150,40 @@ def test_topk_check_host_checks(lib):
     bits.value = 7
     assert f(16, 2, None, ctypes.byref(bits)) == 0 and bits.value == 0
     assert f(20, 1024, None, ctypes.byref(bits)) == -3
+
+
+class GatherKey(ctypes.Structure):
+    _fields_ = [("key", ctypes.c_void_p), ("dtype", ctypes.c_int), ("len", ctypes.c_int64),
+                ("dim", ctypes.c_int64), ("batch_stride", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64), ("out", ctypes.c_void_p)]
+
+
+def _topk_gather(lib, keys, n_keys=None, pad=0, rows=4, rpb=2):
+    f = lib.dsel_topk_gather
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(GatherKey),
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
+                  ctypes.c_void_p]
+    arr = (GatherKey * max(1, len(keys)))(*keys)
+    nb = ctypes.c_size_t(0)
+    return f(16, 0, rows, 64, 64, 8, None, 0, 0, 16, 16, None, rpb, arr,
+             len(keys) if n_keys is None else n_keys, pad, None, ctypes.byref(nb), None)
+
+
+def test_topk_gather_host_checks(lib):
+    """dsel_topk_gather refuses bad key descriptors, key counts, pad modes
+    and batch shapes before anything reaches a device."""
+    good = GatherKey(16, 0, 32, 128, 32 * 128, 128, 16)
+    assert _topk_gather(lib, [good], n_keys=0) == -1         # no key
+    assert _topk_gather(lib, [good] * 5) == -1               # more than four keys
+    assert _topk_gather(lib, [good], pad=2) == -1            # no such pad mode
+    assert _topk_gather(lib, [good], rows=5, rpb=2) == -1    # rows not a multiple
+    assert _topk_gather(lib, [good], rpb=0) == -1
+    assert _topk_gather(lib, [GatherKey(16, 2, 32, 128, 4096, 128, 16)]) == -1   # key dtype
+    assert _topk_gather(lib, [GatherKey(16, 0, 0, 128, 4096, 128, 16)]) == -1    # len 0
+    assert _topk_gather(lib, [GatherKey(16, 0, 32, 100, 3200, 100, 16)]) == -3   # 200-byte rows
+    assert _topk_gather(lib, [GatherKey(24, 0, 32, 128, 4096, 128, 16)]) == -3   # key pointer
+    assert _topk_gather(lib, [GatherKey(16, 0, 32, 128, 4096, 129, 16)]) == -3   # row stride
+    assert _topk_gather(lib, [good, GatherKey(16, 0, 32, 128, 4096, 128, 8)]) == -3  # out pointer

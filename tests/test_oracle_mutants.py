@@ -24,6 +24,7 @@ MUTANTS = {
     11: "ascending instead of descending",
     12: "input row stride ignored",
     13: "value order reversed",
+    14: "masked fill lets position len through",
 }
 
 
