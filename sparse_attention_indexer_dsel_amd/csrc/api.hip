@@ -145,15 +145,16 @@ int plan_topk(int dtype, int64_t rows, int64_t cols, int64_t k, int ret_val, int
         pl->cap = 0;
         int per_cu = 0;
         pl->fused = gather && dtype == DSEL_BF16 && !ret_val;
+        const int waves = wave_kernel_waves(kTopkWave, pl->fused ? 1 : 0);
         // (the instance the call launches: the values instance may differ)
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                 &per_cu, topk_kernel_ptr(dtype, pl->ept, kTopkWave, ret_val, pl->fused ? 1 : 0),
-                kTopkThreads, topk_dyn_lds(dtype, 0, pl->ept, kTopkWave)) != hipSuccess ||
+                waves * 64, topk_dyn_lds(dtype, 0, pl->ept, kTopkWave, pl->fused ? k : 0)) != hipSuccess ||
             per_cu <= 0)
             return DSEL_ERR_DEVICE;
         pl->per_cu = per_cu;
         const int64_t slots = (int64_t)per_cu * cus;
-        const int64_t wgs = cdiv(rows, kTopkThreads / 64);
+        const int64_t wgs = cdiv(rows, waves);
         pl->rows_per_launch = rows;
         pl->grid = wgs < slots ? wgs : slots;
         pl->ws_bytes = 0;
@@ -309,9 +310,14 @@ int topk_entry(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_r
         return DSEL_ERR_ALIGN;
 
     TopkPlan pl;
-    // (value order sorts after the select: its gather runs after the sort)
-    const int st = plan_topk(dtype, rows, cols, k, return_value ? 1 : 0, max_ws_words, &pl,
-                             fg != nullptr && sorted_index != 2);
+    // (value order sorts after the select: its gather runs after the sort;
+    // the fused copy addresses a key's batch with 32-bit offsets)
+    bool fuse = fg != nullptr && sorted_index != 2;
+    for (int g = 0; fuse && g < fg->n; ++g) {
+        const GatherKeyArgs &kg = fg->k[g];
+        if ((kg.len - 1) * kg.row_bytes + (int64_t)kg.vecs * 16 >= ((int64_t)1 << 31) - 16) fuse = false;
+    }
+    const int st = plan_topk(dtype, rows, cols, k, return_value ? 1 : 0, max_ws_words, &pl, fuse);
     if (st != DSEL_OK) return st;
     if (!workspace) {
         *workspace_bytes = pl.ws_bytes;

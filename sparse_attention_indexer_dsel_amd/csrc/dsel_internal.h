@@ -77,6 +77,8 @@ inline int64_t slot_words(int G, int dtype) {
 // select, the workers that selected it copy out_g[row, j, :] = key_g[b, p, :]
 // for its k slots (b = row / rows_per_batch, p the slot's position).
 constexpr int kMaxGatherKeys = 4;
+// Waves per workgroup of the one-wave rows' kernel that fuses the gather.
+constexpr int kGatherWaves = 8;
 struct GatherKeyArgs {
     const char *key;
     char *out;                 // contiguous [rows, k, row bytes]
@@ -160,6 +162,9 @@ inline int topk_vec(int dtype) { return dtype == 0 ? 8 : 4; }
 // one-wave rows: with each wave's histogram only; gather_k > 0: whole rows
 // that fuse the gather also stage that many positions).
 size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind, int64_t gather_k = 0);
+// Waves per workgroup of a top-k launch (kTopkThreads / 64, or kGatherWaves
+// for one-wave rows that fuse the gather).
+int wave_kernel_waves(int kind, int gather);
 // One-wave rows: LDS words of a wave's histogram, and the LDS words per wave
 // of a separate stage for the row's output (k indices of idx_bytes each, and
 // k values when ret_val) when it does not fit the histogram's space and

@@ -2601,40 +2601,60 @@ __global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Key g's rows of one selected row, by all NTH threads of the workgroup.
+// First each slot's position becomes a byte offset in s_off (k words of
+// LDS): clamped into the key, or, for a zero-filled slot, an offset past the
+// end of a buffer view of the row's batch of the key (32-bit offsets: the
+// host fuses only keys whose batch spans less than 2^31 bytes), which reads
+// as zero.  Then each 16-byte vector costs an LDS read, a load and a store.
 template <int NTH, class Pos>
-__device__ __forceinline__ void gather_tail(const TopkArgs &a, int64_t row, int me, Pos pos) {
-    constexpr int U = 8;
+__device__ __forceinline__ void gather_key_rows(const TopkArgs &a, const GatherKeyArgs &kg,
+                                                int64_t row, int me, Pos pos, uint32_t *s_off) {
+    // loads in flight per thread (measured: 16 for the 512-thread copy of
+    // the one-wave rows' kernel, 8 for whole rows' 256 threads)
+    constexpr int U = NTH > 256 ? 16 : 8;
+    constexpr uint32_t kOutside = 0x80000000u;  // past every view
     const int64_t b = row / a.fg.rows_per_batch;
+    const char *kb = kg.key + b * kg.batch_bytes;
+    const int64_t span = (kg.len - 1) * kg.row_bytes + (int64_t)kg.vecs * 16;
+    const __amdgpu_buffer_rsrc_t kv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kb), (short)0, (int)span, 0x00020000);
     const uint32_t k = (uint32_t)a.k;
+    const int64_t len = kg.len;
+    const bool zero = a.fg.pad_zero != 0;
+    for (uint32_t j = (uint32_t)me; j < k; j += NTH) {
+        const int64_t p = pos(j);
+        const bool in = p >= 0 && p < len;
+        const int64_t pc = in ? p : (p < 0 ? 0 : len - 1);
+        s_off[j] = (zero && !in) ? kOutside : (uint32_t)(pc * kg.row_bytes);
+    }
+    __syncthreads();
+    u32x4 *ob = reinterpret_cast<u32x4 *>(kg.out) + row * (int64_t)k * kg.vecs;
+    const uint32_t total = k * (uint32_t)kg.vecs, vecs = (uint32_t)kg.vecs;
+    const int l2 = kg.vecs_log2;
 #pragma unroll 1
-    for (int g = 0; g < a.fg.n; ++g) {  // uniform
-        const GatherKeyArgs &kg = a.fg.k[g];
-        const char *kb = kg.key + b * kg.batch_bytes;
-        u32x4 *ob = reinterpret_cast<u32x4 *>(kg.out) + row * (int64_t)k * kg.vecs;
-        const uint32_t total = k * (uint32_t)kg.vecs;
-        const int l2 = kg.vecs_log2;
-#pragma unroll 1
-        for (uint32_t i0 = (uint32_t)me; i0 < total; i0 += (uint32_t)(NTH * U)) {
-            u32x4 v[U];
+    for (uint32_t i0 = (uint32_t)me; i0 < total; i0 += (uint32_t)(NTH * U)) {
+        u32x4 v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t i = min(i0 + (uint32_t)(u * NTH), total - 1u);
-                const uint32_t j = l2 >= 0 ? i >> l2 : i / (uint32_t)kg.vecs;
-                const uint32_t vi = i - j * (uint32_t)kg.vecs;
-                const int64_t p = pos(j);
-                const bool in = p >= 0 && p < kg.len;
-                const int64_t pc = in ? p : (p < 0 ? 0 : kg.len - 1);
-                v[u] = (a.fg.pad_zero && !in)
-                           ? u32x4{0u, 0u, 0u, 0u}
-                           : *reinterpret_cast<const u32x4 *>(kb + pc * kg.row_bytes + (int64_t)vi * 16);
-            }
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i = min(i0 + (uint32_t)(u * NTH), total - 1u);
+            const uint32_t j = l2 >= 0 ? i >> l2 : i / vecs;
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(kv, s_off[j] + (i - j * vecs) * 16u, 0u, 0);
+        }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t i = i0 + (uint32_t)(u * NTH);
-                if (i < total) __builtin_nontemporal_store(v[u], ob + i);
-            }
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i = i0 + (uint32_t)(u * NTH);
+            if (i < total) __builtin_nontemporal_store(v[u], ob + i);
         }
     }
+    __syncthreads();  // s_off is read: the next key may rewrite it
+}
+
+template <int NTH, class Pos>
+__device__ __forceinline__ void gather_tail(const TopkArgs &a, int64_t row, int me, Pos pos,
+                                            uint32_t *s_off) {
+#pragma unroll 1
+    for (int g = 0; g < a.fg.n; ++g) gather_key_rows<NTH>(a, a.fg.k[g], row, me, pos, s_off);  // uniform
 }
 
 // ---------------------------------------------------------------------------
@@ -2736,7 +2756,8 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
                                  row * a.idx_stride * (a.idx64 ? 2 : 1);
             for (int j = tid(); j < a.k; j += NT) s_pos[j] = (int32_t)ld_agent(ib + (a.idx64 ? 2 * j : j));
             __syncthreads();
-            gather_tail<NT>(a, row, tid(), [&](uint32_t j) -> int64_t { return s_pos[j]; });
+            gather_tail<NT>(a, row, tid(), [&](uint32_t j) -> int64_t { return s_pos[j]; },
+                            reinterpret_cast<uint32_t *>(s_dyn) + a.k);
         }
         __syncthreads();  // LDS is reused by the next row
     }
@@ -3237,10 +3258,15 @@ __device__ __forceinline__ void w16_stage(const uint32_t (&kw)[LPL * 4], int any
     }
 }
 
+// GATHER: workgroups of kGatherWaves waves; each wave selects a row, then
+// the whole workgroup copies the gathered keys of its rows one row at a time
+// (a row's keys written by many threads at once keep few output streams
+// open, which the HBM writes favour over one stream per wave).
 template <int LPL, bool RV, bool GATHER = false>
-__global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
+__global__ __launch_bounds__(GATHER ? kGatherWaves * 64 : NT) void topk_rows_wave_bf16(const TopkArgs a) {
     using K = Bf16Key;
     constexpr int SPAN = 64 * 8;  // columns per load over the wave
+    constexpr int NW = GATHER ? kGatherWaves : NWAVE;
     extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // one region per wave
     const int wid = __builtin_amdgcn_readfirstlane(tid() >> 6);
     uint32_t *hist = s_dyn + wid * W16_WORDS;
@@ -3248,17 +3274,27 @@ __global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
     uint32_t stage_cap = W16_WORDS * 4u;
     if constexpr (RV) {
         if (a.stage_words) {
-            stage = reinterpret_cast<char *>(s_dyn + NWAVE * W16_WORDS + wid * a.stage_words);
+            stage = reinterpret_cast<char *>(s_dyn + NW * W16_WORDS + wid * a.stage_words);
             stage_cap = a.stage_words * 4u;
         }
     }
+    // GATHER: each wave's row, valid length and where its positions are
+    // (0: a short row's, 1: this wave's stage, 2: the index row in memory)
+    __shared__ int64_t g_row[GATHER ? NW : 1], g_n[GATHER ? NW : 1];
+    __shared__ int g_mode[GATHER ? NW : 1];
     const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x);
-    const int64_t step = (int64_t)gridDim.x * NWAVE;
+    const int64_t step = (int64_t)gridDim.x * NW;
 
     const int64_t R = a.rows - a.row0;
 
 #pragma unroll 1
-    for (int64_t t = (int64_t)blockIdx.x * NWAVE + wid; t < R; t += step) {
+    for (int64_t base = (int64_t)blockIdx.x * NW; base < R; base += step) {  // uniform
+      const int64_t t = base + wid;
+      if constexpr (GATHER) {
+          if (tid() % 64 == 0) g_row[wid] = -1;
+      }
+      do {  // this wave's row ("continue" ends it)
+        if (t >= R) continue;
         const int64_t row = a.row0 + taker_row(a.row_order, t, R);
         // the lane index again, opaque: the per-lane column numbers derived
         // from it must not be hoisted out of the row loop into VGPRs
@@ -3273,8 +3309,13 @@ __global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
             } else {
                 write_short_row<K>(a, row, n, 0, 1, xr, lane, 64);
             }
-            if constexpr (GATHER)
-                gather_tail<64>(a, row, lane, [&](uint32_t j) -> int64_t { return (int64_t)j < n ? (int64_t)j : -1; });
+            if constexpr (GATHER) {
+                if (lane == 0) {
+                    g_row[wid] = row;
+                    g_n[wid] = n;
+                    g_mode[wid] = 0;
+                }
+            }
             continue;
         }
         const int len = (int)n;
@@ -3530,17 +3571,39 @@ __global__ __launch_bounds__(NT) void topk_rows_wave_bf16(const TopkArgs a) {
         }
         if (lane == 0 && a.nan_flag) a.nan_flag[row] = row_nan ? 1u : 0u;
         if constexpr (GATHER) {
-            // the row's positions: the stage (low words of int64 slots), or
-            // the index row this wave just wrote
-            const int32_t *sp = reinterpret_cast<const int32_t *>(stage);
-            const uint32_t *ib = reinterpret_cast<const uint32_t *>(a.out_idx) +
-                                 row * a.idx_stride * (a.idx64 ? 2 : 1);
-            if (!staged) __builtin_amdgcn_s_waitcnt(0);  // the index stores are done
-            const int sh = a.idx64 ? 1 : 0;
-            gather_tail<64>(a, row, lane, [&](uint32_t j) -> int64_t {
-                return staged ? sp[j << sh] : (int32_t)ld_agent(ib + (j << sh));
-            });
+            if (lane == 0) {
+                g_row[wid] = row;
+                g_n[wid] = n;
+                g_mode[wid] = staged ? 1 : 2;
+            }
         }
+      } while (false);
+      if constexpr (GATHER) {
+          // every wave's row selected and its index row written: the
+          // workgroup copies their keys, row by row
+          __syncthreads();
+#pragma unroll 1
+          for (int w = 0; w < NW; ++w) {
+              const int64_t grow = g_row[w];
+              if (grow < 0) continue;  // uniform
+              const int64_t gn = g_n[w];
+              const int mode = g_mode[w];
+              const int sh = a.idx64 ? 1 : 0;
+              // the positions: a short row's, the wave's stage (low words of
+              // int64 slots), or the index row in memory
+              const int32_t *sp = reinterpret_cast<const int32_t *>(s_dyn + w * W16_WORDS);
+              const uint32_t *ib = reinterpret_cast<const uint32_t *>(a.out_idx) +
+                                   grow * a.idx_stride * (a.idx64 ? 2 : 1);
+              uint32_t *s_off = s_dyn + NW * W16_WORDS;  // k words past the waves' regions
+              if (mode == 0)
+                  gather_tail<NW * 64>(a, grow, tid(), [&](uint32_t j) -> int64_t { return (int64_t)j < gn ? (int64_t)j : -1; }, s_off);
+              else if (mode == 1)
+                  gather_tail<NW * 64>(a, grow, tid(), [&](uint32_t j) -> int64_t { return sp[j << sh]; }, s_off);
+              else
+                  gather_tail<NW * 64>(a, grow, tid(), [&](uint32_t j) -> int64_t { return (int32_t)ld_agent(ib + (j << sh)); }, s_off);
+          }
+          __syncthreads();  // the stages are read: the next rows may reuse them
+      }
     }
 }
 
@@ -3802,14 +3865,20 @@ const void *topk_kernel_ptr(int dtype, int ept, int kind, int ret_val, int gathe
 
 // The histogram, and the candidate list: cap entries plus one spare per
 // lane (one word per bf16 entry, two per fp32 entry), from list_base.
+int wave_kernel_waves(int kind, int gather) {
+    return kind == kTopkWave && gather ? kGatherWaves : NWAVE;
+}
+
 size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind, int64_t gather_k) {
     (void)ept;
-    if (kind == kTopkWhole && gather_k > 0) {  // the fused gather stages k positions
+    if (kind == kTopkWhole && gather_k > 0) {  // the fused gather stages k positions and k offsets
         const size_t sel = topk_dyn_lds(dtype, cap, ept, kind, 0);
-        return sel > (size_t)gather_k * 4u ? sel : (size_t)gather_k * 4u;
+        return sel > (size_t)gather_k * 8u ? sel : (size_t)gather_k * 8u;
     }
-    if (kind == kTopkWave)
-        return (size_t)NWAVE * (dtype == 0 ? wave_lds_words<Bf16Key>() : wave_lds_words<F32Key>()) * 4;
+    if (kind == kTopkWave)  // (the fused gather: k offsets past the waves' regions)
+        return ((size_t)(gather_k > 0 ? kGatherWaves : NWAVE) *
+                    (dtype == 0 ? wave_lds_words<Bf16Key>() : wave_lds_words<F32Key>()) +
+                (size_t)gather_k) * 4;
     const uint64_t hist = (uint64_t)(kBins + 64);
     if (kind == kTopkSplitWx)  // the histogram, the list with a spare entry per lane, group sums
         return (size_t)(kWxBins + 64 + 2 * ((uint64_t)cap + 64) + 256) * 4;
@@ -3848,9 +3917,11 @@ hipError_t launch_topk(int dtype, int ept, int kind, const TopkArgs &a, unsigned
     if (!fn) return hipErrorInvalidValue;
     TopkArgs copy = a;
     size_t lds = topk_dyn_lds(dtype, a.cap, ept, kind, gather ? a.k : 0);
-    if (kind == kTopkWave) lds = (size_t)NWAVE * (wave_hist_words(dtype) + copy.stage_words) * 4u;
+    const int waves = wave_kernel_waves(kind, gather);
+    if (kind == kTopkWave)
+        lds = ((size_t)waves * (wave_hist_words(dtype) + copy.stage_words) + (gather ? (size_t)a.k : 0u)) * 4u;
     void *args[] = {&copy};
-    return hipLaunchKernel(fn, dim3(grid), dim3(NT), args, lds, stream);
+    return hipLaunchKernel(fn, dim3(grid), dim3(waves * 64), args, lds, stream);
 }
 
 // LDS bytes of a value-order launch: k pair words (rounded up to even), the
