@@ -56,6 +56,32 @@
 namespace dsel {
 namespace {
 
+// Phase stamps, compiled only into the instrumented build (DSEL_PHASE_STAMPS,
+// built and read by sparse_attention_indexer_dsel_amd/phase_stamps.py): at
+// a phase boundary one thread waits for its memory operations and records
+// the 100 MHz real-time clock in slot (unit, i) of a device array, where a
+// unit is a row (one-wave rows) or a workgroup.  The product build compiles
+// every stamp to nothing.
+#ifdef DSEL_PHASE_STAMPS
+constexpr int kStampUnits = 4096, kStampsPerUnit = 24;
+__device__ unsigned long long g_stamps[kStampUnits * kStampsPerUnit];
+__device__ __forceinline__ void stamp_at(bool who, int64_t unit, int i) {
+    __builtin_amdgcn_s_waitcnt(0);
+    const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+    __builtin_amdgcn_s_waitcnt(0);
+    if (who && unit >= 0 && unit < kStampUnits && g_stamps[unit * kStampsPerUnit + i] == 0)
+        g_stamps[unit * kStampsPerUnit + i] = t;
+}
+__device__ __forceinline__ void stamp_value(bool who, int64_t unit, int i, unsigned long long v) {
+    if (who && unit >= 0 && unit < kStampUnits) g_stamps[unit * kStampsPerUnit + i] = v;
+}
+#define DSEL_STAMP(who, unit, i) stamp_at((who), (unit), (i))
+#define DSEL_STAMP_VALUE(who, unit, i, v) stamp_value((who), (unit), (i), (v))
+#else
+#define DSEL_STAMP(who, unit, i) ((void)0)
+#define DSEL_STAMP_VALUE(who, unit, i, v) ((void)0)
+#endif
+
 constexpr int NT = kTopkThreads;
 constexpr int NWAVE = NT / 64;
 
@@ -1771,10 +1797,12 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         uint64_t qs = (q * slen + (uint64_t)len - 1) / (uint64_t)len;
         qs = qs < 1 ? 1 : (qs > slen ? slen : qs);
         const Digit d = find_digit_4096(L.hist, (uint32_t)qs, ent.w + 2 * (cap + 64), L.red, L.out);
+        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 8);
         wlo = d.v > 0 ? d.v - 1 : 0;
         whi = d.v < (uint32_t)kWxBins - 1 ? d.v + 1 : d.v;
         const uint32_t T1 = max(wlo << SH, 1u);
         run = compact_candidates<K, LOADS, true>(kw, len, T1, L.wtot, L.base, ent, cap);
+        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 9);
         if (run > cap) {
             ok = 0;  // uniform
         } else {
@@ -1795,6 +1823,7 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
             ok = (cw0 + cw1 + cw2 < (uint32_t)kWxKeys) ? 1u : 0u;  // each count then fits 10 bits
         }
     }
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 14);
     uint32_t *mine = area + (int64_t)c * kWxWords;
     if (ok && !empty) {
         // the window keys, bin by bin: thread t owns list entries [t E, t E + E)
@@ -1826,7 +1855,9 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         st_agent(mine + 3, cw1);
         st_agent(mine + 4, cw2);
     }
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 2);
     row_rendezvous(slot, (uint32_t)G, err, a.spin_limit);
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 6);
 
     // ---- every chunk's header ---------------------------------------------
     uint32_t *hdr = L.hist + HDR;
@@ -1901,6 +1932,7 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     const uint32_t need1 = k - R1;  // keys to take from bin B1, 1..M
     __syncthreads();
 
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 10);
     // ---- gather bin B1's keys of every chunk: NT / G threads per chunk ------
     {
         const uint32_t *chk = L.hist + CHK;
@@ -1926,6 +1958,7 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         }
     }
     __syncthreads();
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 11);
     // ---- the (need1)-th largest of them: digits (key >> 10) & 1023, then
     // key & 1023, over the workgroup
     uint32_t *sel = L.hist + SEL;
@@ -1951,6 +1984,7 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         T = (B1 << SH) | (dA.v << 10) | dB.v;
         needT = needA - dB.above;
     }
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 12);
     // ---- per chunk: its keys of B1 above / at T (wave w: chunks w, w + 4, ...)
     {
         uint32_t *chk = L.hist + CHK;
@@ -2511,6 +2545,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
     const int64_t lrow = (int64_t)(blockIdx.x / (unsigned)G);
     const int64_t row = a.row0 + lrow;
     if (row >= a.rows) return;  // uniform over the row's workgroups
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 0);
 
     const int64_t n = valid_length(a, row);
     const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
@@ -2537,9 +2572,11 @@ __global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
         for (int b = t; b < kWxBins + 64; b += NT) L.hist[b] = 0;
         __syncthreads();
         // the 12-bit histogram, filled load by load as the data arrives
+        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 13);
         nan = f32_keys_hist12<LOADS>(v, len, kw, L.hist) ? 1u : 0u;
     }
     const bool blk_nan = __syncthreads_or((int)nan) != 0;
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 1);
     if (blk_nan) {
         // rare: every NaN key to the top, and the histogram again
         for (int b = t; b < kWxBins + 64; b += NT) L.hist[b] = 0;
@@ -2556,16 +2593,20 @@ __global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
     const WxResult r = window_exchange<K, LOADS>(a, c, G, len, n, kw, blk_nan, L, ent, cap, area,
                                                  slot, err);
     if (r.ok) {
+        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 3);
         // every read of the row's shared words is done: depart now, so the
         // returning atomic overlaps the write
         uint32_t dep = 0;
         if (t == 0) dep = add_agent(slot + 1 + opaque(0u), 1u);
         write_exact<K>(a, row, ent, r.run, r.T, r.need, r.gt0, r.eq0, (uint32_t)lo, L.red, L.hist, xr);
+        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 4);
         if (t == 0) {
             if (c == 0 && a.nan_flag) a.nan_flag[row] = r.nan ? 1u : 0u;
             L.out[3] = dep == (uint32_t)G - 1u ? 1u : 0u;
         }
         __syncthreads();
+        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 5);
+        DSEL_STAMP_VALUE((t == 0), (int64_t)blockIdx.x, 7, 1);
         if (L.out[3] && t == 0) {  // last out: the counters back to zero
             st_agent(slot + 0, 0u);
             st_agent(slot + 1, 0u);
@@ -2683,15 +2724,19 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
     const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
     const int len = (int)n;
 
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 1);
     uint32_t kw[LOADS * 4];
     const uint32_t nan = keys_of_loads<K, LOADS>(buf, len, kw);
     for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
     const uint32_t block_nan = __syncthreads_or((int)nan) ? 1u : 0u;
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 2);
 
     first_digit_histogram<K, LOADS>(kw, len, L.hist);
     __syncthreads();
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 3);
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
     const uint32_t C = d1.above + d1.cnt;
+    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 4);
 
     if (LOADS <= 2 && 4 * (int64_t)C >= n) {
         // a few keys per thread and dense candidates: no list
@@ -2703,8 +2748,11 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
         write_from_regs<K, LOADS>(a, row, kw, len, b, 0u, 0u, row_view<K>(xr, n), 0, L.red, xr);
     } else if (C <= cap) {
         compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, L.base, ent, cap);
+        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 5);
         const Bound b = refine_on_list<K>(ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
+        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 6);
         write_from_list<K>(a, row, ent, C, b, L.red, xr);
+        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 7);
     } else {
         // the candidates do not fit the list: the passes re-read the row
         const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
@@ -2739,6 +2787,7 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     for (int64_t t = blockIdx.x; t < R; t += gridDim.x) {
         const int64_t row = a.row0 + taker_row(a.row_order, t, R);
         const int64_t n = valid_length(a, row);
+        DSEL_STAMP((tid() == 0), (int64_t)blockIdx.x, 0);
         const raw_t *xr = x + row * a.x_stride;
         if (n <= a.k) {
             write_short_row<K>(a, row, n, 0, 1, xr);
@@ -2759,6 +2808,7 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
             gather_tail<NT>(a, row, tid(), [&](uint32_t j) -> int64_t { return s_pos[j]; },
                             reinterpret_cast<uint32_t *>(s_dyn) + a.k);
         }
+        DSEL_STAMP((tid() == 0), (int64_t)blockIdx.x, 8);
         __syncthreads();  // LDS is reused by the next row
     }
 }
@@ -3301,6 +3351,8 @@ __global__ __launch_bounds__(GATHER ? kGatherWaves * 64 : NT) void topk_rows_wav
         const int lane = tid() & 63;
         const uint16_t *xr = x + row * a.x_stride;
         const int64_t n = valid_length(a, row);
+        DSEL_STAMP((lane == 0), row, 0);
+        DSEL_STAMP_VALUE((lane == 0), row, 7, (unsigned long long)n);
         if (n <= a.k) {
             if constexpr (RV) {
                 write_short_idx(a, row, n, 0, 0, a.k, lane, 64);
@@ -3309,6 +3361,7 @@ __global__ __launch_bounds__(GATHER ? kGatherWaves * 64 : NT) void topk_rows_wav
             } else {
                 write_short_row<K>(a, row, n, 0, 1, xr, lane, 64);
             }
+            DSEL_STAMP((lane == 0), row, 4);
             if constexpr (GATHER) {
                 if (lane == 0) {
                     g_row[wid] = row;
@@ -3378,6 +3431,7 @@ __global__ __launch_bounds__(GATHER ? kGatherWaves * 64 : NT) void topk_rows_wav
         // a NaN key lies above +inf's (0xFF80) or below -inf's (0x0080)
         const bool row_nan =
             __ballot(max(kmax & 0xFFFFu, kmax >> 16) > 0xFF80u || min(kmin & 0xFFFFu, kmin >> 16) < 0x0080u) != 0ull;
+        DSEL_STAMP((lane == 0), row, 1);
         if (row_nan) {
             // rare: every NaN to the top key, and the histogram again
             wave_sync();
@@ -3403,6 +3457,7 @@ __global__ __launch_bounds__(GATHER ? kGatherWaves * 64 : NT) void topk_rows_wav
         wave_sync();
         const uint32_t k = (uint32_t)a.k;
         const Digit d1 = w16_find1024(hist, k, lane);
+        DSEL_STAMP((lane == 0), row, 2);
         // every valid key is at least -inf's 0x0080, so the boundary bin is
         // >= 2 and no empty slot (key 0) is ever counted in it
         uint32_t T, cut = 0xFFFFFFFFu;  // take: key > T, or key == T at a column <= cut
@@ -3470,6 +3525,7 @@ __global__ __launch_bounds__(GATHER ? kGatherWaves * 64 : NT) void topk_rows_wav
             }
         }
 
+        DSEL_STAMP((lane == 0), row, 3);
         // the write
         const bool rv = RV && a.ret_val;  // (the values instance is launched only with values)
         const uint32_t idx_bytes = a.idx64 ? 8u : 4u;
@@ -3570,6 +3626,7 @@ __global__ __launch_bounds__(GATHER ? kGatherWaves * 64 : NT) void topk_rows_wav
                               (uint32_t)a.k * 2u, lane);
         }
         if (lane == 0 && a.nan_flag) a.nan_flag[row] = row_nan ? 1u : 0u;
+        DSEL_STAMP((lane == 0), row, 4);
         if constexpr (GATHER) {
             if (lane == 0) {
                 g_row[wid] = row;
@@ -3957,3 +4014,15 @@ hipError_t launch_value_sort(int dtype, const TopkArgs &a, unsigned grid, hipStr
 }
 
 }  // namespace dsel
+
+#ifdef DSEL_PHASE_STAMPS
+// The instrumented build's stamps: copy out (host buffer of
+// kStampUnits * kStampsPerUnit words) and clear.
+extern "C" int dsel_stamps_read(unsigned long long *host) {
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(dsel::g_stamps), sizeof(dsel::g_stamps));
+}
+extern "C" int dsel_stamps_clear() {
+    static unsigned long long zero[dsel::kStampUnits * dsel::kStampsPerUnit];
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(dsel::g_stamps), zero, sizeof(zero));
+}
+#endif
