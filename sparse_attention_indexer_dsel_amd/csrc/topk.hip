@@ -231,6 +231,33 @@ __device__ Scan block_scan(uint32_t x, uint32_t *s_red) {
     return Scan{w + off, tot};
 }
 
+// block_scan of two values at once (one pair of barriers); s_red2 holds
+// 2 * NWAVE words.
+struct Scan2 {
+    uint32_t incl0, incl1, total0, total1;
+};
+
+__device__ Scan2 block_scan2(uint32_t x0, uint32_t x1, uint32_t *s_red2) {
+    const int t = tid();
+    const uint32_t w0 = wave_incl_scan(x0), w1 = wave_incl_scan(x1);
+    if ((t & 63) == 63) {
+        s_red2[t >> 6] = w0;
+        s_red2[NWAVE + (t >> 6)] = w1;
+    }
+    __syncthreads();
+    Scan2 r{w0, w1, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NWAVE; ++i) {
+        const uint32_t v0 = s_red2[i], v1 = s_red2[NWAVE + i];
+        r.incl0 += (i < (t >> 6)) ? v0 : 0u;
+        r.incl1 += (i < (t >> 6)) ? v1 : 0u;
+        r.total0 += v0;
+        r.total1 += v1;
+    }
+    __syncthreads();
+    return r;
+}
+
 struct Digit {
     uint32_t v;      // boundary digit
     uint32_t above;  // count in digits above it
@@ -1806,47 +1833,43 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         if (run > cap) {
             ok = 0;  // uniform
         } else {
-            // the window's counts from the list (it holds every key of bin
-            // wlo and up: the rest lie above the window)
+            // one pass over the list (it holds every key of bin wlo and up:
+            // the rest lie above the window): thread t owns entries
+            // [t E, t E + E) and counts its keys of each window bin; one
+            // scan gives the window's counts and each thread's offsets in
+            // the published keys, grouped by bin
             const uint32_t nwin = whi - wlo + 1u;
-            uint32_t c01 = 0, c2 = 0;
-            for (uint32_t i = (uint32_t)t; i < run; i += NT) {
+            const uint32_t E = (run + NT - 1) / NT;
+            const uint32_t i0 = min(run, (uint32_t)t * E), i1 = min(run, i0 + E);
+            uint32_t m01 = 0, m2 = 0;  // bins 0 | 1 << 16, and bin 2
+            for (uint32_t i = i0; i < i1; ++i) {
                 const uint32_t w = (list_key<K>(ent, i) >> SH) - wlo;
-                c01 += w == 0 ? 1u : (w == 1 && nwin > 1 ? 0x10000u : 0u);
-                c2 += w == 2 && nwin > 2 ? 1u : 0u;
+                m01 += w == 0 ? 1u : (w == 1 && nwin > 1 ? 0x10000u : 0u);
+                m2 += w == 2 && nwin > 2 ? 1u : 0u;
             }
-            c01 = block_scan(c01, L.red).total;
-            cw2 = block_scan(c2, L.red).total;
-            cw0 = c01 & 0xFFFFu;
-            cw1 = c01 >> 16;
+            const Scan2 sc = block_scan2(m01, m2, L.base);
+            cw0 = sc.total0 & 0xFFFFu;
+            cw1 = sc.total0 >> 16;
+            cw2 = sc.total1;
             above = run - cw0 - cw1 - cw2;
             ok = (cw0 + cw1 + cw2 < (uint32_t)kWxKeys) ? 1u : 0u;  // each count then fits 10 bits
+            DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 14);
+            if (ok) {  // uniform
+                const uint32_t ex01 = sc.incl0 - m01;
+                uint32_t o0 = ex01 & 0xFFFFu, o1 = cw0 + (ex01 >> 16), o2 = cw0 + cw1 + (sc.incl1 - m2);
+                uint32_t *dst = area + (int64_t)c * kWxWords + kWxHdr;
+                for (uint32_t i = i0; i < i1; ++i) {
+                    const uint32_t key = list_key<K>(ent, i);
+                    const uint32_t w = (key >> SH) - wlo;
+                    if (w >= nwin) continue;
+                    if (w == 0) st_agent(dst + o0++, key);
+                    else if (w == 1) st_agent(dst + o1++, key);
+                    else st_agent(dst + o2++, key);
+                }
+            }
         }
     }
-    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 14);
     uint32_t *mine = area + (int64_t)c * kWxWords;
-    if (ok && !empty) {
-        // the window keys, bin by bin: thread t owns list entries [t E, t E + E)
-        const uint32_t E = (run + NT - 1) / NT;
-        const uint32_t i0 = (uint32_t)t * E, i1 = min(run, i0 + E);
-        uint32_t m = 0;
-        const uint32_t nwin = whi - wlo + 1u;
-        for (uint32_t i = i0; i < i1; ++i) {
-            const uint32_t w = (list_key<K>(ent, i) >> SH) - wlo;
-            m += w >= nwin ? 0u : (w == 0 ? 1u : (w == 1 ? (1u << 10) : (1u << 20)));
-        }
-        const uint32_t ex = block_scan(m, L.red).incl - m;
-        uint32_t o0 = ex & 0x3FFu, o1 = cw0 + ((ex >> 10) & 0x3FFu), o2 = cw0 + cw1 + (ex >> 20);
-        uint32_t *dst = mine + kWxHdr;
-        for (uint32_t i = i0; i < i1; ++i) {
-            const uint32_t key = list_key<K>(ent, i);
-            const uint32_t w = (key >> SH) - wlo;
-            if (w >= nwin) continue;
-            if (w == 0) st_agent(dst + o0++, key);
-            else if (w == 1) st_agent(dst + o1++, key);
-            else st_agent(dst + o2++, key);
-        }
-    }
     if (t == 0) {
         st_agent(mine + 0, wlo | (whi << 12) | (ok << 24) | (empty ? 1u << 25 : 0u) |
                                (blk_nan ? 1u << 26 : 0u));
