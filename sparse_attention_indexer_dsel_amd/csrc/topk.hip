@@ -3903,13 +3903,16 @@ const void *pick_wave(int epl) {
             case 32: return reinterpret_cast<const void *>(&topk_rows_wave_bf16<4, RV, GATHER>);
             default: return nullptr;
         }
-    }
-    if constexpr (GATHER) return nullptr;  // fp32 one-wave rows do not fuse the gather
-    switch (epl) {
-        case 8: return reinterpret_cast<const void *>(&topk_rows_wave<K, 8, RV>);
-        case 16: return reinterpret_cast<const void *>(&topk_rows_wave<K, 16, RV>);
-        case 32: return reinterpret_cast<const void *>(&topk_rows_wave<K, 32, RV>);
-        default: return nullptr;
+    } else if constexpr (GATHER) {
+        return nullptr;  // fp32 one-wave rows do not fuse the gather
+    } else {
+        // (only fp32 rows instantiate the generic one-wave kernel)
+        switch (epl) {
+            case 8: return reinterpret_cast<const void *>(&topk_rows_wave<K, 8, RV>);
+            case 16: return reinterpret_cast<const void *>(&topk_rows_wave<K, 16, RV>);
+            case 32: return reinterpret_cast<const void *>(&topk_rows_wave<K, 32, RV>);
+            default: return nullptr;
+        }
     }
 }
 
