@@ -2042,49 +2042,6 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     return r;
 }
 
-// Keys of a workgroup's loads (coalesced layout), each load turned into keys
-// and, with_hist, histogrammed (12-bit first digit) as soon as it arrives.
-// Columns at or past len get key 0 (the spare bin of this lane).  Returns
-// whether this thread saw a NaN.
-template <class K, int LOADS>
-__device__ __forceinline__ uint32_t keys_hist12(const uint4 (&v)[LOADS], int len,
-                                                uint32_t (&kw)[LOADS * 4], uint32_t *hist,
-                                                bool with_hist) {
-    constexpr int VEC = K::VEC, EPW = K::EPW, SPAN = NT * VEC;
-    const int me = tid();
-    const int full = len / SPAN, any = (len + SPAN - 1) / SPAN;
-    const uint32_t spare = (uint32_t)kWxBins + (uint32_t)(me & 63);
-    uint32_t nan = 0;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-        if (j >= any) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) kw[4 * j + q] = 0u;
-            continue;
-        }
-        uint4 x = v[j];
-        int valid = VEC;
-        if (j >= full) {
-            valid = len - (j * NT + me) * VEC;
-            valid = valid < 0 ? 0 : (valid > VEC ? VEC : valid);
-            x.x = K::keep_raw(x.x, valid);
-            x.y = K::keep_raw(x.y, valid - EPW);
-            x.z = K::keep_raw(x.z, valid - 2 * EPW);
-            x.w = K::keep_raw(x.w, valid - 3 * EPW);
-        }
-        nan |= keys_of<K>(x, &kw[4 * j]) ? 1u : 0u;
-        if (j >= full) clear_tail<K>(&kw[4 * j], valid);
-        if (with_hist) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t key = kw[4 * j + q];
-                atomicAdd(&hist[(j < full || key) ? (key >> 20) : spare], 1u);
-            }
-        }
-    }
-    return nan;
-}
-
 // The multi-pass select of a split row, from each workgroup's first-digit
 // histogram in LDS (hist): the histograms meet in the row's workspace slot,
 // one rendezvous per radix pass (nren rendezvous of this launch are already
