@@ -29,7 +29,12 @@ Timing protocol
     with rocprofv3's kernel trace;
   * ``floors`` gives the launch floor (a graph of empty-work kernels, per
     launch) and streaming read, write and copy rates of plain device
-    kernels over 1 GiB, for scale.
+    kernels over 1 GiB, for scale;
+  * each workload's top-k and gathers are also timed cold (``cold``): 10
+    warm-up calls, then 100 single eager calls, each after 1 GiB is written
+    on the call's stream (four times the Infinity Cache), with an event
+    pair around the call alone; the median (and p10, p90) is reported.
+    It includes the launch latency that graph replay hides.
 
 Byte accounting (algorithmic bytes: what the method must move)
   top-k  = sum over rows of the valid-prefix read (a row of valid length
@@ -318,13 +323,46 @@ def graph_time(torch, stream, fn, steps: int, warmup: int, reps: int = 1):
     return best, best_ev
 
 
+COLD_FLUSH_BYTES = 1 << 30  # written before each cold call: four times the Infinity Cache
+_FLUSH = []
+
+
+def cold_time(torch, stream, fn, reps: int = 100, warmup: int = 10) -> dict:
+    """Cold-cache timing: before each call a 1 GiB buffer is written on the
+    call's stream (evicting L2 and the Infinity Cache), and a HIP event pair
+    brackets the call alone (eager launch, so the launch latency is in).
+    `warmup` untimed calls first; the median of `reps` calls is reported."""
+    if not _FLUSH:
+        _FLUSH.append(torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device="cuda"))
+    flush = _FLUSH[0]
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn(i)
+    stream.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        for i, (e0, e1) in enumerate(evs):
+            flush.fill_(i & 0xFF)
+            e0.record(stream)
+            fn(i)
+            e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    return {"median_us": float(np.median(t)), "p10_us": t[len(t) // 10],
+            "p90_us": t[(9 * len(t)) // 10], "reps": reps, "warmup": warmup,
+            "how": "1 GiB written on the stream before each call; events around the call only"}
+
+
 def topk_kernel_name(case, by_value=False) -> str:
     return "dsel_topk" + (" + value order" if by_value else "") + f" ({case.name})"
 
 
-def measure_topk(dsel, torch, case, stream, steps, warmup, by_value=False, traffic=None):
+def measure_topk(dsel, torch, case, stream, steps, warmup, by_value=False, traffic=None,
+                 cold=False):
     """One top-k call per step (with by_value, the select and then the
-    value-order pass: kernel_us covers both)."""
+    value-order pass: kernel_us covers both).  cold: also the cold-cache
+    median of 100 single calls."""
     tb = TopkBench(dsel, torch, case, stream, by_value)
     steps = min(max(steps, tb.ncopy), 256)  # every input copy read once per replay
     t_step, t_kern = graph_time(torch, stream, tb.call, steps, warmup, reps=3)
@@ -341,6 +379,9 @@ def measure_topk(dsel, torch, case, stream, steps, warmup, by_value=False, traff
         "steps": steps,
         "roofline": roofline(nbytes, t_kern, topk_kernel_name(case, by_value), traffic),
     }
+    if cold:
+        res["cold"] = cold_time(torch, stream, tb.call)
+        res["cold"]["pct_peak"] = 100.0 * nbytes / (res["cold"]["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS
     del tb
     torch.cuda.empty_cache()
     return res
@@ -372,6 +413,8 @@ def measure_gather(dsel, torch, case, stream, steps, warmup, traffic=None):
         psz = pos.element_size()
         alg = gather_algorithmic_bytes(npos, D, esz, psz, distinct)
         out_bytes = npos * D * esz
+        cold = cold_time(torch, stream, fn)
+        cold["pct_peak"] = 100.0 * alg / (cold["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS
         out.append({
             "key": "contiguous" if key.is_contiguous() else "strided view",
             "us_per_call": t * 1e6,
@@ -381,6 +424,7 @@ def measure_gather(dsel, torch, case, stream, steps, warmup, traffic=None):
             "pct_peak": 100.0 * alg / t / 1e9 / HBM_PEAK_GBPS,
             "output_convention_gbps": output_convention_gbps(out_bytes, t),
             "roofline": roofline(alg, tk, f"dsel_gather_rows ({case.name})", traffic),
+            "cold": cold,
         })
         del dst, kd
     torch.cuda.empty_cache()
@@ -713,7 +757,8 @@ def main(argv=None):
         "roofline": roofline(nbytes, t_kern, topk_kernel_name(case),
                              traffic_for(traffic, case.name, "topk")),
         "timing": "warm back-to-back graph replay over rotating input copies (> 2x the "
-                  "Infinity Cache), events on the kernels' stream",
+                  "Infinity Cache), events on the kernels' stream; per_config entries also "
+                  "carry a cold-cache median of 100 single calls ('cold')",
     }
 
     cases = [case if i == cfg_id else W.make_config(i) for i in sorted(W.CONFIGS)]
@@ -724,7 +769,7 @@ def main(argv=None):
         per = {}
         for c in cases:
             entry = {"topk": measure_topk(dsel, torch, c, stream, 20, 3,
-                                          traffic=traffic_for(traffic, c.name, "topk"))}
+                                          traffic=traffic_for(traffic, c.name, "topk"), cold=True)}
             if c.x.shape[0] and c.name == case.name:
                 entry["topk"]["headline"] = True
             if int(c.name[3:]) in VALUE_ORDER_CONFIGS:
