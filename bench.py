@@ -1,7 +1,7 @@
 """Benchmark of the selection step (row-wise top-k, then key gather) on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg4]
-                    [--no-per-config] [--no-cpu-baseline] [--no-floors]
+                    [--no-per-config] [--no-cpu-baseline] [--no-floors] [--no-cold]
     python bench.py --profile-run cfgN      # a few calls of one workload, for counter runs
     python bench.py --traffic-from DIR      # no GPU: counter files -> profiles/traffic.json
 
@@ -387,7 +387,7 @@ def measure_topk(dsel, torch, case, stream, steps, warmup, by_value=False, traff
     return res
 
 
-def measure_gather(dsel, torch, case, stream, steps, warmup, traffic=None):
+def measure_gather(dsel, torch, case, stream, steps, warmup, traffic=None, cold=True):
     """Gather(s) of the case's keys at the top-k positions (one call per key)."""
     dev = torch.device("cuda")
     _, idx, _ = dsel.topk(case.x.to(dev), case.k,
@@ -413,8 +413,10 @@ def measure_gather(dsel, torch, case, stream, steps, warmup, traffic=None):
         psz = pos.element_size()
         alg = gather_algorithmic_bytes(npos, D, esz, psz, distinct)
         out_bytes = npos * D * esz
-        cold = cold_time(torch, stream, fn)
-        cold["pct_peak"] = 100.0 * alg / (cold["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS
+        cold_t = None
+        if cold:
+            cold_t = cold_time(torch, stream, fn)
+            cold_t["pct_peak"] = 100.0 * alg / (cold_t["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS
         out.append({
             "key": "contiguous" if key.is_contiguous() else "strided view",
             "us_per_call": t * 1e6,
@@ -424,8 +426,9 @@ def measure_gather(dsel, torch, case, stream, steps, warmup, traffic=None):
             "pct_peak": 100.0 * alg / t / 1e9 / HBM_PEAK_GBPS,
             "output_convention_gbps": output_convention_gbps(out_bytes, t),
             "roofline": roofline(alg, tk, f"dsel_gather_rows ({case.name})", traffic),
-            "cold": cold,
         })
+        if cold_t is not None:
+            out[-1]["cold"] = cold_t
         del dst, kd
     torch.cuda.empty_cache()
     return out
@@ -670,6 +673,8 @@ def main(argv=None):
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-floors", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache single calls (kernel traces of the warm replay)")
     ap.add_argument("--profile-run", metavar="CFG",
                     help="a few calls of one workload (cfgN, or cfgNv ordered by value) for counter runs")
     ap.add_argument("--counters-from", metavar="DIR",
@@ -769,7 +774,8 @@ def main(argv=None):
         per = {}
         for c in cases:
             entry = {"topk": measure_topk(dsel, torch, c, stream, 20, 3,
-                                          traffic=traffic_for(traffic, c.name, "topk"), cold=True)}
+                                          traffic=traffic_for(traffic, c.name, "topk"),
+                                          cold=not args.no_cold)}
             if c.x.shape[0] and c.name == case.name:
                 entry["topk"]["headline"] = True
             if int(c.name[3:]) in VALUE_ORDER_CONFIGS:
@@ -779,7 +785,8 @@ def main(argv=None):
                     dsel, torch, dataclasses.replace(c, return_value=True), stream, 20, 3)
             if c.keys:
                 entry["gather"] = measure_gather(dsel, torch, c, stream, 10, 2,
-                                                 traffic=traffic_for(traffic, c.name, "gather"))
+                                                 traffic=traffic_for(traffic, c.name, "gather"),
+                                                 cold=not args.no_cold)
                 entry["topk_gather"] = measure_fused(dsel, torch, c, stream, 10, 2)
             per[c.name] = entry
             print(f"# {c.name}: {json.dumps(entry)}", file=sys.stderr, flush=True)
