@@ -715,7 +715,7 @@ __device__ __forceinline__ uint32_t keys_of_loads(const uint4 (&v)[LOADS], int l
     constexpr int VEC = K::VEC, EPW = K::EPW;
     const int full = len / (TW * VEC);  // loads valid for every thread (uniform)
     const int any = (len + TW * VEC - 1) / (TW * VEC);
-    uint32_t nan = 0;
+    uint32_t m = 0;  // NaN probe over every load: one branch, taken only with a NaN
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         if (j >= any) {
@@ -733,10 +733,18 @@ __device__ __forceinline__ uint32_t keys_of_loads(const uint4 (&v)[LOADS], int l
             x.z = K::keep_raw(x.z, valid - 2 * EPW);
             x.w = K::keep_raw(x.w, valid - 3 * EPW);
         }
-        nan |= keys_of<K>(x, &kw[4 * j]) ? 1u : 0u;
+        kw[4 * j] = K::keyword(x.x, m);
+        kw[4 * j + 1] = K::keyword(x.y, m);
+        kw[4 * j + 2] = K::keyword(x.z, m);
+        kw[4 * j + 3] = K::keyword(x.w, m);
         if (j >= full) clear_tail<K>(&kw[4 * j], valid);
     }
-    return nan;
+    const bool nan = K::probe_nan(m);
+    if (nan) {
+#pragma unroll
+        for (int w = 0; w < LOADS * 4; ++w) kw[w] = K::fix_nan_word(kw[w]);
+    }
+    return nan ? 1u : 0u;
 }
 
 // Histogram the first digit of every element of a key word.
