@@ -709,7 +709,10 @@ __device__ __forceinline__ void clear_tail(uint32_t *kw, int valid) {
 // Columns at or past len get key 0 and are not probed for NaN; loads wholly
 // past len are not transformed at all.  Returns whether this thread saw a
 // NaN.
-template <class K, int LOADS, int TW = NT>
+// PER_VECTOR: the NaN fix-up branch per 16-byte vector instead of once over
+// every load (the fused gather's whole-row kernel keeps its registers that
+// way).
+template <class K, int LOADS, int TW = NT, bool PER_VECTOR = false>
 __device__ __forceinline__ uint32_t keys_of_loads(const uint4 (&v)[LOADS], int len,
                                                   uint32_t (&kw)[LOADS * 4], int me = tid()) {
     constexpr int VEC = K::VEC, EPW = K::EPW;
@@ -733,12 +736,17 @@ __device__ __forceinline__ uint32_t keys_of_loads(const uint4 (&v)[LOADS], int l
             x.z = K::keep_raw(x.z, valid - 2 * EPW);
             x.w = K::keep_raw(x.w, valid - 3 * EPW);
         }
-        kw[4 * j] = K::keyword(x.x, m);
-        kw[4 * j + 1] = K::keyword(x.y, m);
-        kw[4 * j + 2] = K::keyword(x.z, m);
-        kw[4 * j + 3] = K::keyword(x.w, m);
+        if constexpr (PER_VECTOR) {
+            m |= keys_of<K>(x, &kw[4 * j]) ? 1u : 0u;
+        } else {
+            kw[4 * j] = K::keyword(x.x, m);
+            kw[4 * j + 1] = K::keyword(x.y, m);
+            kw[4 * j + 2] = K::keyword(x.z, m);
+            kw[4 * j + 3] = K::keyword(x.w, m);
+        }
         if (j >= full) clear_tail<K>(&kw[4 * j], valid);
     }
+    if constexpr (PER_VECTOR) return m;
     const bool nan = K::probe_nan(m);
     if (nan) {
 #pragma unroll
@@ -2782,8 +2790,8 @@ __device__ __forceinline__ void load_row(const typename K::raw_t *xr, int64_t n,
 }
 
 // One row of valid length n > k whose raw 16-byte vectors are in buf
-// (coalesced layout).
-template <class K, int LOADS>
+// (coalesced layout).  GATHER: the instance that also copies the row's keys.
+template <class K, int LOADS, bool GATHER = false>
 __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64_t n,
                                            const uint4 (&buf)[LOADS],
                                            const TopkLds &L, List ent) {
@@ -2795,7 +2803,7 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
 
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 1);
     uint32_t kw[LOADS * 4];
-    const uint32_t nan = keys_of_loads<K, LOADS>(buf, len, kw);
+    const uint32_t nan = keys_of_loads<K, LOADS, NT, GATHER>(buf, len, kw);
     for (int b = t; b < kHistCopies * kBins + 64; b += NT) L.hist[b] = 0;
     const uint32_t block_nan = __syncthreads_or((int)nan) ? 1u : 0u;
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 2);
@@ -2863,7 +2871,7 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
         } else {
             uint4 v[LOADS];
             load_row<K, LOADS>(xr, n, v);
-            select_row<K, LOADS>(a, row, n, v, L, ent);
+            select_row<K, LOADS, GATHER>(a, row, n, v, L, ent);
         }
         if constexpr (GATHER) {
             // the row's positions, as this workgroup wrote them, into LDS
