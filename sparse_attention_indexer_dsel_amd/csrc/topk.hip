@@ -792,87 +792,6 @@ __device__ __forceinline__ void first_digit_histogram(const uint32_t (&kw)[LOADS
     }
 }
 
-// Whole rows keep their first-digit histogram in kHistCopies copies, bin b
-// of copy c at word kHistCopies b + c, each lane adding to copy lane %
-// kHistCopies (spare bins from word kHistCopies kBins): the crowded bins of
-// bell-shaped scores take fewer same-address LDS atomics per instruction.
-constexpr int kHistCopies = 2;  // (measured: three copies were slower)
-template <class K, int LOADS>
-__device__ __forceinline__ void first_digit_histogram2(const uint32_t (&kw)[LOADS * 4], int len,
-                                                       uint32_t *hist) {
-    constexpr int SPAN = NT * K::VEC;
-    const int full = len / SPAN, any = (len + SPAN - 1) / SPAN;
-    const int lane = tid() & 63;
-    uint32_t *const hp = hist + (lane % kHistCopies);
-    uint32_t *const spare = hist + kHistCopies * kBins + lane;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-        if (j < full) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int h = 0; h < K::EPW; ++h)
-                    atomicAdd(&hp[kHistCopies * (K::elem(kw[4 * j + q], h) >> K::SH1)], 1u);
-        } else if (j < any) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int h = 0; h < K::EPW; ++h) {
-                    const uint32_t key = K::elem(kw[4 * j + q], h);
-                    atomicAdd(key ? &hp[kHistCopies * (key >> K::SH1)] : spare, 1u);
-                }
-        }
-    }
-}
-
-// find_digit over the copied histogram of kBins bins: thread t sums its 8
-// bins [kBins - 8 (t + 1), kBins - 8 t) over the copies (16-byte reads),
-// one workgroup scan finds the thread, and it walks its bins.
-__device__ Digit find_digit2(const uint32_t *hist, uint32_t need, uint32_t *s_red, uint32_t *s_out) {
-    static_assert(kBins == 8 * NT, "eight bins per thread");
-    const int t = tid();
-    constexpr int R = kHistCopies;
-    const uint4 *p = reinterpret_cast<const uint4 *>(hist + R * (kBins - 8 * (t + 1)));
-    uint32_t w[8 * R];
-#pragma unroll
-    for (int i = 0; i < 2 * R; ++i) {
-        const uint4 q = p[i];
-        w[4 * i] = q.x;
-        w[4 * i + 1] = q.y;
-        w[4 * i + 2] = q.z;
-        w[4 * i + 3] = q.w;
-    }
-    uint32_t hb[8];
-    uint32_t local = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        hb[i] = 0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) hb[i] += w[R * i + r];
-        local += hb[i];
-    }
-    const uint32_t incl = block_scan(local, s_red).incl;
-    const uint32_t excl = incl - local;
-    if (excl < need && need <= incl) {
-        uint32_t acc = excl;
-        bool found = false;
-#pragma unroll
-        for (int i = 7; i >= 0; --i) {
-            if (!found && acc + hb[i] >= need) {
-                s_out[0] = (uint32_t)(kBins - 8 * (t + 1) + i);
-                s_out[1] = acc;
-                s_out[2] = hb[i];
-                found = true;
-            }
-            acc += hb[i];
-        }
-    }
-    __syncthreads();
-    const Digit d{s_out[0], s_out[1], s_out[2]};
-    __syncthreads();
-    return d;
-}
-
 // A candidate list in LDS, cap entries plus one spare entry per lane.  A
 // bf16 entry is one word, key << 16 | column (columns of a workgroup's range
 // are below 2^16); an fp32 entry is two words, key then column.  Either way
@@ -2804,14 +2723,14 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 1);
     uint32_t kw[LOADS * 4];
     const uint32_t nan = keys_of_loads<K, LOADS, NT, GATHER>(buf, len, kw);
-    for (int b = t; b < kHistCopies * kBins + 64; b += NT) L.hist[b] = 0;
+    for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
     const uint32_t block_nan = __syncthreads_or((int)nan) ? 1u : 0u;
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 2);
 
-    first_digit_histogram2<K, LOADS>(kw, len, L.hist);
+    first_digit_histogram<K, LOADS>(kw, len, L.hist);
     __syncthreads();
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 3);
-    const Digit d1 = find_digit2(L.hist, (uint32_t)a.k, L.red, L.out);
+    const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
     const uint32_t C = d1.above + d1.cnt;
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 4);
 
@@ -4016,7 +3935,7 @@ size_t topk_dyn_lds(int dtype, int64_t cap, int ept, int kind, int64_t gather_k)
         return ((size_t)(gather_k > 0 ? kGatherWaves : NWAVE) *
                     (dtype == 0 ? wave_lds_words<Bf16Key>() : wave_lds_words<F32Key>()) +
                 (size_t)gather_k) * 4;
-    const uint64_t hist = (uint64_t)((kind == kTopkWhole ? kHistCopies : 1) * kBins + 64);
+    const uint64_t hist = (uint64_t)(kBins + 64);
     if (kind == kTopkSplitWx)  // the histogram, the list with a spare entry per lane, group sums
         return (size_t)(kWxBins + 64 + 2 * ((uint64_t)cap + 64) + 256) * 4;
     const uint64_t base = kind == kTopkSplit ? split_list_base()
