@@ -297,10 +297,14 @@ __device__ Digit find_digit(const uint32_t *hist, int nb, uint32_t need, uint32_
 }
 
 // find_digit for histograms of at least NT bins (nb = NT * bpt, bpt <= 16,
-// a multiple of 4): each thread sums its bpt bins with 16-byte reads, one
-// workgroup scan finds the thread holding the need-th largest element, and
+// a multiple of 4) whose bins each pack two counts: all elements in the low
+// 16 bits, a subset of them in the high 16 (every sum stays below 2^16).
+// Each thread sums its bpt bins with 16-byte reads, one workgroup scan finds
+// the thread holding the need-th largest element (by the low counts), and
 // every wave then resolves the bin among that thread's bpt bins with one
-// 16-lane scan (no serial walk).
+// 16-lane scan (no serial walk).  The Digit's `above` and `cnt` keep both
+// halves: above & 0xFFFF elements lie in higher digits, above >> 16 of them
+// in the subset, and likewise for cnt in the digit itself.
 __device__ Digit find_digit_fast(const uint32_t *hist, int nb, uint32_t need, uint32_t *s_red,
                                  uint32_t *s_out) {
     const int t = tid();
@@ -314,7 +318,7 @@ __device__ Digit find_digit_fast(const uint32_t *hist, int nb, uint32_t need, ui
     }
     const uint32_t incl = block_scan(local, s_red).incl;
     const uint32_t excl = incl - local;
-    if (excl < need && need <= incl) {
+    if ((excl & 0xFFFFu) < need && need <= (incl & 0xFFFFu)) {
         s_out[0] = (uint32_t)t;
         s_out[1] = excl;
     }
@@ -325,7 +329,7 @@ __device__ Digit find_digit_fast(const uint32_t *hist, int nb, uint32_t need, ui
     const int bin = topT - 1 - (lane & 15);  // descending over the thread's bins
     const uint32_t h = (lane & 15) < bpt ? hist[bin] : 0u;
     const uint32_t cum = ex + row16_incl_scan(h);
-    const int L = (int)__builtin_ctzll(__ballot(lane < bpt && cum >= need));
+    const int L = (int)__builtin_ctzll(__ballot(lane < bpt && (cum & 0xFFFFu) >= need));
     const Digit d{rdlane((uint32_t)bin, L), rdlane(cum - h, L), rdlane(h, L)};
     __syncthreads();  // s_out may be rewritten by the next search
     return d;
@@ -1805,9 +1809,12 @@ __device__ __forceinline__ uint32_t wx_sample_len(int len) {
 // words 2..4 = keys in bins lo, lo+1, lo+2, then the window keys from word
 // kWxHdr, bin by bin.
 // LDS after the rendezvous (the histogram's space): gathered keys [0, 2048),
-// the local radix histogram [2048, 3072), per-chunk words [3072, 3397) (five
-// arrays of G + 1 <= 65: segment starts, offsets, counts above B1, above T,
-// at T), headers [3584, 3904).
+// the local radix histogram [2048, 3072), per-chunk words [3072, 3202) (two
+// arrays of G + 1 <= 65: segment starts, offsets), headers [3584, 3904).
+// The local histograms count each key twice in one word: once in the low
+// half, and once in the high half when it comes from a chunk before this
+// workgroup's, so the digit searches also give this workgroup's counts of
+// earlier keys above and at T.
 // ---------------------------------------------------------------------------
 struct WxResult {
     bool ok, nan;
@@ -1948,7 +1955,6 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         const uint32_t w1 = B1 - clo;  // bin B1 in this lane's window (live lanes)
         const uint32_t mc = !live ? 0u : (w1 == 0 ? cc0 : (w1 == 1 ? cc1 : cc2));
         const uint32_t boff = w1 == 0 ? 0u : (w1 == 1 ? cc0 : cc0 + cc1);
-        const uint32_t ac = at_or_above(B1 + 1);
         const uint32_t incl = wave_incl_scan(mc);
         M = rdlane(incl, 63);
         good = M <= (uint32_t)kWxGather;
@@ -1957,7 +1963,6 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
             if (in) {
                 chk[lane] = incl - mc;      // segment start of this chunk's keys in B1
                 chk[65 + lane] = boff;      // their offset in its area
-                chk[130 + lane] = ac;       // its keys above bin B1
             }
             if (lane == 0) chk[G] = M;
         }
@@ -1969,10 +1974,14 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     }
     const uint32_t R1 = wave_sum(at_or_above(B1 + 1));
     const uint32_t need1 = k - R1;  // keys to take from bin B1, 1..M
+    const uint32_t ab0 = wave_sum(lane < c ? at_or_above(B1 + 1) : 0u);  // earlier chunks, above B1
+    uint32_t *sel = L.hist + SEL;
+    for (int i = t; i < 1024; i += NT) sel[i] = 0;
     __syncthreads();
 
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 10);
-    // ---- gather bin B1's keys of every chunk: NT / G threads per chunk ------
+    // ---- gather bin B1's keys of every chunk (NT / G threads per chunk), and
+    // histogram their first local digit (key >> 10) & 1023 as they arrive
     {
         const uint32_t *chk = L.hist + CHK;
         const int tpc = NT / G;
@@ -1991,7 +2000,10 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const uint32_t ii = i + (uint32_t)(u * tpc);
-                    if (ii < m) L.hist[GAT + seg + ii] = v[u];
+                    if (ii < m) {
+                        L.hist[GAT + seg + ii] = v[u];
+                        atomicAdd(&sel[(v[u] >> 10) & 1023u], cc < c ? 0x10001u : 1u);
+                    }
                 }
             }
         }
@@ -1999,57 +2011,34 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     __syncthreads();
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 11);
     // ---- the (need1)-th largest of them: digits (key >> 10) & 1023, then
-    // key & 1023, over the workgroup
-    uint32_t *sel = L.hist + SEL;
-    for (int i = t; i < 1024; i += NT) sel[i] = 0;
-    __syncthreads();
-    for (uint32_t i = (uint32_t)t; i < M; i += NT) atomicAdd(&sel[(L.hist[GAT + i] >> 10) & 1023u], 1u);
-    __syncthreads();
+    // key & 1023, over the workgroup; a key of an earlier chunk (gathered
+    // before this chunk's segment) also counts in the high half of its bin
+    const uint32_t segc = L.hist[CHK + c];
     const Digit dA = find_digit_fast(sel, 1024, need1, L.red, L.out);
-    const uint32_t needA = need1 - dA.above;
-    uint32_t T, needT;
-    if (dA.cnt == needA) {
+    const uint32_t needA = need1 - (dA.above & 0xFFFFu);
+    uint32_t T, needT, gtE, eqE;  // earlier chunks' keys of B1 above T, at T
+    if ((dA.cnt & 0xFFFFu) == needA) {
         T = ((B1 << SH) | (dA.v << 10)) - 1u;  // the digit's bin is taken whole
         needT = 0;
+        gtE = (dA.above >> 16) + (dA.cnt >> 16);
+        eqE = 0;  // (no key at T is taken)
     } else {
         for (int i = t; i < 1024; i += NT) sel[i] = 0;
         __syncthreads();
         for (uint32_t i = (uint32_t)t; i < M; i += NT) {
             const uint32_t key = L.hist[GAT + i];
-            if (((key >> 10) & 1023u) == dA.v) atomicAdd(&sel[key & 1023u], 1u);
+            if (((key >> 10) & 1023u) == dA.v) atomicAdd(&sel[key & 1023u], i < segc ? 0x10001u : 1u);
         }
         __syncthreads();
         const Digit dB = find_digit_fast(sel, 1024, needA, L.red, L.out);
         T = (B1 << SH) | (dA.v << 10) | dB.v;
-        needT = needA - dB.above;
+        needT = needA - (dB.above & 0xFFFFu);
+        gtE = (dA.above >> 16) + (dB.above >> 16);
+        eqE = dB.cnt >> 16;
     }
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 12);
-    // ---- per chunk: its keys of B1 above / at T (wave w: chunks w, w + 4, ...)
-    {
-        uint32_t *chk = L.hist + CHK;
-        for (int cc = t >> 6; cc < G; cc += NWAVE) {
-            const uint32_t s0 = chk[cc], s1 = chk[cc + 1];
-            uint32_t g = 0, qn = 0;
-            for (uint32_t i = s0 + (uint32_t)lane; i < s1; i += 64) {
-                const uint32_t key = L.hist[GAT + i];
-                g += key > T ? 1u : 0u;
-                qn += key == T ? 1u : 0u;
-            }
-            g = wave_sum(g);
-            qn = wave_sum(qn);
-            if (lane == 0) {
-                chk[195 + cc] = g;
-                chk[260 + cc] = qn;
-            }
-        }
-    }
-    __syncthreads();
-    {
-        const uint32_t *chk = L.hist + CHK;
-        const bool before = lane < c;
-        r.gt0 = wave_sum(before ? chk[130 + lane] + chk[195 + lane] : 0u);
-        r.eq0 = wave_sum(before ? chk[260 + lane] : 0u);
-    }
+    r.gt0 = ab0 + gtE;
+    r.eq0 = eqE;
     r.T = T;
     r.need = needT;
     r.run = run;

@@ -126,8 +126,9 @@ def report(kernel: str, cfg: int) -> str:
         for name, a, b in (("loads arrived", 0, 13), ("keys, sampled histogram", 13, 1),
                            ("window digit", 1, 8), ("candidate list", 8, 9),
                            ("window counts", 9, 14), ("publish", 14, 2), ("rendezvous wait", 2, 6),
-                           ("headers, boundary bin", 6, 10), ("gather boundary keys", 10, 11),
-                           ("select in them", 11, 12), ("per-chunk counts", 12, 3),
+                           ("headers, boundary bin", 6, 10),
+                           ("gather keys, 1st digit", 10, 11),
+                           ("select, earlier counts", 11, 3),
                            ("write", 3, 4), ("finish", 4, 5)):
             lines.append(_stats(name, (ns(b) - ns(a))[ok]))
         lines.append(_stats("end", ns(5)[ok]))

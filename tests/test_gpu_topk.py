@@ -187,6 +187,40 @@ def test_nan_just_past_row_end(dsel, orc, dt, G):
     assert not got[2].any(), "no row holds a NaN in range"
 
 
+@pytest.mark.parametrize("G", [4, 8])
+def test_split_f32_nan_in_each_load(dsel, orc, G):
+    """fp32 split rows whose NaNs sit in the loads a chunk histograms (every
+    fourth 1024-column load of a chunk, load 0 first) and in the loads it
+    does not, positive and negative NaN payloads, one or several per row,
+    up to the chunk's partial last load."""
+    rows, cols = 8, 40000
+    x = W.random_rows(131, rows, cols, W.F32, "normal")
+    xi = x.view(torch.int32)
+    chunk = cols // G
+    neg_nan = -4194304  # 0xFFC00000
+    # row 0: no NaN; 1: load 1 of chunk 1 (not sampled); 2: load 0 of chunk 2
+    # (sampled); 3: the last column; 4: three loads not sampled, over two
+    # chunks; 5: a negative NaN in load 5; 6: sampled and not sampled; 7:
+    # load 2 and a negative NaN in load 3 of chunk 0
+    x[1, chunk + 1500] = float("nan")
+    x[2, 2 * chunk + 100] = float("nan")
+    x[3, cols - 1] = float("nan")
+    x[4, 1100] = float("nan")
+    x[4, 3 * 1024 + 7] = float("nan")
+    x[4, chunk + 2 * 1024 + 500] = float("nan")
+    xi[5, 5 * 1024 + 33] = neg_nan
+    x[6, 4 * 1024 + 1] = float("nan")
+    x[6, 6 * 1024 + 2] = float("nan")
+    x[7, 2 * 1024 + 9] = float("nan")
+    xi[7, 3 * 1024 + 10] = neg_nan
+    re = torch.tensor([cols] * 7 + [cols - 777], dtype=torch.int32)
+    for k, sorted_index, itype, ret in ((2000, True, torch.int64, True), (37, False, torch.int32, True),
+                                        (4096, False, torch.int32, False)):
+        got = check_case(dsel, orc, f"f32_nan_loads/G{G}/k{k}", x, k, re, sorted_index, itype, ret, G)
+        assert got[2].tolist() == [0, 1, 1, 1, 1, 1, 1, 1]
+    assert_workspaces_clean(dsel)
+
+
 @pytest.mark.parametrize("dist", ["ascending", "descending", "ties", "narrow"])
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
 def test_split_crowded_chunks(dsel, orc, dt, dist):
