@@ -853,10 +853,18 @@ __device__ __forceinline__ uint2 list_entry(List ent, uint32_t i) {
 // holds LP*NWAVE words, base LOADS*NWAVE + 1: one wave turns the per-(load,
 // wave) counts into list offsets once, so each load costs a thread one LDS
 // read.
-template <class K, int LOADS, bool CHECKED = false>
+// RAWF (fp32 only): kw holds raw float bits and T1 the bits of a float; the
+// candidates are the elements x >= T1 as floats (-0 == +0; a NaN, the filler
+// of columns past len, never qualifies).
+template <class K, int LOADS, bool CHECKED = false, bool RAWF = false>
 __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4], int len,
                                                        uint32_t T1, uint32_t *wtot,
                                                        uint32_t *base, List ent, uint32_t cap) {
+    static_assert(!RAWF || !K::PACK, "raw float candidates: 32-bit elements");
+    auto qualifies = [](uint32_t key, uint32_t t1) {
+        if constexpr (RAWF) return __uint_as_float(key) >= __uint_as_float(t1);
+        return key >= t1;
+    };
     constexpr int VEC = K::VEC, EPW = K::EPW, LP = (LOADS + 1) / 2, SPAN = NT * VEC;
     const int t = tid();
     const int lane = t & 63, wid = t >> 6;
@@ -872,7 +880,7 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int h = 0; h < EPW; ++h) m += K::elem(kw[4 * j + q], h) >= T1 ? 1u : 0u;
+                for (int h = 0; h < EPW; ++h) m += qualifies(K::elem(kw[4 * j + q], h), T1) ? 1u : 0u;
             pk[j >> 1] |= m << ((j & 1) * 16);
         }
     }
@@ -921,7 +929,7 @@ __device__ __forceinline__ uint32_t compact_candidates(uint32_t (&kw)[LOADS * 4]
 #pragma unroll
                 for (int h = 0; h < EPW; ++h) {
                     const uint32_t key = K::elem(kw[4 * j + q], h);
-                    const bool cand = key >= T1w;
+                    const bool cand = qualifies(key, T1w);
                     list_store<K>(cand ? next : spare, key, p + q * EPW + h);
                     next += cand ? WPE : 0u;
                 }
@@ -1798,11 +1806,16 @@ __device__ __forceinline__ uint32_t wx_sample_len(int len) {
 // The chunks' counts above and at T follow, and each workgroup writes its
 // part of the output from its list as in the bf16 exchange.
 //
-// The exchange holds when every chunk's list and window fit, the windows of
-// the non-empty chunks meet and hold the boundary, and the row's keys in B1
-// fit the gather buffer.  Otherwise (skewed or short chunks, heavy ties) the
-// row runs the multi-pass select; every workgroup reads the same headers,
-// so the choice is uniform over the row.
+// The exchange holds when no chunk holds a NaN, every chunk's list and
+// window fit, the windows of the non-empty chunks meet and hold the
+// boundary, and the row's keys in B1 fit the gather buffer.  Otherwise (NaN
+// rows, skewed or short chunks, heavy ties) the row runs the multi-pass
+// select; every workgroup reads the same headers, so the choice is uniform
+// over the row.  Until the list is made the chunk's values stay raw floats:
+// the list takes every value at or above the float whose key is wlo << 20
+// (float compares order the values as their keys do, with -0 == +0, and
+// only NaN compares unordered, which is why a NaN chunk places no window),
+// and its entries become keys in the pass that counts the window.
 //
 // Area of a workgroup: word 0 = lo | hi << 12 | ok << 24 | empty << 25 |
 // nan << 26 (the window bins [lo, hi]), word 1 = keys above the window,
@@ -1816,6 +1829,25 @@ __device__ __forceinline__ uint32_t wx_sample_len(int len) {
 // workgroup's, so the digit searches also give this workgroup's counts of
 // earlier keys above and at T.
 // ---------------------------------------------------------------------------
+// fp32 key of one value: 0x80000000 + magnitude (positive), 0x80000000 -
+// magnitude (negative), so -0 and +0 meet: (x ^ (s | 0x80000000)) - s with
+// s the sign spread over the word.  A NaN lands above +inf's key
+// (0xFF800000) or below -inf's (0x00800000) and is moved to the top apart.
+__device__ __forceinline__ uint32_t f32_key(uint32_t x) {
+    const uint32_t s = (uint32_t)((int32_t)x >> 31);
+    return (x ^ (s | 0x80000000u)) - s;
+}
+
+// The bits of the smallest float whose key is at least T (T a multiple of
+// 2^20, at most +inf's key): keys from 0x80000000 up are +0 .. +inf, keys
+// below are the negative floats by falling magnitude, and keys at or below
+// -inf's hold only NaNs, so -inf stands for them.
+__device__ __forceinline__ uint32_t f32_floor_bits(uint32_t T) {
+    if (T >= 0x80000000u) return T - 0x80000000u;
+    const uint32_t m = 0x80000000u - T;
+    return m >= 0x7F800000u ? 0xFF800000u : (0x80000000u | m);
+}
+
 struct WxResult {
     bool ok, nan;
     uint32_t T, need, gt0, eq0, run;
@@ -1839,7 +1871,9 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     // ---- this chunk: window, counts, list -----------------------------------
     uint32_t wlo = 0, whi = 0, above = 0, cw0 = 0, cw1 = 0, cw2 = 0, ok = 1, run = 0;
     const bool empty = len <= 0;
-    if (!empty) {
+    if (!empty && blk_nan) {
+        ok = 0;  // a NaN in the chunk: the row takes the multi-pass select
+    } else if (!empty) {
         // q: the chunk's share of k; qs: the same share of the sample
         uint64_t q = ((uint64_t)k * (uint64_t)len + (uint64_t)n - 1) / (uint64_t)n;
         q = q < 1 ? 1 : (q > (uint64_t)len ? (uint64_t)len : q);
@@ -1850,8 +1884,10 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
         DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 8);
         wlo = d.v > 0 ? d.v - 1 : 0;
         whi = d.v < (uint32_t)kWxBins - 1 ? d.v + 1 : d.v;
-        const uint32_t T1 = max(wlo << SH, 1u);
-        run = compact_candidates<K, LOADS, true>(kw, len, T1, L.wtot, L.base, ent, cap);
+        // the list: every value whose key is T1 = max(wlo << SH, 1) or more
+        // (kw and the list hold raw float bits until the pass below)
+        run = compact_candidates<K, LOADS, true, true>(kw, len, f32_floor_bits(max(wlo << SH, 1u)),
+                                                       L.wtot, L.base, ent, cap);
         DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 9);
         if (run > cap) {
             ok = 0;  // uniform
@@ -1866,7 +1902,9 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
             const uint32_t i0 = min(run, (uint32_t)t * E), i1 = min(run, i0 + E);
             uint32_t m01 = 0, m2 = 0;  // bins 0 | 1 << 16, and bin 2
             for (uint32_t i = i0; i < i1; ++i) {
-                const uint32_t w = (list_key<K>(ent, i) >> SH) - wlo;
+                const uint32_t key = f32_key(ent.w[2 * i]);  // the entries' keys from here on
+                ent.w[2 * i] = key;
+                const uint32_t w = (key >> SH) - wlo;
                 m01 += w == 0 ? 1u : (w == 1 && nwin > 1 ? 0x10000u : 0u);
                 m2 += w == 2 && nwin > 2 ? 1u : 0u;
             }
@@ -2449,60 +2487,51 @@ __global__ __launch_bounds__(NT) void topk_rows_split(const TopkArgs a) {
     }
 }
 
-// fp32 key of one value: 0x80000000 + magnitude (positive), 0x80000000 -
-// magnitude (negative), so -0 and +0 meet: (x ^ (s | 0x80000000)) - s with
-// s the sign spread over the word.  A NaN lands above +inf's key
-// (0xFF800000) or below -inf's (0x00800000) and is moved to the top apart.
-__device__ __forceinline__ uint32_t f32_key(uint32_t x) {
-    const uint32_t s = (uint32_t)((int32_t)x >> 31);
-    return (x ^ (s | 0x80000000u)) - s;
-}
 
-// The window exchange's first pass: each 16-byte load turned into four keys
-// as soon as it arrives, and one load in kWxSample histogrammed (12-bit
-// first digit), with a running max / min of the keys as the NaN probe.  Columns at or past len
-// get key 0 (and this lane's spare bin).  If this thread saw a NaN (rare),
-// returns true with the NaN keys NOT yet moved to the top: the caller fixes
-// them and rebuilds the histogram.
+// The window exchange's first pass: each 16-byte load kept as four raw
+// floats as soon as it arrives (columns at or past len get a NaN, which no
+// float compare selects), one load in kWxSample histogrammed by key (12-bit
+// first digit; invalid columns into this lane's spare bin), and each valid
+// pair of values tested for a NaN.  Returns whether this thread saw a NaN.
+constexpr uint32_t kF32Filler = 0x7FFFFFFFu;
+
 template <int LOADS>
-__device__ __forceinline__ bool f32_keys_hist12(const uint4 (&v)[LOADS], int len,
-                                                uint32_t (&kw)[LOADS * 4], uint32_t *hist) {
+__device__ __forceinline__ bool f32_raw_hist12(const uint4 (&v)[LOADS], int len,
+                                               uint32_t (&kw)[LOADS * 4], uint32_t *hist) {
     constexpr int VEC = 4, SPAN = NT * VEC;
     const int me = tid();
     const int full = len / SPAN, any = (len + SPAN - 1) / SPAN;
     const uint32_t spare = (uint32_t)kWxBins + (uint32_t)(me & 63);
-    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+    bool nan = false;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         if (j >= any) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) kw[4 * j + q] = 0u;
+            for (int q = 0; q < 4; ++q) kw[4 * j + q] = kF32Filler;
             continue;
         }
-        uint32_t x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        const uint32_t x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         if (j < full) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) kw[4 * j + q] = f32_key(x[q]);
-            kmax = max(kmax, max(max(kw[4 * j], kw[4 * j + 1]), max(kw[4 * j + 2], kw[4 * j + 3])));
-            kmin = min(kmin, min(min(kw[4 * j], kw[4 * j + 1]), min(kw[4 * j + 2], kw[4 * j + 3])));
+            for (int q = 0; q < 4; ++q) kw[4 * j + q] = x[q];
+            nan |= __builtin_isunordered(__uint_as_float(x[0]), __uint_as_float(x[1]));
+            nan |= __builtin_isunordered(__uint_as_float(x[2]), __uint_as_float(x[3]));
             if (j % kWxSample == 0) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) atomicAdd(&hist[kw[4 * j + q] >> 20], 1u);
+                for (int q = 0; q < 4; ++q) atomicAdd(&hist[f32_key(x[q]) >> 20], 1u);
             }
         } else {
             int valid = len - (j * NT + me) * VEC;
             valid = valid < 0 ? 0 : (valid > VEC ? VEC : valid);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t kk = f32_key(q < valid ? x[q] : 0u);  // raw 0: a harmless key
-                kmax = max(kmax, kk);
-                kmin = min(kmin, kk);
-                kw[4 * j + q] = q < valid ? kk : 0u;
-                if (j % kWxSample == 0) atomicAdd(&hist[q < valid ? (kk >> 20) : spare], 1u);
+                kw[4 * j + q] = q < valid ? x[q] : kF32Filler;
+                nan |= q < valid && __builtin_isnan(__uint_as_float(x[q]));
+                if (j % kWxSample == 0) atomicAdd(&hist[q < valid ? (f32_key(x[q]) >> 20) : spare], 1u);
             }
         }
     }
-    return kmax > 0xFF800000u || kmin < 0x00800000u;
+    return nan;
 }
 
 // ---------------------------------------------------------------------------
@@ -2547,7 +2576,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
     const int64_t lo = (int64_t)c * a.chunk;
     const int64_t hi = min(lo + a.chunk, n);
     const int len = hi > lo ? (int)(hi - lo) : 0;
-    uint32_t kw[LOADS * 4];
+    uint32_t kw[LOADS * 4];  // raw float bits (kF32Filler past the chunk's end)
     uint32_t nan;
     {
         const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, len ? hi : 0);
@@ -2558,23 +2587,12 @@ __global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
         __syncthreads();
         // the 12-bit histogram, filled load by load as the data arrives
         DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 13);
-        nan = f32_keys_hist12<LOADS>(v, len, kw, L.hist) ? 1u : 0u;
+        nan = f32_raw_hist12<LOADS>(v, len, kw, L.hist) ? 1u : 0u;
     }
+    // a chunk with a NaN does not place a window: its row takes the
+    // multi-pass select
     const bool blk_nan = __syncthreads_or((int)nan) != 0;
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 1);
-    if (blk_nan) {
-        // rare: every NaN key to the top, and the histogram again
-        for (int b = t; b < kWxBins + 64; b += NT) L.hist[b] = 0;
-        __syncthreads();
-        const uint32_t spare = (uint32_t)kWxBins + (uint32_t)(t & 63);
-#pragma unroll
-        for (int w = 0; w < LOADS * 4; ++w) {
-            const uint32_t key = K::fix_nan_word(kw[w]);
-            kw[w] = key;
-            if ((w / 4) % kWxSample == 0) atomicAdd(&L.hist[key ? (key >> 20) : spare], 1u);
-        }
-        __syncthreads();
-    }
     const WxResult r = window_exchange<K, LOADS>(a, c, G, len, n, kw, blk_nan, L, ent, cap, area,
                                                  slot, err);
     if (r.ok) {

@@ -221,6 +221,39 @@ def test_split_f32_nan_in_each_load(dsel, orc, G):
     assert_workspaces_clean(dsel)
 
 
+@pytest.mark.parametrize("G", [4, 8])
+def test_split_f32_boundary_among_special_values(dsel, orc, G):
+    """fp32 split rows without NaN whose k-th largest value falls among
+    denormals, signed zeros or infinities (the exchange compares raw floats
+    before it makes keys): -0 and +0 tie, denormals of both signs order by
+    value, -inf and +inf sit at the ends."""
+    rows, cols = 6, 40000
+    g = torch.Generator().manual_seed(141)
+    x = -1.0 - torch.rand(rows, cols, generator=g)  # every value below -1 ...
+    tiny = torch.tensor(1e-45, dtype=torch.float32)  # the smallest denormal
+    mags = torch.randint(1, 1 << 20, (rows, cols), generator=g).float() * tiny
+    sign = torch.where(torch.rand(rows, cols, generator=g) < 0.5, -1.0, 1.0)
+    pick = torch.rand(rows, cols, generator=g)
+    # ... but these: row 0 denormals of both signs; row 1 signed zeros; row 2
+    # zeros and denormals; row 3 +inf and denormals; row 4 mostly -inf; row 5
+    # the largest negative denormal and -0
+    x[0] = torch.where(pick[0] < 0.15, mags[0] * sign[0], x[0])
+    x[1] = torch.where(pick[1] < 0.10, torch.where(sign[1] > 0, 0.0, -0.0), x[1])
+    x[2] = torch.where(pick[2] < 0.05, torch.where(sign[2] > 0, 0.0, -0.0),
+                       torch.where(pick[2] < 0.12, mags[2] * sign[2], x[2]))
+    x[3] = torch.where(pick[3] < 0.02, float("inf"), torch.where(pick[3] < 0.2, mags[3], x[3]))
+    x[4] = torch.where(pick[4] < 0.95, float("-inf"), x[4])
+    x[4, :5] = float("-inf")
+    x[5] = torch.where(pick[5] < 0.04, -tiny, torch.where(pick[5] < 0.08, -0.0, x[5]))
+    assert not torch.isnan(x).any()
+    re = torch.tensor([cols, cols - 3, cols, 31111, cols, cols - 1], dtype=torch.int32)
+    for k, sorted_index, itype, ret in ((4096, True, torch.int64, True), (1000, False, torch.int32, True),
+                                        (3000, True, torch.int32, True)):
+        got = check_case(dsel, orc, f"f32_special_bound/G{G}/k{k}", x, k, re, sorted_index, itype, ret, G)
+        assert not got[2].any()
+    assert_workspaces_clean(dsel)
+
+
 @pytest.mark.parametrize("dist", ["ascending", "descending", "ties", "narrow"])
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
 def test_split_crowded_chunks(dsel, orc, dt, dist):
