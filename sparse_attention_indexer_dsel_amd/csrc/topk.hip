@@ -57,20 +57,20 @@ namespace dsel {
 namespace {
 
 // Phase stamps, compiled only into the instrumented build (DSEL_PHASE_STAMPS,
-// built and read by sparse_attention_indexer_dsel_amd/phase_stamps.py): at
-// a phase boundary one thread waits for its memory operations and records
-// the 100 MHz real-time clock in slot (unit, i) of a device array, where a
-// unit is a row (one-wave rows) or a workgroup.  The product build compiles
-// every stamp to nothing.
+// built and read by sparse_attention_indexer_dsel_amd/phase_stamps.py): when
+// one thread reaches a phase boundary it records the 100 MHz real-time clock
+// in slot (unit, i) of a device array, where a unit is a row (one-wave and
+// whole rows) or a workgroup (split fp32 rows).  The stamp does not wait for
+// the thread's memory operations (a wait would hold back the loads' overlap
+// with the work), so it marks when the boundary's instructions issue; a
+// phase that ends in a workgroup barrier ends when every wave has reached
+// it.  The product build compiles every stamp to nothing.
 #ifdef DSEL_PHASE_STAMPS
 constexpr int kStampUnits = 4096, kStampsPerUnit = 24;
 __device__ unsigned long long g_stamps[kStampUnits * kStampsPerUnit];
 __device__ __forceinline__ void stamp_at(bool who, int64_t unit, int i) {
-    __builtin_amdgcn_s_waitcnt(0);
     const unsigned long long t = __builtin_amdgcn_s_memrealtime();
-    __builtin_amdgcn_s_waitcnt(0);
-    if (who && unit >= 0 && unit < kStampUnits && g_stamps[unit * kStampsPerUnit + i] == 0)
-        g_stamps[unit * kStampsPerUnit + i] = t;
+    if (who && unit >= 0 && unit < kStampUnits) g_stamps[unit * kStampsPerUnit + i] = t;
 }
 __device__ __forceinline__ void stamp_value(bool who, int64_t unit, int i, unsigned long long v) {
     if (who && unit >= 0 && unit < kStampUnits) g_stamps[unit * kStampsPerUnit + i] = v;
@@ -1823,7 +1823,7 @@ __device__ __forceinline__ uint32_t wx_sample_len(int len) {
 // kWxHdr, bin by bin.
 // LDS after the rendezvous (the histogram's space): gathered keys [0, 2048),
 // the local radix histogram [2048, 3072), per-chunk words [3072, 3202) (two
-// arrays of G + 1 <= 65: segment starts, offsets), headers [3584, 3904).
+// arrays of G + 1 <= 65: segment starts, offsets).
 // The local histograms count each key twice in one word: once in the low
 // half, and once in the high half when it comes from a chunk before this
 // workgroup's, so the digit searches also give this workgroup's counts of
@@ -1862,7 +1862,7 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
                                     uint32_t *err) {
     static_assert(!K::PACK, "window exchange: 32-bit keys");
     constexpr int SH = 20;                 // 12-bit first digit
-    constexpr uint32_t GAT = 0, SEL = 2048, CHK = 3072, HDR = 3584;
+    constexpr uint32_t GAT = 0, SEL = 2048, CHK = 3072;
     const int t = tid();
     const int lane = t & 63;
     const uint32_t k = (uint32_t)a.k;
@@ -1943,18 +1943,20 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     row_rendezvous(slot, (uint32_t)G, err, a.spin_limit);
     DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 6);
 
-    // ---- every chunk's header ---------------------------------------------
-    uint32_t *hdr = L.hist + HDR;
-    for (int i = t; i < G * 5; i += NT) hdr[i] = ld_agent(area + (int64_t)(i / 5) * kWxWords + i % 5);
-    __syncthreads();
-    // every wave decides on its own (lane = chunk; no barrier to share it)
+    // ---- every chunk's header: each wave reads them all (lane = chunk) and
+    // decides on its own, so no barrier shares them
     const bool in = lane < G;
-    const uint32_t h0 = in ? hdr[lane * 5] : (1u << 25);
+    uint32_t h0 = 1u << 25, cab = 0, cc0 = 0, cc1 = 0, cc2 = 0;
+    if (in) {
+        const uint32_t *hl = area + (int64_t)lane * kWxWords;
+        h0 = ld_agent(hl);
+        cab = ld_agent(hl + 1);
+        cc0 = ld_agent(hl + 2);
+        cc1 = ld_agent(hl + 3);
+        cc2 = ld_agent(hl + 4);
+    }
     const uint32_t clo = h0 & 0xFFFu, chi = (h0 >> 12) & 0xFFFu;
     const bool cok = (h0 >> 24) & 1u, cempty = (h0 >> 25) & 1u;
-    const uint32_t cab = in ? hdr[lane * 5 + 1] : 0u;
-    const uint32_t cc0 = in ? hdr[lane * 5 + 2] : 0u, cc1 = in ? hdr[lane * 5 + 3] : 0u,
-                   cc2 = in ? hdr[lane * 5 + 4] : 0u;
     const bool live = in && !cempty;
     r.nan = __ballot(in && ((h0 >> 26) & 1u)) != 0ull;
     // a header this call wrote always passes these checks; they keep every
@@ -2727,19 +2729,19 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
     const raw_t *xr = reinterpret_cast<const raw_t *>(a.x) + row * a.x_stride;
     const int len = (int)n;
 
-    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 1);
+    DSEL_STAMP((t == 0), row, 1);
     uint32_t kw[LOADS * 4];
     const uint32_t nan = keys_of_loads<K, LOADS, NT, GATHER>(buf, len, kw);
     for (int b = t; b < kBins + 64; b += NT) L.hist[b] = 0;
     const uint32_t block_nan = __syncthreads_or((int)nan) ? 1u : 0u;
-    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 2);
+    DSEL_STAMP((t == 0), row, 2);
 
     first_digit_histogram<K, LOADS>(kw, len, L.hist);
     __syncthreads();
-    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 3);
+    DSEL_STAMP((t == 0), row, 3);
     const Digit d1 = find_digit(L.hist, kBins, (uint32_t)a.k, L.red, L.out);
     const uint32_t C = d1.above + d1.cnt;
-    DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 4);
+    DSEL_STAMP((t == 0), row, 4);
 
     if (LOADS <= 2 && 4 * (int64_t)C >= n) {
         // a few keys per thread and dense candidates: no list
@@ -2751,11 +2753,11 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
         write_from_regs<K, LOADS>(a, row, kw, len, b, 0u, 0u, row_view<K>(xr, n), 0, L.red, xr);
     } else if (C <= cap) {
         compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, L.base, ent, cap);
-        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 5);
+        DSEL_STAMP((t == 0), row, 5);
         const Bound b = refine_on_list<K>(ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
-        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 6);
+        DSEL_STAMP((t == 0), row, 6);
         write_from_list<K>(a, row, ent, C, b, L.red, xr);
-        DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 7);
+        DSEL_STAMP((t == 0), row, 7);
     } else {
         // the candidates do not fit the list: the passes re-read the row
         const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
@@ -2790,7 +2792,7 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
     for (int64_t t = blockIdx.x; t < R; t += gridDim.x) {
         const int64_t row = a.row0 + taker_row(a.row_order, t, R);
         const int64_t n = valid_length(a, row);
-        DSEL_STAMP((tid() == 0), (int64_t)blockIdx.x, 0);
+        DSEL_STAMP((tid() == 0), row, 0);
         const raw_t *xr = x + row * a.x_stride;
         if (n <= a.k) {
             write_short_row<K>(a, row, n, 0, 1, xr);
@@ -2811,7 +2813,7 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
             gather_tail<NT>(a, row, tid(), [&](uint32_t j) -> int64_t { return s_pos[j]; },
                             reinterpret_cast<uint32_t *>(s_dyn) + a.k);
         }
-        DSEL_STAMP((tid() == 0), (int64_t)blockIdx.x, 8);
+        DSEL_STAMP((tid() == 0), row, 8);
         __syncthreads();  // LDS is reused by the next row
     }
 }

@@ -7,12 +7,14 @@
 ``libdsel_stamps.so`` beside ``libdsel.so``, with ``DSEL_PHASE_STAMPS``
 defined: at each phase boundary of the one-wave rows' kernel (per row), the
 fp32 window-exchange kernel (per workgroup) and the whole-row kernel (per
-workgroup, its first row) one thread waits for its memory operations and
-records the GPU's 100 MHz real-time clock.  ``run`` loads that build, warms
-it up on the workload, clears the stamps, runs one top-k call and prints
-each phase's duration (mean, percentiles, max) in nanoseconds.  The waits
-at every stamp slow the kernel; the phases' proportions, not the total, are
-what the stamps are for.
+row) one thread records the GPU's 100 MHz real-time clock.  A stamp does
+not wait for memory: it marks when the thread's instructions reach the
+boundary (a phase that ends in a workgroup barrier ends when every wave is
+there), so the kernel's loads still overlap its work as in the product
+build, and a phase that starts with loads shows when they were issued, the
+next one when their data was used.  ``run`` loads that build, warms it up
+on the workload, clears the stamps, runs one top-k call and prints each
+phase's duration (mean, percentiles, max) in nanoseconds.
 """
 from __future__ import annotations
 
@@ -123,7 +125,7 @@ def report(kernel: str, cfg: int) -> str:
     elif kernel == "wx":  # per workgroup; 7 = exchange held
         ok = used & (raw[:, 7] == 1)
         lines.append(f"the exchange held in {int(ok.sum())} of {int(used.sum())} workgroups")
-        for name, a, b in (("loads arrived", 0, 13), ("keys, sampled histogram", 13, 1),
+        for name, a, b in (("loads issued, hist zeroed", 0, 13), ("keys, sampled histogram", 13, 1),
                            ("window digit", 1, 8), ("candidate list", 8, 9),
                            ("window counts", 9, 14), ("publish", 14, 2), ("rendezvous wait", 2, 6),
                            ("headers, boundary bin", 6, 10),
@@ -132,10 +134,10 @@ def report(kernel: str, cfg: int) -> str:
                            ("write", 3, 4), ("finish", 4, 5)):
             lines.append(_stats(name, (ns(b) - ns(a))[ok]))
         lines.append(_stats("end", ns(5)[ok]))
-    elif kernel == "whole":  # per workgroup, its first row (list path)
+    elif kernel == "whole":  # per row (list path)
         lst = used & (raw[:, 7] > 0)
-        lines.append(f"workgroups whose first row took the list path: {int(lst.sum())}")
-        for name, a, b in (("loads", 0, 1), ("keys, zero histogram", 1, 2), ("histogram", 2, 3),
+        lines.append(f"rows that took the list path: {int(lst.sum())} of {int(used.sum())}")
+        for name, a, b in (("loads issued", 0, 1), ("keys, zero histogram", 1, 2), ("histogram", 2, 3),
                            ("first digit", 3, 4), ("candidate list", 4, 5), ("later digits", 5, 6),
                            ("write", 6, 7), ("finish", 7, 8), ("total", 0, 8)):
             lines.append(_stats(name, (ns(b) - ns(a))[lst]))
