@@ -554,11 +554,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_view(const typename K::raw
                                              (int)bytes, 0x00020000);
 }
 
-// 16 bytes of raw values at column p of a row view.
-template <class K>
+// 16 bytes of raw values at column p of a row view.  NT: with the
+// non-temporal hint (cache policy bit nt), for the whole-row and split
+// kernels, which read each value once (a streaming read of 66 MB measured
+// 7% faster with it); the slow paths' re-reads of a range and the one-wave
+// kernels (measured slower with it) use the default policy.
+template <class K, bool NT = true>
 __device__ __forceinline__ uint4 load_vec(__amdgpu_buffer_rsrc_t view, int64_t p) {
+    constexpr int kNonTemporal = 2;  // the nt bit of a buffer load's cache policy
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-        view, (unsigned)(p * (int64_t)sizeof(typename K::raw_t)), 0u, 0);
+        view, (unsigned)(p * (int64_t)sizeof(typename K::raw_t)), 0u, NT ? kNonTemporal : 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -1281,7 +1286,7 @@ __device__ __forceinline__ void reload_keys(__amdgpu_buffer_rsrc_t view, int64_t
                                             int j, uint32_t (&w4)[4]) {
     constexpr int VEC = K::VEC, EPW = K::EPW;
     const int p = (j * NT + tid()) * VEC;
-    uint4 x = load_vec<K>(view, base + p);
+    uint4 x = load_vec<K, false>(view, base + p);
     int valid = len - p;
     valid = valid < 0 ? 0 : (valid > VEC ? VEC : valid);
     x.x = K::keep_raw(x.x, valid);
@@ -3083,7 +3088,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wave(const TopkArgs a) {
         {
             const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
 #pragma unroll
-            for (int j = 0; j < LPL; ++j) v[j] = load_vec<K>(view, (int64_t)(j * 64 + lane) * VEC);
+            for (int j = 0; j < LPL; ++j) v[j] = load_vec<K, false>(view, (int64_t)(j * 64 + lane) * VEC);
         }
         wave_sync();  // the previous row's reads of the histogram are done
         for (int i = lane; i < D::HB + 64; i += 64) hist[i] = 0;
@@ -3383,7 +3388,7 @@ __global__ __launch_bounds__(GATHER ? kGatherWaves * 64 : NT) void topk_rows_wav
             const __amdgpu_buffer_rsrc_t view = row_view<K>(xr, n);
 #pragma unroll
             for (int j = 0; j < LPL; ++j)
-                if (j < any) v[j] = load_vec<K>(view, (int64_t)(j * 64 + lane) * 8);
+                if (j < any) v[j] = load_vec<K, false>(view, (int64_t)(j * 64 + lane) * 8);
         }
         wave_sync();  // the previous row's reads of this wave's LDS are done
         {
