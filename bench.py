@@ -28,8 +28,10 @@ Timing protocol
     kernel's mean duration back to back (the roofline figure), comparable
     with rocprofv3's kernel trace;
   * ``floors`` gives the launch floor (a graph of empty-work kernels, per
-    launch) and streaming read, write and copy rates of plain device
-    kernels over 1 GiB, for scale;
+    launch), streaming read, write and copy rates of plain device kernels
+    over 1 GiB, and the library's read floor (``dsel_read_floor``: one
+    launch reading with the select's own loads) over 1 GiB and at the
+    headline input's size, for scale;
   * each workload's top-k and gathers are also timed cold (``cold``): 10
     warm-up calls, then 100 single eager calls, each after 1 GiB is written
     on the call's stream (four times the Infinity Cache), with an event
@@ -503,9 +505,11 @@ def measure_fused(dsel, torch, case, stream, steps, warmup) -> dict:
     return res
 
 
-def measure_floors(torch, stream) -> dict:
+def measure_floors(torch, stream, dsel=None, head_bytes: int = 0) -> dict:
     """Launch floor and plain streaming rates of device kernels over 1 GiB
-    (torch's own kernels: a reduction for read, a fill for write, a copy)."""
+    (torch's own kernels: a reduction for read, a fill for write, a copy),
+    and the library's read floor (dsel_read_floor: the select's own load
+    form) at the headline input size and at 1 GiB."""
     dev = torch.device("cuda")
     tiny = torch.zeros(1, device=dev)
     _, launch = graph_time(torch, stream, lambda i: tiny.add_(1.0), 200, 5, reps=3)
@@ -524,6 +528,24 @@ def measure_floors(torch, stream) -> dict:
            "how": "launch: a graph of 200 one-element adds, event time per launch; "
                   "read 1 GiB (torch.sum), write 1 GiB (fill_), copy 512 MiB -> 512 MiB, "
                   "best of 5 event-timed eager calls"}
+    if dsel is not None:
+        words = torch.empty(-(-(1 << 30) // 65536), dtype=torch.int32, device=dev)
+        t_big = _event_time(torch, stream, lambda: dsel.read_floor(a, out=words, stream=stream))
+        res["read_floor_1gib_gbps"] = (1 << 30) / t_big / 1e9
+        if head_bytes >= 16:
+            hb = head_bytes // 16 * 16
+            ncopy = max(2, -(-(512 << 20) // hb))  # past twice the Infinity Cache
+            copies = [torch.ones(hb // 4, dtype=torch.int32, device=dev) for _ in range(ncopy)]
+            _, t_head = graph_time(torch, stream,
+                                   lambda i: dsel.read_floor(copies[i % ncopy], out=words, stream=stream),
+                                   max(64, ncopy), 5, reps=3)
+            res["read_floor_headline"] = {"bytes": hb, "us": t_head * 1e6, "gbps": hb / t_head / 1e9}
+            del copies
+        res["how_read_floor"] = ("dsel_read_floor: one launch reading the buffer once with the "
+                                 "select's loads (16-byte, non-temporal hint, 16 per thread); 1 GiB "
+                                 "best of 5 eager calls, the headline input's size back to back in a "
+                                 "graph over rotating copies")
+        del words
     del a, b
     torch.cuda.empty_cache()
     return res
@@ -768,7 +790,8 @@ def main(argv=None):
 
     cases = [case if i == cfg_id else W.make_config(i) for i in sorted(W.CONFIGS)]
     if not args.no_floors:
-        line["floors"] = measure_floors(torch, stream)
+        line["floors"] = measure_floors(torch, stream, dsel,
+                                        case.x.numel() * case.x.element_size())
         print(f"# floors: {json.dumps(line['floors'])}", file=sys.stderr, flush=True)
     if not args.no_per_config:
         per = {}

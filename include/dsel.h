@@ -283,6 +283,24 @@ int dsel_topk_gather(const void *x, int dtype, int64_t rows, int64_t cols, int64
                      int64_t rows_per_batch, const DselGatherKey *keys, int n_keys, int pad,
                      void *workspace, size_t *workspace_bytes, void *stream);
 
+/*
+ * dsel_read_floor — a measurement helper, not part of the selection: the
+ * streaming-read floor of the select's input.  One launch reads `bytes`
+ * bytes at x once, with the load form of the whole-row and split top-k
+ * kernels (16-byte loads with the non-temporal hint, sixteen in flight per
+ * thread of 256-thread workgroups, each workgroup a 64 KiB block), and
+ * writes the XOR of the 32-bit words of block b to out[b], so a caller can
+ * check that every byte was read.  Timing it at a workload's input size
+ * gives the read time no top-k kernel of that size can beat on the device.
+ *
+ * x      device memory, 16-byte aligned (else DSEL_ERR_ALIGN).
+ * bytes  a positive multiple of 16 (else DSEL_ERR_ARG).
+ * out    device memory for ceil(bytes / 65536) words (NULL: DSEL_ERR_ARG).
+ * stream the HIP stream (NULL: the default stream).
+ * Returns DSEL_ERR_DEVICE if the launch fails.
+ */
+int dsel_read_floor(const void *x, int64_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["stride_requirement", "topk", "gather_rows", "topk_gather", "check_workspaces",
-           "DselError", "LIB_PATH"]
+           "read_floor", "DselError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsel.so")
 
@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.dsel_gather_rows.restype = i32
     lib.dsel_gather_rows.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i32, i64, i64, i64,
                                      vp, vp]
+    lib.dsel_read_floor.restype = i32
+    lib.dsel_read_floor.argtypes = [vp, i64, vp, vp]
     return lib
 
 
@@ -308,6 +310,27 @@ def gather_rows(key: torch.Tensor, pos: torch.Tensor, *, out: Optional[torch.Ten
             key.stride(0), key.stride(1), pos.data_ptr(), _index_code(pos.dtype), R, P, prs,
             out.data_ptr(), sptr), "dsel_gather_rows")
     return out
+
+
+def read_floor(x: torch.Tensor, *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The streaming-read floor (a measurement helper): one launch reads all
+    of the contiguous GPU tensor x once with the select's load form and
+    returns int32 words, word b the XOR of the 32-bit words of x's b-th
+    64 KiB block.  x's size in bytes must be a multiple of 16."""
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    nbytes = x.numel() * x.element_size()
+    words = -(-nbytes // 65536)
+    with torch.cuda.device(x.device):
+        s = torch.cuda.current_stream(x.device) if stream is None else stream
+        if out is None:
+            with torch.cuda.stream(s):
+                out = torch.empty(max(words, 1), dtype=torch.int32, device=x.device)
+        elif out.dtype != torch.int32 or out.numel() < words or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous int32 tensor of at least {words} words")
+        _check(_lib.dsel_read_floor(x.data_ptr(), nbytes, out.data_ptr(), int(s.cuda_stream)),
+               "dsel_read_floor")
+    return out[:words]
 
 
 class _GatherKey(ctypes.Structure):

@@ -40,7 +40,7 @@ def build(verbose: bool = False) -> str:
     out = os.path.join(bl.BUILD, "stamps")
     os.makedirs(out, exist_ok=True)
     objs = []
-    for name in ("topk", "api", "gather"):
+    for name in ("topk", "api", "gather", "floor"):
         o = os.path.join(out, name + ".o")
         cmd = [bl._hipcc(), *bl.HIPCC_FLAGS, "-DDSEL_PHASE_STAMPS", "-I", os.path.join(ROOT, "include"),
                "-c", os.path.join(bl.CSRC, name + ".hip"), "-o", o]

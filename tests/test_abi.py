@@ -35,8 +35,8 @@ def declared():
 
 
 def test_header_declares_the_calls():
-    assert declared() == ["dsel_gather_rows", "dsel_stride_requirement", "dsel_topk",
-                          "dsel_topk_check", "dsel_topk_ex", "dsel_topk_gather",
+    assert declared() == ["dsel_gather_rows", "dsel_read_floor", "dsel_stride_requirement",
+                          "dsel_topk", "dsel_topk_check", "dsel_topk_ex", "dsel_topk_gather",
                           "dsel_topk_noalloc"]
 
 
@@ -150,6 +150,20 @@ def test_topk_check_host_checks(lib):
     bits.value = 7
     assert f(16, 2, None, ctypes.byref(bits)) == 0 and bits.value == 0
     assert f(20, 1024, None, ctypes.byref(bits)) == -3
+
+
+def test_read_floor_host_checks(lib):
+    """dsel_read_floor refuses NULL pointers, sizes that are not a positive
+    multiple of 16 and a misaligned buffer before it launches anything."""
+    f = lib.dsel_read_floor
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 64, 16, None) == -1
+    assert f(16, 64, None, None) == -1
+    assert f(16, 0, 16, None) == -1
+    assert f(16, -16, 16, None) == -1
+    assert f(16, 40, 16, None) == -1
+    assert f(24, 64, 16, None) == -3
 
 
 class GatherKey(ctypes.Structure):
