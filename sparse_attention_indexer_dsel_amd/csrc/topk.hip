@@ -598,6 +598,13 @@ __device__ __forceinline__ void write_short_values(typename K::raw_t *ov, typena
 
 // The index slots [s0, s1) of a short row (int32 in 16-byte stores) and its
 // NaN flag.
+// 16 bytes of output with the non-temporal hint: the outputs are written
+// once and not read back by the select.
+__device__ __forceinline__ void store16_nt(void *p, uint4 v) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
+}
+
 __device__ __forceinline__ void write_short_idx(const TopkArgs &a, int64_t row, int64_t n, int c,
                                                 int s0, int s1, int me, int nthr) {
     if (!a.idx64 && (s0 & 3) == 0) {
@@ -612,7 +619,7 @@ __device__ __forceinline__ void write_short_idx(const TopkArgs &a, int64_t row, 
             q.y = s + 1 < n ? s + 1 : fill;
             q.z = s + 2 < n ? s + 2 : fill;
             q.w = s + 3 < n ? s + 3 : fill;
-            *reinterpret_cast<int4 *>(o + s) = q;
+            store16_nt(o + s, make_uint4((uint32_t)q.x, (uint32_t)q.y, (uint32_t)q.z, (uint32_t)q.w));
         }
         for (int s = s0 + 4 * nv + me; s < s1; s += nthr) o[s] = s < n ? s : fill;
     } else {
@@ -665,7 +672,7 @@ __device__ __forceinline__ void write_short_row(const TopkArgs &a, int64_t row, 
             q.y = s + 1 < n ? s + 1 : fill;
             q.z = s + 2 < n ? s + 2 : fill;
             q.w = s + 3 < n ? s + 3 : fill;
-            *reinterpret_cast<int4 *>(o + s) = q;
+            store16_nt(o + s, make_uint4((uint32_t)q.x, (uint32_t)q.y, (uint32_t)q.z, (uint32_t)q.w));
         }
         for (int s = s0 + 4 * nv + me; s < s1; s += nthr) o[s] = s < n ? s : fill;
     } else {
@@ -2961,7 +2968,7 @@ __device__ __forceinline__ uint32_t stage_bytes(const TopkArgs &a) {
 __device__ __forceinline__ void wave_copy_out(const char *src, char *dst, uint32_t bytes, int lane) {
     const uint32_t full = bytes & ~15u;
     for (uint32_t off = (uint32_t)lane * 16u; off < full; off += 64u * 16u)
-        *reinterpret_cast<uint4 *>(dst + off) = *reinterpret_cast<const uint4 *>(src + off);
+        store16_nt(dst + off, *reinterpret_cast<const uint4 *>(src + off));
     const uint32_t words = bytes & ~3u;
     const uint32_t w = full + (uint32_t)lane * 4u;
     if (w < words) *reinterpret_cast<uint32_t *>(dst + w) = *reinterpret_cast<const uint32_t *>(src + w);
