@@ -596,8 +596,6 @@ __device__ __forceinline__ void write_short_values(typename K::raw_t *ov, typena
     for (int s = ve + me; s < s1; s += nthr) ov[s] = s < n ? xr[s] : fill;
 }
 
-// The index slots [s0, s1) of a short row (int32 in 16-byte stores) and its
-// NaN flag.
 // 16 bytes of output with the non-temporal hint: the outputs are written
 // once and not read back by the select.
 __device__ __forceinline__ void store16_nt(void *p, uint4 v) {
@@ -605,6 +603,8 @@ __device__ __forceinline__ void store16_nt(void *p, uint4 v) {
     __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
 }
 
+// The index slots [s0, s1) of a short row (int32 in 16-byte stores) and its
+// NaN flag.
 __device__ __forceinline__ void write_short_idx(const TopkArgs &a, int64_t row, int64_t n, int c,
                                                 int s0, int s1, int me, int nthr) {
     if (!a.idx64 && (s0 & 3) == 0) {
