@@ -516,30 +516,46 @@ __device__ __forceinline__ RowOut row_out(const TopkArgs &a, int64_t row) {
     return o;
 }
 
+// 16 bytes of output with the non-temporal hint: the outputs are written
+// once and not read back by the select.
+__device__ __forceinline__ void store16_nt(void *p, uint4 v) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
+}
+
 // Output slot `pos`: its column, and (with values) the value bits.
+// NT: with the non-temporal hint (the whole-row writers: measured faster
+// there; the split rows' writes, a few slots per workgroup, measured slower).
+template <bool NT = false, class T>
+__device__ __forceinline__ void store_out(T *p, T v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+template <bool NT = false>
 __device__ __forceinline__ void store_index(const RowOut &o, uint32_t pos, uint32_t col) {
     if (pos >= o.k) return;  // never write past the row's k slots
     if (o.idx64)
-        reinterpret_cast<int64_t *>(o.idx)[pos] = (int64_t)col;
+        store_out<NT>(reinterpret_cast<int64_t *>(o.idx) + pos, (int64_t)col);
     else
-        reinterpret_cast<int32_t *>(o.idx)[pos] = (int32_t)col;
+        store_out<NT>(reinterpret_cast<int32_t *>(o.idx) + pos, (int32_t)col);
 }
 
-template <class K>
+template <class K, bool NT = false>
 __device__ __forceinline__ void store_value(const RowOut &o, uint32_t pos, uint32_t bits) {
     if (pos >= o.k) return;
-    reinterpret_cast<typename K::raw_t *>(o.val)[pos] = (typename K::raw_t)bits;
+    store_out<NT>(reinterpret_cast<typename K::raw_t *>(o.val) + pos, (typename K::raw_t)bits);
 }
 
 // One selected element: its column at output slot `pos`, and its value,
 // rebuilt from the key (read back from the row only for +-0 and NaN keys,
 // whose bits the key does not determine).
-template <class K>
+template <class K, bool NT = false>
 __device__ __forceinline__ void emit(const RowOut &o, uint32_t pos, uint32_t col, uint32_t key,
                                      const typename K::raw_t *xr) {
-    store_index(o, pos, col);
+    store_index<NT>(o, pos, col);
     if (o.val)
-        store_value<K>(o, pos, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
+        store_value<K, NT>(o, pos, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
 }
 
 // Range-checked view of one row's first `end` columns for raw buffer loads:
@@ -591,16 +607,9 @@ __device__ __forceinline__ void write_short_values(typename K::raw_t *ov, typena
 #pragma unroll
         for (int i = 0; i < VEC; ++i) e[i] = s + i < n ? e[i] : fill;
         __builtin_memcpy(&q, e, 16);
-        *reinterpret_cast<uint4 *>(ov + s) = q;
+        store16_nt(ov + s, q);
     }
     for (int s = ve + me; s < s1; s += nthr) ov[s] = s < n ? xr[s] : fill;
-}
-
-// 16 bytes of output with the non-temporal hint: the outputs are written
-// once and not read back by the select.
-__device__ __forceinline__ void store16_nt(void *p, uint4 v) {
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
 }
 
 // The index slots [s0, s1) of a short row (int32 in 16-byte stores) and its
@@ -1087,13 +1096,13 @@ __device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, 
             const uint32_t pre = e[u].x >> b.s;
             if (e[u].x && pre > b.P) {
                 const uint32_t pos = gb + min(qb, b.need);
-                store_index(o, pos, e[u].y + col0);
-                if (o.val) store_value<K>(o, pos, K::value_bits(e[u].x));
+                store_index<true>(o, pos, e[u].y + col0);
+                if (o.val) store_value<K, true>(o, pos, K::value_bits(e[u].x));
                 ++gb;
             } else if (e[u].x && pre == b.P) {
                 if (qb < b.need) {
-                    store_index(o, gb + qb, e[u].y + col0);
-                    if (o.val) store_value<K>(o, gb + qb, K::value_bits(e[u].x));
+                    store_index<true>(o, gb + qb, e[u].y + col0);
+                    if (o.val) store_value<K, true>(o, gb + qb, K::value_bits(e[u].x));
                 }
                 ++qb;
             }
@@ -1107,11 +1116,11 @@ __device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, 
         const uint32_t pre = e.x >> b.s;
         if (e.x && pre > b.P) {
             if (K::ambiguous(e.x))
-                store_value<K>(o, gb + min(qb, b.need), (uint32_t)xr[e.y + col0]);
+                store_value<K, true>(o, gb + min(qb, b.need), (uint32_t)xr[e.y + col0]);
             ++gb;
         } else if (e.x && pre == b.P) {
             if (qb < b.need && K::ambiguous(e.x))
-                store_value<K>(o, gb + qb, (uint32_t)xr[e.y + col0]);
+                store_value<K, true>(o, gb + qb, (uint32_t)xr[e.y + col0]);
             ++qb;
         }
     }
@@ -1401,10 +1410,10 @@ __device__ __forceinline__ void write_from_stream(const TopkArgs &a, int64_t row
                 const uint32_t pre = key >> b.s;
                 const uint32_t col = p + qq * EPW + h;
                 if (key && pre > b.P) {
-                    emit<K>(o, g1 + min(q1, b.need), col, key, xr);
+                    emit<K, true>(o, g1 + min(q1, b.need), col, key, xr);
                     ++g1;
                 } else if (key && pre == b.P) {
-                    if (q1 < b.need) emit<K>(o, g1 + q1, col, key, xr);
+                    if (q1 < b.need) emit<K, true>(o, g1 + q1, col, key, xr);
                     ++q1;
                 }
             }
@@ -1485,8 +1494,8 @@ __device__ __forceinline__ void write_from_regs(const TopkArgs &a, int64_t row,
                     const bool take = gt || (eq && q1 < b.need);
                     const uint32_t pos = gt ? g1 + min(q1, b.need) : g1 + q1;
                     if (take) {
-                        store_index(o, pos, p + qq * EPW + h);
-                        if (o.val) store_value<K>(o, pos, K::value_bits(key));
+                        store_index<true>(o, pos, p + qq * EPW + h);
+                        if (o.val) store_value<K, true>(o, pos, K::value_bits(key));
                         amb |= K::ambiguous(key) ? 1u : 0u;
                     }
                     g1 += gt ? 1u : 0u;
