@@ -524,38 +524,41 @@ __device__ __forceinline__ void store16_nt(void *p, uint4 v) {
 }
 
 // Output slot `pos`: its column, and (with values) the value bits.
-// NT: with the non-temporal hint (the whole-row writers: measured faster
-// there; the split rows' writes, a few slots per workgroup, measured slower).
-template <bool NT = false, class T>
+// NTS: with the non-temporal hint.  The whole-row kernel's writers take it
+// (measured faster, though its scattered 4-byte stores then leave L2 as
+// partial lines: 2.5x the write bytes); its instance that fuses the gather,
+// whose workers read the positions back at once, and the split rows' writes
+// (a few slots per workgroup, measured slower with it) do not.
+template <bool NTS = false, class T>
 __device__ __forceinline__ void store_out(T *p, T v) {
-    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    if constexpr (NTS) __builtin_nontemporal_store(v, p);
     else *p = v;
 }
 
-template <bool NT = false>
+template <bool NTS = false>
 __device__ __forceinline__ void store_index(const RowOut &o, uint32_t pos, uint32_t col) {
     if (pos >= o.k) return;  // never write past the row's k slots
     if (o.idx64)
-        store_out<NT>(reinterpret_cast<int64_t *>(o.idx) + pos, (int64_t)col);
+        store_out<NTS>(reinterpret_cast<int64_t *>(o.idx) + pos, (int64_t)col);
     else
-        store_out<NT>(reinterpret_cast<int32_t *>(o.idx) + pos, (int32_t)col);
+        store_out<NTS>(reinterpret_cast<int32_t *>(o.idx) + pos, (int32_t)col);
 }
 
-template <class K, bool NT = false>
+template <class K, bool NTS = false>
 __device__ __forceinline__ void store_value(const RowOut &o, uint32_t pos, uint32_t bits) {
     if (pos >= o.k) return;
-    store_out<NT>(reinterpret_cast<typename K::raw_t *>(o.val) + pos, (typename K::raw_t)bits);
+    store_out<NTS>(reinterpret_cast<typename K::raw_t *>(o.val) + pos, (typename K::raw_t)bits);
 }
 
 // One selected element: its column at output slot `pos`, and its value,
 // rebuilt from the key (read back from the row only for +-0 and NaN keys,
 // whose bits the key does not determine).
-template <class K, bool NT = false>
+template <class K, bool NTS = false>
 __device__ __forceinline__ void emit(const RowOut &o, uint32_t pos, uint32_t col, uint32_t key,
                                      const typename K::raw_t *xr) {
-    store_index<NT>(o, pos, col);
+    store_index<NTS>(o, pos, col);
     if (o.val)
-        store_value<K, NT>(o, pos, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
+        store_value<K, NTS>(o, pos, K::ambiguous(key) ? (uint32_t)xr[col] : K::value_bits(key));
 }
 
 // Range-checked view of one row's first `end` columns for raw buffer loads:
@@ -570,16 +573,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_view(const typename K::raw
                                              (int)bytes, 0x00020000);
 }
 
-// 16 bytes of raw values at column p of a row view.  NT: with the
+// 16 bytes of raw values at column p of a row view.  NTL: with the
 // non-temporal hint (cache policy bit nt), for the whole-row and split
 // kernels, which read each value once (a streaming read of 66 MB measured
 // 7% faster with it); the slow paths' re-reads of a range and the one-wave
 // kernels (measured slower with it) use the default policy.
-template <class K, bool NT = true>
+template <class K, bool NTL = true>
 __device__ __forceinline__ uint4 load_vec(__amdgpu_buffer_rsrc_t view, int64_t p) {
     constexpr int kNonTemporal = 2;  // the nt bit of a buffer load's cache policy
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-        view, (unsigned)(p * (int64_t)sizeof(typename K::raw_t)), 0u, NT ? kNonTemporal : 0);
+        view, (unsigned)(p * (int64_t)sizeof(typename K::raw_t)), 0u, NTL ? kNonTemporal : 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -1052,7 +1055,7 @@ __device__ uint32_t list_counts(List ent, uint32_t C, Bound b, uint32_t *s_red) 
 // keys, so the write loop issues no loads (a load there would make every
 // store wait for the ones before it); the rare +-0 / NaN keys get their bits
 // from the row in a third pass, run only when some thread holds one.
-template <class K>
+template <class K, bool NTS = false>
 __device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, List ent,
                                                 uint32_t C, Bound b, uint32_t *s_red,
                                                 const typename K::raw_t *xr, uint32_t gt0 = 0,
@@ -1096,13 +1099,13 @@ __device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, 
             const uint32_t pre = e[u].x >> b.s;
             if (e[u].x && pre > b.P) {
                 const uint32_t pos = gb + min(qb, b.need);
-                store_index<true>(o, pos, e[u].y + col0);
-                if (o.val) store_value<K, true>(o, pos, K::value_bits(e[u].x));
+                store_index<NTS>(o, pos, e[u].y + col0);
+                if (o.val) store_value<K, NTS>(o, pos, K::value_bits(e[u].x));
                 ++gb;
             } else if (e[u].x && pre == b.P) {
                 if (qb < b.need) {
-                    store_index<true>(o, gb + qb, e[u].y + col0);
-                    if (o.val) store_value<K, true>(o, gb + qb, K::value_bits(e[u].x));
+                    store_index<NTS>(o, gb + qb, e[u].y + col0);
+                    if (o.val) store_value<K, NTS>(o, gb + qb, K::value_bits(e[u].x));
                 }
                 ++qb;
             }
@@ -1116,11 +1119,11 @@ __device__ __forceinline__ void write_from_list(const TopkArgs &a, int64_t row, 
         const uint32_t pre = e.x >> b.s;
         if (e.x && pre > b.P) {
             if (K::ambiguous(e.x))
-                store_value<K, true>(o, gb + min(qb, b.need), (uint32_t)xr[e.y + col0]);
+                store_value<K, NTS>(o, gb + min(qb, b.need), (uint32_t)xr[e.y + col0]);
             ++gb;
         } else if (e.x && pre == b.P) {
             if (qb < b.need && K::ambiguous(e.x))
-                store_value<K, true>(o, gb + qb, (uint32_t)xr[e.y + col0]);
+                store_value<K, NTS>(o, gb + qb, (uint32_t)xr[e.y + col0]);
             ++qb;
         }
     }
@@ -1384,7 +1387,7 @@ __device__ uint32_t range_counts(__amdgpu_buffer_rsrc_t view, int64_t base, int 
 // Write the selection of the range (columns base + ...).  gt0 / eq0 are the
 // taken-above and equal counts of the columns before the range; each load is
 // one workgroup scan.
-template <class K>
+template <class K, bool NTS = false>
 __device__ __forceinline__ void write_from_stream(const TopkArgs &a, int64_t row,
                                                   __amdgpu_buffer_rsrc_t view, int64_t base,
                                                   int len, Bound b, uint32_t gt0, uint32_t eq0,
@@ -1410,10 +1413,10 @@ __device__ __forceinline__ void write_from_stream(const TopkArgs &a, int64_t row
                 const uint32_t pre = key >> b.s;
                 const uint32_t col = p + qq * EPW + h;
                 if (key && pre > b.P) {
-                    emit<K, true>(o, g1 + min(q1, b.need), col, key, xr);
+                    emit<K, NTS>(o, g1 + min(q1, b.need), col, key, xr);
                     ++g1;
                 } else if (key && pre == b.P) {
-                    if (q1 < b.need) emit<K, true>(o, g1 + q1, col, key, xr);
+                    if (q1 < b.need) emit<K, NTS>(o, g1 + q1, col, key, xr);
                     ++q1;
                 }
             }
@@ -1465,7 +1468,7 @@ __device__ __forceinline__ uint32_t counts_regs(const uint32_t (&kw)[LOADS * 4],
 // load there would make every store wait for the ones before it); if a +-0
 // or NaN key was taken, whose bits the key does not determine, the range is
 // written again from the row.
-template <class K, int LOADS>
+template <class K, int LOADS, bool NTS = false>
 __device__ __forceinline__ void write_from_regs(const TopkArgs &a, int64_t row,
                                                 const uint32_t (&kw)[LOADS * 4], int len, Bound b,
                                                 uint32_t gt0, uint32_t eq0,
@@ -1494,8 +1497,8 @@ __device__ __forceinline__ void write_from_regs(const TopkArgs &a, int64_t row,
                     const bool take = gt || (eq && q1 < b.need);
                     const uint32_t pos = gt ? g1 + min(q1, b.need) : g1 + q1;
                     if (take) {
-                        store_index<true>(o, pos, p + qq * EPW + h);
-                        if (o.val) store_value<K, true>(o, pos, K::value_bits(key));
+                        store_index<NTS>(o, pos, p + qq * EPW + h);
+                        if (o.val) store_value<K, NTS>(o, pos, K::value_bits(key));
                         amb |= K::ambiguous(key) ? 1u : 0u;
                     }
                     g1 += gt ? 1u : 0u;
@@ -1506,7 +1509,7 @@ __device__ __forceinline__ void write_from_regs(const TopkArgs &a, int64_t row,
         }
     }
     if (o.val && __syncthreads_or((int)amb))
-        write_from_stream<K>(a, row, view, base, len, b, gt0, eq0, s_red, xr);
+        write_from_stream<K, NTS>(a, row, view, base, len, b, gt0, eq0, s_red, xr);
 }
 
 __device__ __forceinline__ int64_t valid_length(const TopkArgs &a, int64_t row) {
@@ -2771,13 +2774,13 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
                                              refine_histogram_regs<K, LOADS>(kw, P, s, sh, dmask,
                                                                              L.hist);
                                          });
-        write_from_regs<K, LOADS>(a, row, kw, len, b, 0u, 0u, row_view<K>(xr, n), 0, L.red, xr);
+        write_from_regs<K, LOADS, !GATHER>(a, row, kw, len, b, 0u, 0u, row_view<K>(xr, n), 0, L.red, xr);
     } else if (C <= cap) {
         compact_candidates<K, LOADS>(kw, len, d1.v << K::SH1, L.wtot, L.base, ent, cap);
         DSEL_STAMP((t == 0), row, 5);
         const Bound b = refine_on_list<K>(ent, C, d1, (uint32_t)a.k, L.hist, L.red, L.out);
         DSEL_STAMP((t == 0), row, 6);
-        write_from_list<K>(a, row, ent, C, b, L.red, xr);
+        write_from_list<K, !GATHER>(a, row, ent, C, b, L.red, xr);
         DSEL_STAMP((t == 0), row, 7);
     } else {
         // the candidates do not fit the list: the passes re-read the row
@@ -2787,7 +2790,7 @@ __device__ __forceinline__ void select_row(const TopkArgs &a, int64_t row, int64
                                              refine_histogram_stream<K>(view, 0, len, P, s, sh,
                                                                         dmask, L.hist);
                                          });
-        write_from_stream<K>(a, row, view, 0, len, b, 0u, 0u, L.red, xr);
+        write_from_stream<K, !GATHER>(a, row, view, 0, len, b, 0u, 0u, L.red, xr);
     }
     if (t == 0 && a.nan_flag) a.nan_flag[row] = (uint8_t)block_nan;
 }
