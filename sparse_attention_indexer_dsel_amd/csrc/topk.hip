@@ -2827,7 +2827,10 @@ __global__ __launch_bounds__(NT) void topk_rows_whole(const TopkArgs a) {
         }
         if constexpr (GATHER) {
             // the row's positions, as this workgroup wrote them, into LDS
-            // (the select's space is free; it holds at least k words)
+            // (the select's space is free; it holds at least k words); each
+            // thread's stores are acknowledged before the barrier, so the
+            // reads after it see them
+            drain_memory();
             __syncthreads();
             int32_t *s_pos = reinterpret_cast<int32_t *>(s_dyn);
             const uint32_t *ib = reinterpret_cast<const uint32_t *>(a.out_idx) +
@@ -3665,8 +3668,10 @@ __global__ __launch_bounds__(GATHER ? kGatherWaves * 64 : NT) void topk_rows_wav
         }
       } while (false);
       if constexpr (GATHER) {
-          // every wave's row selected and its index row written: the
+          // every wave's row selected and its index row written (and the
+          // stores acknowledged, for the rows read back from memory): the
           // workgroup copies their keys, row by row
+          drain_memory();
           __syncthreads();
 #pragma unroll 1
           for (int w = 0; w < NW; ++w) {
