@@ -62,6 +62,7 @@ constexpr int kOneMaxEpt = 64;
 constexpr int kWxBins = 4096;              // first digit: key >> 20
 constexpr int kWxHdr = 16;                 // header words
 constexpr int kWxKeys = 1024;              // window keys one workgroup may publish
+constexpr int kWxBinCap = kWxKeys / 3;     // ... of each of the window's three bins
 constexpr int kWxWords = kWxHdr + kWxKeys;
 constexpr int kWxGather = 2048;            // boundary-bin keys of a row a workgroup may gather
 

@@ -1831,7 +1831,7 @@ __device__ __forceinline__ uint32_t wx_sample_len(int len) {
 // part of the output from its list as in the bf16 exchange.
 //
 // The exchange holds when no chunk holds a NaN, every chunk's list and
-// window fit, the windows of the non-empty chunks meet and hold the
+// window bins fit, the windows of the non-empty chunks meet and hold the
 // boundary, and the row's keys in B1 fit the gather buffer.  Otherwise (NaN
 // rows, skewed or short chunks, heavy ties) the row runs the multi-pass
 // select; every workgroup reads the same headers, so the choice is uniform
@@ -1844,7 +1844,8 @@ __device__ __forceinline__ uint32_t wx_sample_len(int len) {
 // Area of a workgroup: word 0 = lo | hi << 12 | ok << 24 | empty << 25 |
 // nan << 26 (the window bins [lo, hi]), word 1 = keys above the window,
 // words 2..4 = keys in bins lo, lo+1, lo+2, then the window keys from word
-// kWxHdr, bin by bin.
+// kWxHdr, bin lo + w at kWxHdr + w kWxBinCap (at most kWxBinCap keys a bin,
+// in no particular order).
 // LDS after the rendezvous (the histogram's space): gathered keys [0, 2048),
 // the local radix histogram [2048, 3072), per-chunk words [3072, 3202) (two
 // arrays of G + 1 <= 65: segment starts, offsets).
@@ -1917,41 +1918,31 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
             ok = 0;  // uniform
         } else {
             // one pass over the list (it holds every key of bin wlo and up:
-            // the rest lie above the window): thread t owns entries
-            // [t E, t E + E) and counts its keys of each window bin; one
-            // scan gives the window's counts and each thread's offsets in
-            // the published keys, grouped by bin
+            // the rest lie above the window): each entry becomes its key,
+            // and a window key takes the next slot of its bin (an LDS
+            // counter; the order within a bin does not matter) and is
+            // published there at once, bin w of the area at w kWxBinCap
             const uint32_t nwin = whi - wlo + 1u;
             const uint32_t E = (run + NT - 1) / NT;
             const uint32_t i0 = min(run, (uint32_t)t * E), i1 = min(run, i0 + E);
-            uint32_t m01 = 0, m2 = 0;  // bins 0 | 1 << 16, and bin 2
+            uint32_t *dst = area + (int64_t)c * kWxWords + kWxHdr;
             for (uint32_t i = i0; i < i1; ++i) {
                 const uint32_t key = f32_key(ent.w[2 * i]);  // the entries' keys from here on
                 ent.w[2 * i] = key;
                 const uint32_t w = (key >> SH) - wlo;
-                m01 += w == 0 ? 1u : (w == 1 && nwin > 1 ? 0x10000u : 0u);
-                m2 += w == 2 && nwin > 2 ? 1u : 0u;
-            }
-            const Scan2 sc = block_scan2(m01, m2, L.base);
-            cw0 = sc.total0 & 0xFFFFu;
-            cw1 = sc.total0 >> 16;
-            cw2 = sc.total1;
-            above = run - cw0 - cw1 - cw2;
-            ok = (cw0 + cw1 + cw2 < (uint32_t)kWxKeys) ? 1u : 0u;  // each count then fits 10 bits
-            DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 14);
-            if (ok) {  // uniform
-                const uint32_t ex01 = sc.incl0 - m01;
-                uint32_t o0 = ex01 & 0xFFFFu, o1 = cw0 + (ex01 >> 16), o2 = cw0 + cw1 + (sc.incl1 - m2);
-                uint32_t *dst = area + (int64_t)c * kWxWords + kWxHdr;
-                for (uint32_t i = i0; i < i1; ++i) {
-                    const uint32_t key = list_key<K>(ent, i);
-                    const uint32_t w = (key >> SH) - wlo;
-                    if (w >= nwin) continue;
-                    if (w == 0) st_agent(dst + o0++, key);
-                    else if (w == 1) st_agent(dst + o1++, key);
-                    else st_agent(dst + o2++, key);
+                if (w < nwin) {
+                    const uint32_t slot = atomicAdd(&L.out[4 + w], 1u);
+                    if (slot < (uint32_t)kWxBinCap) st_agent(dst + w * (uint32_t)kWxBinCap + slot, key);
                 }
             }
+            __syncthreads();
+            cw0 = L.out[4];
+            cw1 = L.out[5];
+            cw2 = L.out[6];
+            above = run - cw0 - cw1 - cw2;
+            ok = (cw0 <= (uint32_t)kWxBinCap && cw1 <= (uint32_t)kWxBinCap && cw2 <= (uint32_t)kWxBinCap)
+                     ? 1u : 0u;
+            DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 14);
         }
     }
     uint32_t *mine = area + (int64_t)c * kWxWords;
@@ -1985,9 +1976,8 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     r.nan = __ballot(in && ((h0 >> 26) & 1u)) != 0ull;
     // a header this call wrote always passes these checks; they keep every
     // read below inside its area should a rendezvous have given up
-    const bool sane = clo <= chi && chi - clo <= 2u && cc0 < (uint32_t)kWxKeys &&
-                      cc1 < (uint32_t)kWxKeys && cc2 < (uint32_t)kWxKeys &&
-                      cc0 + cc1 + cc2 < (uint32_t)kWxKeys;
+    const bool sane = clo <= chi && chi - clo <= 2u && cc0 <= (uint32_t)kWxBinCap &&
+                      cc1 <= (uint32_t)kWxBinCap && cc2 <= (uint32_t)kWxBinCap;
     const bool all_ok = __ballot(live && !(cok && sane)) == 0ull;
     const bool any_live = __ballot(live) != 0ull;
     const uint32_t maxlo = wave_max_u32(live ? clo : 0u);
@@ -2018,7 +2008,7 @@ __device__ __forceinline__ WxResult window_exchange(const TopkArgs &a, int c, in
     if (good) {
         const uint32_t w1 = B1 - clo;  // bin B1 in this lane's window (live lanes)
         const uint32_t mc = !live ? 0u : (w1 == 0 ? cc0 : (w1 == 1 ? cc1 : cc2));
-        const uint32_t boff = w1 == 0 ? 0u : (w1 == 1 ? cc0 : cc0 + cc1);
+        const uint32_t boff = w1 * (uint32_t)kWxBinCap;
         const uint32_t incl = wave_incl_scan(mc);
         M = rdlane(incl, 63);
         good = M <= (uint32_t)kWxGather;
@@ -2610,6 +2600,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wx(const TopkArgs a) {
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) v[j] = load_vec<K>(view, lo + (int64_t)(j * NT + t) * VEC);
         for (int b = t; b < kWxBins + 64; b += NT) L.hist[b] = 0;
+        if (t < 3) L.out[4 + t] = 0;  // the window bins' publish counters
         __syncthreads();
         // the 12-bit histogram, filled load by load as the data arrives
         DSEL_STAMP((t == 0), (int64_t)blockIdx.x, 13);
