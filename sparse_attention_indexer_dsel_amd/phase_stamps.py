@@ -127,7 +127,7 @@ def report(kernel: str, cfg: int) -> str:
         lines.append(f"the exchange held in {int(ok.sum())} of {int(used.sum())} workgroups")
         for name, a, b in (("loads issued, hist zeroed", 0, 13), ("keys, sampled histogram", 13, 1),
                            ("window digit", 1, 8), ("candidate list", 8, 9),
-                           ("window counts", 9, 14), ("publish", 14, 2), ("rendezvous wait", 2, 6),
+                           ("window keys published", 9, 14), ("header", 14, 2), ("rendezvous wait", 2, 6),
                            ("headers, boundary bin", 6, 10),
                            ("gather keys, 1st digit", 10, 11),
                            ("select, earlier counts", 11, 3),
