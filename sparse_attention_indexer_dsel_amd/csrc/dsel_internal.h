@@ -55,7 +55,8 @@ constexpr int kOneMaxEpt = 64;
 // Window exchange of split fp32 rows (at most kOneMaxSplit workgroups per
 // row, one rendezvous): each workgroup's area in the same exchange region
 // holds a header and the keys of a three-bin window of a 12-bit first digit
-// around its estimate of the row's boundary bin, grouped by bin.  Like the
+// around its estimate of the row's boundary bin, each bin at a fixed place
+// (kWxBinCap keys a bin).  Like the
 // bf16 areas it is never cleared: a reader uses only words the header says
 // this call wrote.  A launch uses it only when its workgroups' areas fit the
 // region.

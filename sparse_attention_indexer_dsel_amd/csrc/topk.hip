@@ -1819,8 +1819,8 @@ __device__ __forceinline__ uint32_t wx_sample_len(int len) {
 // own keys: the bin b_c of its q_c-th largest key, q_c = ceil(k len_c / n),
 // the row's selected share of its own keys.  It lists its keys from bin
 // b_c - 1 up (column order, LDS), publishes the keys of the window
-// [b_c - 1, b_c + 1] grouped by bin, their counts, and its count above the
-// window.  After one rendezvous every workgroup reads the G headers.  For a
+// [b_c - 1, b_c + 1], each bin at a fixed place of its area, their counts,
+// and its count above the window.  After one rendezvous every workgroup reads the G headers.  For a
 // bin B inside every non-empty chunk's window the row's count of keys at or
 // above B is known exactly (above-window counts plus window counts from B
 // up), so the boundary bin B1 (the highest bin whose count reaches k) is
