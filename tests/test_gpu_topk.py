@@ -222,6 +222,30 @@ def test_split_f32_nan_in_each_load(dsel, orc, G):
 
 
 @pytest.mark.parametrize("G", [4, 8])
+def test_split_f32_window_bin_capacity(dsel, orc, G):
+    """fp32 split rows whose boundary bin holds exactly as many keys as one
+    window bin of a workgroup's exchange area takes (341), and one more, in
+    one chunk: the first row goes through the window exchange, the second
+    overflows the bin and takes the multi-pass select; both exact."""
+    rows, cols = 4, 40000
+    g = torch.Generator().manual_seed(151)
+    x = -20.0 - torch.rand(rows, cols, generator=g)  # far below the boundary bin
+    chunk = cols // G
+    k0 = 200
+    for r, m in enumerate((341, 342, 340, 700)):
+        # values in [1.5, 1.625), one 12-bit key bin: m of them in chunk 1,
+        # three times each chunk's share of k in every other chunk (so that
+        # every chunk's window holds the bin)
+        for c in range(G):
+            cnt = m if c == 1 else 3 * (k0 // G)
+            x[r, c * chunk + torch.randperm(chunk, generator=g)[:cnt]] = \
+                1.5 + 0.12 * torch.rand(cnt, generator=g)
+    for k in (k0, 150):
+        check_case(dsel, orc, f"f32_bin_cap/G{G}/k{k}", x, k, None, True, torch.int64, True, G)
+    assert_workspaces_clean(dsel)
+
+
+@pytest.mark.parametrize("G", [4, 8])
 def test_split_f32_boundary_among_special_values(dsel, orc, G):
     """fp32 split rows without NaN whose k-th largest value falls among
     denormals, signed zeros or infinities (the exchange compares raw floats
